@@ -1,0 +1,414 @@
+// W4A16 INT4 MoE expert path -- plain CPU oracle.
+//
+// TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+// call this file; only the tests, the smoke check and the benchmark's CPU
+// baseline leg use it.  It shares no code, header, table or helper with the
+// HIP library: it is written from the definition of the computation, slowly
+// and obviously, so that it can be checked by eye against the source page.
+//
+// Source page (cited below as "Chord page"): "vLLM x Novita AI: Chord W4A16
+// INT4 MoE kernels for Kimi K2.x" (novita.ai blog).  Section names are given
+// in English translation.
+//
+// What is computed (the dense MoE expert FFN on dequantised INT4 weights):
+//   weights  : unsigned 4-bit codes q[e][n][c] with one bf16 scale per group
+//              of 32 along K, s[e][n][c/32]  (Chord page, "Grouped SM90
+//              kernels", operator entry-point listing: weight [G,N,K] uint4,
+//              scale [G,N,K/32] bf16; TL;DR: BF16 activations, INT4 weights,
+//              group-32 scales)
+//   dequant  : w = (q - 8) * s, i.e. subtract the offset, then scale
+//              (Chord page, "H200 and Blackwell indexed decode": the dequant
+//              subtracts and then scales).  Exact in fp32: a 4-bit integer
+//              times an 8-bit-significand bf16 needs at most 12 bits.
+//   gate/up  : Y13[f,n] = bf16( sum_c X[t,c] * w13[e,n,c] ), fp32 accumulate
+//   act      : Z[f,j]   = bf16( silu(Y13[f,j]) * Y13[f,I+j] )
+//   down     : Y2[f,h]  = bf16( sum_c Z[f,c] * w2[e,h,c] ), fp32 accumulate
+//   combine  : out[t,h] = bf16( sum_j w[t,j] * Y2[row(t,j),h] ), fp32
+//   routing  : indexed sorted_ids / expert_ids / num_tokens_padded ("Two
+//              kernel families", "vLLM integration") and the grouped masked
+//              layout with per-expert valid counts ("Grouped SM90 kernels").
+//
+// Readings where the page is silent (each listed with its reason in the
+// design notes): low nibble of a 32-bit word = lowest K index; code 8 is
+// zero; gate = first I rows of W13, up = last I rows; fp32 accumulation in
+// ascending K order (the page rules out f16 accumulation, "vLLM
+// integration"); bf16 rounding is round-to-nearest-even; the combine weight
+// is applied to the bf16-rounded down output.
+//
+// Build: g++ -O2 -std=c++17 -fopenmp -ffp-contract=off -shared -fPIC
+// (-ffp-contract=off keeps every multiply and add a separate rounding step.)
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+namespace {
+
+// ---- bf16 <-> binary32/64 (round to nearest, ties to even) ----------------
+
+float bf16_to_float(uint16_t b) {
+    uint32_t u = static_cast<uint32_t>(b) << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+
+// Round a double to the nearest bf16 (ties to even) with one rounding step.
+// bf16 has 8 significant bits, exponent range as binary32; below 2^-126 the
+// quantum is fixed at 2^-133 (subnormals).
+uint16_t bf16_from_double(double d) {
+    if (std::isnan(d)) return 0x7FC0;
+    uint16_t sign = std::signbit(d) ? 0x8000 : 0;
+    double a = std::fabs(d);
+    if (std::isinf(a)) return sign | 0x7F80;
+    if (a == 0.0) return sign;
+    int e;
+    std::frexp(a, &e);                       // a = m * 2^e, m in [0.5, 1)
+    int qexp = (e - 1 >= -126) ? (e - 8) : -133;   // exponent of one ulp
+    double q = std::ldexp(1.0, qexp);
+    double r = std::nearbyint(a / q) * q;    // default mode: ties to even
+    if (r >= std::ldexp(1.0, 128)) return sign | 0x7F80;   // overflow -> inf
+    float rf = static_cast<float>(r);        // exact: r has <= 8 significant bits
+    uint32_t u;
+    std::memcpy(&u, &rf, 4);
+    return sign | static_cast<uint16_t>(u >> 16);
+}
+
+uint16_t bf16_from_float(float f) { return bf16_from_double(static_cast<double>(f)); }
+
+// ---- weight format ---------------------------------------------------------
+
+// Code c of a row of K codes, stored eight per 32-bit word along K.
+inline uint32_t code_at(const uint32_t* row_words, int64_t c) {
+    return (row_words[c / 8] >> (4 * (c % 8))) & 0xFu;
+}
+
+// Dequantised weight w[c] of one output row: (q - 8) * s, exact in fp32.
+// wmode 1 rounds it to bf16 (the round-after-scale order a bf16 tensor-core
+// operand requires).
+inline float weight_at(const uint32_t* row_words, const uint16_t* row_scales,
+                       int64_t c, int wmode) {
+    float q = static_cast<float>(static_cast<int>(code_at(row_words, c)) - 8);
+    float w = q * bf16_to_float(row_scales[c / 32]);
+    if (wmode == 1) w = bf16_to_float(bf16_from_float(w));
+    return w;
+}
+
+// Local expert of routed slot f, or -1 (non-local or out of range).
+inline int local_expert(const int32_t* topk_ids, int64_t f, int E_global,
+                        const int32_t* expert_map, int E_local) {
+    int g = topk_ids[f];
+    if (g < 0 || g >= E_global) return -1;
+    int e = expert_map ? expert_map[g] : g;
+    if (e < 0 || e >= E_local) return -1;
+    return e;
+}
+
+// One output element: sum over c ascending of a[c] * w[c] in fp32 (acc = 0),
+// or in fp64 when acc64 is set (used only to measure the fp32 error).
+inline double dot_row(const uint16_t* a, const uint32_t* row_words,
+                      const uint16_t* row_scales, int64_t K, int wmode, int acc64) {
+    if (acc64) {
+        double acc = 0.0;
+        for (int64_t c = 0; c < K; ++c)
+            acc += static_cast<double>(bf16_to_float(a[c])) *
+                   static_cast<double>(weight_at(row_words, row_scales, c, wmode));
+        return acc;
+    }
+    float acc = 0.0f;
+    for (int64_t c = 0; c < K; ++c)
+        acc += bf16_to_float(a[c]) * weight_at(row_words, row_scales, c, wmode);
+    return static_cast<double>(acc);
+}
+
+}  // namespace
+
+extern "C" {
+
+int oracle_version(void) { return 1; }
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+// ---- element helpers exposed for the pins ---------------------------------
+
+void oracle_bf16_from_f64(const double* x, int64_t n, uint16_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = bf16_from_double(x[i]);
+}
+
+// Unpack codes [rows, K/8] words -> [rows, K] bytes in 0..15.
+void oracle_unpack_codes(const uint32_t* words, int64_t rows, int64_t K, uint8_t* q) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < K; ++c)
+            q[r * K + c] = static_cast<uint8_t>(code_at(words + r * (K / 8), c));
+}
+
+// Inverse of the above: [rows, K] codes (low 4 bits used) -> [rows, K/8] words.
+void oracle_pack_codes(const uint8_t* q, int64_t rows, int64_t K, uint32_t* words) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t wi = 0; wi < K / 8; ++wi) {
+            uint32_t w = 0;
+            for (int i = 0; i < 8; ++i)
+                w |= (static_cast<uint32_t>(q[r * K + wi * 8 + i]) & 0xFu) << (4 * i);
+            words[r * (K / 8) + wi] = w;
+        }
+}
+
+// Dequantised matrix [rows, K] as fp32 (wmode 0 exact, 1 bf16-rounded).
+void oracle_dequant(const uint32_t* words, const uint16_t* scales, int64_t rows,
+                    int64_t K, int wmode, float* w) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < K; ++c)
+            w[r * K + c] = weight_at(words + r * (K / 8), scales + r * (K / 32), c, wmode);
+}
+
+// ---- O3: routing metadata, indexed layout ---------------------------------
+//
+// Chord page, "Two kernel families" and "vLLM integration": the indexed path
+// consumes vLLM's sorted_ids / expert_ids / num_tokens_padded, produced into
+// over-allocated buffers; Figure 3: activations are not padded, the routing
+// indices carry the padding sentinels.  The plain stable counting sort:
+//   for each local expert e (ascending), the slots routed to it in ascending
+//   flat order f = t*k + j, then sentinels (T*k) up to a multiple of block_m;
+//   expert_ids holds e for every block_m block of that segment; experts with
+//   no slot get no block; num_tokens_padded is the padded total; the buffers'
+//   tails hold the sentinel and -1; row_of[f] is the position of slot f in
+//   sorted_ids (or -1 when f is not local).
+// Returns 0, or 1 when the capacities are too small (outputs then undefined).
+int oracle_moe_align(const int32_t* topk_ids, int T, int top_k, int E_global,
+                     const int32_t* expert_map, int E_local, int block_m,
+                     int32_t* sorted_ids, int sorted_cap, int32_t* expert_ids,
+                     int blocks_cap, int32_t* num_tokens_padded, int32_t* row_of) {
+    const int64_t slots = static_cast<int64_t>(T) * top_k;
+    const int32_t sentinel = static_cast<int32_t>(slots);
+    std::vector<std::vector<int32_t>> lists(E_local);
+    for (int64_t f = 0; f < slots; ++f) {
+        int e = local_expert(topk_ids, f, E_global, expert_map, E_local);
+        if (e >= 0) lists[e].push_back(static_cast<int32_t>(f));
+    }
+    int64_t total = 0;
+    for (int e = 0; e < E_local; ++e) {
+        int64_t c = static_cast<int64_t>(lists[e].size());
+        total += (c + block_m - 1) / block_m * block_m;
+    }
+    if (total > sorted_cap || total / block_m > blocks_cap) return 1;
+    if (row_of)
+        for (int64_t f = 0; f < slots; ++f) row_of[f] = -1;
+    int64_t off = 0;
+    for (int e = 0; e < E_local; ++e) {
+        int64_t c = static_cast<int64_t>(lists[e].size());
+        int64_t p = (c + block_m - 1) / block_m * block_m;
+        for (int64_t j = 0; j < p; ++j) {
+            int32_t v = j < c ? lists[e][j] : sentinel;
+            sorted_ids[off + j] = v;
+            if (j < c && row_of) row_of[v] = static_cast<int32_t>(off + j);
+        }
+        for (int64_t b = 0; b < p / block_m; ++b) expert_ids[off / block_m + b] = e;
+        off += p;
+    }
+    for (int64_t i = off; i < sorted_cap; ++i) sorted_ids[i] = sentinel;
+    for (int64_t b = off / block_m; b < blocks_cap; ++b) expert_ids[b] = -1;
+    num_tokens_padded[0] = static_cast<int32_t>(off);
+    return 0;
+}
+
+// ---- O4 / O6: one grouped W4A16 GEMM over an explicit row list ------------
+//
+// out[r, n] = bf16( sum_{c<K} A[a_row[r], c] * w[expert[r], n, c] ) for every
+// r with expert[r] >= 0 (other rows are left untouched).  A is bf16 [*, K];
+// codes [E, N, K/8]; scales [E, N, K/32].  out_f32 != 0 writes the fp32
+// accumulator instead (float [R, N]).
+void oracle_grouped_gemm(const uint16_t* A, const int32_t* a_row, const int32_t* expert,
+                         int64_t R, const uint32_t* codes, const uint16_t* scales,
+                         int E, int N, int K, int wmode, int acc64, int out_f32,
+                         void* out) {
+    (void)E;
+    const int64_t wpr = K / 8, spr = K / 32;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < R; ++r) {
+        int e = expert[r];
+        if (e < 0) continue;
+        const uint16_t* a = A + static_cast<int64_t>(a_row[r]) * K;
+        for (int n = 0; n < N; ++n) {
+            const int64_t wr = static_cast<int64_t>(e) * N + n;
+            double acc = dot_row(a, codes + wr * wpr, scales + wr * spr, K, wmode, acc64);
+            if (out_f32)
+                static_cast<float*>(out)[r * N + n] = static_cast<float>(acc);
+            else
+                static_cast<uint16_t*>(out)[r * N + n] = bf16_from_double(acc);
+        }
+    }
+}
+
+// gate/up for every local slot f (row f of Y13 [T*k, 2I]; token t = f / k).
+void oracle_moe_gate_up(const uint16_t* X, const int32_t* topk_ids, int T, int top_k,
+                        int E_global, const int32_t* expert_map, int E_local,
+                        const uint32_t* codes13, const uint16_t* scales13, int H, int I,
+                        int wmode, uint16_t* Y13) {
+    const int64_t slots = static_cast<int64_t>(T) * top_k;
+    std::vector<int32_t> a_row(slots), expert(slots);
+    for (int64_t f = 0; f < slots; ++f) {
+        a_row[f] = static_cast<int32_t>(f / top_k);
+        expert[f] = local_expert(topk_ids, f, E_global, expert_map, E_local);
+    }
+    oracle_grouped_gemm(X, a_row.data(), expert.data(), slots, codes13, scales13,
+                        E_local, 2 * I, H, wmode, 0, 0, Y13);
+}
+
+// O5: Z[r, j] = bf16( silu(g) * u ), g = Y13[r, j], u = Y13[r, I + j], in
+// fp64 from the bf16 inputs with one final rounding; silu(g) = g / (1 + e^-g).
+void oracle_silu_mul(const uint16_t* Y13, int64_t rows, int I, uint16_t* Z) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int j = 0; j < I; ++j) {
+            double g = bf16_to_float(Y13[r * 2 * I + j]);
+            double u = bf16_to_float(Y13[r * 2 * I + I + j]);
+            double s = g / (1.0 + std::exp(-g));
+            Z[r * I + j] = bf16_from_double(s * u);
+        }
+}
+
+// down for every local slot f (row f of Z [T*k, I] -> row f of Y2 [T*k, H]).
+void oracle_moe_down(const uint16_t* Z, const int32_t* topk_ids, int T, int top_k,
+                     int E_global, const int32_t* expert_map, int E_local,
+                     const uint32_t* codes2, const uint16_t* scales2, int H, int I,
+                     int wmode, uint16_t* Y2) {
+    const int64_t slots = static_cast<int64_t>(T) * top_k;
+    std::vector<int32_t> a_row(slots), expert(slots);
+    for (int64_t f = 0; f < slots; ++f) {
+        a_row[f] = static_cast<int32_t>(f);
+        expert[f] = local_expert(topk_ids, f, E_global, expert_map, E_local);
+    }
+    oracle_grouped_gemm(Z, a_row.data(), expert.data(), slots, codes2, scales2, E_local,
+                        H, I, wmode, 0, 0, Y2);
+}
+
+// O7: out[t, h] = bf16( sum_{j<k, row_of[t*k+j] >= 0} w[t,j] * Y[row_of[t*k+j], h] )
+// in fp32, j ascending (multiply, then add, each rounded).  A token with no
+// local slot yields +0.
+void oracle_combine(const uint16_t* Y, const int32_t* row_of, const float* topk_w, int T,
+                    int top_k, int H, uint16_t* out) {
+    for (int t = 0; t < T; ++t)
+        for (int h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int j = 0; j < top_k; ++j) {
+                int32_t r = row_of[static_cast<int64_t>(t) * top_k + j];
+                if (r < 0) continue;
+                float y = bf16_to_float(Y[static_cast<int64_t>(r) * H + h]);
+                float p = topk_w[static_cast<int64_t>(t) * top_k + j] * y;
+                acc = acc + p;
+            }
+            out[static_cast<int64_t>(t) * H + h] = bf16_from_float(acc);
+        }
+}
+
+// O8: grouped masked layout.  a3 is [G, max_m, K] (or flat [G*max_m, K]);
+// masked_m[g] rows of expert g are valid; the output is flat [G*max_m, N]
+// (Chord page, "Grouped SM90 kernels": masked output is flat even for a
+// 3-D input, rows past each expert's valid count are to be ignored).  Rows
+// past masked_m[g] are left untouched; expected_m plays no part in the result.
+void oracle_masked_gemm(const uint16_t* a3, const int32_t* masked_m, int G, int max_m,
+                        const uint32_t* codes, const uint16_t* scales, int N, int K,
+                        int wmode, uint16_t* out) {
+    const int64_t R = static_cast<int64_t>(G) * max_m;
+    std::vector<int32_t> a_row(R), expert(R);
+    for (int g = 0; g < G; ++g)
+        for (int r = 0; r < max_m; ++r) {
+            int64_t i = static_cast<int64_t>(g) * max_m + r;
+            a_row[i] = static_cast<int32_t>(i);
+            expert[i] = (r < masked_m[g]) ? g : -1;
+        }
+    oracle_grouped_gemm(a3, a_row.data(), expert.data(), R, codes, scales, G, N, K, wmode,
+                        0, 0, out);
+}
+
+// Whole indexed path O4 -> O5 -> O6 -> O7 in the slot-indexed layout.
+// Intermediates may be NULL; when given they are [T*k, 2I], [T*k, I], [T*k, H]
+// (rows of non-local slots are zero).
+void oracle_moe_forward(const uint16_t* X, const int32_t* topk_ids, const float* topk_w,
+                        int T, int top_k, int E_global, const int32_t* expert_map,
+                        int E_local, const uint32_t* codes13, const uint16_t* scales13,
+                        const uint32_t* codes2, const uint16_t* scales2, int H, int I,
+                        int wmode, uint16_t* out, uint16_t* Y13_opt, uint16_t* Z_opt,
+                        uint16_t* Y2_opt) {
+    const int64_t slots = static_cast<int64_t>(T) * top_k;
+    std::vector<uint16_t> y13v, zv, y2v;
+    uint16_t* Y13 = Y13_opt;
+    uint16_t* Z = Z_opt;
+    uint16_t* Y2 = Y2_opt;
+    if (!Y13) { y13v.resize(slots * 2 * I); Y13 = y13v.data(); }
+    if (!Z) { zv.resize(slots * I); Z = zv.data(); }
+    if (!Y2) { y2v.resize(slots * H); Y2 = y2v.data(); }
+    std::memset(Y13, 0, slots * 2 * I * sizeof(uint16_t));
+    std::memset(Z, 0, slots * I * sizeof(uint16_t));
+    std::memset(Y2, 0, slots * H * sizeof(uint16_t));
+    oracle_moe_gate_up(X, topk_ids, T, top_k, E_global, expert_map, E_local, codes13,
+                       scales13, H, I, wmode, Y13);
+    oracle_silu_mul(Y13, slots, I, Z);
+    oracle_moe_down(Z, topk_ids, T, top_k, E_global, expert_map, E_local, codes2, scales2,
+                    H, I, wmode, Y2);
+    std::vector<int32_t> row_of(slots);
+    for (int64_t f = 0; f < slots; ++f)
+        row_of[f] = local_expert(topk_ids, f, E_global, expert_map, E_local) >= 0
+                        ? static_cast<int32_t>(f) : -1;
+    oracle_combine(Y2, row_of.data(), topk_w, T, top_k, H, out);
+}
+
+// O9: a second, direct formulation used as brute force.  Token by token and
+// slot by slot, with the weights dequantised on the fly, no routing metadata
+// and no intermediate buffers beyond one row; the same rounding points as the
+// staged path, so the two agree bit for bit.
+void oracle_direct_forward(const uint16_t* X, const int32_t* topk_ids, const float* topk_w,
+                           int T, int top_k, int E_global, const int32_t* expert_map,
+                           int E_local, const uint32_t* codes13, const uint16_t* scales13,
+                           const uint32_t* codes2, const uint16_t* scales2, int H, int I,
+                           int wmode, uint16_t* out) {
+    const int64_t wpr13 = H / 8, spr13 = H / 32, wpr2 = I / 8, spr2 = I / 32;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int t = 0; t < T; ++t) {
+        std::vector<float> acc(H, 0.0f);
+        std::vector<uint16_t> z(I);
+        const uint16_t* x = X + static_cast<int64_t>(t) * H;
+        for (int j = 0; j < top_k; ++j) {
+            int g = topk_ids[static_cast<int64_t>(t) * top_k + j];
+            if (g < 0 || g >= E_global) continue;
+            int e = expert_map ? expert_map[g] : g;
+            if (e < 0 || e >= E_local) continue;
+            for (int i = 0; i < I; ++i) {
+                int64_t rg = static_cast<int64_t>(e) * 2 * I + i;        // gate row
+                int64_t ru = rg + I;                                      // up row
+                float sg = 0.0f, su = 0.0f;
+                for (int c = 0; c < H; ++c) {
+                    float xv = bf16_to_float(x[c]);
+                    sg += xv * weight_at(codes13 + rg * wpr13, scales13 + rg * spr13, c, wmode);
+                    su += xv * weight_at(codes13 + ru * wpr13, scales13 + ru * spr13, c, wmode);
+                }
+                double gb = bf16_to_float(bf16_from_float(sg));
+                double ub = bf16_to_float(bf16_from_float(su));
+                z[i] = bf16_from_double(gb / (1.0 + std::exp(-gb)) * ub);
+            }
+            float wt = topk_w[static_cast<int64_t>(t) * top_k + j];
+            for (int h = 0; h < H; ++h) {
+                int64_t rd = static_cast<int64_t>(e) * H + h;
+                float s = 0.0f;
+                for (int c = 0; c < I; ++c)
+                    s += bf16_to_float(z[c]) * weight_at(codes2 + rd * wpr2, scales2 + rd * spr2, c, wmode);
+                float y = bf16_to_float(bf16_from_float(s));
+                float p = wt * y;
+                acc[h] = acc[h] + p;
+            }
+        }
+        for (int h = 0; h < H; ++h) out[static_cast<int64_t>(t) * H + h] = bf16_from_float(acc[h]);
+    }
+}
+
+}  // extern "C"
