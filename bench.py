@@ -1,0 +1,332 @@
+"""Benchmark of the W4A16 INT4 MoE expert path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|tp8|masked|tiny]
+
+One step = one call of the whole path on one batch of seeded synthetic input
+already resident in HBM: routing sort (align) -> gate/up GEMM with SiLU*gate ->
+down GEMM -> top-k combine (for the masked workload: the two GEMMs and the
+combine).  W untimed warm-up steps, then exactly K timed steps between two
+device synchronisations.  Rank 0 prints one JSON line.
+
+The default workload is the decode share of a Kimi-K2-like layer on one GPU of
+an EP8 deployment (48 local experts, hidden 7168, intermediate 2048, 64 tokens
+x top-8, about 9-15 routed rows per local expert): a weight-streaming problem,
+so its roofline is HBM bandwidth on the algorithmic weight bytes.  Two
+prepacked copies of the weights are used alternately so that no call finds the
+previous call's weights in the 256 MB last-level cache.
+
+Extra figures in the line: per-stage microseconds (HIP events on the stream the
+kernels run on), the page's unit (gate/up + down), the HIP-graph replay time of
+the same step, the roofline object of the dominant kernel and the CPU oracle's
+time on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+METRIC = "MoE layer µs/call; decode weight HBM GB/s and prefill TFLOP/s (% of peak)"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="decode",
+                   choices=["decode", "prefill", "tp8", "masked", "tiny"])
+    p.add_argument("--copies", type=int, default=2, help="prepacked weight copies rotated per call")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--cpu-budget-s", type=float, default=20.0)
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "w4a16_int4_mixture_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str, src_hash: str):
+    """HBM bytes per launch of the dominant kernel from committed PMC summaries
+    (FETCH_SIZE and WRITE_SIZE runs scaled by a plain copy of known size), or
+    None when no summary matches the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"pmc_gate_up_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this path runs on one GPU; multi-GPU sharding (EP all-to-all, TP "
+              "reduce-scatter) is described in DESIGN.md but not built. Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import w4a16_int4_mixture_amd as m
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    t0 = time.time()
+    d = synth.make_workload(args.workload, seed=0)
+    wl = d["wl"]
+    profile = m.PROFILE_PREFILL if args.workload == "prefill" else m.PROFILE_DECODE
+    print(f"[bench] workload {args.workload}: generated inputs in {time.time() - t0:.1f}s",
+          file=sys.stderr, flush=True)
+
+    codes13, scales13 = to_dev(d["codes13"]), to_dev(d["scales13"])
+    codes2, scales2 = to_dev(d["codes2"]), to_dev(d["scales2"])
+    copies = []
+    for _ in range(max(1, args.copies)):
+        copies.append((m.prepare_weight(codes13, scales13, profile),
+                       m.prepare_weight(codes2, scales2, profile)))
+    del codes13, scales13, codes2, scales2
+    torch.cuda.synchronize()
+
+    X = to_dev(d["X"])
+    ids = to_dev(d["topk_ids"])
+    tw = to_dev(d["topk_weights"])
+    em = None if d["expert_map"] is None else to_dev(d["expert_map"])
+    masked = args.workload == "masked"
+
+    # local routed rows and active experts (host-side knowledge of the draw)
+    if masked:
+        counts = d["masked_m"].astype(np.int64)
+    else:
+        flat = d["topk_ids"].ravel()
+        loc = flat if d["expert_map"] is None else d["expert_map"][flat]
+        loc = loc[(loc >= 0) & (loc < wl.E_local)]
+        counts = np.bincount(loc, minlength=wl.E_local).astype(np.int64)
+    rows = int(counts.sum())
+    active = int((counts > 0).sum())
+    H, I = wl.H, wl.I
+    w13_bytes_per_expert = 2 * I * H // 2 + 2 * I * (H // 32) * 2
+    w2_bytes_per_expert = H * I // 2 + H * (I // 32) * 2
+    bytes13 = active * w13_bytes_per_expert
+    bytes2 = active * w2_bytes_per_expert
+    flops13 = 2.0 * rows * (2 * I) * H
+    flops2 = 2.0 * rows * H * I
+
+    if masked:
+        max_m = d["max_m"]
+        paths = [m.MaskedPath(w13, w2, max_m, wl.expected_m, wl.T, wl.top_k, device=dev)
+                 for (w13, w2) in copies]
+        a3 = to_dev(d["a3"].reshape(wl.E_local * max_m, H))
+        mm = to_dev(d["masked_m"])
+        row_of = to_dev(d["row_of"])
+
+        def stages(p):
+            return [("gate_up", lambda: m._capi.w4a16_moe_w4a16_gemm(p.gate_up_args(a3, mm))),
+                    ("down", lambda: m._capi.w4a16_moe_w4a16_gemm(p.down_args(mm))),
+                    ("combine", lambda: m._capi.w4a16_moe_combine(
+                        p.Y2, p.Y2.shape[0], H, row_of, tw, wl.T, wl.top_k, p.out))]
+    else:
+        paths = [m.IndexedPath(w13, w2, wl.T, wl.top_k, wl.E_global, rows_hint=rows, device=dev)
+                 for (w13, w2) in copies]
+
+        def stages(p):
+            return [("align", lambda: p.routing.align(ids, wl.E_global, em)),
+                    ("gate_up", lambda: m._capi.w4a16_moe_w4a16_gemm(p.gate_up_args(X))),
+                    ("down", lambda: m._capi.w4a16_moe_w4a16_gemm(p.down_args())),
+                    ("combine", lambda: m._capi.w4a16_moe_combine(
+                        p.Y2, p.Y2.shape[0], H, p.routing.row_of, tw, wl.T, wl.top_k, p.out))]
+
+    # pre-built argument structs: the timed loop only launches
+    stage_lists = [stages(p) for p in paths]
+    for p in paths:  # resolve workspaces once
+        if masked:
+            p.gate_up_args(a3, mm)
+            p.down_args(mm)
+        else:
+            p.gate_up_args(X)
+            p.down_args()
+
+    def step(i, events=None):
+        st = stage_lists[i % len(stage_lists)]
+        for j, (_, fn) in enumerate(st):
+            if events is not None:
+                events[j].record()
+            fn()
+        if events is not None:
+            events[len(st)].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed steps (wall clock between synchronisations), stage events per step
+    n_st = len(stage_lists[0])
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_st + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    stage_us = {}
+    for j, (name, _) in enumerate(stage_lists[0]):
+        vals = [ev[i][j].elapsed_time(ev[i][j + 1]) * 1000.0 for i in range(args.steps)]
+        stage_us[name] = float(np.median(vals))
+    event_total = float(np.median([ev[i][0].elapsed_time(ev[i][n_st]) * 1000.0
+                                   for i in range(args.steps)]))
+    ms_per_step = wall * 1000.0 / args.steps
+    us_call = ms_per_step * 1000.0
+
+    # HIP graph of one step per weight copy, replayed alternately
+    graph_us = None
+    if not args.no_graph:
+        try:
+            graphs = []
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for k in range(len(paths)):
+                    step(k)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            for k in range(len(paths)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    step(k)
+                graphs.append(g)
+            for i in range(args.warmup):
+                graphs[i % len(graphs)].replay()
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            for i in range(args.steps):
+                graphs[i % len(graphs)].replay()
+            torch.cuda.synchronize()
+            graph_us = (time.perf_counter() - t1) * 1e6 / args.steps
+        except Exception as exc:  # report, never hide
+            print(f"[bench] graph capture failed: {exc}", file=sys.stderr)
+
+    gu, dn = stage_us["gate_up"], stage_us["down"]
+    src_hash = kernel_source_hash()
+    if args.workload == "prefill":
+        bound, unit_rf = "mfma", "TFLOP/s"
+        achieved = flops13 / (gu * 1e-6) / 1e12
+        peak = BF16_PEAK_TFLOPS
+    else:
+        bound, unit_rf = "hbm", "GB/s"
+        achieved = bytes13 / (gu * 1e-6) / 1e9
+        peak = HBM_PEAK_GBS
+    roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit_rf,
+                "frac": round(achieved / peak, 4),
+                "traffic": traffic_from_profiles(args.workload, src_hash),
+                "kernel": "gate_up stage (w4a16_moe_w4a16_gemm)",
+                "algorithmic_per_launch": bytes13 if bound == "hbm" else flops13}
+
+    cpu = None
+    if not args.no_cpu_baseline and args.workload in ("decode", "tiny", "masked"):
+        cpu = cpu_baseline(d, wl, args.workload, args.cpu_budget_s)
+
+    weight_bytes = bytes13 + bytes2
+    line = {
+        "metric": METRIC,
+        "value": round(us_call, 2),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 activations x int4 weights (fp32 accumulate)",
+        "data": "synthetic (seeded, random-init weights)",
+        "config": {"workload": workload_name(args.workload, wl), "tokens": wl.T,
+                   "top_k": wl.top_k, "local_experts": wl.E_local, "hidden": H,
+                   "intermediate": I, "routed_rows": rows, "active_experts": active,
+                   "weight_copies": len(paths)},
+        "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "event_total_us": round(event_total, 2),
+        "gate_up_plus_down_us": round(gu + dn, 2),
+        "graph_us_per_call": None if graph_us is None else round(graph_us, 2),
+        "weight_GBps_path": round(weight_bytes / (us_call * 1e-6) / 1e9, 1),
+        "weight_GBps_gate_up_plus_down": round(weight_bytes / ((gu + dn) * 1e-6) / 1e9, 1),
+        "tflops_gate_up_plus_down": round((flops13 + flops2) / ((gu + dn) * 1e-6) / 1e12, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernel_source_hash": src_hash,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def workload_name(name, wl):
+    return {
+        "decode": "EP8 decode share: 48 local experts, H7168 I2048, 64 tokens x top-8 (~10.7 rows/expert)",
+        "prefill": "EP8 prefill share: 48 local experts, H7168 I2048, 8192 tokens x top-8 over 384",
+        "tp8": "TP8 share: 384 experts, H7168 I256, 1024 tokens x top-8",
+        "masked": "grouped masked EP32 share: 12 experts, 256 rows Zipf(1.2), expected_m 32",
+        "tiny": "tiny: 8 experts, top-2, H256 I128, 16 tokens",
+    }[name]
+
+
+def cpu_baseline(d, wl, workload, budget_s):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    oracle.build(force=False)
+    threads = oracle.num_threads()
+    if workload == "masked":
+        G, max_m = wl.E_local, d["max_m"]
+        a3 = d["a3"].reshape(G * max_m, wl.H)
+        t0 = time.perf_counter()
+        Z = oracle.silu_mul(oracle.masked_gemm(a3, d["masked_m"], d["codes13"], d["scales13"]))
+        Y2 = oracle.masked_gemm(Z, d["masked_m"], d["codes2"], d["scales2"])
+        oracle.combine(Y2, d["row_of"], d["topk_weights"])
+        dt = time.perf_counter() - t0
+        return {"value": round(dt * 1e6, 1), "unit": "us/call", "cores": threads, "kind": "oracle",
+                "sample": "the full masked workload, one call"}
+    # tokens sampled so that the run stays inside the time budget (full when it fits)
+    T = wl.T
+    probe = max(1, min(T, 4))
+    t0 = time.perf_counter()
+    oracle.moe_forward(d["X"][:probe], d["topk_ids"][:probe], d["topk_weights"][:probe],
+                       wl.E_global, d["expert_map"], d["codes13"], d["scales13"], d["codes2"],
+                       d["scales2"])
+    per_tok = (time.perf_counter() - t0) / probe
+    n = int(max(probe, min(T, budget_s / max(per_tok, 1e-9))))
+    t0 = time.perf_counter()
+    oracle.moe_forward(d["X"][:n], d["topk_ids"][:n], d["topk_weights"][:n], wl.E_global,
+                       d["expert_map"], d["codes13"], d["scales13"], d["codes2"], d["scales2"])
+    dt = time.perf_counter() - t0
+    return {"value": round(dt * 1e6 * T / n, 1), "unit": "us/call", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} of {T} tokens of the same workload (time scaled to the full call)",
+            "measured_s": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

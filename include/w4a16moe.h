@@ -1,0 +1,314 @@
+/*
+ * w4a16moe.h -- C ABI of the W4A16 INT4 Mixture-of-Experts expert path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Source page for every operation declared here ("Chord page"): "vLLM x Novita
+ * AI: Chord W4A16 INT4 MoE kernels for Kimi K2.x" (novita.ai blog).  Section
+ * names are given in English translation.
+ *
+ * The path: BF16 activations X [T, H]; INT4 expert weights with one BF16 scale
+ * per group of 32 along K (TL;DR; "Grouped SM90 kernels", operator listing:
+ * weight [G, N, K] uint4, scale [G, N, K/32] bf16); routed rows grouped by
+ * expert in the indexed layout (sorted_ids / expert_ids / num_tokens_padded,
+ * "Two kernel families") or the grouped masked layout (per-expert valid count
+ * masked_m on the device plus a host hint expected_m, "Grouped SM90
+ * kernels"); then gate/up GEMM -> SiLU(gate) * up -> down GEMM -> top-k
+ * weighted combine.
+ *
+ * Conventions shared by every call
+ *   - Device pointers point to GPU memory of the current HIP device; host
+ *     pointers are marked "host".  The caller owns every buffer.  The library
+ *     never allocates or frees device memory and keeps no pointer after a call
+ *     returns.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call that
+ *     launches work is asynchronous on that stream and never synchronises the
+ *     host, except w4a16_moe_align with W4A16_ALIGN_VALIDATE set.
+ *   - bf16 tensors are arrays of uint16 bit patterns; all tensors are dense,
+ *     row-major, without padding between rows.
+ *   - Every call returns a w4a16_status.  Argument checks run on the host
+ *     before anything is launched; on failure nothing is launched and
+ *     w4a16_last_error() describes the problem.  No call falls back to another
+ *     implementation silently.
+ *
+ * Weight boundary format (what the caller hands to w4a16_prepack)
+ *   codes  : int32 [E, N, K/8]; code c of a row sits in word c/8 at bits
+ *            4*(c%8) .. 4*(c%8)+3 (low nibble = lowest K); the code q in
+ *            0..15 stands for the signed value q - 8.
+ *   scales : bf16 [E, N, K/32]; w[e][n][c] = (q - 8) * scales[e][n][c/32]
+ *            (subtract, then scale: "H200 and Blackwell indexed decode").
+ *   The gate projection is W13 rows [0, I), the up projection rows [I, 2I).
+ */
+#ifndef W4A16MOE_H
+#define W4A16MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* Status codes                                                             */
+/* ------------------------------------------------------------------------ */
+typedef enum {
+    W4A16_OK = 0,
+    W4A16_ERR_INVALID_ARG = 1,   /* null pointer, bad shape, misaligned pointer, expected_m <= 0 */
+    W4A16_ERR_UNSUPPORTED = 2,   /* group != 32, K or N not a multiple of the packing unit, profile */
+    W4A16_ERR_MODE_MISMATCH = 3, /* prepared weight used in a mode it was not packed for */
+    W4A16_ERR_CAPACITY = 4,      /* a caller buffer (routing, tiles, output, workspace) too small */
+    W4A16_ERR_ROUTING = 5,       /* expert id out of range (reported only under VALIDATE) */
+    W4A16_ERR_HIP = 6            /* a HIP runtime call or kernel launch failed */
+} w4a16_status;
+
+/* Thread-local, human-readable message for the last non-OK status of this
+ * thread ("" when none).  The pointer stays valid until the next call. */
+const char* w4a16_last_error(void);
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int32_t w4a16_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Load time: prepacking (Chord page, "Indexed kernels" and Figure 2: the    */
+/* profile and the weight layout are fixed when the model is loaded; the     */
+/* token count only tunes the schedule inside a profile.  "vLLM             */
+/* integration": unsupported quantisation schemes fail at load time.         */
+/* "Grouped SM90 kernels": the mode is recorded in the prepared weight and   */
+/* checked at dispatch).                                                     */
+/* ------------------------------------------------------------------------ */
+typedef enum {
+    W4A16_PROFILE_DECODE = 1,  /* few routed rows per expert: weight streaming,
+                                  64 output columns per wavefront chunk        */
+    W4A16_PROFILE_PREFILL = 2  /* many routed rows per expert: MFMA-bound,
+                                  128 output columns per wavefront chunk       */
+} w4a16_profile;
+
+/* Prepack flags. */
+#define W4A16_PACK_GATE_UP_INTERLEAVE 0x1u /* W13 only: interleave gate and up
+    column blocks so that one wavefront owns matching gate/up columns (allows
+    the SiLU(gate)*up epilogue inside the gate/up GEMM) */
+
+#define W4A16_DESC_MAGIC 0x4D413457u   /* "W4AM" as little-endian bytes */
+#define W4A16_DESC_VERSION 1u
+
+/* Plain-old-data record of a prepared weight.  Produced by w4a16_prepack,
+ * passed back unchanged with the packed buffer to every GEMM call, where its
+ * magic, version, profile, flags and shape are checked. */
+typedef struct {
+    uint32_t magic;          /* W4A16_DESC_MAGIC */
+    uint32_t version;        /* W4A16_DESC_VERSION */
+    int32_t profile;         /* w4a16_profile */
+    uint32_t flags;          /* W4A16_PACK_* */
+    int32_t E;               /* experts */
+    int32_t N;               /* output columns (2I for W13, H for W2) */
+    int32_t K;               /* reduction length (H for W13, I for W2) */
+    int32_t group;           /* always 32 */
+    int32_t chunk_n;         /* output columns per packed wavefront chunk */
+    int32_t reserved;
+    uint64_t codes_bytes;    /* bytes of packed codes at offset 0 */
+    uint64_t scales_offset;  /* byte offset of the packed scales */
+    uint64_t bytes;          /* total bytes of the packed buffer */
+} w4a16_desc;
+
+/* Size of the packed buffer for a profile and shape (host call, no GPU).
+ * UNSUPPORTED if group != 32, K % 32 != 0 or N is not a multiple of the
+ * profile's chunk width (64 DECODE, 128 PREFILL). */
+w4a16_status w4a16_prepack_bytes(int32_t profile, uint32_t flags, int32_t E, int32_t N,
+                                 int32_t K, int32_t group, uint64_t* bytes /* host out */);
+
+/* Permute canonical codes and scales into the profile's device layout.
+ *   codes  : device int32 [E, N, K/8], canonical format above
+ *   scales : device bf16 [E, N, K/32]
+ *   packed : device, caller-owned, >= w4a16_prepack_bytes(...) bytes, 256-byte aligned
+ *   desc   : host out, filled on success
+ * One launch on `stream`; a pure bit permutation (no arithmetic on values). */
+w4a16_status w4a16_prepack(int32_t profile, uint32_t flags, const int32_t* codes,
+                           const uint16_t* scales, int32_t E, int32_t N, int32_t K,
+                           int32_t group, void* packed, uint64_t packed_bytes,
+                           w4a16_desc* desc /* host out */, void* stream);
+
+/* Host-side reference of the same permutation (no GPU), for load-time
+ * tooling and tests.  Buffers are host memory. */
+w4a16_status w4a16_prepack_host(int32_t profile, uint32_t flags, const int32_t* codes,
+                                const uint16_t* scales, int32_t E, int32_t N, int32_t K,
+                                int32_t group, void* packed, uint64_t packed_bytes,
+                                w4a16_desc* desc);
+
+/* ------------------------------------------------------------------------ */
+/* Routing metadata, indexed layout (Chord page, "Two kernel families": the  */
+/* indexed family consumes vLLM's sorted_ids / expert_ids /                  */
+/* num_tokens_padded; "vLLM integration": the over-allocated align buffers   */
+/* are consumed without reading routing counts back to the host, which keeps */
+/* the path graph-capturable; Figure 3: activations are never padded, the    */
+/* routing indices carry the padding sentinels).                             */
+/* ------------------------------------------------------------------------ */
+
+/* Buffers written by w4a16_moe_align (all device memory, caller-owned). */
+typedef struct {
+    int32_t* sorted_ids;        /* [sorted_cap]: for each local expert e in
+                                   ascending order, its routed slots f = t*k+j in
+                                   ascending order, then the sentinel T*k up to a
+                                   multiple of block_m; the tail after
+                                   num_tokens_padded also holds the sentinel */
+    int32_t sorted_cap;
+    int32_t* expert_ids;        /* [blocks_cap]: local expert of each block_m
+                                   block of sorted_ids; -1 past the last block */
+    int32_t blocks_cap;
+    int32_t* num_tokens_padded; /* [1]: padded total (sum of padded segments) */
+    int32_t* row_of;            /* [T*k] or NULL: position of slot f in
+                                   sorted_ids, -1 if f is not routed to a local
+                                   expert */
+    int32_t* tiles;             /* [tiles_cap][4] or NULL: GEMM row tiles
+                                   {expert, first position, rows, 0}: each local
+                                   expert's rows cut into pieces of at most tile_m
+                                   rows (expert-major, ascending); entries past
+                                   *tile_count are not written */
+    int32_t tiles_cap;
+    int32_t* tile_count;        /* [1] (required when tiles != NULL) */
+    int32_t tile_m;             /* rows per tile, multiple of 16, <= 256 */
+} w4a16_routing;
+
+#define W4A16_ALIGN_VALIDATE 0x1u  /* read routing back and report ROUTING for
+                                      out-of-range expert ids (synchronises) */
+
+/* Capacities that always suffice for T tokens, top_k, E_local experts. */
+w4a16_status w4a16_moe_align_capacity(int32_t T, int32_t top_k, int32_t E_local,
+                                      int32_t block_m, int32_t tile_m,
+                                      int32_t* sorted_cap, int32_t* blocks_cap,
+                                      int32_t* tiles_cap /* host outs */);
+
+/* Stable counting sort of routed slots by local expert.
+ *   topk_ids   : device int32 [T, top_k], global expert ids
+ *   expert_map : device int32 [E_global] global -> local id or -1; NULL = identity
+ *   Ids outside [0, E_global), or mapping outside [0, E_local), are skipped
+ *   like non-local experts.  1 <= E_local <= 1024, 1 <= block_m <= 256.
+ * Output is fully determined by the input (bit-reproducible). */
+w4a16_status w4a16_moe_align(const int32_t* topk_ids, int32_t T, int32_t top_k,
+                             int32_t E_global, const int32_t* expert_map, int32_t E_local,
+                             int32_t block_m, const w4a16_routing* routing, uint32_t flags,
+                             void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Grouped W4A16 GEMM (Chord page, "H200 prefill and TP8", "H200 and        */
+/* Blackwell indexed decode", "Grouped SM90 kernels").                       */
+/*   out[p, n] = bf16( sum_c A[row(p), c] * (q[e,n,c] - 8) * s[e,n,c/32] )   */
+/* with fp32 accumulation, for every routed row p of expert e.  The INT4     */
+/* codes are unpacked and scaled in registers; no dequantised copy exists.   */
+/* ------------------------------------------------------------------------ */
+typedef enum { W4A16_LAYOUT_INDEXED = 0, W4A16_LAYOUT_MASKED = 1 } w4a16_layout;
+
+/* How an indexed row position p finds its activation row. */
+typedef enum {
+    W4A16_AROW_TOKEN = 0,    /* A row = sorted_ids[p] / top_k (gate/up on X [T, K]) */
+    W4A16_AROW_SLOT = 1,     /* A row = sorted_ids[p]         (A is [T*k, K])       */
+    W4A16_AROW_POSITION = 2  /* A row = p                     (A is compact, e.g. Z) */
+} w4a16_arow;
+
+/* Where an indexed row position p writes its output row. */
+typedef enum {
+    W4A16_OROW_POSITION = 0, /* out row p (compact [sorted_cap, N]) */
+    W4A16_OROW_SLOT = 1      /* out row sorted_ids[p] ([T*k, N]) */
+} w4a16_orow;
+
+typedef enum {
+    W4A16_EPI_STORE = 0,     /* store bf16(acc) */
+    W4A16_EPI_SILU_MUL = 1   /* W13 only: store bf16(silu(bf16(gate)) * bf16(up)),
+                                out is [rows, N/2] */
+} w4a16_epilogue;
+
+#define W4A16_GEMM_F32_OUT 0x1u  /* store the fp32 accumulator (float) instead of
+                                    bf16; EPI_STORE only (exactness tests) */
+
+typedef struct {
+    int32_t layout;                 /* w4a16_layout */
+    int32_t epilogue;               /* w4a16_epilogue */
+    uint32_t flags;                 /* W4A16_GEMM_* */
+    int32_t split_k;                /* 0 = automatic; >1 forces K splits (INDEXED
+                                       only: MASKED rejects it, MODE_MISMATCH) */
+    const uint16_t* A;              /* device bf16 activations, [A_rows, K] */
+    int64_t A_rows;
+    /* INDEXED */
+    int32_t arow;                   /* w4a16_arow */
+    int32_t orow;                   /* w4a16_orow */
+    int32_t top_k;                  /* for AROW_TOKEN; sentinel = num_slots */
+    int32_t num_slots;              /* T * top_k (the sentinel value) */
+    const int32_t* sorted_ids;      /* device [sorted_cap] */
+    int32_t sorted_cap;
+    const int32_t* expert_ids;      /* device [blocks_cap]; used when tiles == NULL */
+    int32_t blocks_cap;
+    int32_t block_m;                /* align granule; tile height when tiles == NULL */
+    const int32_t* num_tokens_padded; /* device [1] */
+    const int32_t* tiles;           /* device [tiles_cap][4] from w4a16_moe_align, or NULL */
+    int32_t tiles_cap;
+    const int32_t* tile_count;      /* device [1] */
+    int32_t tile_m;                 /* rows per tile of the tile table */
+    int32_t rows_hint;              /* host: expected routed rows on this GPU (launch
+                                       choice only; 0 = unknown) */
+    /* MASKED */
+    const int32_t* masked_m;        /* device int32 [G]: valid rows of each expert */
+    int32_t max_m;                  /* rows reserved per expert; A is [G*max_m, K] */
+    int32_t expected_m;             /* host hint > 0, launch choice only */
+    /* weights */
+    const void* packed;             /* device, from w4a16_prepack */
+    const w4a16_desc* desc;         /* host */
+    /* output */
+    void* out;                      /* device; bf16 (or float with F32_OUT) */
+    int64_t out_rows;               /* rows available in out */
+    /* scratch */
+    void* workspace;                /* device, >= w4a16_gemm_workspace_bytes(...) */
+    uint64_t workspace_bytes;
+} w4a16_gemm_args;
+
+/* Workspace needed by this GEMM call (0 when none).  Host call. */
+w4a16_status w4a16_gemm_workspace_bytes(const w4a16_gemm_args* args, uint64_t* bytes);
+
+/* Run one grouped GEMM stage.  Checks the descriptor (magic, version, shape,
+ * flags vs epilogue) before launching: a weight packed with gate/up
+ * interleave used with EPI_STORE, or a plain weight with EPI_SILU_MUL, is a
+ * MODE_MISMATCH; so is any split_k override under MASKED (the grouped
+ * dispatch owns its schedule).  Rows of padding, rows past masked_m and
+ * experts with no rows are never stored; experts with masked_m == 0 read no
+ * weights. */
+w4a16_status w4a16_moe_w4a16_gemm(const w4a16_gemm_args* args, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Activation between the GEMMs: Z[r, j] = bf16( silu(g) * u ), g = Y13[r, j],
+ * u = Y13[r, I + j], silu(g) = g / (1 + exp(-g)), evaluated in fp32.
+ * Rows [0, *rows_dev) when rows_dev != NULL (device count, e.g.
+ * num_tokens_padded), else [0, rows).                                       */
+/* ------------------------------------------------------------------------ */
+w4a16_status w4a16_moe_silu_mul(const uint16_t* y13, int64_t rows, const int32_t* rows_dev,
+                                int32_t I, uint16_t* z, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Top-k weighted combine:                                                   */
+/*   out[t, h] = bf16( sum_{j<k, row_of[t*k+j] >= 0} w[t, j] * y[row_of[t*k+j], h] ) */
+/* fp32, j ascending, each product and sum rounded separately; a token with */
+/* no local slot gives +0.  y: device bf16 [y_rows, H]; row_of: device       */
+/* int32 [T*k]; topk_weights: device float [T, k]; out: device bf16 [T, H].  */
+/* ------------------------------------------------------------------------ */
+w4a16_status w4a16_moe_combine(const uint16_t* y, int64_t y_rows, int32_t H,
+                               const int32_t* row_of, const float* topk_weights, int32_t T,
+                               int32_t top_k, uint16_t* out, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Schedule choice (Chord page, "H200 prefill and TP8": block-M from routed */
+/* tokens per expert with an 80-rows/expert threshold and a 176-row cap;     */
+/* shape-aware stream-K gating; "Grouped SM90 kernels": masked BM from       */
+/* expected_m, wave-aware BN, latency-tuned buffered K).  Host only; the     */
+/* constants are this library's own, measured on gfx950.                    */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    int32_t block_m;   /* align granule (sorted_ids padding) */
+    int32_t tile_m;    /* rows per GEMM tile */
+    int32_t split_k;   /* K splits (1 = none) */
+    int32_t kernel;    /* 1 = small-M streaming kernel, 2 = large-M LDS kernel */
+} w4a16_plan;
+
+w4a16_status w4a16_plan_gemm(const w4a16_desc* desc, int32_t layout, int32_t rows_hint,
+                             int32_t expected_m, int32_t tile_m, w4a16_plan* plan /* host out */);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16MOE_H */

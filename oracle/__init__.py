@@ -126,6 +126,20 @@ def moe_align(topk_ids, E_global: int, E_local: int, block_m: int, expert_map=No
             "num_tokens_padded": int(ntp[0]), "row_of": row_of}
 
 
+def moe_tiles(topk_ids, E_global: int, E_local: int, block_m: int, tile_m: int,
+              expert_map=None) -> np.ndarray:
+    """int32 [n_tiles, 4] = {expert, first position, rows, 0}."""
+    ids = _c(topk_ids, np.int32)
+    T, k = ids.shape
+    cap = -(-T * k // tile_m) + E_local
+    tiles = np.zeros((max(cap, 1), 4), dtype=np.int32)
+    n = _load().oracle_moe_tiles(_p(ids), T, k, E_global, _p(_c(expert_map, np.int32)),
+                                 E_local, block_m, tile_m, _p(tiles), cap)
+    if n < 0:
+        raise ValueError("tile capacity too small")
+    return tiles[:n]
+
+
 # ---- GEMM stages -----------------------------------------------------------
 
 def grouped_gemm(A, a_row, expert, codes, scales, N: int, K: int, wmode: int = 0,

@@ -222,6 +222,37 @@ int oracle_moe_align(const int32_t* topk_ids, int T, int top_k, int E_global,
     return 0;
 }
 
+// GEMM row tiles over the indexed layout: each local expert's routed rows
+// (its segment of sorted_ids, which starts at the padded offset off_e) cut in
+// order into pieces of at most tile_m rows, {expert, first position, rows, 0},
+// experts ascending.  Returns the number of tiles, or -1 when tiles_cap is too
+// small.  (The page leaves the schedule of row blocks open; this is the plain
+// in-order cut that keeps every piece inside one expert.)
+int oracle_moe_tiles(const int32_t* topk_ids, int T, int top_k, int E_global,
+                     const int32_t* expert_map, int E_local, int block_m, int tile_m,
+                     int32_t* tiles, int tiles_cap) {
+    const int64_t slots = static_cast<int64_t>(T) * top_k;
+    std::vector<int64_t> count(E_local, 0);
+    for (int64_t f = 0; f < slots; ++f) {
+        int e = local_expert(topk_ids, f, E_global, expert_map, E_local);
+        if (e >= 0) ++count[e];
+    }
+    int64_t off = 0;
+    int n = 0;
+    for (int e = 0; e < E_local; ++e) {
+        for (int64_t s = 0; s < count[e]; s += tile_m) {
+            if (n >= tiles_cap) return -1;
+            tiles[4 * n + 0] = e;
+            tiles[4 * n + 1] = static_cast<int32_t>(off + s);
+            tiles[4 * n + 2] = static_cast<int32_t>(count[e] - s < tile_m ? count[e] - s : tile_m);
+            tiles[4 * n + 3] = 0;
+            ++n;
+        }
+        off += (count[e] + block_m - 1) / block_m * block_m;
+    }
+    return n;
+}
+
 // ---- O4 / O6: one grouped W4A16 GEMM over an explicit row list ------------
 //
 // out[r, n] = bf16( sum_{c<K} A[a_row[r], c] * w[expert[r], n, c] ) for every

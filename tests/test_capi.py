@@ -1,0 +1,266 @@
+"""Host-side tests of the C-ABI library (no GPU needed).
+
+* every function declared in include/w4a16moe.h is exported by libw4a16moe.so;
+* the ctypes structures agree with the C layout (sizes and offsets printed by a
+  program compiled from the header with gcc);
+* argument checks reject bad calls before anything is launched, with the
+  documented status codes;
+* the host prepack writes exactly the documented device layout;
+* the schedule chooser follows its stated rules.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16moe.h")
+
+capi = pytest.importorskip("w4a16_int4_mixture_amd._capi")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert len(names) >= 12
+    lib = capi.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", capi.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    assert set(names) <= exported
+    assert set(names) == set(capi.SIGNATURES)
+
+
+def _c_layout(tmp_path):
+    structs = {
+        "w4a16_desc": [f[0] for f in capi.w4a16_desc._fields_],
+        "w4a16_routing": [f[0] for f in capi.w4a16_routing._fields_],
+        "w4a16_gemm_args": [f[0] for f in capi.w4a16_gemm_args._fields_],
+        "w4a16_plan": [f[0] for f in capi.w4a16_plan._fields_],
+    }
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void){"]
+    for s, fields in structs.items():
+        lines.append(f'printf("{s} sizeof %zu\\n", sizeof({s}));')
+        for f in fields:
+            lines.append(f'printf("{s} {f} %zu\\n", offsetof({s}, {f}));')
+    lines.append("return 0;}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
+    return [l.split() for l in out.splitlines()]
+
+
+def test_ctypes_structs_match_c_layout(tmp_path):
+    for s, what, val in _c_layout(tmp_path):
+        cls = getattr(capi, s)
+        if what == "sizeof":
+            assert ctypes.sizeof(cls) == int(val), s
+        else:
+            assert getattr(cls, what).offset == int(val), (s, what)
+
+
+def test_header_compiles_as_c_and_cpp(tmp_path):
+    src = tmp_path / "h.c"
+    src.write_text(f'#include "{HEADER}"\nint main(void){{return 0;}}\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-c", str(src), "-o",
+                    str(tmp_path / "h.o")], check=True)
+    subprocess.run(["g++", "-std=c++17", "-Wall", "-Wextra", "-Werror", "-x", "c++", "-c",
+                    str(src), "-o", str(tmp_path / "hpp.o")], check=True)
+
+
+# ---- argument checks (nothing is launched) -----------------------------------
+
+def status_of(fn, *a):
+    try:
+        fn(*a)
+    except capi.W4A16Error as e:
+        return e.status
+    return capi.W4A16_OK
+
+
+def test_prepack_bytes_rejects_unsupported_schemes():
+    P = capi.W4A16_PROFILE_DECODE
+    assert capi.w4a16_prepack_bytes(P, 0, 48, 4096, 7168, 32) == 48 * 4096 * 7168 // 2 + 48 * 4096 * 224 * 2
+    assert status_of(capi.w4a16_prepack_bytes, P, 0, 1, 64, 64, 64) == capi.W4A16_ERR_UNSUPPORTED
+    assert status_of(capi.w4a16_prepack_bytes, P, 0, 1, 64, 48, 32) == capi.W4A16_ERR_UNSUPPORTED
+    assert status_of(capi.w4a16_prepack_bytes, P, 0, 1, 96, 64, 32) == capi.W4A16_ERR_UNSUPPORTED
+    assert status_of(capi.w4a16_prepack_bytes, capi.W4A16_PROFILE_PREFILL, 0, 1, 64, 64, 32) == \
+        capi.W4A16_ERR_UNSUPPORTED
+    assert status_of(capi.w4a16_prepack_bytes, 7, 0, 1, 64, 64, 32) == capi.W4A16_ERR_UNSUPPORTED
+    assert status_of(capi.w4a16_prepack_bytes, P, 0x80, 1, 64, 64, 32) == capi.W4A16_ERR_UNSUPPORTED
+    assert status_of(capi.w4a16_prepack_bytes, P, 0, 0, 64, 64, 32) == capi.W4A16_ERR_INVALID_ARG
+    assert "group" in capi.w4a16_last_error() or capi.w4a16_last_error() != ""
+
+
+def test_align_capacity_and_checks():
+    sc, bc, tc = capi.w4a16_moe_align_capacity(64, 8, 48, 16, 32)
+    assert sc == 512 + 48 * 15 and bc == sc // 16 and tc == 16 + 48
+    assert status_of(capi.w4a16_moe_align_capacity, 4, 2, 0, 16, 0) == capi.W4A16_ERR_INVALID_ARG
+    assert status_of(capi.w4a16_moe_align_capacity, 4, 2, 8, 0, 0) == capi.W4A16_ERR_INVALID_ARG
+    assert status_of(capi.w4a16_moe_align_capacity, 4, 2, 8, 16, 24) == capi.W4A16_ERR_INVALID_ARG
+    # capacity too small -> CAPACITY, before any launch
+    fake = 1 << 20
+    r = capi.w4a16_routing(sorted_ids=fake, sorted_cap=8, expert_ids=fake, blocks_cap=1,
+                           num_tokens_padded=fake)
+    st = capi.lib().w4a16_moe_align(fake, 4, 2, 8, None, 8, 16, ctypes.byref(r), 0, None)
+    assert st == capi.W4A16_ERR_CAPACITY
+    st = capi.lib().w4a16_moe_align(fake, 4, 2, 8, None, 2000, 16, ctypes.byref(r), 0, None)
+    assert st == capi.W4A16_ERR_INVALID_ARG
+    st = capi.lib().w4a16_moe_align(fake, 4, 2, 8, None, 8, 16, None, 0, None)
+    assert st == capi.W4A16_ERR_INVALID_ARG
+    r2 = capi.w4a16_routing(sorted_ids=fake, sorted_cap=1000, expert_ids=fake, blocks_cap=100,
+                            num_tokens_padded=fake, tiles=fake + 8, tiles_cap=100, tile_count=fake,
+                            tile_m=16)
+    st = capi.lib().w4a16_moe_align(fake, 4, 2, 8, None, 8, 16, ctypes.byref(r2), 0, None)
+    assert st == capi.W4A16_ERR_INVALID_ARG            # misaligned tile table
+
+
+def host_desc(profile=capi.W4A16_PROFILE_DECODE, flags=0, E=2, N=128, K=64):
+    codes = np.zeros((E, N, K // 8), np.int32)
+    scales = np.zeros((E, N, K // 32), np.uint16)
+    nb = capi.w4a16_prepack_bytes(profile, flags, E, N, K)
+    packed = np.zeros(nb, np.uint8)
+    return capi.w4a16_prepack_host(profile, flags, codes, scales, E, N, K, 32, packed)
+
+
+def gemm_args(desc, **kw):
+    fake = 1 << 20
+    a = capi.w4a16_gemm_args()
+    a.layout = capi.W4A16_LAYOUT_INDEXED
+    a.A, a.A_rows, a.out, a.out_rows = fake, 64, fake, 4096
+    a.packed = fake
+    a.desc = ctypes.pointer(desc)
+    a.sorted_ids, a.sorted_cap, a.num_tokens_padded = fake, 256, fake
+    a.tiles, a.tiles_cap, a.tile_count, a.tile_m = fake, 8, fake, 32
+    a.num_slots, a.top_k = 64, 2
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def ws_status(a):
+    return status_of(capi.w4a16_gemm_workspace_bytes, a)
+
+
+def test_gemm_argument_checks():
+    d = host_desc()
+    assert ws_status(gemm_args(d)) == capi.W4A16_OK
+    bad = capi.w4a16_desc.from_buffer_copy(d)
+    bad.magic = 0
+    assert ws_status(gemm_args(bad)) == capi.W4A16_ERR_MODE_MISMATCH
+    bad = capi.w4a16_desc.from_buffer_copy(d)
+    bad.bytes += 256
+    assert ws_status(gemm_args(bad)) == capi.W4A16_ERR_MODE_MISMATCH
+    assert ws_status(gemm_args(d, A=(1 << 20) + 2)) == capi.W4A16_ERR_INVALID_ARG
+    assert ws_status(gemm_args(d, packed=(1 << 20) + 64)) == capi.W4A16_ERR_INVALID_ARG
+    assert ws_status(gemm_args(d, tile_m=24)) == capi.W4A16_ERR_INVALID_ARG
+    assert ws_status(gemm_args(d, tile_m=512)) == capi.W4A16_ERR_UNSUPPORTED
+    assert ws_status(gemm_args(d, out_rows=10)) == capi.W4A16_ERR_CAPACITY
+    assert ws_status(gemm_args(d, epilogue=capi.W4A16_EPI_SILU_MUL,
+                               flags=capi.W4A16_GEMM_F32_OUT)) == capi.W4A16_ERR_INVALID_ARG
+    # interleaved W13 with a plain store: the columns would come out permuted
+    di = host_desc(flags=capi.W4A16_PACK_GATE_UP_INTERLEAVE)
+    assert ws_status(gemm_args(di)) == capi.W4A16_ERR_MODE_MISMATCH
+    # masked: expected_m must be positive; split_k overrides are refused
+    m = dict(layout=capi.W4A16_LAYOUT_MASKED, masked_m=1 << 20, max_m=32, expected_m=32,
+             A_rows=64, out_rows=64)
+    assert ws_status(gemm_args(d, **m)) == capi.W4A16_OK
+    assert ws_status(gemm_args(d, **{**m, "expected_m": 0})) == capi.W4A16_ERR_INVALID_ARG
+    assert ws_status(gemm_args(d, **{**m, "split_k": 2})) == capi.W4A16_ERR_MODE_MISMATCH
+    assert ws_status(gemm_args(d, **{**m, "A_rows": 10})) == capi.W4A16_ERR_CAPACITY
+    # launching with a too-small workspace fails before the launch
+    a = gemm_args(d, split_k=2)
+    assert capi.w4a16_gemm_workspace_bytes(a) == 2 * 256 * 128 * 4
+    assert capi.lib().w4a16_moe_w4a16_gemm(ctypes.byref(a), None) == capi.W4A16_ERR_CAPACITY
+
+
+def test_combine_and_silu_checks():
+    fake = 1 << 20
+    assert capi.lib().w4a16_moe_combine(fake, 4, 12, fake, fake, 1, 1, fake, None) == \
+        capi.W4A16_ERR_INVALID_ARG
+    assert capi.lib().w4a16_moe_combine(fake + 2, 4, 16, fake, fake, 1, 1, fake, None) == \
+        capi.W4A16_ERR_INVALID_ARG
+    assert capi.lib().w4a16_moe_silu_mul(fake, 4, None, 12, fake, None) == \
+        capi.W4A16_ERR_INVALID_ARG
+
+
+# ---- host prepack = documented layout -------------------------------------------
+
+def decode_packed(packed, desc):
+    """Read the packed buffer back into canonical codes and scales, from the
+    layout as documented in the library (codes lane-major per K group, nibble i
+    holding K offset 2*(i%4) + i/4; scales [chunk][group][16][CW/16])."""
+    E, N, K, CW = desc.E, desc.N, desc.K, desc.chunk_n
+    NC, KS, WPL = N // CW, K // 32, CW // 16
+    words = packed[: desc.codes_bytes].view(np.uint32).reshape(E, NC, KS, 4, 16, WPL)
+    # axes: e, chunk, ks, lane//16 (K octet), lane%16 (column in block), j (block)
+    off = np.array([2 * (i % 4) + i // 4 for i in range(8)])
+    nib = (words[..., None] >> (4 * np.arange(8, dtype=np.uint32))) & 0xF   # [..., i]
+    q = np.zeros(nib.shape, np.uint32)
+    q[..., off] = nib                                                        # -> K offset order
+    # -> [e, chunk, j, c16, ks, octet, 8]
+    q = q.transpose(0, 1, 5, 4, 2, 3, 6).reshape(E, N, K)
+    codes = np.zeros((E, N, K // 8), np.uint32)
+    for o in range(8):
+        codes |= q[:, :, o::8] << (4 * o)
+    sc = packed[desc.scales_offset: desc.scales_offset + E * N * KS * 2].view(np.uint16)
+    sc = sc.reshape(E, NC, KS, 16, WPL).transpose(0, 1, 4, 3, 2).reshape(E, N, KS)
+    return codes.view(np.int32), sc
+
+
+@pytest.mark.parametrize("profile,flags", [(capi.W4A16_PROFILE_DECODE, 0),
+                                           (capi.W4A16_PROFILE_PREFILL, 0),
+                                           (capi.W4A16_PROFILE_DECODE, capi.W4A16_PACK_GATE_UP_INTERLEAVE),
+                                           (capi.W4A16_PROFILE_PREFILL, capi.W4A16_PACK_GATE_UP_INTERLEAVE)])
+def test_host_prepack_matches_documented_layout(profile, flags):
+    rng = np.random.default_rng(profile * 10 + flags)
+    E, N, K = 3, 256, 96
+    codes = rng.integers(0, 2**32, size=(E, N, K // 8), dtype=np.uint32).view(np.int32)
+    scales = rng.integers(0, 2**16, size=(E, N, K // 32), dtype=np.uint16)
+    packed = np.zeros(capi.w4a16_prepack_bytes(profile, flags, E, N, K), np.uint8)
+    desc = capi.w4a16_prepack_host(profile, flags, codes, scales, E, N, K, 32, packed)
+    assert desc.magic == capi.W4A16_DESC_MAGIC and desc.profile == profile
+    c2, s2 = decode_packed(packed, desc)
+    if flags & capi.W4A16_PACK_GATE_UP_INTERLEAVE:
+        CW = desc.chunk_n
+        half = CW // 2
+        perm = []
+        for nn in range(N):
+            c, w = divmod(nn, CW)
+            perm.append(c * half + w if w < half else N // 2 + c * half + (w - half))
+        codes, scales = codes[:, perm], scales[:, perm]
+    assert np.array_equal(c2, codes)
+    assert np.array_equal(s2, scales)
+
+
+# ---- schedule chooser -------------------------------------------------------------
+
+def test_plan_rules():
+    d13 = host_desc(E=48, N=4096, K=7168)
+    d2 = host_desc(E=48, N=7168, K=2048)
+    p = capi.w4a16_plan_gemm(d13, capi.W4A16_LAYOUT_INDEXED, 512)       # ~10.7 rows/expert
+    assert p.tile_m == 32 and p.block_m == 16 and p.split_k >= 1
+    p_small = capi.w4a16_plan_gemm(d13, capi.W4A16_LAYOUT_INDEXED, 96)
+    assert p_small.tile_m == 16
+    assert p_small.split_k >= p.split_k                                   # fewer tiles -> more splits
+    assert capi.w4a16_plan_gemm(d13, capi.W4A16_LAYOUT_INDEXED, 0, tile_m=48).tile_m == 48
+    # masked: ~1.3 x expected_m for deep-K gate/up, ~1.25 x for short-K down
+    assert capi.w4a16_plan_gemm(d13, capi.W4A16_LAYOUT_MASKED, 0, 32).tile_m == 48
+    assert capi.w4a16_plan_gemm(d2, capi.W4A16_LAYOUT_MASKED, 0, 32).tile_m == 48
+    assert capi.w4a16_plan_gemm(d2, capi.W4A16_LAYOUT_MASKED, 0, 16).tile_m == 32
+    assert status_of(capi.w4a16_plan_gemm, d13, capi.W4A16_LAYOUT_MASKED, 0, 0) == \
+        capi.W4A16_ERR_INVALID_ARG
+    for pl in (p, p_small):
+        assert 4096 // 64 * pl.split_k >= 1 and 224 // pl.split_k >= 8

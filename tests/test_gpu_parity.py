@@ -1,0 +1,379 @@
+"""Parity of the HIP path with the CPU oracle on the same seeded inputs.
+
+Bars (stated once, used throughout):
+  * integer work (prepack, routing metadata, tile table): bit-exact;
+  * exactness invariant (integer activations, power-of-two scales): every
+    product and sum is exact in fp32, so bf16 (and fp32) outputs are
+    bit-identical to the oracle's;
+  * general inputs: per output tensor, max|gpu - oracle| / max|oracle| <= 2e-2
+    with no NaN/Inf, and at least 95% of the elements bit-identical (the fp32
+    summation order differs, so a bf16 rounding step may flip by one ulp).
+
+All calls go through the C ABI (ctypes binding).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def m():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import w4a16_int4_mixture_amd as mod
+    return mod
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def host(t, dtype=None):
+    a = t.detach().cpu().numpy()
+    if dtype is not None:
+        a = a.view(dtype)
+    return a
+
+
+def bf(a):
+    return synth.bf16_bits_to_f32(a).astype(np.float64)
+
+
+def check_close(gpu, ref, what, exact_frac=0.95):
+    g, r = bf(gpu), bf(ref)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite GPU values"
+    denom = max(np.abs(r).max(), 1e-30)
+    err = np.abs(g - r).max() / denom
+    same = np.mean(gpu == ref)
+    print(f"  {what}: max-abs-rel {err:.3e}, bit-identical {same:.4f}", flush=True)
+    assert err <= TOL, f"{what}: max-abs-rel {err} > {TOL}"
+    assert same >= exact_frac, f"{what}: only {same:.3f} bit-identical"
+
+
+def prepare(m, codes, scales, profile):
+    return m.prepare_weight(dev(codes), dev(scales), profile)
+
+
+# ------------------------------------------------------------------ prepack ----
+
+@pytest.mark.parametrize("profile", [1, 2])
+@pytest.mark.parametrize("flags", [0, 1])
+def test_prepack_device_equals_host(m, profile, flags):
+    from w4a16_int4_mixture_amd import _capi
+    rng = np.random.default_rng(profile + 2 * flags)
+    E, N, K = 3, 256, 160
+    codes = rng.integers(0, 2**32, size=(E, N, K // 8), dtype=np.uint32).view(np.int32)
+    scales = rng.integers(0, 2**16, size=(E, N, K // 32), dtype=np.uint16)
+    w = prepare(m, codes, scales, profile) if flags == 0 else \
+        m.prepare_weight(dev(codes), dev(scales), profile, flags)
+    torch.cuda.synchronize()
+    ref = np.zeros(w.desc.bytes, np.uint8)
+    _capi.w4a16_prepack_host(profile, flags, codes, scales, E, N, K, 32, ref)
+    got = host(w.packed)
+    assert np.array_equal(got[: w.desc.codes_bytes], ref[: w.desc.codes_bytes])
+    so = w.desc.scales_offset
+    assert np.array_equal(got[so: so + E * N * (K // 32) * 2], ref[so: so + E * N * (K // 32) * 2])
+
+
+# ------------------------------------------------------------------ routing ----
+
+def check_align(m, ids, E_global, E_local, expert_map, block_m, tile_m):
+    T, k = ids.shape
+    r = m.Routing(T, k, E_local, block_m, tile_m, "cuda")
+    r.sorted_ids.fill_(-7)
+    r.expert_ids.fill_(-7)
+    r.align(dev(ids) if T else r.sorted_ids, E_global, None if expert_map is None else dev(expert_map))
+    torch.cuda.synchronize()
+    ref = oracle.moe_align(ids, E_global, E_local, block_m, expert_map,
+                           sorted_cap=r.sorted_cap, blocks_cap=r.blocks_cap)
+    assert np.array_equal(host(r.sorted_ids), ref["sorted_ids"])
+    assert np.array_equal(host(r.expert_ids), ref["expert_ids"])
+    assert int(host(r.num_tokens_padded)[0]) == ref["num_tokens_padded"]
+    if T:
+        assert np.array_equal(host(r.row_of)[: T * k], ref["row_of"])
+    tiles = oracle.moe_tiles(ids, E_global, E_local, block_m, tile_m, expert_map)
+    n = int(host(r.tile_count)[0])
+    assert n == len(tiles)
+    assert np.array_equal(host(r.tiles)[:n], tiles)
+    return r
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "tp8"])
+def test_align_bit_exact_on_workloads(m, name):
+    d = synth.make_workload(name, weights=False)
+    wl = d["wl"]
+    print(f"align {name}: T={wl.T} k={wl.top_k} E_local={wl.E_local}", flush=True)
+    check_align(m, d["topk_ids"], wl.E_global, wl.E_local, d["expert_map"], 16, 32)
+
+
+@pytest.mark.parametrize("T,k,Eg,El,bm,tm", [(1, 1, 1, 1, 1, 16), (5, 3, 7, 7, 16, 16),
+                                              (33, 2, 40, 9, 32, 64), (200, 8, 300, 1000, 8, 48),
+                                              (700, 6, 64, 64, 64, 256), (0, 8, 16, 16, 16, 16)])
+def test_align_edge_cases(m, T, k, Eg, El, bm, tm):
+    rng = np.random.default_rng(T + Eg)
+    ids = np.argsort(rng.random((max(T, 1), Eg)), axis=1)[:T, :k].astype(np.int32)
+    if T > 2:
+        ids[0, 0] = -1                                  # out-of-range ids are skipped
+        ids[1, 0] = Eg + 3
+    em = None
+    if El != Eg:
+        em = np.full(Eg, -1, np.int32)
+        sel = rng.permutation(Eg)[: min(El, Eg)]
+        em[sel] = rng.permutation(El)[: sel.size].astype(np.int32)
+    check_align(m, ids.reshape(T, k), Eg, El, em, bm, tm)
+
+
+def test_align_validate_reports_bad_ids(m):
+    from w4a16_int4_mixture_amd import _capi
+    ids = np.array([[0, 1], [2, 9]], np.int32)
+    r = m.Routing(2, 2, 4, 16, 16, "cuda")
+    with pytest.raises(_capi.W4A16Error) as ei:
+        r.align(dev(ids), 4, None, flags=_capi.W4A16_ALIGN_VALIDATE)
+    assert ei.value.status == _capi.W4A16_ERR_ROUTING
+    r.align(dev(np.array([[0, 1], [2, 3]], np.int32)), 4, None, flags=_capi.W4A16_ALIGN_VALIDATE)
+
+
+# ------------------------------------------------------- exactness invariant ----
+
+def exact_problem(seed, E, H, I, T, k):
+    rng = np.random.default_rng(seed)
+    d = synth.random_small(seed, E, H, I, T, k)
+    d["X"] = synth.bf16_trunc(rng.integers(-4, 5, size=(T, H)).astype(np.float32))
+    d["scales13"] = synth.bf16_trunc(np.exp2(-rng.integers(6, 9, size=(E, 2 * I, H // 32))).astype(np.float32))
+    d["scales2"] = synth.bf16_trunc(np.exp2(-rng.integers(6, 9, size=(E, H, I // 32))).astype(np.float32))
+    return d
+
+
+def slot_rows(routing, T, k):
+    """position p -> slot f, for valid positions"""
+    s = host(routing.sorted_ids)
+    n = int(host(routing.num_tokens_padded)[0])
+    pos = np.nonzero(s[:n] < T * k)[0]
+    return pos, s[pos]
+
+
+@pytest.mark.parametrize("tile_m,split", [(16, 1), (32, 1), (48, 2), (64, 3), (32, 7)])
+@pytest.mark.parametrize("profile", [1, 2])
+def test_gate_up_and_down_exact_invariant(m, tile_m, split, profile):
+    E, H, I, T, k = 4, 512, 128, 40, 3
+    d = exact_problem(tile_m + split, E, H, I, T, k)
+    print(f"exact: tile_m={tile_m} split={split} profile={profile}", flush=True)
+    w13 = prepare(m, d["codes13"], d["scales13"], profile)
+    w2 = prepare(m, d["codes2"], d["scales2"], profile)
+    path = m.IndexedPath(w13, w2, T, k, E, rows_hint=T * k, tile_m=tile_m,
+                         split_k13=split, split_k2=split)
+    X = dev(d["X"])
+    path.routing.align(dev(d["topk_ids"]), E)
+    Y13 = torch.full((path.routing.sorted_cap, 2 * I), -1, dtype=torch.int16, device="cuda")
+    m.run_gemm(path.gate_up_args(X, out=Y13, epilogue=0), "cuda")
+    pos, f = slot_rows(path.routing, T, k)
+    ref13 = oracle.moe_gate_up(d["X"], d["topk_ids"], E, None, d["codes13"], d["scales13"])
+    assert np.array_equal(host(Y13, np.uint16)[pos], ref13[f])
+    # fp32 accumulators, bit for bit
+    Y13f = torch.zeros((path.routing.sorted_cap, 2 * I), dtype=torch.float32, device="cuda")
+    m.run_gemm(path.gate_up_args(X, out=Y13f, epilogue=0, flags=1), "cuda")
+    ref13f = oracle.grouped_gemm(d["X"], f // k, d["topk_ids"].ravel()[f], d["codes13"],
+                                 d["scales13"], 2 * I, H, out_f32=True)
+    assert np.array_equal(host(Y13f)[pos], ref13f)
+    # down on integer activations
+    rng = np.random.default_rng(3)
+    Zi = synth.bf16_trunc(rng.integers(-4, 5, size=(path.routing.sorted_cap, I)).astype(np.float32))
+    Y2 = torch.zeros((path.routing.sorted_cap, H), dtype=torch.int16, device="cuda")
+    m.run_gemm(path.down_args(Z=dev(Zi), out=Y2), "cuda")
+    Zslot = np.zeros((T * k, I), np.uint16)
+    Zslot[f] = Zi[pos]
+    ref2 = oracle.moe_down(Zslot, d["topk_ids"], E, None, d["codes2"], d["scales2"])
+    assert np.array_equal(host(Y2, np.uint16)[pos], ref2[f])
+
+
+# --------------------------------------------------------- general inputs ----
+
+def run_indexed(m, d, E_global, profile, tile_m=0, split=0, rows_hint=None):
+    wl_T, k = d["topk_ids"].shape
+    E = d["codes13"].shape[0]
+    w13 = prepare(m, d["codes13"], d["scales13"], profile)
+    w2 = prepare(m, d["codes2"], d["scales2"], profile)
+    rows_hint = wl_T * k if rows_hint is None else rows_hint
+    path = m.IndexedPath(w13, w2, wl_T, k, E_global, rows_hint=rows_hint, tile_m=tile_m,
+                         split_k13=split, split_k2=split)
+    em = d.get("expert_map")
+    out = path(dev(d["X"]), dev(d["topk_ids"]), dev(d["topk_weights"]),
+               None if em is None else dev(em))
+    torch.cuda.synchronize()
+    return path, host(out, np.uint16)
+
+
+@pytest.mark.parametrize("seed,E,H,I,T,k,Eg,tile_m,split,profile", [
+    (0, 4, 256, 128, 16, 2, 4, 16, 1, 1),
+    (1, 6, 512, 256, 50, 4, 6, 32, 2, 1),
+    (2, 5, 384, 128, 70, 3, 9, 48, 4, 2),
+    (3, 3, 256, 512, 33, 2, 3, 64, 1, 2),
+    (4, 8, 1024, 256, 9, 8, 16, 0, 0, 1),
+])
+def test_stages_and_path_random(m, seed, E, H, I, T, k, Eg, tile_m, split, profile):
+    print(f"random path seed={seed} E={E} H={H} I={I} T={T} k={k}", flush=True)
+    d = synth.random_small(seed, E, H, I, T, k, E_global=Eg)
+    path, out = run_indexed(m, d, Eg, profile, tile_m, split)
+    ref = oracle.moe_forward(d["X"], d["topk_ids"], d["topk_weights"], Eg, d["expert_map"],
+                             d["codes13"], d["scales13"], d["codes2"], d["scales2"],
+                             intermediates=True)
+    pos, f = slot_rows(path.routing, T, k)
+    check_close(host(path.Z, np.uint16)[pos], ref["Z"][f], "Z")
+    check_close(host(path.Y2, np.uint16)[pos], ref["Y2"][f], "Y2")
+    check_close(out, ref["out"], "out")
+    # the separate activation kernel as well
+    Y13 = torch.zeros((path.routing.sorted_cap, 2 * I), dtype=torch.int16, device="cuda")
+    m.run_gemm(path.gate_up_args(dev(d["X"]), out=Y13, epilogue=0), "cuda")
+    check_close(host(Y13, np.uint16)[pos], ref["Y13"][f], "Y13")
+    Z2 = torch.zeros((path.routing.sorted_cap, I), dtype=torch.int16, device="cuda")
+    from w4a16_int4_mixture_amd import _capi
+    _capi.w4a16_moe_silu_mul(Y13, Y13.shape[0], path.routing.num_tokens_padded, I, Z2)
+    torch.cuda.synchronize()
+    check_close(host(Z2, np.uint16)[pos], oracle.silu_mul(host(Y13, np.uint16)[pos]), "silu",
+                exact_frac=0.99)
+
+
+def test_tiny_workload_full_path(m):
+    d = synth.make_workload("tiny")
+    wl = d["wl"]
+    path, out = run_indexed(m, d, wl.E_global, 1)
+    ref = oracle.moe_forward(d["X"], d["topk_ids"], d["topk_weights"], wl.E_global, None,
+                             d["codes13"], d["scales13"], d["codes2"], d["scales2"])
+    check_close(out, ref, "tiny out")
+
+
+def test_repeat_calls_bit_identical_and_poison_free(m):
+    d = synth.random_small(11, 6, 512, 256, 40, 4, E_global=8)
+    w13 = prepare(m, d["codes13"], d["scales13"], 1)
+    w2 = prepare(m, d["codes2"], d["scales2"], 1)
+    path = m.IndexedPath(w13, w2, 40, 4, 8, rows_hint=160)
+    args = (dev(d["X"]), dev(d["topk_ids"]), dev(d["topk_weights"]), dev(d["expert_map"]))
+    path.Z.fill_(0x7FC0)
+    path.Y2.fill_(0x7FC0)
+    a = host(path(*args), np.uint16).copy()
+    b = host(path(*args), np.uint16).copy()
+    assert np.array_equal(a, b)
+    assert np.all(np.isfinite(bf(a)))
+    # changed routing in the same buffers
+    d2 = synth.random_small(12, 6, 512, 256, 40, 4, E_global=8)
+    c = host(path(dev(d["X"]), dev(d2["topk_ids"]), dev(d2["topk_weights"]), dev(d["expert_map"])),
+             np.uint16)
+    ref = oracle.moe_forward(d["X"], d2["topk_ids"], d2["topk_weights"], 8, d["expert_map"],
+                             d["codes13"], d["scales13"], d["codes2"], d["scales2"])
+    check_close(c, ref, "rerouted out")
+
+
+def test_no_local_slots_and_empty_batch(m):
+    d = synth.random_small(13, 4, 256, 128, 8, 2, E_global=16)
+    d["topk_ids"][:] = 10 + (np.arange(16).reshape(8, 2) % 6)      # all non-local
+    path, out = run_indexed(m, d, 16, 1)
+    assert np.all(out == 0)
+    d0 = synth.random_small(14, 4, 256, 128, 0, 2)
+    w13 = prepare(m, d0["codes13"], d0["scales13"], 1)
+    w2 = prepare(m, d0["codes2"], d0["scales2"], 1)
+    path0 = m.IndexedPath(w13, w2, 0, 2, 4)
+    path0.routing.align(path0.routing.sorted_ids, 4)
+    torch.cuda.synchronize()
+    assert int(host(path0.routing.num_tokens_padded)[0]) == 0
+
+
+def test_block_metadata_mode_and_slot_rows(m):
+    """vLLM-style use: no tile table, blocks of block_m rows from expert_ids,
+    outputs written to slot rows."""
+    from w4a16_int4_mixture_amd import _capi
+    E, H, I, T, k = 5, 256, 128, 30, 3
+    d = synth.random_small(21, E, H, I, T, k)
+    w13 = prepare(m, d["codes13"], d["scales13"], 1)
+    for bm in (16, 32, 64):
+        r = m.Routing(T, k, E, bm, 0, "cuda")
+        r.align(dev(d["topk_ids"]), E)
+        out = torch.full((T * k, 2 * I), -1, dtype=torch.int16, device="cuda")
+        a = m.gemm_args_indexed(w13, dev(d["X"]), r, out, _capi.W4A16_AROW_TOKEN,
+                                orow=_capi.W4A16_OROW_SLOT, use_tiles=False)
+        m.run_gemm(a, "cuda")
+        torch.cuda.synchronize()
+        ref = oracle.moe_gate_up(d["X"], d["topk_ids"], E, None, d["codes13"], d["scales13"])
+        check_close(host(out, np.uint16), ref, f"slot rows bm={bm}")
+
+
+# ------------------------------------------------------------ workloads ----
+
+@pytest.fixture(scope="module")
+def decode_data():
+    return synth.make_workload("decode")
+
+
+def test_decode_workload_full_parity(m, decode_data):
+    d = decode_data
+    wl = d["wl"]
+    print("decode workload: full oracle comparison", flush=True)
+    path, out = run_indexed(m, d, wl.E_global, 1)
+    ref = oracle.moe_forward(d["X"], d["topk_ids"], d["topk_weights"], wl.E_global,
+                             d["expert_map"], d["codes13"], d["scales13"], d["codes2"],
+                             d["scales2"], intermediates=True)
+    pos, f = slot_rows(path.routing, wl.T, wl.top_k)
+    check_close(host(path.Z, np.uint16)[pos], ref["Z"][f], "decode Z")
+    check_close(host(path.Y2, np.uint16)[pos], ref["Y2"][f], "decode Y2")
+    check_close(out, ref["out"], "decode out")
+
+
+def sampled_reference(d, E_global, tokens):
+    """Oracle output rows for a sample of tokens (computes only their slots)."""
+    ids = d["topk_ids"][tokens]
+    w = d["topk_weights"][tokens]
+    return oracle.moe_forward(d["X"][tokens], ids, w, E_global, d["expert_map"], d["codes13"],
+                              d["scales13"], d["codes2"], d["scales2"])
+
+
+@pytest.mark.parametrize("name", ["prefill", "tp8"])
+def test_large_workloads_sampled_parity(m, name):
+    d = synth.make_workload(name)
+    wl = d["wl"]
+    print(f"{name} workload: sampled oracle comparison", flush=True)
+    profile = 2 if name == "prefill" else 1
+    local = None if d["expert_map"] is None else d["expert_map"][d["topk_ids"]] >= 0
+    rows_hint = wl.T * wl.top_k if local is None else int(local.sum())
+    path, out = run_indexed(m, d, wl.E_global, profile, rows_hint=rows_hint)
+    rng = np.random.default_rng(5)
+    tokens = np.sort(rng.choice(wl.T, size=24, replace=False))
+    ref = sampled_reference(d, wl.E_global, tokens)
+    check_close(out[tokens], ref, f"{name} out (24 sampled tokens)")
+
+
+def test_masked_workload_parity(m):
+    d = synth.make_workload("masked")
+    wl = d["wl"]
+    G, max_m = wl.E_local, d["max_m"]
+    print(f"masked workload: G={G} max_m={max_m} counts={d['masked_m'].tolist()}", flush=True)
+    w13 = prepare(m, d["codes13"], d["scales13"], 1)
+    w2 = prepare(m, d["codes2"], d["scales2"], 1)
+    path = m.MaskedPath(w13, w2, max_m, wl.expected_m, wl.T, wl.top_k)
+    a3 = dev(d["a3"].reshape(G * max_m, wl.H))
+    mm = dev(d["masked_m"])
+    path.Z.fill_(0x7FC0)
+    out = host(path(a3, mm, dev(d["row_of"]), dev(d["topk_weights"])), np.uint16)
+    torch.cuda.synchronize()
+    a3h = d["a3"].reshape(G * max_m, wl.H)
+    refZ = oracle.silu_mul(oracle.masked_gemm(a3h, d["masked_m"], d["codes13"], d["scales13"]))
+    valid = np.concatenate([g * max_m + np.arange(c) for g, c in enumerate(d["masked_m"])])
+    check_close(host(path.Z, np.uint16)[valid], refZ[valid], "masked Z")
+    Zin = np.zeros_like(refZ)
+    Zin[valid] = host(path.Z, np.uint16)[valid]
+    refY2 = oracle.masked_gemm(Zin, d["masked_m"], d["codes2"], d["scales2"])
+    check_close(host(path.Y2, np.uint16)[valid], refY2[valid], "masked Y2")
+    ref_out = oracle.combine(refY2, d["row_of"], d["topk_weights"])
+    check_close(out, ref_out, "masked out")
+    # expected_m is a launch hint only: another value gives the same valid rows
+    path2 = m.MaskedPath(w13, w2, max_m, 8, wl.T, wl.top_k)
+    out2 = host(path2(a3, mm, dev(d["row_of"]), dev(d["topk_weights"])), np.uint16)
+    check_close(out2, ref_out, "masked out, expected_m=8")

@@ -420,3 +420,33 @@ def test_masked_layout_equals_row_list_gemm_and_ignores_padding():
         assert np.array_equal(out[valid], ref)
         assert np.all(out[rows[counts[g]:]] == 0xABCD)             # untouched
     assert not np.any(np.isnan(f32_of_bf16(out[out != 0xABCD])))
+
+
+@pytest.mark.parametrize("T,k,Eg,El,bm,tm", [(64, 8, 384, 48, 16, 32), (37, 3, 10, 4, 8, 16),
+                                              (300, 8, 16, 16, 16, 64)])
+def test_tiles_cover_each_expert_segment_in_order(T, k, Eg, El, bm, tm):
+    """Brute force: the tiles of expert e are its valid rows [off_e, off_e + c_e) cut
+    into consecutive pieces of at most tm rows, experts ascending."""
+    rng = np.random.default_rng(T + tm)
+    ids = np.argsort(rng.random((T, Eg)), axis=1)[:, :k].astype(np.int32)
+    em = None
+    if El != Eg:
+        em = np.full(Eg, -1, np.int32)
+        em[:El] = np.arange(El, dtype=np.int32)
+    tiles = oracle.moe_tiles(ids, Eg, El, bm, tm, em)
+    al = oracle.moe_align(ids, Eg, El, bm, em)
+    s = al["sorted_ids"]
+    want = []
+    p = 0
+    while p < al["num_tokens_padded"]:
+        e = al["expert_ids"][p // bm]
+        seg_end = p
+        while seg_end < al["num_tokens_padded"] and al["expert_ids"][seg_end // bm] == e:
+            seg_end += bm
+        valid = [q for q in range(p, seg_end) if s[q] < T * k]
+        for i in range(0, len(valid), tm):
+            piece = valid[i:i + tm]
+            assert piece == list(range(piece[0], piece[0] + len(piece)))
+            want.append([e, piece[0], len(piece), 0])
+        p = seg_end
+    assert tiles.tolist() == want

@@ -1,0 +1,268 @@
+"""W4A16 INT4 MoE expert path for AMD MI355X (gfx950).
+
+Python side of the C-ABI library ``libw4a16moe.so``: ``_capi`` forwards each
+C entry point one to one; the helpers below only allocate device buffers with
+PyTorch and chain those calls.  Every step of the path (routing sort, both
+grouped GEMMs, activation, combine, prepacking) runs in the library's HIP
+kernels.
+
+Typical use (indexed layout)::
+
+    w13 = prepare_weight(codes13, scales13, PROFILE_DECODE)
+    w2 = prepare_weight(codes2, scales2, PROFILE_DECODE)
+    path = IndexedPath(w13, w2, T=64, top_k=8, E_global=384, rows_hint=512)
+    out = path(X, topk_ids, topk_weights, expert_map)          # bf16 [T, H]
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _capi
+from ._capi import (W4A16Error, W4A16_PROFILE_DECODE as PROFILE_DECODE,  # noqa: F401
+                    W4A16_PROFILE_PREFILL as PROFILE_PREFILL,
+                    W4A16_PACK_GATE_UP_INTERLEAVE as PACK_GATE_UP_INTERLEAVE)
+
+BF16 = torch.int16  # bf16 tensors travel as raw 16-bit patterns
+
+
+def _dev_empty(shape, dtype, device):
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+@dataclass
+class PreparedWeight:
+    packed: torch.Tensor        # uint8 device buffer
+    desc: _capi.w4a16_desc
+
+    @property
+    def E(self):
+        return self.desc.E
+
+    @property
+    def N(self):
+        return self.desc.N
+
+    @property
+    def K(self):
+        return self.desc.K
+
+
+def prepare_weight(codes: torch.Tensor, scales: torch.Tensor, profile: int, flags: int = 0,
+                   stream=None) -> PreparedWeight:
+    """codes int32 [E, N, K/8], scales bf16 bits [E, N, K/32] (device) -> packed weight."""
+    E, N, K8 = codes.shape
+    K = K8 * 8
+    nbytes = _capi.w4a16_prepack_bytes(profile, flags, E, N, K, 32)
+    packed = _dev_empty((nbytes,), torch.uint8, codes.device)
+    desc = _capi.w4a16_prepack(profile, flags, codes.contiguous(), scales.contiguous(), E, N, K,
+                               32, packed, stream)
+    return PreparedWeight(packed, desc)
+
+
+class Routing:
+    """Device buffers of the indexed routing metadata (over-allocated)."""
+
+    def __init__(self, T, top_k, E_local, block_m, tile_m, device):
+        sc, bc, tc = _capi.w4a16_moe_align_capacity(T, top_k, E_local, block_m, tile_m)
+        self.T, self.top_k, self.E_local = T, top_k, E_local
+        self.block_m, self.tile_m = block_m, tile_m
+        self.sorted_cap, self.blocks_cap, self.tiles_cap = sc, bc, tc
+        self.sorted_ids = _dev_empty((sc,), torch.int32, device)
+        self.expert_ids = _dev_empty((bc,), torch.int32, device)
+        self.num_tokens_padded = _dev_empty((1,), torch.int32, device)
+        self.row_of = _dev_empty((max(1, T * top_k),), torch.int32, device)
+        self.tiles = _dev_empty((max(1, tc), 4), torch.int32, device)
+        self.tile_count = _dev_empty((1,), torch.int32, device)
+        self.c = _capi.w4a16_routing(
+            sorted_ids=self.sorted_ids.data_ptr(), sorted_cap=sc,
+            expert_ids=self.expert_ids.data_ptr(), blocks_cap=bc,
+            num_tokens_padded=self.num_tokens_padded.data_ptr(),
+            row_of=self.row_of.data_ptr(), tiles=self.tiles.data_ptr() if tc else None,
+            tiles_cap=tc, tile_count=self.tile_count.data_ptr(), tile_m=tile_m)
+
+    def align(self, topk_ids, E_global, expert_map=None, flags=0, stream=None):
+        _capi.w4a16_moe_align(topk_ids, self.T, self.top_k, E_global, expert_map, self.E_local,
+                              self.block_m, self.c, flags, stream)
+
+
+def gemm_args_indexed(w: PreparedWeight, A, routing: Routing, out, arow, epilogue=0, flags=0,
+                      split_k=0, rows_hint=0, workspace=None, orow=_capi.W4A16_OROW_POSITION,
+                      use_tiles=True):
+    a = _capi.w4a16_gemm_args()
+    a.layout = _capi.W4A16_LAYOUT_INDEXED
+    a.epilogue = epilogue
+    a.flags = flags
+    a.split_k = split_k
+    a.A = A.data_ptr()
+    a.A_rows = A.shape[0]
+    a.arow = arow
+    a.orow = orow
+    a.top_k = routing.top_k
+    a.num_slots = routing.T * routing.top_k
+    a.sorted_ids = routing.sorted_ids.data_ptr()
+    a.sorted_cap = routing.sorted_cap
+    a.expert_ids = routing.expert_ids.data_ptr()
+    a.blocks_cap = routing.blocks_cap
+    a.block_m = routing.block_m
+    a.num_tokens_padded = routing.num_tokens_padded.data_ptr()
+    if use_tiles and routing.tiles_cap:
+        a.tiles = routing.tiles.data_ptr()
+        a.tiles_cap = routing.tiles_cap
+        a.tile_count = routing.tile_count.data_ptr()
+        a.tile_m = routing.tile_m
+    a.rows_hint = rows_hint
+    a.packed = w.packed.data_ptr()
+    a.desc = ctypes.pointer(w.desc)
+    a.out = out.data_ptr()
+    a.out_rows = out.shape[0]
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return a
+
+
+def gemm_args_masked(w: PreparedWeight, A, masked_m, max_m, expected_m, out, epilogue=0,
+                     flags=0, workspace=None):
+    a = _capi.w4a16_gemm_args()
+    a.layout = _capi.W4A16_LAYOUT_MASKED
+    a.epilogue = epilogue
+    a.flags = flags
+    a.A = A.data_ptr()
+    a.A_rows = A.shape[0]
+    a.masked_m = masked_m.data_ptr()
+    a.max_m = max_m
+    a.expected_m = expected_m
+    a.packed = w.packed.data_ptr()
+    a.desc = ctypes.pointer(w.desc)
+    a.out = out.data_ptr()
+    a.out_rows = out.shape[0]
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return a
+
+
+def run_gemm(args: _capi.w4a16_gemm_args, device, keep=None, stream=None):
+    """Run one GEMM stage, allocating its workspace when the call needs one."""
+    need = _capi.w4a16_gemm_workspace_bytes(args)
+    ws = None
+    if need and not args.workspace:
+        ws = _dev_empty(((need + 15) // 16 * 16,), torch.uint8, device)
+        args.workspace = ws.data_ptr()
+        args.workspace_bytes = ws.numel()
+    _capi.w4a16_moe_w4a16_gemm(args, stream)
+    if keep is not None and ws is not None:
+        keep.append(ws)
+    return ws
+
+
+class IndexedPath:
+    """The whole indexed path with every buffer allocated once:
+    align -> gate/up GEMM (+ SiLU*gate) -> down GEMM -> top-k combine."""
+
+    def __init__(self, w13: PreparedWeight, w2: PreparedWeight, T: int, top_k: int,
+                 E_global: int, rows_hint: int = 0, tile_m: int = 0, split_k13: int = 0,
+                 split_k2: int = 0, device="cuda"):
+        assert w13.E == w2.E and w13.N == 2 * w2.K and w13.K == w2.N
+        self.w13, self.w2 = w13, w2
+        self.T, self.top_k, self.E_global, self.E = T, top_k, E_global, w13.E
+        self.H, self.I = w13.K, w2.K
+        self.rows_hint = rows_hint
+        plan = _capi.w4a16_plan_gemm(w13.desc, _capi.W4A16_LAYOUT_INDEXED, rows_hint, 0, tile_m)
+        self.plan = plan
+        self.routing = Routing(T, top_k, self.E, plan.block_m, plan.tile_m, device)
+        cap = self.routing.sorted_cap
+        self.Z = _dev_empty((cap, self.I), BF16, device)
+        self.Y2 = _dev_empty((cap, self.H), BF16, device)
+        self.out = _dev_empty((max(T, 1), self.H), BF16, device)
+        self.split_k13, self.split_k2 = split_k13, split_k2
+        self.device = device
+        self._ws = {}
+
+    def _ws_for(self, key, args):
+        need = _capi.w4a16_gemm_workspace_bytes(args)
+        if need == 0:
+            return
+        buf = self._ws.get(key)
+        if buf is None or buf.numel() < need:
+            buf = _dev_empty(((need + 255) // 256 * 256,), torch.uint8, self.device)
+            self._ws[key] = buf
+        args.workspace = buf.data_ptr()
+        args.workspace_bytes = buf.numel()
+
+    def gate_up_args(self, X, out=None, epilogue=_capi.W4A16_EPI_SILU_MUL, flags=0):
+        out = self.Z if out is None else out
+        a = gemm_args_indexed(self.w13, X, self.routing, out, _capi.W4A16_AROW_TOKEN,
+                              epilogue=epilogue, flags=flags, split_k=self.split_k13,
+                              rows_hint=self.rows_hint)
+        self._ws_for(("g", epilogue, flags), a)
+        return a
+
+    def down_args(self, Z=None, out=None, flags=0):
+        Z = self.Z if Z is None else Z
+        out = self.Y2 if out is None else out
+        a = gemm_args_indexed(self.w2, Z, self.routing, out, _capi.W4A16_AROW_POSITION,
+                              flags=flags, split_k=self.split_k2, rows_hint=self.rows_hint)
+        self._ws_for(("d", flags), a)
+        return a
+
+    def __call__(self, X, topk_ids, topk_weights, expert_map=None, stream=None):
+        self.routing.align(topk_ids, self.E_global, expert_map, stream=stream)
+        _capi.w4a16_moe_w4a16_gemm(self.gate_up_args(X), stream)
+        _capi.w4a16_moe_w4a16_gemm(self.down_args(), stream)
+        _capi.w4a16_moe_combine(self.Y2, self.Y2.shape[0], self.H, self.routing.row_of,
+                                topk_weights, self.T, self.top_k, self.out, stream)
+        return self.out
+
+
+class MaskedPath:
+    """Grouped masked layout: gate/up (+ SiLU*gate) -> down on [G*max_m] rows,
+    then the top-k combine through the caller's row map."""
+
+    def __init__(self, w13: PreparedWeight, w2: PreparedWeight, max_m: int, expected_m: int,
+                 T: int, top_k: int, device="cuda"):
+        self.w13, self.w2 = w13, w2
+        self.G, self.max_m, self.expected_m = w13.E, max_m, expected_m
+        self.T, self.top_k = T, top_k
+        self.H, self.I = w13.K, w2.K
+        rows = self.G * max_m
+        self.Z = _dev_empty((rows, self.I), BF16, device)
+        self.Y2 = _dev_empty((rows, self.H), BF16, device)
+        self.out = _dev_empty((max(T, 1), self.H), BF16, device)
+        self.device = device
+        self._ws = {}
+
+    def _ws_for(self, key, args):
+        need = _capi.w4a16_gemm_workspace_bytes(args)
+        if need == 0:
+            return
+        buf = self._ws.get(key)
+        if buf is None or buf.numel() < need:
+            buf = _dev_empty(((need + 255) // 256 * 256,), torch.uint8, self.device)
+            self._ws[key] = buf
+        args.workspace = buf.data_ptr()
+        args.workspace_bytes = buf.numel()
+
+    def gate_up_args(self, a3, masked_m, out=None, epilogue=_capi.W4A16_EPI_SILU_MUL, flags=0):
+        out = self.Z if out is None else out
+        a = gemm_args_masked(self.w13, a3, masked_m, self.max_m, self.expected_m, out,
+                             epilogue=epilogue, flags=flags)
+        self._ws_for(("g", epilogue, flags), a)
+        return a
+
+    def down_args(self, masked_m, Z=None, out=None, flags=0):
+        Z = self.Z if Z is None else Z
+        out = self.Y2 if out is None else out
+        a = gemm_args_masked(self.w2, Z, masked_m, self.max_m, self.expected_m, out, flags=flags)
+        self._ws_for(("d", flags), a)
+        return a
+
+    def __call__(self, a3, masked_m, row_of, topk_weights, stream=None):
+        _capi.w4a16_moe_w4a16_gemm(self.gate_up_args(a3, masked_m), stream)
+        _capi.w4a16_moe_w4a16_gemm(self.down_args(masked_m), stream)
+        _capi.w4a16_moe_combine(self.Y2, self.Y2.shape[0], self.H, row_of, topk_weights, self.T,
+                                self.top_k, self.out, stream)
+        return self.out

@@ -1,0 +1,197 @@
+// Routing metadata for the indexed layout: a stable counting sort of routed
+// slots by local expert, padded per expert to a multiple of block_m.
+//
+// Chord page, "Two kernel families": the indexed family consumes vLLM's
+// sorted_ids / expert_ids / num_tokens_padded; "vLLM integration": these
+// buffers are over-allocated and consumed without a host read-back, so the
+// path stays graph-capturable; Figure 3: activations are not padded, the
+// routing indices carry the padding sentinels.
+//
+// One workgroup of W wavefronts.  Wavefront w owns a contiguous range of
+// 64-slot chunks (flat slot f = t*k + j, ascending).  For one chunk, lane l
+// holds slot f = 64*c + l and sets bit l of mask[w][e] (64-bit LDS OR) for
+// its local expert e.  Then popcount(mask[w][e]) counts the chunk's slots of
+// expert e and popcount(mask[w][e] & lanes_below_l) is the rank of lane l's
+// slot among them: both are independent of the order in which the ORs land,
+// so the sort is stable and bit-reproducible without ordered atomics.
+//   pass 1: per (wave, expert) counts
+//   pass 2: per-expert totals, padded offsets (wave prefix scan), per-wave
+//           bases, expert_ids, padding sentinels, GEMM tile table, tails
+//   pass 3: scatter each local slot to base + rank, record row_of
+
+#include "internal.h"
+
+namespace w4a16 {
+
+namespace {
+
+__device__ inline void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ inline int local_expert(const AlignArgs& a, int64_t f, int* bad) {
+    int g = a.topk_ids[f];
+    if (g < 0 || g >= a.E_global) {
+        *bad = 1;
+        return -1;
+    }
+    int e = a.expert_map ? a.expert_map[g] : g;
+    if (e < -1 || e >= a.E_local) *bad = 1;
+    return (e >= 0 && e < a.E_local) ? e : -1;
+}
+
+// In-place exclusive prefix sum of v[0..n) by one wavefront; returns the total.
+__device__ int wave_exclusive_scan(int* v, int n, int lane) {
+    int carry = 0;
+    for (int base = 0; base < n; base += 64) {
+        int i = base + lane;
+        int x = i < n ? v[i] : 0;
+        int incl = x;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            int y = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += y;
+        }
+        if (i < n) v[i] = carry + incl - x;
+        carry += __shfl(incl, 63, 64);
+    }
+    return carry;
+}
+
+}  // namespace
+
+__global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
+    extern __shared__ unsigned char smem[];
+    const int E = a.E_local;
+    const int W = blockDim.x / 64;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    uint64_t* masks = reinterpret_cast<uint64_t*>(smem);          // [W][E]
+    int* cnt = reinterpret_cast<int*>(masks + W * E);             // [W][E] counts, then bases
+    int* pad = cnt + W * E;                                       // [E] padded counts -> offsets
+    int* ntile = pad + E;                                         // [E] tiles -> tile offsets
+    int* tot = ntile + E;                                         // [E] slot counts
+    int* red = tot + E;                                           // [4] totals
+    uint64_t* my_mask = masks + w * E;
+    int* my_cnt = cnt + w * E;
+
+    const int64_t S = static_cast<int64_t>(a.T) * a.top_k;
+    const int32_t sentinel = static_cast<int32_t>(S);
+    const int64_t chunks = (S + 63) / 64;
+    const int64_t cpw = (chunks + W - 1) / W;
+    const int64_t c_begin = w * cpw;
+    const int64_t c_end = c_begin + cpw < chunks ? c_begin + cpw : chunks;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int bad = 0;
+
+    // ---- pass 1: counts per (wave, expert)
+    for (int e = lane; e < E; e += 64) my_cnt[e] = 0;
+    for (int64_t c = c_begin; c < c_end; ++c) {
+        for (int e = lane; e < E; e += 64) my_mask[e] = 0;
+        wave_sync();
+        int64_t f = c * 64 + lane;
+        int e = f < S ? local_expert(a, f, &bad) : -1;
+        if (e >= 0) atomicOr(reinterpret_cast<unsigned long long*>(&my_mask[e]), 1ull << lane);
+        wave_sync();
+        for (int ee = lane; ee < E; ee += 64) my_cnt[ee] += __popcll(my_mask[ee]);
+        wave_sync();
+    }
+    if (bad && a.err_flag) atomicAdd(a.err_flag, 1);
+    __syncthreads();
+
+    // ---- pass 2: totals, offsets, metadata
+    const int bm = a.block_m;
+    const int tm = a.r.tile_m > 0 ? a.r.tile_m : 1;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        int c = 0;
+        for (int ww = 0; ww < W; ++ww) c += cnt[ww * E + e];
+        tot[e] = c;
+        pad[e] = (c + bm - 1) / bm * bm;
+        ntile[e] = (c + tm - 1) / tm;
+    }
+    __syncthreads();
+    if (w == 0) {
+        int total = wave_exclusive_scan(pad, E, lane);
+        int ntiles = wave_exclusive_scan(ntile, E, lane);
+        if (lane == 0) {
+            red[0] = total;
+            red[1] = ntiles;
+        }
+    }
+    __syncthreads();
+    const int total = red[0];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        const int off = pad[e];
+        int run = off;
+        for (int ww = 0; ww < W; ++ww) {
+            int b = cnt[ww * E + e];
+            cnt[ww * E + e] = run;
+            run += b;
+        }
+        const int c = tot[e];
+        const int p = (c + bm - 1) / bm * bm;
+        for (int j = c; j < p; ++j) a.r.sorted_ids[off + j] = sentinel;
+        for (int b = 0; b < p / bm; ++b) a.r.expert_ids[off / bm + b] = e;
+        if (a.r.tiles) {
+            int t0 = ntile[e];
+            for (int i = 0; i * tm < c; ++i) {
+                int4 v;
+                v.x = e;
+                v.y = off + i * tm;
+                v.z = (c - i * tm) < tm ? (c - i * tm) : tm;
+                v.w = 0;
+                reinterpret_cast<int4*>(a.r.tiles)[t0 + i] = v;
+            }
+        }
+    }
+    if (threadIdx.x == 0) {
+        a.r.num_tokens_padded[0] = total;
+        if (a.r.tiles) a.r.tile_count[0] = red[1];
+    }
+    for (int i = total + threadIdx.x; i < a.r.sorted_cap; i += blockDim.x)
+        a.r.sorted_ids[i] = sentinel;
+    for (int b = total / bm + threadIdx.x; b < a.r.blocks_cap; b += blockDim.x)
+        a.r.expert_ids[b] = -1;
+    __syncthreads();
+
+    // ---- pass 3: scatter
+    for (int64_t c = c_begin; c < c_end; ++c) {
+        for (int e = lane; e < E; e += 64) my_mask[e] = 0;
+        wave_sync();
+        int64_t f = c * 64 + lane;
+        int e = f < S ? local_expert(a, f, &bad) : -1;
+        if (e >= 0) atomicOr(reinterpret_cast<unsigned long long*>(&my_mask[e]), 1ull << lane);
+        wave_sync();
+        if (f < S) {
+            int pos = -1;
+            if (e >= 0) {
+                pos = my_cnt[e] + __popcll(my_mask[e] & below);
+                a.r.sorted_ids[pos] = static_cast<int32_t>(f);
+            }
+            if (a.r.row_of) a.r.row_of[f] = pos;
+        }
+        wave_sync();
+        for (int ee = lane; ee < E; ee += 64) my_cnt[ee] += __popcll(my_mask[ee]);
+        wave_sync();
+    }
+}
+
+int align_waves(int E_local) {
+    // keep the LDS footprint (12 bytes per wave and expert) under 60 KiB
+    int w = 16;
+    while (w > 1 && static_cast<int64_t>(w) * E_local * 12 + E_local * 12 + 64 > 60 * 1024) w >>= 1;
+    return w;
+}
+
+size_t align_lds_bytes(int W, int E_local) {
+    return static_cast<size_t>(W) * E_local * 12 + static_cast<size_t>(E_local) * 12 + 16;
+}
+
+void launch_align(const AlignArgs& a, hipStream_t s) {
+    int W = align_waves(a.E_local);
+    k_align<<<dim3(1), dim3(64 * W), align_lds_bytes(W, a.E_local), s>>>(a);
+}
+
+}  // namespace w4a16

@@ -1,0 +1,472 @@
+// C ABI entry points: argument checks, schedule choice, launches.
+//
+// Every check runs on the host before anything is launched (Chord page,
+// "vLLM integration": unsupported schemes fail loudly instead of selecting a
+// wrong kernel; "Grouped SM90 kernels": a weight prepared for one mode fails
+// loudly in another, and the grouped dispatch owns its schedule and refuses
+// tuning overrides).
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+
+#include "internal.h"
+
+namespace w4a16 {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+}
+
+void clear_error() { g_err[0] = 0; }
+
+w4a16_status check_launch(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        set_error("%s: HIP launch failed: %s", what, hipGetErrorString(e));
+        return W4A16_ERR_HIP;
+    }
+    return W4A16_OK;
+}
+
+static bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// Largest tile height the streaming kernel supports (4 MFMA row blocks).
+static constexpr int kSmallMaxTile = 64;
+
+__device__ int32_t g_routing_errors;
+
+// ---- schedule choice ---------------------------------------------------------
+//
+// The indexed rule follows the shape of the page's resolver (block height from
+// routed rows per expert tok_e, not from the total), with CDNA4 constants:
+// the tile is sized to hold an expert's rows in one pass (about twice the mean
+// so that Poisson-like tails rarely spill into a second pass, which would
+// stream the expert's weights again), in 16-row MFMA steps.  The masked rule
+// sizes tiles from expected_m: ~1.3x for deep-K gate/up (a spill re-reads the
+// whole K), ~1.25x for short-K down.  K splits are added until the grid holds
+// enough wavefronts to keep every CU streaming (shape-aware split-K gating),
+// but never below 8 groups of K per split.
+
+static int choose_split(int64_t tiles_est, int64_t rows_est, int NC, int KS, int N,
+                        int64_t weight_bytes) {
+    const int64_t target_waves = 4096;       // ~1.3 rounds of 3 wavefronts per SIMD
+    const int64_t waves = tiles_est * NC;
+    // every extra split writes and reads one fp32 [rows, N] partial: keep that
+    // under a quarter of the weight stream
+    const int64_t partial_bytes = std::max<int64_t>(rows_est, 1) * N * 8;
+    int split = 1;
+    while (waves * split < target_waves && KS / (split * 2) >= 8 &&
+           partial_bytes * (split * 2) <= weight_bytes / 4)
+        split *= 2;
+    return split;
+}
+
+static w4a16_status plan_impl(const w4a16_desc* d, int layout, int rows_hint, int expected_m,
+                              int tile_m_in, w4a16_plan* p) {
+    const int E = d->E;
+    const int KS = d->K / 32;
+    const int NC = d->N / d->chunk_n;
+    int tile_m;
+    int64_t tiles_est;
+    if (layout == W4A16_LAYOUT_MASKED) {
+        if (expected_m <= 0) {
+            set_error("expected_m must be a positive integer (got %d)", expected_m);
+            return W4A16_ERR_INVALID_ARG;
+        }
+        const bool deep_k = d->K >= 4096;
+        const int64_t want = deep_k ? ceil_div(13LL * expected_m, 10) : ceil_div(5LL * expected_m, 4);
+        tile_m = static_cast<int>(std::min<int64_t>(std::max<int64_t>(round_up(want, 16), 16), kSmallMaxTile));
+        tiles_est = E;
+    } else {
+        if (tile_m_in > 0) {
+            tile_m = tile_m_in;
+        } else {
+            const double tok_e = rows_hint > 0 ? static_cast<double>(rows_hint) / E : 16.0;
+            tile_m = static_cast<int>(std::min<int64_t>(
+                std::max<int64_t>(round_up(static_cast<int64_t>(2.0 * tok_e + 0.999), 16), 16), kSmallMaxTile));
+        }
+        tiles_est = rows_hint > 0 ? ceil_div(rows_hint, tile_m) + E / 2 : E;
+    }
+    p->block_m = 16;
+    p->tile_m = tile_m;
+    p->kernel = 1;
+    const int64_t rows_est = layout == W4A16_LAYOUT_MASKED
+                                 ? static_cast<int64_t>(E) * expected_m
+                                 : std::max<int64_t>(rows_hint, E);
+    const int64_t active = std::min<int64_t>(E, std::max<int64_t>(tiles_est, 1));
+    const int64_t weight_bytes = active * static_cast<int64_t>(d->N) * d->K * 17 / 32;
+    p->split_k = choose_split(tiles_est, rows_est, NC, KS, d->N, weight_bytes);
+    return W4A16_OK;
+}
+
+// ---- GEMM ------------------------------------------------------------------
+
+struct Resolved {
+    GemmArgs g;
+    int mt;
+    int split;
+    int64_t rows_cap;        // rows of the position-indexed output space
+    uint64_t ws_partial;     // bytes of fp32 partials
+    uint64_t ws_y13;         // bytes of the bf16 gate/up staging (SiLU not fused)
+    bool reduce;             // run the split-K reduction
+    bool silu_separate;      // run the SiLU kernel on staged Y13
+};
+
+static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
+    W4A16_CHECK_ARG(a, "null GEMM arguments");
+    w4a16_status st = check_desc(a->desc);
+    if (st != W4A16_OK) return st;
+    const w4a16_desc* d = a->desc;
+    W4A16_CHECK_ARG(a->packed && aligned(a->packed, 256), "packed weights null or not 256-byte aligned");
+    W4A16_CHECK_ARG(a->A && aligned(a->A, 16), "activations null or not 16-byte aligned");
+    W4A16_CHECK_ARG(a->out && aligned(a->out, 16), "output null or not 16-byte aligned");
+    W4A16_CHECK_ARG(a->epilogue == W4A16_EPI_STORE || a->epilogue == W4A16_EPI_SILU_MUL,
+                    "unknown epilogue %d", a->epilogue);
+    W4A16_CHECK_ARG((a->flags & ~W4A16_GEMM_F32_OUT) == 0, "unknown GEMM flags 0x%x", a->flags);
+    const bool f32_out = (a->flags & W4A16_GEMM_F32_OUT) != 0;
+    const bool interleaved = (d->flags & W4A16_PACK_GATE_UP_INTERLEAVE) != 0;
+    if (a->epilogue == W4A16_EPI_STORE && interleaved) {
+        set_error("weight packed with gate/up interleave used with a plain store epilogue");
+        return W4A16_ERR_MODE_MISMATCH;
+    }
+    if (a->epilogue == W4A16_EPI_SILU_MUL && interleaved) {
+        set_error("the in-register SiLU epilogue is not available in this build");
+        return W4A16_ERR_UNSUPPORTED;
+    }
+    W4A16_CHECK_ARG(!(f32_out && a->epilogue != W4A16_EPI_STORE), "F32_OUT needs EPI_STORE");
+    W4A16_CHECK_ARG(a->epilogue != W4A16_EPI_SILU_MUL || d->N % 16 == 0,
+                    "SiLU epilogue needs N %% 16 == 0");
+
+    GemmArgs& g = r->g;
+    g = GemmArgs{};
+    g.A = a->A;
+    g.codes = static_cast<const uint32_t*>(a->packed);
+    g.scales = reinterpret_cast<const uint16_t*>(static_cast<const char*>(a->packed) + d->scales_offset);
+    g.N = d->N;
+    g.K = d->K;
+    g.CW = d->chunk_n;
+    g.NC = d->N / d->chunk_n;
+    g.KS = d->K / 32;
+    g.E = d->E;
+    W4A16_CHECK_ARG(a->A_rows >= 1, "A_rows must be positive");
+    g.A_rows = a->A_rows;
+
+    w4a16_plan plan;
+    if (a->layout == W4A16_LAYOUT_INDEXED) {
+        W4A16_CHECK_ARG(a->sorted_ids && a->num_tokens_padded, "indexed layout needs sorted_ids and num_tokens_padded");
+        W4A16_CHECK_ARG(a->sorted_cap >= 1, "sorted_cap must be positive");
+        W4A16_CHECK_ARG(a->num_slots >= 1, "num_slots (T * top_k) must be positive");
+        W4A16_CHECK_ARG(a->arow >= W4A16_AROW_TOKEN && a->arow <= W4A16_AROW_POSITION, "bad arow %d", a->arow);
+        W4A16_CHECK_ARG(a->orow == W4A16_OROW_POSITION || a->orow == W4A16_OROW_SLOT, "bad orow %d", a->orow);
+        W4A16_CHECK_ARG(a->arow != W4A16_AROW_TOKEN || a->top_k >= 1, "AROW_TOKEN needs top_k >= 1");
+        W4A16_CHECK_ARG(a->split_k >= 0, "split_k must be >= 0");
+        int tile_m;
+        if (a->tiles) {
+            W4A16_CHECK_ARG(a->tile_count && aligned(a->tiles, 16), "tile table needs tile_count and 16-byte alignment");
+            W4A16_CHECK_ARG(a->tiles_cap >= 1, "tiles_cap must be positive");
+            W4A16_CHECK_ARG(a->tile_m >= 16 && a->tile_m % 16 == 0, "tile_m must be a positive multiple of 16");
+            if (a->tile_m > kSmallMaxTile) {
+                set_error("tile_m %d exceeds the supported %d", a->tile_m, kSmallMaxTile);
+                return W4A16_ERR_UNSUPPORTED;
+            }
+            tile_m = a->tile_m;
+        } else {
+            W4A16_CHECK_ARG(a->expert_ids && a->blocks_cap >= 1, "indexed layout without tiles needs expert_ids");
+            W4A16_CHECK_ARG(a->block_m >= 16 && a->block_m % 16 == 0, "block_m must be a positive multiple of 16");
+            if (a->block_m > kSmallMaxTile) {
+                set_error("block_m %d exceeds the supported %d", a->block_m, kSmallMaxTile);
+                return W4A16_ERR_UNSUPPORTED;
+            }
+            tile_m = a->block_m;
+        }
+        st = plan_impl(d, W4A16_LAYOUT_INDEXED, a->rows_hint, 0, tile_m, &plan);
+        if (st != W4A16_OK) return st;
+        int split = a->split_k > 0 ? a->split_k : plan.split_k;
+        if (a->orow == W4A16_OROW_SLOT || f32_out) split = 1;
+        split = std::max(1, std::min(split, g.KS));
+        {
+            const int64_t need_a = a->arow == W4A16_AROW_POSITION ? a->sorted_cap
+                                   : a->arow == W4A16_AROW_SLOT   ? a->num_slots
+                                                                  : ceil_div(a->num_slots, a->top_k);
+            if (a->A_rows < need_a) {
+                set_error("activations have %lld rows, this row mode needs %lld",
+                          static_cast<long long>(a->A_rows), static_cast<long long>(need_a));
+                return W4A16_ERR_CAPACITY;
+            }
+        }
+        g.sorted_cap = a->sorted_cap;
+        g.tile_src = a->tiles ? TILE_TABLE : TILE_BLOCKS;
+        g.arow = a->arow;
+        g.orow = a->orow;
+        g.top_k = a->top_k;
+        g.num_slots = a->num_slots;
+        g.sorted_ids = a->sorted_ids;
+        g.expert_ids = a->expert_ids;
+        g.ntp = a->num_tokens_padded;
+        g.tiles = a->tiles;
+        g.tile_count = a->tile_count;
+        g.block_m = a->block_m;
+        g.tile_m = tile_m;
+        if (a->tiles) {
+            int64_t want = a->rows_hint > 0 ? ceil_div(a->rows_hint, tile_m) + d->E : a->tiles_cap;
+            g.grid_tiles = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(a->tiles_cap, want)));
+        } else {
+            g.grid_tiles = a->blocks_cap;
+        }
+        g.grid_tiles = std::min(g.grid_tiles, 65535);
+        r->mt = tile_m / 16;
+        r->split = split;
+        r->rows_cap = a->sorted_cap;
+        const int64_t need_rows = a->orow == W4A16_OROW_SLOT ? a->num_slots : a->sorted_cap;
+        const int64_t out_w = a->epilogue == W4A16_EPI_SILU_MUL ? d->N / 2 : d->N;
+        (void)out_w;
+        if (a->out_rows < need_rows) {
+            set_error("output has %lld rows, needs %lld", static_cast<long long>(a->out_rows),
+                      static_cast<long long>(need_rows));
+            return W4A16_ERR_CAPACITY;
+        }
+    } else if (a->layout == W4A16_LAYOUT_MASKED) {
+        W4A16_CHECK_ARG(a->masked_m, "masked layout needs masked_m");
+        W4A16_CHECK_ARG(a->max_m >= 1, "max_m must be positive");
+        if (a->expected_m <= 0) {
+            set_error("expected_m must be a positive integer (got %d)", a->expected_m);
+            return W4A16_ERR_INVALID_ARG;
+        }
+        if (a->split_k != 0) {
+            set_error("the grouped masked dispatch chooses its own schedule: split_k override refused");
+            return W4A16_ERR_MODE_MISMATCH;
+        }
+        st = plan_impl(d, W4A16_LAYOUT_MASKED, 0, a->expected_m, 0, &plan);
+        if (st != W4A16_OK) return st;
+        const int64_t rows = static_cast<int64_t>(d->E) * a->max_m;
+        if (a->A_rows < rows) {
+            set_error("masked activations have %lld rows, need E*max_m = %lld",
+                      static_cast<long long>(a->A_rows), static_cast<long long>(rows));
+            return W4A16_ERR_CAPACITY;
+        }
+        if (a->out_rows < rows) {
+            set_error("masked output has %lld rows, needs %lld", static_cast<long long>(a->out_rows),
+                      static_cast<long long>(rows));
+            return W4A16_ERR_CAPACITY;
+        }
+        g.tile_src = TILE_MASKED;
+        g.arow = W4A16_AROW_POSITION;
+        g.orow = W4A16_OROW_POSITION;
+        g.masked_m = a->masked_m;
+        g.max_m = a->max_m;
+        g.tile_m = plan.tile_m;
+        g.chunks_per_expert = static_cast<int>(ceil_div(a->max_m, plan.tile_m));
+        g.grid_tiles_total = d->E * g.chunks_per_expert;
+        g.grid_tiles = std::min(g.grid_tiles_total, 65535);
+        int split = f32_out ? 1 : plan.split_k;
+        r->mt = plan.tile_m / 16;
+        r->split = std::max(1, std::min(split, g.KS));
+        r->rows_cap = rows;
+    } else {
+        W4A16_CHECK_ARG(false, "unknown layout %d", a->layout);
+    }
+    g.split_k = r->split;
+    r->reduce = r->split > 1;
+    r->silu_separate = a->epilogue == W4A16_EPI_SILU_MUL && !r->reduce;
+    r->ws_partial = r->reduce ? static_cast<uint64_t>(r->split) * r->rows_cap * d->N * 4 : 0;
+    r->ws_y13 = r->silu_separate ? static_cast<uint64_t>(r->rows_cap) * d->N * 2 : 0;
+    g.ws_stride = r->rows_cap * d->N;
+    if (r->reduce) {
+        g.out_kind = OUT_PARTIAL;
+        g.out = a->workspace;
+    } else if (r->silu_separate) {
+        g.out_kind = OUT_BF16;
+        g.out = a->workspace;
+    } else {
+        g.out_kind = f32_out ? OUT_F32 : OUT_BF16;
+        g.out = a->out;
+    }
+    return W4A16_OK;
+}
+
+}  // namespace w4a16
+
+using namespace w4a16;
+
+extern "C" {
+
+const char* w4a16_last_error(void) { return g_err; }
+
+int32_t w4a16_version(void) { return 100; }
+
+w4a16_status w4a16_plan_gemm(const w4a16_desc* desc, int32_t layout, int32_t rows_hint,
+                             int32_t expected_m, int32_t tile_m, w4a16_plan* plan) {
+    clear_error();
+    W4A16_CHECK_ARG(plan, "null plan pointer");
+    w4a16_status st = check_desc(desc);
+    if (st != W4A16_OK) return st;
+    W4A16_CHECK_ARG(layout == W4A16_LAYOUT_INDEXED || layout == W4A16_LAYOUT_MASKED, "unknown layout %d", layout);
+    W4A16_CHECK_ARG(tile_m == 0 || (tile_m >= 16 && tile_m % 16 == 0 && tile_m <= kSmallMaxTile),
+                    "tile_m must be 0 or a multiple of 16 up to %d", kSmallMaxTile);
+    return plan_impl(desc, layout, rows_hint, expected_m, tile_m, plan);
+}
+
+w4a16_status w4a16_moe_align_capacity(int32_t T, int32_t top_k, int32_t E_local, int32_t block_m,
+                                      int32_t tile_m, int32_t* sorted_cap, int32_t* blocks_cap,
+                                      int32_t* tiles_cap) {
+    clear_error();
+    W4A16_CHECK_ARG(sorted_cap && blocks_cap && tiles_cap, "null output pointer");
+    W4A16_CHECK_ARG(T >= 0 && top_k >= 1 && E_local >= 1 && E_local <= 1024, "bad T/top_k/E_local");
+    W4A16_CHECK_ARG(block_m >= 1 && block_m <= 256, "block_m must be in [1, 256]");
+    W4A16_CHECK_ARG(tile_m == 0 || (tile_m >= 16 && tile_m <= 256 && tile_m % 16 == 0),
+                    "tile_m must be 0 or a multiple of 16 up to 256");
+    const int64_t slots = static_cast<int64_t>(T) * top_k;
+    int64_t sc = round_up(slots + static_cast<int64_t>(E_local) * (block_m - 1), block_m);
+    sc = std::max<int64_t>(sc, block_m);
+    W4A16_CHECK_ARG(sc < (1LL << 31), "routing too large");
+    *sorted_cap = static_cast<int32_t>(sc);
+    *blocks_cap = static_cast<int32_t>(sc / block_m);
+    *tiles_cap = tile_m > 0 ? static_cast<int32_t>(ceil_div(slots, tile_m) + E_local) : 0;
+    return W4A16_OK;
+}
+
+w4a16_status w4a16_moe_align(const int32_t* topk_ids, int32_t T, int32_t top_k, int32_t E_global,
+                             const int32_t* expert_map, int32_t E_local, int32_t block_m,
+                             const w4a16_routing* routing, uint32_t flags, void* stream) {
+    clear_error();
+    W4A16_CHECK_ARG(routing, "null routing buffers");
+    W4A16_CHECK_ARG(T >= 0 && top_k >= 1, "bad T=%d top_k=%d", T, top_k);
+    W4A16_CHECK_ARG(T == 0 || topk_ids, "null topk_ids");
+    W4A16_CHECK_ARG(E_global >= 1, "E_global must be positive");
+    W4A16_CHECK_ARG(E_local >= 1 && E_local <= 1024, "E_local must be in [1, 1024]");
+    W4A16_CHECK_ARG(block_m >= 1 && block_m <= 256, "block_m must be in [1, 256]");
+    W4A16_CHECK_ARG((flags & ~W4A16_ALIGN_VALIDATE) == 0, "unknown align flags 0x%x", flags);
+    const w4a16_routing& r = *routing;
+    W4A16_CHECK_ARG(r.sorted_ids && r.expert_ids && r.num_tokens_padded, "routing needs sorted_ids, expert_ids, num_tokens_padded");
+    int32_t sc, bc, tc;
+    w4a16_status st = w4a16_moe_align_capacity(T, top_k, E_local, block_m,
+                                               r.tiles ? r.tile_m : 0, &sc, &bc, &tc);
+    if (st != W4A16_OK) return st;
+    if (r.sorted_cap < sc || r.blocks_cap < bc) {
+        set_error("routing capacity too small: sorted_cap %d < %d or blocks_cap %d < %d",
+                  r.sorted_cap, sc, r.blocks_cap, bc);
+        return W4A16_ERR_CAPACITY;
+    }
+    if (r.tiles) {
+        W4A16_CHECK_ARG(r.tile_count && aligned(r.tiles, 16), "tile table needs tile_count and 16-byte alignment");
+        if (r.tiles_cap < tc) {
+            set_error("tiles_cap %d < %d", r.tiles_cap, tc);
+            return W4A16_ERR_CAPACITY;
+        }
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    AlignArgs a{};
+    a.topk_ids = topk_ids;
+    a.T = T;
+    a.top_k = top_k;
+    a.E_global = E_global;
+    a.E_local = E_local;
+    a.block_m = block_m;
+    a.expert_map = expert_map;
+    a.r = r;
+    int32_t* flag = nullptr;
+    if (flags & W4A16_ALIGN_VALIDATE) {
+        if (hipGetSymbolAddress(reinterpret_cast<void**>(&flag), HIP_SYMBOL(g_routing_errors)) != hipSuccess) {
+            set_error("cannot locate the routing error counter");
+            return W4A16_ERR_HIP;
+        }
+        int32_t zero = 0;
+        if (hipMemcpyAsync(flag, &zero, sizeof(zero), hipMemcpyHostToDevice, s) != hipSuccess) {
+            set_error("cannot reset the routing error counter");
+            return W4A16_ERR_HIP;
+        }
+    }
+    a.err_flag = flag;
+    launch_align(a, s);
+    st = check_launch("moe_align");
+    if (st != W4A16_OK) return st;
+    if (flag) {
+        int32_t nbad = 0;
+        if (hipMemcpyAsync(&nbad, flag, sizeof(nbad), hipMemcpyDeviceToHost, s) != hipSuccess ||
+            hipStreamSynchronize(s) != hipSuccess) {
+            set_error("routing validation read-back failed");
+            return W4A16_ERR_HIP;
+        }
+        if (nbad) {
+            set_error("%d routed slot(s) name an expert id out of range", nbad);
+            return W4A16_ERR_ROUTING;
+        }
+    }
+    return W4A16_OK;
+}
+
+w4a16_status w4a16_gemm_workspace_bytes(const w4a16_gemm_args* args, uint64_t* bytes) {
+    clear_error();
+    W4A16_CHECK_ARG(bytes, "null bytes pointer");
+    Resolved r;
+    w4a16_status st = resolve(args, &r);
+    if (st != W4A16_OK) return st;
+    *bytes = r.ws_partial + r.ws_y13;
+    return W4A16_OK;
+}
+
+w4a16_status w4a16_moe_w4a16_gemm(const w4a16_gemm_args* args, void* stream) {
+    clear_error();
+    Resolved r;
+    w4a16_status st = resolve(args, &r);
+    if (st != W4A16_OK) return st;
+    const uint64_t need = r.ws_partial + r.ws_y13;
+    if (need > 0) {
+        if (!args->workspace || args->workspace_bytes < need || !aligned(args->workspace, 16)) {
+            set_error("workspace too small or misaligned: %llu bytes needed",
+                      static_cast<unsigned long long>(need));
+            return W4A16_ERR_CAPACITY;
+        }
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    launch_gemm_small(r.g, r.mt, s);
+    st = check_launch("w4a16 gemm");
+    if (st != W4A16_OK) return st;
+    const bool masked = args->layout == W4A16_LAYOUT_MASKED;
+    const int32_t* rows_dev = masked ? nullptr : args->num_tokens_padded;
+    const int32_t* mm = masked ? args->masked_m : nullptr;
+    const bool silu = args->epilogue == W4A16_EPI_SILU_MUL;
+    if (r.reduce) {
+        launch_splitk_reduce(static_cast<const float*>(args->workspace), r.split, r.g.ws_stride,
+                             r.rows_cap, rows_dev, args->desc->N, silu, mm, args->max_m,
+                             static_cast<uint16_t*>(args->out), s);
+        st = check_launch("split-K reduce");
+    } else if (r.silu_separate) {
+        launch_silu_mul(static_cast<const uint16_t*>(args->workspace), r.rows_cap, rows_dev,
+                        args->desc->N / 2, mm, args->max_m, static_cast<uint16_t*>(args->out), s);
+        st = check_launch("silu_mul");
+    }
+    return st;
+}
+
+w4a16_status w4a16_moe_silu_mul(const uint16_t* y13, int64_t rows, const int32_t* rows_dev,
+                                int32_t I, uint16_t* z, void* stream) {
+    clear_error();
+    W4A16_CHECK_ARG(y13 && z && aligned(y13, 16) && aligned(z, 16), "null or misaligned buffers");
+    W4A16_CHECK_ARG(rows >= 0 && I >= 8 && I % 8 == 0, "rows must be >= 0 and I a multiple of 8");
+    launch_silu_mul(y13, rows, rows_dev, I, nullptr, 1, z, static_cast<hipStream_t>(stream));
+    return check_launch("silu_mul");
+}
+
+w4a16_status w4a16_moe_combine(const uint16_t* y, int64_t y_rows, int32_t H, const int32_t* row_of,
+                               const float* topk_weights, int32_t T, int32_t top_k, uint16_t* out,
+                               void* stream) {
+    clear_error();
+    W4A16_CHECK_ARG(T >= 0 && top_k >= 1 && y_rows >= 1, "bad T/top_k/y_rows");
+    W4A16_CHECK_ARG(H >= 8 && H % 8 == 0, "H must be a positive multiple of 8");
+    W4A16_CHECK_ARG(y && out && row_of && topk_weights, "null buffer");
+    W4A16_CHECK_ARG(aligned(y, 16) && aligned(out, 16), "y and out must be 16-byte aligned");
+    if (T == 0) return W4A16_OK;
+    launch_combine(y, y_rows, H, row_of, topk_weights, T, top_k, out, static_cast<hipStream_t>(stream));
+    return check_launch("combine");
+}
+
+}  // extern "C"

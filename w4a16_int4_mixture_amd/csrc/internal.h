@@ -1,0 +1,121 @@
+// Internal declarations of the W4A16 MoE library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+
+#include "../../include/w4a16moe.h"
+
+namespace w4a16 {
+
+// ---- errors ---------------------------------------------------------------
+
+void set_error(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+void clear_error();
+
+#define W4A16_CHECK_ARG(cond, ...)                                  \
+    do {                                                            \
+        if (!(cond)) {                                              \
+            ::w4a16::set_error(__VA_ARGS__);                        \
+            return W4A16_ERR_INVALID_ARG;                           \
+        }                                                           \
+    } while (0)
+
+// Map the sticky launch status to W4A16_ERR_HIP after launching on a stream.
+w4a16_status check_launch(const char* what);
+
+// ---- packed weight geometry ------------------------------------------------
+//
+// Codes: word (e, chunk, ks, lane, j) at index
+//   (((e * NC + chunk) * KS + ks) * 64 + lane) * WPL + j
+// holds the eight codes of column  chunk*CW + 16*j + lane%16  (packed column
+// order) for K = ks*32 + 8*(lane/16) + o, o = 0..7, with the code of offset o
+// in nibble  nib_of(o)  where the nibble order is
+//   nibble i holds offset 2*(i%4) + i/4   (i.e. 0,2,4,6,1,3,5,7)
+// so that (word >> 4p) & 0x000F000F selects offsets (2p, 2p+1) in the two
+// 16-bit halves, and (word >> 4b') & 0x0F0F0F0F gives four bytes.
+// Scales: bf16 (e, chunk, ks, c16, j) at index
+//   (((e * NC + chunk) * KS + ks) * 16 + c16) * WPL + j
+// holds the scale of column chunk*CW + 16*j + c16, group ks.
+// WPL = CW / 16 words (and scales) per lane per group.
+struct PackGeom {
+    int E, N, K, CW, NC, KS, WPL;
+    bool interleave;
+    uint64_t codes_bytes, scales_offset, scales_bytes, bytes;
+};
+
+__host__ __device__ inline int nibble_k_offset(int i) { return 2 * (i & 3) + (i >> 2); }
+
+// Packed column -> canonical column (gate/up interleave: within each CW
+// chunk, the first CW/2 packed columns are gate columns and the last CW/2 the
+// matching up columns).
+__host__ __device__ inline int canonical_column(int nn, int N, int CW, bool interleave) {
+    if (!interleave) return nn;
+    int c = nn / CW, w = nn % CW, half = CW / 2;
+    return w < half ? c * half + w : N / 2 + c * half + (w - half);
+}
+
+int chunk_width_of(int profile);
+w4a16_status make_geom(int profile, uint32_t flags, int E, int N, int K, int group,
+                       PackGeom* g);
+w4a16_status check_desc(const w4a16_desc* d);
+
+// ---- launchers (defined next to their kernels) ------------------------------
+
+void launch_prepack(const PackGeom& g, const uint32_t* codes, const uint16_t* scales,
+                    void* packed, hipStream_t s);
+
+struct AlignArgs {
+    const int32_t* topk_ids;
+    int T, top_k, E_global, E_local, block_m;
+    const int32_t* expert_map;
+    w4a16_routing r;
+    int32_t* err_flag;  // device int or nullptr (validation)
+};
+void launch_align(const AlignArgs& a, hipStream_t s);
+
+// How a GEMM block finds its rows.
+enum TileSrc { TILE_TABLE = 0, TILE_BLOCKS = 1, TILE_MASKED = 2 };
+// What the GEMM stores.
+enum OutKind { OUT_BF16 = 0, OUT_F32 = 1, OUT_PARTIAL = 2 };
+
+struct GemmArgs {
+    // rows
+    int tile_src, arow, orow, top_k, num_slots;
+    const uint16_t* A;
+    const int32_t* sorted_ids;
+    const int32_t* expert_ids;
+    const int32_t* ntp;
+    const int32_t* tiles;
+    const int32_t* tile_count;
+    int block_m, tile_m;
+    const int32_t* masked_m;
+    int max_m, chunks_per_expert;
+    int grid_tiles;        // grid.y
+    int grid_tiles_total;  // masked: experts * chunks_per_expert
+    // weights
+    const uint32_t* codes;
+    const uint16_t* scales;
+    int NC, KS, N, K, CW, E;
+    int64_t A_rows;    // rows of A (row indices are clamped below it)
+    int sorted_cap;    // entries of sorted_ids
+    // output
+    void* out;
+    int out_kind;
+    int split_k;
+    int64_t ws_stride;  // elements between split partials (OUT_PARTIAL)
+};
+void launch_gemm_small(const GemmArgs& a, int mt, hipStream_t s);
+
+// masked_m != nullptr: rows r with r % max_m >= masked_m[r / max_m] are skipped.
+void launch_silu_mul(const uint16_t* y13, int64_t rows, const int32_t* rows_dev, int I,
+                     const int32_t* masked_m, int max_m, uint16_t* z, hipStream_t s);
+void launch_splitk_reduce(const float* ws, int split_k, int64_t ws_stride, int64_t rows,
+                          const int32_t* rows_dev, int N, bool silu, const int32_t* masked_m,
+                          int max_m, uint16_t* out, hipStream_t s);
+void launch_combine(const uint16_t* y, int64_t y_rows, int H, const int32_t* row_of,
+                    const float* w, int T, int top_k, uint16_t* out, hipStream_t s);
+
+}  // namespace w4a16

@@ -1,0 +1,259 @@
+// Load-time weight prepacking: canonical INT4 codes + bf16 group scales ->
+// the device layout read by the GEMM kernels.
+//
+// Chord page, "Indexed kernels" / Figure 2: the kernel profile and the weight
+// layout are fixed when the model is loaded; "Grouped SM90 kernels": the
+// packers permute the INT4 buffer bit by bit and re-lay the scales, and the
+// prepared weight records its mode.  Here the permutation serves CDNA4: each
+// wavefront lane fetches, with one 16-byte load per K group of 32, the codes
+// of its MFMA B-operand fragments for CW/16 column blocks, and the nibble
+// order lets two bf16 operands be formed per VALU op (see the codes layout in
+// internal.h).  Values are never touched: the permutation is exact.
+
+#include "internal.h"
+
+namespace w4a16 {
+
+int chunk_width_of(int profile) {
+    switch (profile) {
+        case W4A16_PROFILE_DECODE: return 64;
+        case W4A16_PROFILE_PREFILL: return 128;
+        default: return 0;
+    }
+}
+
+static uint64_t round_up(uint64_t x, uint64_t m) { return (x + m - 1) / m * m; }
+
+w4a16_status make_geom(int profile, uint32_t flags, int E, int N, int K, int group,
+                       PackGeom* g) {
+    int cw = chunk_width_of(profile);
+    if (cw == 0) {
+        set_error("unknown profile %d", profile);
+        return W4A16_ERR_UNSUPPORTED;
+    }
+    if (flags & ~W4A16_PACK_GATE_UP_INTERLEAVE) {
+        set_error("unknown prepack flags 0x%x", flags);
+        return W4A16_ERR_UNSUPPORTED;
+    }
+    if (E <= 0 || N <= 0 || K <= 0) {
+        set_error("bad shape E=%d N=%d K=%d", E, N, K);
+        return W4A16_ERR_INVALID_ARG;
+    }
+    if (group != 32) {
+        set_error("only group size 32 is supported (got %d)", group);
+        return W4A16_ERR_UNSUPPORTED;
+    }
+    if (K % 32 != 0) {
+        set_error("K=%d is not a multiple of the group size 32", K);
+        return W4A16_ERR_UNSUPPORTED;
+    }
+    if (N % cw != 0) {
+        set_error("N=%d is not a multiple of the profile's chunk width %d", N, cw);
+        return W4A16_ERR_UNSUPPORTED;
+    }
+    g->E = E;
+    g->N = N;
+    g->K = K;
+    g->CW = cw;
+    g->NC = N / cw;
+    g->KS = K / 32;
+    g->WPL = cw / 16;
+    g->interleave = (flags & W4A16_PACK_GATE_UP_INTERLEAVE) != 0;
+    g->codes_bytes = static_cast<uint64_t>(E) * N * (K / 8) * 4;
+    g->scales_offset = round_up(g->codes_bytes, 256);
+    g->scales_bytes = static_cast<uint64_t>(E) * N * (K / 32) * 2;
+    g->bytes = g->scales_offset + round_up(g->scales_bytes, 256);
+    return W4A16_OK;
+}
+
+w4a16_status check_desc(const w4a16_desc* d) {
+    if (!d) {
+        set_error("null weight descriptor");
+        return W4A16_ERR_INVALID_ARG;
+    }
+    if (d->magic != W4A16_DESC_MAGIC || d->version != W4A16_DESC_VERSION) {
+        set_error("weight descriptor has bad magic/version (0x%x/%u): not a prepared weight",
+                  d->magic, d->version);
+        return W4A16_ERR_MODE_MISMATCH;
+    }
+    PackGeom g;
+    w4a16_status st = make_geom(d->profile, d->flags, d->E, d->N, d->K, d->group, &g);
+    if (st != W4A16_OK) return W4A16_ERR_MODE_MISMATCH;
+    if (g.CW != d->chunk_n || g.bytes != d->bytes || g.scales_offset != d->scales_offset) {
+        set_error("weight descriptor is inconsistent with its profile/shape");
+        return W4A16_ERR_MODE_MISMATCH;
+    }
+    return W4A16_OK;
+}
+
+__host__ __device__ static inline uint32_t permute_word(uint32_t w) {
+    uint32_t out = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out |= ((w >> (4 * nibble_k_offset(i))) & 0xFu) << (4 * i);
+    return out;
+}
+
+__global__ void k_prepack_codes(const uint32_t* __restrict__ codes, uint32_t* __restrict__ out,
+                                int N, int K, int NC, int KS, int CW, int WPL, int interleave,
+                                int64_t total) {
+    int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= total) return;
+    int64_t r = idx;
+    int j = static_cast<int>(r % WPL);
+    r /= WPL;
+    int lane = static_cast<int>(r % 64);
+    r /= 64;
+    int ks = static_cast<int>(r % KS);
+    r /= KS;
+    int chunk = static_cast<int>(r % NC);
+    int64_t e = r / NC;
+    int nn = chunk * CW + 16 * j + (lane & 15);
+    int n = canonical_column(nn, N, CW, interleave != 0);
+    uint32_t w = codes[(e * N + n) * (K / 8) + ks * 4 + (lane >> 4)];
+    out[idx] = permute_word(w);
+}
+
+__global__ void k_prepack_scales(const uint16_t* __restrict__ scales, uint16_t* __restrict__ out,
+                                 int N, int NC, int KS, int CW, int WPL, int interleave,
+                                 int64_t total) {
+    int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= total) return;
+    int64_t r = idx;
+    int j = static_cast<int>(r % WPL);
+    r /= WPL;
+    int c16 = static_cast<int>(r % 16);
+    r /= 16;
+    int ks = static_cast<int>(r % KS);
+    r /= KS;
+    int chunk = static_cast<int>(r % NC);
+    int64_t e = r / NC;
+    int nn = chunk * CW + 16 * j + c16;
+    int n = canonical_column(nn, N, CW, interleave != 0);
+    out[idx] = scales[(e * N + n) * KS + ks];
+}
+
+void launch_prepack(const PackGeom& g, const uint32_t* codes, const uint16_t* scales,
+                    void* packed, hipStream_t s) {
+    int64_t nw = static_cast<int64_t>(g.E) * g.N * (g.K / 8);
+    int64_t ns = static_cast<int64_t>(g.E) * g.N * (g.K / 32);
+    uint32_t* oc = static_cast<uint32_t*>(packed);
+    uint16_t* os = reinterpret_cast<uint16_t*>(static_cast<char*>(packed) + g.scales_offset);
+    k_prepack_codes<<<dim3(static_cast<unsigned>((nw + 255) / 256)), dim3(256), 0, s>>>(
+        codes, oc, g.N, g.K, g.NC, g.KS, g.CW, g.WPL, g.interleave, nw);
+    k_prepack_scales<<<dim3(static_cast<unsigned>((ns + 255) / 256)), dim3(256), 0, s>>>(
+        scales, os, g.N, g.NC, g.KS, g.CW, g.WPL, g.interleave, ns);
+}
+
+// Host reference of the same permutation.
+static void prepack_host(const PackGeom& g, const uint32_t* codes, const uint16_t* scales,
+                         void* packed) {
+    uint32_t* oc = static_cast<uint32_t*>(packed);
+    uint16_t* os = reinterpret_cast<uint16_t*>(static_cast<char*>(packed) + g.scales_offset);
+    int64_t idx = 0;
+    for (int64_t e = 0; e < g.E; ++e)
+        for (int chunk = 0; chunk < g.NC; ++chunk)
+            for (int ks = 0; ks < g.KS; ++ks)
+                for (int lane = 0; lane < 64; ++lane)
+                    for (int j = 0; j < g.WPL; ++j, ++idx) {
+                        int n = canonical_column(chunk * g.CW + 16 * j + (lane & 15), g.N, g.CW,
+                                                 g.interleave);
+                        oc[idx] = permute_word(codes[(e * g.N + n) * (g.K / 8) + ks * 4 + (lane >> 4)]);
+                    }
+    idx = 0;
+    for (int64_t e = 0; e < g.E; ++e)
+        for (int chunk = 0; chunk < g.NC; ++chunk)
+            for (int ks = 0; ks < g.KS; ++ks)
+                for (int c16 = 0; c16 < 16; ++c16)
+                    for (int j = 0; j < g.WPL; ++j, ++idx) {
+                        int n = canonical_column(chunk * g.CW + 16 * j + c16, g.N, g.CW, g.interleave);
+                        os[idx] = scales[(e * g.N + n) * g.KS + ks];
+                    }
+}
+
+static void fill_desc(const PackGeom& g, int profile, uint32_t flags, w4a16_desc* d) {
+    d->magic = W4A16_DESC_MAGIC;
+    d->version = W4A16_DESC_VERSION;
+    d->profile = profile;
+    d->flags = flags;
+    d->E = g.E;
+    d->N = g.N;
+    d->K = g.K;
+    d->group = 32;
+    d->chunk_n = g.CW;
+    d->reserved = 0;
+    d->codes_bytes = g.codes_bytes;
+    d->scales_offset = g.scales_offset;
+    d->bytes = g.bytes;
+}
+
+static w4a16_status prepack_common(int32_t profile, uint32_t flags, const int32_t* codes,
+                                   const uint16_t* scales, int32_t E, int32_t N, int32_t K,
+                                   int32_t group, void* packed, uint64_t packed_bytes,
+                                   w4a16_desc* desc, PackGeom* g, bool device) {
+    w4a16_status st = make_geom(profile, flags, E, N, K, group, g);
+    if (st != W4A16_OK) return st;
+    W4A16_CHECK_ARG(codes && scales && packed && desc, "null pointer argument to prepack");
+    W4A16_CHECK_ARG(!device || (reinterpret_cast<uintptr_t>(packed) & 255) == 0,
+                    "packed buffer must be 256-byte aligned");
+    W4A16_CHECK_ARG((reinterpret_cast<uintptr_t>(codes) & 3) == 0 &&
+                        (reinterpret_cast<uintptr_t>(scales) & 1) == 0,
+                    "codes/scales misaligned");
+    if ((flags & W4A16_PACK_GATE_UP_INTERLEAVE) && (N % 2 != 0)) {
+        set_error("gate/up interleave needs an even N");
+        return W4A16_ERR_UNSUPPORTED;
+    }
+    if (packed_bytes < g->bytes) {
+        set_error("packed buffer too small: %llu < %llu bytes",
+                  static_cast<unsigned long long>(packed_bytes),
+                  static_cast<unsigned long long>(g->bytes));
+        return W4A16_ERR_CAPACITY;
+    }
+    return W4A16_OK;
+}
+
+}  // namespace w4a16
+
+using namespace w4a16;
+
+extern "C" w4a16_status w4a16_prepack_bytes(int32_t profile, uint32_t flags, int32_t E,
+                                            int32_t N, int32_t K, int32_t group,
+                                            uint64_t* bytes) {
+    clear_error();
+    W4A16_CHECK_ARG(bytes, "null bytes pointer");
+    PackGeom g;
+    w4a16_status st = make_geom(profile, flags, E, N, K, group, &g);
+    if (st != W4A16_OK) return st;
+    *bytes = g.bytes;
+    return W4A16_OK;
+}
+
+extern "C" w4a16_status w4a16_prepack(int32_t profile, uint32_t flags, const int32_t* codes,
+                                      const uint16_t* scales, int32_t E, int32_t N, int32_t K,
+                                      int32_t group, void* packed, uint64_t packed_bytes,
+                                      w4a16_desc* desc, void* stream) {
+    clear_error();
+    PackGeom g;
+    w4a16_status st = prepack_common(profile, flags, codes, scales, E, N, K, group, packed,
+                                     packed_bytes, desc, &g, true);
+    if (st != W4A16_OK) return st;
+    launch_prepack(g, reinterpret_cast<const uint32_t*>(codes), scales, packed,
+                   static_cast<hipStream_t>(stream));
+    st = check_launch("prepack");
+    if (st != W4A16_OK) return st;
+    fill_desc(g, profile, flags, desc);
+    return W4A16_OK;
+}
+
+extern "C" w4a16_status w4a16_prepack_host(int32_t profile, uint32_t flags, const int32_t* codes,
+                                           const uint16_t* scales, int32_t E, int32_t N,
+                                           int32_t K, int32_t group, void* packed,
+                                           uint64_t packed_bytes, w4a16_desc* desc) {
+    clear_error();
+    PackGeom g;
+    w4a16_status st = prepack_common(profile, flags, codes, scales, E, N, K, group, packed,
+                                     packed_bytes, desc, &g, false);
+    if (st != W4A16_OK) return st;
+    prepack_host(g, reinterpret_cast<const uint32_t*>(codes), scales, packed);
+    fill_desc(g, profile, flags, desc);
+    return W4A16_OK;
+}
