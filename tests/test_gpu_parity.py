@@ -196,6 +196,31 @@ def test_gate_up_and_down_exact_invariant(m, tile_m, split, profile):
     assert np.array_equal(host(Y2, np.uint16)[pos], ref2[f])
 
 
+@pytest.mark.parametrize("H", [1024, 1056, 1248])    # 4 stages; 4 stages + 1 group; 5 - 7 groups
+@pytest.mark.parametrize("tile_m", [16, 32, 48, 64])
+@pytest.mark.parametrize("profile", [1, 2])
+def test_pipelined_main_loop_exact(m, H, tile_m, profile):
+    """The K loop's ring and LDS stages, for every active row-block count and
+    both chunk widths, bit-exact under the exactness invariant (about 67 rows
+    per expert, so tiles of 64 rows occur)."""
+    E, I, T, k = 3, 128, 100, 2
+    d = exact_problem(H + tile_m + profile, E, H, I, T, k)
+    print(f"main loop: H={H} tile_m={tile_m} profile={profile}", flush=True)
+    from w4a16_int4_mixture_amd import _capi
+    w13 = prepare(m, d["codes13"], d["scales13"], profile)     # H is K here: any multiple of 32
+    r = m.Routing(T, k, E, 16, tile_m, "cuda")
+    r.align(dev(d["topk_ids"]), E)
+    Y13 = torch.full((r.sorted_cap, 2 * I), -1, dtype=torch.int16, device="cuda")
+    m.run_gemm(m.gemm_args_indexed(w13, dev(d["X"]), r, Y13, _capi.W4A16_AROW_TOKEN, split_k=1,
+                                   rows_hint=T * k), "cuda")
+    torch.cuda.synchronize()
+    pos, f = slot_rows(r, T, k)
+    ref13 = oracle.moe_gate_up(d["X"], d["topk_ids"], E, None, d["codes13"], d["scales13"])
+    got = host(Y13, np.uint16)[pos]
+    bad = np.nonzero(np.any(got != ref13[f], axis=1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first positions {pos[bad[:8]]}"
+
+
 # --------------------------------------------------------- general inputs ----
 
 def run_indexed(m, d, E_global, profile, tile_m=0, split=0, rows_hint=None):

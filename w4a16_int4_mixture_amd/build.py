@@ -32,6 +32,7 @@ def hipcc() -> str:
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 
 

@@ -274,6 +274,8 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
         W4A16_CHECK_ARG(false, "unknown layout %d", a->layout);
     }
     g.split_k = r->split;
+    g.unpack_mask = 0x000F000Fu;
+    g.unpack_bits = 0x43004300u;
     r->reduce = r->split > 1;
     r->silu_separate = a->epilogue == W4A16_EPI_SILU_MUL && !r->reduce;
     r->ws_partial = r->reduce ? static_cast<uint64_t>(r->split) * r->rows_cap * d->N * 4 : 0;

@@ -92,12 +92,16 @@ __global__ void k_splitk_reduce(const float* __restrict__ ws, int S, int64_t str
     }
 }
 
-// One workgroup per token; each thread accumulates 8 consecutive columns.
-__global__ void k_combine(const uint16_t* __restrict__ y, int64_t y_rows, int H,
-                          const int32_t* __restrict__ row_of, const float* __restrict__ w,
-                          int top_k, uint16_t* __restrict__ out) {
+// grid (T, ceil(H / 512)), one wavefront per block; each lane accumulates 8
+// consecutive columns of one token.
+__global__ void __launch_bounds__(64) k_combine(const uint16_t* __restrict__ y, int64_t y_rows,
+                                                int H, const int32_t* __restrict__ row_of,
+                                                const float* __restrict__ w, int top_k,
+                                                uint16_t* __restrict__ out) {
     const int t = blockIdx.x;
-    for (int h = threadIdx.x * 8; h < H; h += blockDim.x * 8) {
+    {
+        const int h = (blockIdx.y * 64 + threadIdx.x) * 8;
+        if (h >= H) return;
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int j = 0; j < top_k; ++j) {
             const int r = row_of[static_cast<int64_t>(t) * top_k + j];
@@ -141,8 +145,7 @@ void launch_splitk_reduce(const float* ws, int split_k, int64_t ws_stride, int64
 
 void launch_combine(const uint16_t* y, int64_t y_rows, int H, const int32_t* row_of,
                     const float* w, int T, int top_k, uint16_t* out, hipStream_t s) {
-    int threads = H / 8 < 256 ? ((H / 8 + 63) / 64) * 64 : 256;
-    k_combine<<<dim3(T), dim3(threads), 0, s>>>(y, y_rows, H, row_of, w, top_k, out);
+    k_combine<<<dim3(T, (H + 511) / 512), dim3(64), 0, s>>>(y, y_rows, H, row_of, w, top_k, out);
 }
 
 }  // namespace w4a16

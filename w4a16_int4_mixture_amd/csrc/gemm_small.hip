@@ -47,25 +47,31 @@ __device__ inline uint16_t f32_to_bf16_rne(float x) {
 // B operand for one 16-column block: the word's eight codes as bf16 128 + q,
 // in MFMA K order (nibble order 0,2,4,6,1,3,5,7 puts offsets 2p and 2p+1 in
 // the two halves of (w >> 4p) & 0x000F000F).
-__device__ inline bf16x8 codes_to_b(uint32_t w) {
+// (x & mask) | bits: with mask and bits arriving as kernel arguments rather
+// than literals, the compiler emits a single v_and_or_b32 per pair.
+__device__ inline uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
+    return (x & mask) | bits;
+}
+
+__device__ inline bf16x8 codes_to_b(uint32_t w, uint32_t mask, uint32_t bits) {
     u32x4 d;
-    d.x = (w & 0x000F000Fu) | 0x43004300u;
-    d.y = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-    d.z = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-    d.w = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+    d.x = and_or(w, mask, bits);
+    d.y = and_or(w >> 4, mask, bits);
+    d.z = and_or(w >> 8, mask, bits);
+    d.w = and_or(w >> 12, mask, bits);
     return __builtin_bit_cast(bf16x8, d);
 }
 
-template <int MT, int WPL>
-struct Frag {
-    u32x4 w[WPL / 4];      // codes: WPL words
-    uint32_t s[WPL / 2];   // scales: WPL bf16
-    u32x4 a[MT];           // activation fragments
+// Codes and scales of one K group for one wavefront (WPL words + WPL scales
+// per lane).
+template <int WPL>
+struct WFrag {
+    u32x4 w[WPL / 4];
+    uint32_t s[WPL / 2];
 };
 
-template <int MT, int WPL>
-__device__ inline void load_frag(Frag<MT, WPL>& f, const uint32_t* cp, const uint16_t* sp,
-                                 const uint16_t* const* ap, int ks, int mt_active) {
+template <int WPL>
+__device__ inline void load_w(WFrag<WPL>& f, const uint32_t* cp, const uint16_t* sp, int ks) {
     const u32x4* c4 = reinterpret_cast<const u32x4*>(cp + static_cast<int64_t>(ks) * 64 * WPL);
 #pragma unroll
     for (int i = 0; i < WPL / 4; ++i) f.w[i] = __builtin_nontemporal_load(c4 + i);
@@ -81,24 +87,25 @@ __device__ inline void load_frag(Frag<MT, WPL>& f, const uint32_t* cp, const uin
         f.s[2] = v.z;
         f.s[3] = v.w;
     }
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-        if (t < mt_active) f.a[t] = *reinterpret_cast<const u32x4*>(ap[t] + ks * 32);
 }
 
+// One K group: MT row blocks x WPL column blocks; A fragments come from LDS.
 template <int MT, int WPL>
-__device__ inline void compute_frag(const Frag<MT, WPL>& f, f32x4 (&acc)[MT][WPL],
-                                    int mt_active) {
+__device__ inline void compute_group(const WFrag<WPL>& f, const u32x4* a_lds,
+                                     f32x4 (&acc)[MT][WPL], uint32_t mask, uint32_t bits) {
     const bf16x8 c136 = __builtin_bit_cast(bf16x8, u32x4{0xC308C308u, 0xC308C308u,
                                                          0xC308C308u, 0xC308C308u});  // -136
+    u32x4 av[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) av[t] = a_lds[t * 64];
     bf16x8 b[WPL];
     float sc[WPL];
 #pragma unroll
     for (int i = 0; i < WPL / 4; ++i) {
-        b[4 * i + 0] = codes_to_b(f.w[i].x);
-        b[4 * i + 1] = codes_to_b(f.w[i].y);
-        b[4 * i + 2] = codes_to_b(f.w[i].z);
-        b[4 * i + 3] = codes_to_b(f.w[i].w);
+        b[4 * i + 0] = codes_to_b(f.w[i].x, mask, bits);
+        b[4 * i + 1] = codes_to_b(f.w[i].y, mask, bits);
+        b[4 * i + 2] = codes_to_b(f.w[i].z, mask, bits);
+        b[4 * i + 3] = codes_to_b(f.w[i].w, mask, bits);
     }
 #pragma unroll
     for (int i = 0; i < WPL / 2; ++i) {
@@ -108,28 +115,120 @@ __device__ inline void compute_frag(const Frag<MT, WPL>& f, f32x4 (&acc)[MT][WPL
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-        if (t < mt_active) {
-            bf16x8 a = __builtin_bit_cast(bf16x8, f.a[t]);
-            f32x4 off = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, c136, zero, 0, 0, 0);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, av[t]);
+        const f32x4 off = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, c136, zero, 0, 0, 0);
 #pragma unroll
-            for (int j = 0; j < WPL; ++j) {
-                f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], off, 0, 0, 0);
-                acc[t][j] += sc[j] * d;
-            }
+        for (int j = 0; j < WPL; ++j) {
+            const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], off, 0, 0, 0);
+            acc[t][j] += sc[j] * d;
         }
     }
 }
 
+// Activation staging: a stage covers SG groups of K; its fragments (SG x MT,
+// 1 KB each: 64 lanes x 16 bytes in MFMA A-operand order) are loaded by the
+// four wavefronts of the workgroup (wavefront w takes the groups g = w mod 4)
+// and read by all of them from LDS.
+constexpr int kSG = 8;
+
+template <int MT>
+struct AStage {
+    u32x4 v[kSG / 4][MT];
+};
+
+template <int MT>
+__device__ inline void load_a_stage(AStage<MT>& st, const uint16_t* const* ap, int ks_stage,
+                                    int ks_min, int wave) {
+#pragma unroll
+    for (int i = 0; i < kSG / 4; ++i) {
+        int g = ks_stage + 4 * i + wave;
+        g = g < ks_min ? ks_min : g;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) st.v[i][t] = *reinterpret_cast<const u32x4*>(ap[t] + g * 32);
+    }
+}
+
+template <int MT>
+__device__ inline void store_a_stage(const AStage<MT>& st, u32x4* buf, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < kSG / 4; ++i)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) buf[((4 * i + wave) * MT + t) * 64 + lane] = st.v[i][t];
+}
+
 }  // namespace
 
-// One (row tile, column chunk, K split) of the GEMM for this wavefront.
+// The K loop of one workgroup tile with MT active 16-row blocks.  Weights and
+// scales run through a register ring kSG groups deep (one 16-byte code load
+// per WPL/4 words per group, issued kSG groups ahead); activations are staged
+// through LDS one stage ahead, double-buffered, one barrier per stage.  The
+// first (K range mod kSG) groups are done before the ring starts.
 template <int MT, int WPL>
-__device__ void gemm_tile(const GemmArgs& a, int e, int p0, int nrows, int chunk, int lane) {
-    constexpr int D = 4;  // groups of K kept in flight per wavefront
-    const int mt_active = (nrows + 15) >> 4;
-    const bool slot_rows = a.tile_src != TILE_MASKED;
+__device__ void stream_loop(const uint32_t* cp, const uint16_t* sp, const uint16_t* const* ap,
+                            int ks0, int ks1, int wave, int lane, u32x4* lds,
+                            f32x4 (&acc)[MT][WPL], uint32_t mask, uint32_t bits) {
+    constexpr int D = kSG;
+    if (ks1 <= ks0) return;
+    u32x4* buf0 = lds;
+    u32x4* buf1 = lds + kSG * MT * 64;
+    // Stages are aligned to the end of the K range: the first stage starts
+    // `pad` groups early; those slots re-read group ks0 and have their scales
+    // zeroed, so they add exactly zero.  Every stage then runs the same code.
+    const int pad = (kSG - (ks1 - ks0) % kSG) % kSG;
+    const int kb = ks0 - pad;
+    const int nst = (ks1 - kb) / kSG;
 
-    // ---- activation row of each of this lane's MFMA A rows
+    // first activation stage is issued before the weight ring so that storing
+    // it to LDS does not wait for the ring's loads
+    WFrag<WPL> ring[D];
+    {
+        AStage<MT> a0;
+        load_a_stage<MT>(a0, ap, kb, ks0, wave);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            load_w<WPL>(ring[i], cp, sp, kb + i < ks0 ? ks0 : kb + i);
+            if (kb + i < ks0) {
+#pragma unroll
+                for (int j = 0; j < WPL / 2; ++j) ring[i].s[j] = 0u;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        store_a_stage<MT>(a0, buf0, wave, lane);
+    }
+    __syncthreads();
+    for (int st = 0; st < nst - 1; ++st) {
+        u32x4* cur = (st & 1) ? buf1 : buf0;
+        u32x4* nxt = (st & 1) ? buf0 : buf1;
+        const int base = kb + st * kSG;
+        AStage<MT> an;
+        load_a_stage<MT>(an, ap, base + kSG, ks0, wave);
+        __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads ahead of the ring refills
+#pragma unroll
+        for (int g = 0; g < kSG; ++g) {
+            compute_group<MT, WPL>(ring[g], cur + g * MT * 64 + lane, acc, mask, bits);
+            load_w<WPL>(ring[g], cp, sp, base + kSG + g);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        store_a_stage<MT>(an, nxt, wave, lane);
+        __syncthreads();
+    }
+    {
+        u32x4* cur = ((nst - 1) & 1) ? buf1 : buf0;
+#pragma unroll
+        for (int g = 0; g < kSG; ++g) compute_group<MT, WPL>(ring[g], cur + g * MT * 64 + lane, acc, mask, bits);
+    }
+}
+
+// One (row tile, 4 column chunks, K split) with MT active row blocks.
+template <int MT, int WPL>
+__device__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, int nrows, int chunk, int wave,
+                             int lane, u32x4* lds) {
+    const bool slot_rows = a.tile_src != TILE_MASKED;
+    const bool active = chunk < a.NC;
+
+    // activation row of each of this lane's MFMA A rows (rows past the tile
+    // reuse its first row: MFMA rows are independent and are not stored)
     const uint16_t* ap[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
@@ -146,11 +245,13 @@ __device__ void gemm_tile(const GemmArgs& a, int e, int p0, int nrows, int chunk
         ap[t] = a.A + row * a.K + 8 * (lane >> 4);
     }
 
-    // ---- K range of this split
     const int s = blockIdx.z;
     const int ks0 = static_cast<int>(static_cast<int64_t>(s) * a.KS / a.split_k);
     const int ks1 = static_cast<int>(static_cast<int64_t>(s + 1) * a.KS / a.split_k);
-    const int64_t cbase = static_cast<int64_t>(e) * a.NC + chunk;
+    // a wavefront past the last chunk re-streams the last chunk (cache hits,
+    // only when N / CW is not a multiple of 4) and stores nothing: the loop
+    // stays free of wavefront-dependent branches
+    const int64_t cbase = static_cast<int64_t>(e) * a.NC + (active ? chunk : a.NC - 1);
     const uint32_t* cp = a.codes + (cbase * a.KS) * 64 * WPL + lane * WPL;
     const uint16_t* sp = a.scales + (cbase * a.KS) * 16 * WPL + (lane & 15) * WPL;
 
@@ -159,26 +260,18 @@ __device__ void gemm_tile(const GemmArgs& a, int e, int p0, int nrows, int chunk
     for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int j = 0; j < WPL; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the exponent pattern lives in a VGPR so that (x & mask) | bits is one
+    // v_and_or_b32 (a VALU op reads at most one scalar operand); the empty asm
+    // only pins the register class and emits nothing
+    uint32_t vbits = a.unpack_bits;
+    asm volatile("" : "+v"(vbits));
+    stream_loop<MT, WPL>(cp, sp, ap, ks0, ks1, wave, lane, lds, acc, a.unpack_mask, vbits);
+    if (!active) return;
 
-    Frag<MT, WPL> fr[D];
-#pragma unroll
-    for (int i = 0; i < D; ++i)
-        if (ks0 + i < ks1) load_frag<MT, WPL>(fr[i], cp, sp, ap, ks0 + i, mt_active);
-    for (int ks = ks0; ks < ks1; ks += D) {
-#pragma unroll
-        for (int i = 0; i < D; ++i) {
-            if (ks + i < ks1) {
-                compute_frag<MT, WPL>(fr[i], acc, mt_active);
-                if (ks + i + D < ks1) load_frag<MT, WPL>(fr[i], cp, sp, ap, ks + i + D, mt_active);
-            }
-        }
-    }
-
-    // ---- epilogue: lane holds rows 16t + 4*(lane/16) + i of column 16j + lane%16
+    // epilogue: lane holds rows 16t + 4*(lane/16) + i of column 16j + lane%16
     const int col0 = chunk * a.CW + (lane & 15);
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-        if (t >= mt_active) continue;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * t + 4 * (lane >> 4) + i;
@@ -203,14 +296,25 @@ __device__ void gemm_tile(const GemmArgs& a, int e, int p0, int nrows, int chunk
     }
 }
 
+template <int MT, int WPL>
+__device__ void gemm_tile(const GemmArgs& a, int e, int p0, int nrows, int chunk, int wave,
+                          int lane, u32x4* lds) {
+    const int mt_active = (nrows + 15) >> 4;
+    if (mt_active <= 1) gemm_tile_mt<1, WPL>(a, e, p0, nrows, chunk, wave, lane, lds);
+    else if (MT >= 2 && mt_active == 2) gemm_tile_mt<(MT >= 2 ? 2 : 1), WPL>(a, e, p0, nrows, chunk, wave, lane, lds);
+    else if (MT >= 3 && mt_active == 3) gemm_tile_mt<(MT >= 3 ? 3 : 1), WPL>(a, e, p0, nrows, chunk, wave, lane, lds);
+    else if (MT >= 4) gemm_tile_mt<(MT >= 4 ? 4 : 1), WPL>(a, e, p0, nrows, chunk, wave, lane, lds);
+}
+
 // Tiles are walked grid-stride along grid.y, so any device-side tile count is
 // fully covered whatever the grid size; every wavefront leaves the loop once
 // its tile index passes the count.
 template <int MT, int WPL>
 __global__ void __launch_bounds__(256) k_gemm_small(GemmArgs a) {
+    __shared__ u32x4 lds[2 * kSG * MT * 64];
     const int lane = threadIdx.x & 63;
-    const int chunk = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (chunk >= a.NC) return;
+    const int wave = threadIdx.x >> 6;
+    const int chunk = blockIdx.x * 4 + wave;
     for (int ty = blockIdx.y;; ty += gridDim.y) {
         int e, p0, nrows;
         if (a.tile_src == TILE_TABLE) {
@@ -235,7 +339,8 @@ __global__ void __launch_bounds__(256) k_gemm_small(GemmArgs a) {
             nrows = cnt - r0 < a.tile_m ? cnt - r0 : a.tile_m;
         }
         if (e < 0 || e >= a.E || nrows <= 0) continue;
-        gemm_tile<MT, WPL>(a, e, p0, nrows, chunk, lane);
+        gemm_tile<MT, WPL>(a, e, p0, nrows, chunk, wave, lane, lds);
+        __syncthreads();  // the next tile reuses the staging buffers
     }
 }
 

@@ -106,6 +106,8 @@ struct GemmArgs {
     int out_kind;
     int split_k;
     int64_t ws_stride;  // elements between split partials (OUT_PARTIAL)
+    uint32_t unpack_mask;  // 0x000F000F: one code in each 16-bit half
+    uint32_t unpack_bits;  // 0x43004300: bf16 exponent of 128 in each half
 };
 void launch_gemm_small(const GemmArgs& a, int mt, hipStream_t s);
 
