@@ -103,15 +103,19 @@ typedef struct {
     int32_t K;               /* reduction length (H for W13, I for W2) */
     int32_t group;           /* always 32 */
     int32_t chunk_n;         /* output columns per packed wavefront chunk */
-    int32_t reserved;
-    uint64_t codes_bytes;    /* bytes of packed codes at offset 0 */
-    uint64_t scales_offset;  /* byte offset of the packed scales */
+    int32_t k_groups;        /* K/32 rounded up to a multiple of 8 (padding groups are zero) */
+    uint64_t stage_bytes;    /* bytes of one 8-group record of one chunk (codes then scales) */
+    uint64_t chunk_bytes;    /* bytes of one chunk over all of K */
     uint64_t bytes;          /* total bytes of the packed buffer */
 } w4a16_desc;
 
 /* Size of the packed buffer for a profile and shape (host call, no GPU).
  * UNSUPPORTED if group != 32, K % 32 != 0 or N is not a multiple of the
- * profile's chunk width (64 DECODE, 128 PREFILL). */
+ * profile's chunk width (64 DECODE, 128 PREFILL).
+ * Layout: for each expert and each chunk of chunk_n packed output columns,
+ * K is cut into records of 8 groups of 32; a record holds the chunk's codes
+ * for those groups (lane-major, in MFMA operand order) followed by their
+ * scales, so one wavefront streams one contiguous region. */
 w4a16_status w4a16_prepack_bytes(int32_t profile, uint32_t flags, int32_t E, int32_t N,
                                  int32_t K, int32_t group, uint64_t* bytes /* host out */);
 
@@ -224,7 +228,9 @@ typedef struct {
     uint32_t flags;                 /* W4A16_GEMM_* */
     int32_t split_k;                /* 0 = automatic; >1 forces K splits (INDEXED
                                        only: MASKED rejects it, MODE_MISMATCH) */
-    const uint16_t* A;              /* device bf16 activations, [A_rows, K] */
+    const uint16_t* A;              /* device bf16 activations, [A_rows, K];
+                                       A_rows * K * 2 bytes must stay below
+                                       4 GiB (else UNSUPPORTED) */
     int64_t A_rows;
     /* INDEXED */
     int32_t arow;                   /* w4a16_arow */

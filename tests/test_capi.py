@@ -92,7 +92,10 @@ def status_of(fn, *a):
 
 def test_prepack_bytes_rejects_unsupported_schemes():
     P = capi.W4A16_PROFILE_DECODE
+    # codes + scales exactly, K in whole records of 8 groups (7168 = 28 records)
     assert capi.w4a16_prepack_bytes(P, 0, 48, 4096, 7168, 32) == 48 * 4096 * 7168 // 2 + 48 * 4096 * 224 * 2
+    # K = 96: 3 groups padded to one record of 8
+    assert capi.w4a16_prepack_bytes(P, 0, 1, 64, 96, 32) == 64 * 256 // 2 + 64 * 8 * 2
     assert status_of(capi.w4a16_prepack_bytes, P, 0, 1, 64, 64, 64) == capi.W4A16_ERR_UNSUPPORTED
     assert status_of(capi.w4a16_prepack_bytes, P, 0, 1, 64, 48, 32) == capi.W4A16_ERR_UNSUPPORTED
     assert status_of(capi.w4a16_prepack_bytes, P, 0, 1, 96, 64, 32) == capi.W4A16_ERR_UNSUPPORTED
@@ -180,8 +183,11 @@ def test_gemm_argument_checks():
     assert ws_status(gemm_args(d, **{**m, "expected_m": 0})) == capi.W4A16_ERR_INVALID_ARG
     assert ws_status(gemm_args(d, **{**m, "split_k": 2})) == capi.W4A16_ERR_MODE_MISMATCH
     assert ws_status(gemm_args(d, **{**m, "A_rows": 10})) == capi.W4A16_ERR_CAPACITY
+    # K splits are whole 8-group records: one record cannot be split
+    assert capi.w4a16_gemm_workspace_bytes(gemm_args(d, split_k=2)) == 0
     # launching with a too-small workspace fails before the launch
-    a = gemm_args(d, split_k=2)
+    d512 = host_desc(K=512)
+    a = gemm_args(d512, split_k=2)
     assert capi.w4a16_gemm_workspace_bytes(a) == 2 * 256 * 128 * 4
     assert capi.lib().w4a16_moe_w4a16_gemm(ctypes.byref(a), None) == capi.W4A16_ERR_CAPACITY
 
@@ -200,24 +206,29 @@ def test_combine_and_silu_checks():
 
 def decode_packed(packed, desc):
     """Read the packed buffer back into canonical codes and scales, from the
-    layout as documented in the library (codes lane-major per K group, nibble i
-    holding K offset 2*(i%4) + i/4; scales [chunk][group][16][CW/16])."""
+    layout as documented in the library: per expert and chunk, records of 8
+    groups, each = codes [8][64 lanes][CW/16 words] (nibble i holding K offset
+    2*(i%4) + i/4) followed by scales [8][16][CW/16] bf16; padding groups zero."""
     E, N, K, CW = desc.E, desc.N, desc.K, desc.chunk_n
-    NC, KS, WPL = N // CW, K // 32, CW // 16
-    words = packed[: desc.codes_bytes].view(np.uint32).reshape(E, NC, KS, 4, 16, WPL)
-    # axes: e, chunk, ks, lane//16 (K octet), lane%16 (column in block), j (block)
+    NC, KS, WPL, KSP = N // CW, K // 32, CW // 16, desc.k_groups
+    rec = packed.view(np.uint32).reshape(E, NC, KSP // 8, 576 * WPL)
+    words = rec[..., : 512 * WPL].reshape(E, NC, KSP // 8, 8, 4, 16, WPL)
+    # axes: e, chunk, record, group-in-record, K octet (lane//16), lane%16, block j
     off = np.array([2 * (i % 4) + i // 4 for i in range(8)])
-    nib = (words[..., None] >> (4 * np.arange(8, dtype=np.uint32))) & 0xF   # [..., i]
+    nib = (words[..., None] >> (4 * np.arange(8, dtype=np.uint32))) & 0xF
     q = np.zeros(nib.shape, np.uint32)
-    q[..., off] = nib                                                        # -> K offset order
-    # -> [e, chunk, j, c16, ks, octet, 8]
-    q = q.transpose(0, 1, 5, 4, 2, 3, 6).reshape(E, N, K)
+    q[..., off] = nib                                       # -> K offset order
+    # -> [e, chunk, j, c16, record, group, octet, 8]
+    q = q.transpose(0, 1, 6, 5, 2, 3, 4, 7).reshape(E, N, KSP * 32)
+    assert not q[:, :, K:].any()                            # padding codes are zero
+    q = q[:, :, :K]
     codes = np.zeros((E, N, K // 8), np.uint32)
     for o in range(8):
         codes |= q[:, :, o::8] << (4 * o)
-    sc = packed[desc.scales_offset: desc.scales_offset + E * N * KS * 2].view(np.uint16)
-    sc = sc.reshape(E, NC, KS, 16, WPL).transpose(0, 1, 4, 3, 2).reshape(E, N, KS)
-    return codes.view(np.int32), sc
+    sc = np.ascontiguousarray(rec[..., 512 * WPL:]).view(np.uint16)
+    sc = sc.reshape(E, NC, KSP // 8, 8, 16, WPL).transpose(0, 1, 5, 4, 2, 3).reshape(E, N, KSP)
+    assert not sc[:, :, KS:].any()                          # padding scales are zero
+    return codes.view(np.int32), sc[:, :, :KS]
 
 
 @pytest.mark.parametrize("profile,flags", [(capi.W4A16_PROFILE_DECODE, 0),

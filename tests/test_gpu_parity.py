@@ -79,10 +79,7 @@ def test_prepack_device_equals_host(m, profile, flags):
     torch.cuda.synchronize()
     ref = np.zeros(w.desc.bytes, np.uint8)
     _capi.w4a16_prepack_host(profile, flags, codes, scales, E, N, K, 32, ref)
-    got = host(w.packed)
-    assert np.array_equal(got[: w.desc.codes_bytes], ref[: w.desc.codes_bytes])
-    so = w.desc.scales_offset
-    assert np.array_equal(got[so: so + E * N * (K // 32) * 2], ref[so: so + E * N * (K // 32) * 2])
+    assert np.array_equal(host(w.packed), ref)
 
 
 # ------------------------------------------------------------------ routing ----

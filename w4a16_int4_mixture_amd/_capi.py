@@ -51,8 +51,8 @@ class w4a16_desc(ctypes.Structure):
                 ("profile", ctypes.c_int32), ("flags", ctypes.c_uint32),
                 ("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("chunk_n", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("codes_bytes", ctypes.c_uint64),
-                ("scales_offset", ctypes.c_uint64), ("bytes", ctypes.c_uint64)]
+                ("k_groups", ctypes.c_int32), ("stage_bytes", ctypes.c_uint64),
+                ("chunk_bytes", ctypes.c_uint64), ("bytes", ctypes.c_uint64)]
 
 
 class w4a16_routing(ctypes.Structure):

@@ -55,7 +55,8 @@ __device__ int32_t g_routing_errors;
 // enough wavefronts to keep every CU streaming (shape-aware split-K gating),
 // but never below 8 groups of K per split.
 
-static int choose_split(int64_t tiles_est, int64_t rows_est, int NC, int KS, int N,
+// K splits are whole 8-group records; every split keeps at least 2 records.
+static int choose_split(int64_t tiles_est, int64_t rows_est, int NC, int stages, int N,
                         int64_t weight_bytes) {
     const int64_t target_waves = 4096;       // ~1.3 rounds of 3 wavefronts per SIMD
     const int64_t waves = tiles_est * NC;
@@ -63,7 +64,7 @@ static int choose_split(int64_t tiles_est, int64_t rows_est, int NC, int KS, int
     // under a quarter of the weight stream
     const int64_t partial_bytes = std::max<int64_t>(rows_est, 1) * N * 8;
     int split = 1;
-    while (waves * split < target_waves && KS / (split * 2) >= 8 &&
+    while (waves * split < target_waves && stages / (split * 2) >= 2 &&
            partial_bytes * (split * 2) <= weight_bytes / 4)
         split *= 2;
     return split;
@@ -72,7 +73,7 @@ static int choose_split(int64_t tiles_est, int64_t rows_est, int NC, int KS, int
 static w4a16_status plan_impl(const w4a16_desc* d, int layout, int rows_hint, int expected_m,
                               int tile_m_in, w4a16_plan* p) {
     const int E = d->E;
-    const int KS = d->K / 32;
+    const int stages = d->k_groups / 8;
     const int NC = d->N / d->chunk_n;
     int tile_m;
     int64_t tiles_est;
@@ -102,8 +103,8 @@ static w4a16_status plan_impl(const w4a16_desc* d, int layout, int rows_hint, in
                                  ? static_cast<int64_t>(E) * expected_m
                                  : std::max<int64_t>(rows_hint, E);
     const int64_t active = std::min<int64_t>(E, std::max<int64_t>(tiles_est, 1));
-    const int64_t weight_bytes = active * static_cast<int64_t>(d->N) * d->K * 17 / 32;
-    p->split_k = choose_split(tiles_est, rows_est, NC, KS, d->N, weight_bytes);
+    const int64_t weight_bytes = active * static_cast<int64_t>(d->N) * d->K * 18 / 32;
+    p->split_k = choose_split(tiles_est, rows_est, NC, stages, d->N, weight_bytes);
     return W4A16_OK;
 }
 
@@ -148,15 +149,22 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
     GemmArgs& g = r->g;
     g = GemmArgs{};
     g.A = a->A;
-    g.codes = static_cast<const uint32_t*>(a->packed);
-    g.scales = reinterpret_cast<const uint16_t*>(static_cast<const char*>(a->packed) + d->scales_offset);
+    g.packed = static_cast<const uint32_t*>(a->packed);
+    g.stage_words = static_cast<int64_t>(d->stage_bytes / 4);
+    g.chunk_words = static_cast<int64_t>(d->chunk_bytes / 4);
     g.N = d->N;
     g.K = d->K;
     g.CW = d->chunk_n;
     g.NC = d->N / d->chunk_n;
     g.KS = d->K / 32;
+    g.KSP = d->k_groups;
     g.E = d->E;
     W4A16_CHECK_ARG(a->A_rows >= 1, "A_rows must be positive");
+    if (static_cast<uint64_t>(a->A_rows) * static_cast<uint64_t>(d->K) * 2 > 0xFFFFFFFFull) {
+        set_error("activations of %lld x %d bf16 exceed the 4 GiB a kernel addresses",
+                  static_cast<long long>(a->A_rows), d->K);
+        return W4A16_ERR_UNSUPPORTED;
+    }
     g.A_rows = a->A_rows;
 
     w4a16_plan plan;
@@ -191,7 +199,7 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
         if (st != W4A16_OK) return st;
         int split = a->split_k > 0 ? a->split_k : plan.split_k;
         if (a->orow == W4A16_OROW_SLOT || f32_out) split = 1;
-        split = std::max(1, std::min(split, g.KS));
+        split = std::max(1, std::min(split, g.KSP / 8));
         {
             const int64_t need_a = a->arow == W4A16_AROW_POSITION ? a->sorted_cap
                                    : a->arow == W4A16_AROW_SLOT   ? a->num_slots
@@ -268,7 +276,7 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
         g.grid_tiles = std::min(g.grid_tiles_total, 65535);
         int split = f32_out ? 1 : plan.split_k;
         r->mt = plan.tile_m / 16;
-        r->split = std::max(1, std::min(split, g.KS));
+        r->split = std::max(1, std::min(split, g.KSP / 8));
         r->rows_cap = rows;
     } else {
         W4A16_CHECK_ARG(false, "unknown layout %d", a->layout);

@@ -1,5 +1,5 @@
-// Grouped W4A16 GEMM for few routed rows per expert (decode-sized tiles of at
-// most 16*MT rows): a weight-streaming kernel for CDNA4.
+// Grouped W4A16 GEMM for few routed rows per expert (tiles of at most 16*MT
+// rows): a weight-streaming kernel for CDNA4.
 //
 //   out[p, n] = sum_c A[row(p), c] * (q[e,n,c] - 8) * s[e,n,c/32]
 //
@@ -10,21 +10,27 @@
 // TP8": deep-K gate/up keeps a split of K (stream-K) where the M x N grid
 // alone cannot fill the machine.
 //
-// CDNA4 design (one wavefront = one packed chunk of CW output columns over a
-// K range; four wavefronts per workgroup on neighbouring chunks of one tile):
-//   * every lane fetches its codes for one K group of 32 with 16-byte loads
-//     (CW/16 words) and its CW/16 group scales: the packed layout makes each
-//     wavefront's stream contiguous, and a ring of D groups is kept in flight;
-//   * the activation fragments (8 bf16 per lane per 16-row M tile) come
-//     straight from L2 (the activations are small and shared by every chunk);
-//   * a code q becomes the bf16 value 128 + q by OR-ing the exponent pattern
-//     0x43 above it, two codes per VALU op; v_mfma_f32_16x16x32_bf16 (K = 32 =
-//     one scale group) then yields P = sum x (128 + q); the offset
-//     -136 * sum x is produced once per M tile by one MFMA against a constant
-//     operand and fed as the accumulator input, so the MFMA returns
-//     sum x (q - 8) exactly as the group's partial; the fp32 group scale is
-//     applied with one FMA per accumulator element.  Weights are never
-//     rounded: the products and the within-group sums are exact.
+// CDNA4 design.  A workgroup is four wavefronts on four neighbouring packed
+// chunks of CW output columns of one row tile, over one K range.
+//   * Codes: every lane fetches its CW/16 words of a K group with 16-byte
+//     non-temporal loads; the packed layout makes each wavefront's stream
+//     contiguous.  A register ring keeps D groups of codes in flight (64
+//     VGPRs), refilled as each group is consumed.
+//   * Activations and scales are staged through LDS, one stage (8 groups)
+//     ahead, double-buffered, one barrier per stage: each wavefront loads a
+//     quarter of the stage's activation fragments (shared by all four) and
+//     its own chunk's scales for the stage (one 16-byte load per lane); the
+//     fragments are read back in MFMA A-operand order (conflict-free).
+//   * A code q becomes the bf16 value 128 + q by OR-ing the exponent pattern
+//     0x43 above it, two codes per v_and_or_b32; v_mfma_f32_16x16x32_bf16 (K
+//     = 32 = one scale group) yields sum x (128 + q); the offset -136 sum x is
+//     produced once per row block by one MFMA against a constant operand and
+//     fed in as the accumulator input, so the MFMA returns the exact group
+//     partial sum x (q - 8); the fp32 group scale is applied with one FMA per
+//     accumulator element.  Weights are never rounded.
+//   * The loop is branch-free: K ranges are aligned to the end of the ring;
+//     leading slots before the range re-read its first group with zeroed
+//     scales (they add exactly zero).
 
 #include "internal.h"
 
@@ -37,22 +43,22 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-__device__ inline float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+constexpr int kSG = 8;  // groups of K per LDS stage
 
 __device__ inline uint16_t f32_to_bf16_rne(float x) {
     __bf16 h = static_cast<__bf16>(x);
     return __builtin_bit_cast(uint16_t, h);
 }
 
-// B operand for one 16-column block: the word's eight codes as bf16 128 + q,
-// in MFMA K order (nibble order 0,2,4,6,1,3,5,7 puts offsets 2p and 2p+1 in
-// the two halves of (w >> 4p) & 0x000F000F).
-// (x & mask) | bits: with mask and bits arriving as kernel arguments rather
-// than literals, the compiler emits a single v_and_or_b32 per pair.
+// (x & mask) | bits: mask and bits arrive as kernel arguments (bits pinned in
+// a VGPR), so the compiler emits one v_and_or_b32 per bf16 pair.
 __device__ inline uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
     return (x & mask) | bits;
 }
 
+// B operand of one 16-column block: the word's eight codes as bf16 128 + q in
+// MFMA K order (the packed nibble order 0,2,4,6,1,3,5,7 puts K offsets 2p and
+// 2p+1 in the two 16-bit halves of (w >> 4p) & 0x000F000F).
 __device__ inline bf16x8 codes_to_b(uint32_t w, uint32_t mask, uint32_t bits) {
     u32x4 d;
     d.x = and_or(w, mask, bits);
@@ -62,166 +68,289 @@ __device__ inline bf16x8 codes_to_b(uint32_t w, uint32_t mask, uint32_t bits) {
     return __builtin_bit_cast(bf16x8, d);
 }
 
-// Codes and scales of one K group for one wavefront (WPL words + WPL scales
-// per lane).
+// Codes of one K group for one lane.
 template <int WPL>
-struct WFrag {
+struct Codes {
     u32x4 w[WPL / 4];
-    uint32_t s[WPL / 2];
 };
 
-template <int WPL>
-__device__ inline void load_w(WFrag<WPL>& f, const uint32_t* cp, const uint16_t* sp, int ks) {
-    const u32x4* c4 = reinterpret_cast<const u32x4*>(cp + static_cast<int64_t>(ks) * 64 * WPL);
-#pragma unroll
-    for (int i = 0; i < WPL / 4; ++i) f.w[i] = __builtin_nontemporal_load(c4 + i);
-    const uint16_t* s = sp + static_cast<int64_t>(ks) * 16 * WPL;
-    if constexpr (WPL == 4) {
-        u32x2 v = *reinterpret_cast<const u32x2*>(s);
-        f.s[0] = v.x;
-        f.s[1] = v.y;
-    } else {
-        u32x4 v = *reinterpret_cast<const u32x4*>(s);
-        f.s[0] = v.x;
-        f.s[1] = v.y;
-        f.s[2] = v.z;
-        f.s[3] = v.w;
-    }
+// Buffer loads address the packed chunk and the activations with a scalar
+// resource and a 32-bit per-lane offset; the K position goes into the scalar
+// offset, so the loop does no per-lane address arithmetic.  Reads past a
+// resource's size return zero.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint64_t bytes) {
+    const uint32_t n = bytes < 0xFFFFFFFFull ? static_cast<uint32_t>(bytes) : 0xFFFFFFFFu;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(n),
+                                             0x00020000);
 }
 
-// One K group: MT row blocks x WPL column blocks; A fragments come from LDS.
-template <int MT, int WPL>
-__device__ inline void compute_group(const WFrag<WPL>& f, const u32x4* a_lds,
-                                     f32x4 (&acc)[MT][WPL], uint32_t mask, uint32_t bits) {
-    const bf16x8 c136 = __builtin_bit_cast(bf16x8, u32x4{0xC308C308u, 0xC308C308u,
-                                                         0xC308C308u, 0xC308C308u});  // -136
-    u32x4 av[MT];
+constexpr int kNonTemporal = 2;  // cache-policy bits of a streaming load
+
+// Where one wavefront reads: its packed chunk, the activations, and this
+// lane's byte offsets into them.
+template <int MT>
+struct Src {
+    __amdgpu_buffer_rsrc_t w;  // the packed chunk (records of codes + scales)
+    __amdgpu_buffer_rsrc_t x;  // activations [A_rows, K] bf16
+    uint32_t code_off;         // lane * WPL words
+    uint32_t a_off[MT];        // row of MFMA A row block t, K offset 8 * (lane / 16)
+};
+
+// Codes of group ks (record ks / 8, slot ks % 8) for this lane; lane_off =
+// lane * WPL words, in bytes.
+template <int WPL>
+__device__ inline void load_codes(Codes<WPL>& c, __amdgpu_buffer_rsrc_t w, uint32_t lane_off,
+                                  int ks) {
+    const int soff = ((ks >> 3) * (576 * WPL) + (ks & 7) * (64 * WPL)) * 4;
 #pragma unroll
-    for (int t = 0; t < MT; ++t) av[t] = a_lds[t * 64];
+    for (int i = 0; i < WPL / 4; ++i)
+        c.w[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(w, lane_off + 16 * i, soff, kNonTemporal));
+}
+
+// One K group is processed in three phases so that consecutive groups overlap:
+//   prep : read the A fragments and scales from LDS, unpack the codes
+//   mfma : offset MFMA, then one MFMA per 16-column block (C = offset)
+//   fma  : acc += scale * partial
+// The loop issues mfma(g), then prep(g + 1) while those MFMAs run, then fma(g).
+template <int MT, int WPL>
+struct Prep {
     bf16x8 b[WPL];
     float sc[WPL];
+    u32x4 av[MT];
+};
+
+template <int MT, int WPL>
+__device__ inline void prep_group(Prep<MT, WPL>& p, const Codes<WPL>& c, const u32x4* a_lds,
+                                  const uint16_t* s_lds, uint32_t mask, uint32_t bits) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) p.av[t] = a_lds[t * 64];
+    uint32_t sw[WPL / 2];
+    if constexpr (WPL == 4) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(s_lds);
+        sw[0] = v.x;
+        sw[1] = v.y;
+    } else {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(s_lds);
+        sw[0] = v.x;
+        sw[1] = v.y;
+        sw[2] = v.z;
+        sw[3] = v.w;
+    }
 #pragma unroll
     for (int i = 0; i < WPL / 4; ++i) {
-        b[4 * i + 0] = codes_to_b(f.w[i].x, mask, bits);
-        b[4 * i + 1] = codes_to_b(f.w[i].y, mask, bits);
-        b[4 * i + 2] = codes_to_b(f.w[i].z, mask, bits);
-        b[4 * i + 3] = codes_to_b(f.w[i].w, mask, bits);
+        p.b[4 * i + 0] = codes_to_b(c.w[i].x, mask, bits);
+        p.b[4 * i + 1] = codes_to_b(c.w[i].y, mask, bits);
+        p.b[4 * i + 2] = codes_to_b(c.w[i].z, mask, bits);
+        p.b[4 * i + 3] = codes_to_b(c.w[i].w, mask, bits);
     }
 #pragma unroll
     for (int i = 0; i < WPL / 2; ++i) {
-        sc[2 * i] = __uint_as_float(f.s[i] << 16);
-        sc[2 * i + 1] = __uint_as_float(f.s[i] & 0xFFFF0000u);
+        p.sc[2 * i] = __uint_as_float(sw[i] << 16);
+        p.sc[2 * i + 1] = __uint_as_float(sw[i] & 0xFFFF0000u);
     }
+}
+
+// Orders the unpack of a ring slot before the load that refills it (the
+// scheduler may otherwise sink the unpack below the load, after which old and
+// new codes need separate registers and the loop ends in copies that wait for
+// the newest loads).  Emits nothing.
+template <int MT, int WPL>
+__device__ inline void unpacked(const Prep<MT, WPL>& p) {
+#pragma unroll
+    for (int j = 0; j < WPL; ++j) asm volatile("" ::"v"(p.b[j]));
+}
+
+template <int MT, int WPL>
+__device__ inline void mfma_group(const Prep<MT, WPL>& p, f32x4 (&d)[MT][WPL]) {
+    const bf16x8 c136 = __builtin_bit_cast(bf16x8, u32x4{0xC308C308u, 0xC308C308u,
+                                                         0xC308C308u, 0xC308C308u});  // -136
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, av[t]);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, p.av[t]);
         const f32x4 off = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, c136, zero, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < WPL; ++j) {
-            const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], off, 0, 0, 0);
-            acc[t][j] += sc[j] * d;
-        }
+        for (int j = 0; j < WPL; ++j)
+            d[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p.b[j], off, 0, 0, 0);
     }
 }
 
-// Activation staging: a stage covers SG groups of K; its fragments (SG x MT,
-// 1 KB each: 64 lanes x 16 bytes in MFMA A-operand order) are loaded by the
-// four wavefronts of the workgroup (wavefront w takes the groups g = w mod 4)
-// and read by all of them from LDS.
-constexpr int kSG = 8;
+template <int MT, int WPL>
+__device__ inline void fma_group(const Prep<MT, WPL>& p, const f32x4 (&d)[MT][WPL],
+                                 f32x4 (&acc)[MT][WPL]) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int j = 0; j < WPL; ++j) acc[t][j] += p.sc[j] * d[t][j];
+}
 
-template <int MT>
-struct AStage {
-    u32x4 v[kSG / 4][MT];
+// The kSG groups of one LDS stage, software-pipelined.  `refill` = false in
+// the ring's last turn.  ring[r0 + g] holds group g of the stage; after its
+// unpack it is refilled with group `next + g`.
+template <int MT, int WPL, int D>
+__device__ inline void stage_groups(Codes<WPL> (&ring)[D], int r0, const u32x4* acur,
+                                    const uint16_t* scur, const Src<MT>& src, int next,
+                                    bool refill, f32x4 (&acc)[MT][WPL], uint32_t mask,
+                                    uint32_t bits, int lane) {
+    Prep<MT, WPL> pc, pn;
+    prep_group<MT, WPL>(pc, ring[r0], acur + lane, scur, mask, bits);
+    unpacked<MT, WPL>(pc);
+    __builtin_amdgcn_sched_barrier(0);
+    if (refill) load_codes<WPL>(ring[r0], src.w, src.code_off, next);
+#pragma unroll
+    for (int g = 0; g < kSG; ++g) {
+        f32x4 d[MT][WPL];
+        mfma_group<MT, WPL>(pc, d);
+        __builtin_amdgcn_sched_barrier(0);
+        if (g + 1 < kSG) {
+            prep_group<MT, WPL>(pn, ring[r0 + g + 1], acur + (g + 1) * MT * 64 + lane,
+                                scur + (g + 1) * 16 * WPL, mask, bits);
+            unpacked<MT, WPL>(pn);
+            __builtin_amdgcn_sched_barrier(0);
+            if (refill) load_codes<WPL>(ring[r0 + g + 1], src.w, src.code_off, next + g + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        fma_group<MT, WPL>(pc, d, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        if (g + 1 < kSG) pc = pn;
+    }
+}
+
+// One LDS stage held in registers between its loads and its store.
+//   a: the activation fragments this wavefront loads (groups g = 4i + wave)
+//   s: this wavefront's scales for the stage (WPL/4 x 16 bytes per lane)
+template <int MT, int WPL>
+struct Stage {
+    u32x4 a[kSG / 4][MT];
+    u32x4 s[WPL / 4];
 };
 
-template <int MT>
-__device__ inline void load_a_stage(AStage<MT>& st, const uint16_t* const* ap, int ks_stage,
-                                    int ks_min, int wave) {
+// Stage starting at group `base` (a multiple of 8).  A record before ks_min
+// (a virtual one ahead of the K range) reads record ks_min / 8 with zeroed
+// scales (only the first stage of a K range can be virtual, so only that load
+// site carries the check); activation columns past K (padding groups, whose
+// scales are zero) are clamped to the last real group.
+template <int MT, int WPL, bool MAYBE_VIRTUAL = false>
+__device__ inline void load_stage(Stage<MT, WPL>& st, const Src<MT>& src, int base, int ks_min,
+                                  int ks_real, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < kSG / 4; ++i) {
-        int g = ks_stage + 4 * i + wave;
-        g = g < ks_min ? ks_min : g;
+        int g = base + 4 * i + wave;
+        if (MAYBE_VIRTUAL) g = g < ks_min ? ks_min : g;
+        g = g < ks_real ? g : ks_real - 1;
 #pragma unroll
-        for (int t = 0; t < MT; ++t) st.v[i][t] = *reinterpret_cast<const u32x4*>(ap[t] + g * 32);
+        for (int t = 0; t < MT; ++t)
+            st.a[i][t] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(src.x, src.a_off[t], g * 64, 0));
+    }
+    // the record's scale block (8 groups x 16 x WPL bf16) follows its codes;
+    // lane l takes 16-byte pieces l, 64 + l, ...
+    const bool virt = MAYBE_VIRTUAL && base < ks_min;
+    const int rec = (virt ? ks_min : base) >> 3;
+    const int soff = (rec * (576 * WPL) + 512 * WPL) * 4;
+#pragma unroll
+    for (int v = 0; v < WPL / 4; ++v) {
+        const u32x4 x = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(src.w, (64 * v + lane) * 16, soff, 0));
+        st.s[v] = virt ? u32x4{0u, 0u, 0u, 0u} : x;
     }
 }
 
-template <int MT>
-__device__ inline void store_a_stage(const AStage<MT>& st, u32x4* buf, int wave, int lane) {
+template <int MT, int WPL>
+__device__ inline void store_stage(const Stage<MT, WPL>& st, u32x4* abuf, u32x4* sbuf, int wave,
+                                   int lane) {
 #pragma unroll
     for (int i = 0; i < kSG / 4; ++i)
 #pragma unroll
-        for (int t = 0; t < MT; ++t) buf[((4 * i + wave) * MT + t) * 64 + lane] = st.v[i][t];
+        for (int t = 0; t < MT; ++t) abuf[((4 * i + wave) * MT + t) * 64 + lane] = st.a[i][t];
+#pragma unroll
+    for (int v = 0; v < WPL / 4; ++v) sbuf[64 * v + lane] = st.s[v];
 }
 
 }  // namespace
 
-// The K loop of one workgroup tile with MT active 16-row blocks.  Weights and
-// scales run through a register ring kSG groups deep (one 16-byte code load
-// per WPL/4 words per group, issued kSG groups ahead); activations are staged
-// through LDS one stage ahead, double-buffered, one barrier per stage.  The
-// first (K range mod kSG) groups are done before the ring starts.
+// LDS per workgroup: activation stages [2][kSG][MT][64] x 16 B and scale
+// stages [2][4 wavefronts][WPL/4 x 64] x 16 B.
 template <int MT, int WPL>
-__device__ void stream_loop(const uint32_t* cp, const uint16_t* sp, const uint16_t* const* ap,
-                            int ks0, int ks1, int wave, int lane, u32x4* lds,
-                            f32x4 (&acc)[MT][WPL], uint32_t mask, uint32_t bits) {
-    constexpr int D = kSG;
-    if (ks1 <= ks0) return;
-    u32x4* buf0 = lds;
-    u32x4* buf1 = lds + kSG * MT * 64;
-    // Stages are aligned to the end of the K range: the first stage starts
-    // `pad` groups early; those slots re-read group ks0 and have their scales
-    // zeroed, so they add exactly zero.  Every stage then runs the same code.
-    const int pad = (kSG - (ks1 - ks0) % kSG) % kSG;
-    const int kb = ks0 - pad;
-    const int nst = (ks1 - kb) / kSG;
+struct Lds {
+    static constexpr int a_stage = kSG * MT * 64;   // u32x4 per activation stage
+    static constexpr int s_wave = WPL / 4 * 64;     // u32x4 per wavefront scale stage
+    static constexpr int s_stage = 4 * s_wave;
+    static constexpr int total = 2 * a_stage + 2 * s_stage;
+};
 
-    // first activation stage is issued before the weight ring so that storing
-    // it to LDS does not wait for the ring's loads
-    WFrag<WPL> ring[D];
-    {
-        AStage<MT> a0;
-        load_a_stage<MT>(a0, ap, kb, ks0, wave);
-        __builtin_amdgcn_sched_barrier(0);
+// The K loop of one workgroup tile with MT active 16-row blocks (MTMAX sizes
+// the LDS layout).
+//
+// Codes: a ring of D = 16 groups in registers, refilled as consumed.
+// Activation fragments and scales: LDS double buffer, one barrier per stage;
+// each stage's global loads are issued two stages ahead into one of two
+// register sets.  Issue order matters because vector-memory completions are
+// waited for in order: storing a stage to LDS waits only for loads issued
+// before it, i.e. ring refills that are due at that point anyway, so the
+// ring keeps its full depth.
+//
+// Iterations cover two stages (16 groups); the K range is padded at its start
+// by one virtual record (zero scales) when it holds an odd number of records.
+template <int MT, int WPL, int MTMAX>
+__device__ void stream_loop(const Src<MT>& src, int ks0, int ks1, int ks_real, int wave,
+                            int lane, u32x4* lds, f32x4 (&acc)[MT][WPL], uint32_t mask,
+                            uint32_t bits) {
+    constexpr int D = 2 * kSG;
+    using L = Lds<MTMAX, WPL>;
+    if (ks1 <= ks0) return;
+    const u32x4* abuf0 = lds;
+    const u32x4* abuf1 = lds + L::a_stage;
+    u32x4* wbuf0 = lds;
+    u32x4* wbuf1 = lds + L::a_stage;
+    u32x4* sbuf0 = lds + 2 * L::a_stage + wave * L::s_wave;
+    u32x4* sbuf1 = sbuf0 + L::s_stage;
+    // this lane's scales of group g in a stage: bf16 (16 g + lane % 16) * WPL
+    const uint16_t* srd0 = reinterpret_cast<const uint16_t*>(sbuf0) + (lane & 15) * WPL;
+    const uint16_t* srd1 = reinterpret_cast<const uint16_t*>(sbuf1) + (lane & 15) * WPL;
+
+    // ks0 and ks1 are multiples of 8: the ring starts pad (0 or 8) groups early
+    // on a virtual record that adds zero
+    const int pad = (D - (ks1 - ks0) % D) % D;
+    const int kb = ks0 - pad;
+    const int nit = (ks1 - kb) / D;             // iterations of two stages
+
+    Codes<WPL> ring[D];
+    Stage<MT, WPL> r0, r1;
+    load_stage<MT, WPL, true>(r0, src, kb, ks0, ks_real, wave, lane);
+    load_stage<MT, WPL>(r1, src, kb + kSG, ks0, ks_real, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);          // stage loads ahead of the ring
 #pragma unroll
-        for (int i = 0; i < D; ++i) {
-            load_w<WPL>(ring[i], cp, sp, kb + i < ks0 ? ks0 : kb + i);
-            if (kb + i < ks0) {
-#pragma unroll
-                for (int j = 0; j < WPL / 2; ++j) ring[i].s[j] = 0u;
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        store_a_stage<MT>(a0, buf0, wave, lane);
-    }
+    for (int i = 0; i < D; ++i) load_codes<WPL>(ring[i], src.w, src.code_off, kb + i < ks0 ? ks0 : kb + i);
+    __builtin_amdgcn_sched_barrier(0);
+    store_stage<MT, WPL>(r0, wbuf0, sbuf0, wave, lane);
     __syncthreads();
-    for (int st = 0; st < nst - 1; ++st) {
-        u32x4* cur = (st & 1) ? buf1 : buf0;
-        u32x4* nxt = (st & 1) ? buf0 : buf1;
-        const int base = kb + st * kSG;
-        AStage<MT> an;
-        load_a_stage<MT>(an, ap, base + kSG, ks0, wave);
-        __builtin_amdgcn_sched_barrier(0);  // keep the stage's loads ahead of the ring refills
-#pragma unroll
-        for (int g = 0; g < kSG; ++g) {
-            compute_group<MT, WPL>(ring[g], cur + g * MT * 64 + lane, acc, mask, bits);
-            load_w<WPL>(ring[g], cp, sp, base + kSG + g);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        store_a_stage<MT>(an, nxt, wave, lane);
+
+    for (int it = 0; it < nit - 1; ++it) {
+        const int base = kb + it * D;
+        // even stage: buffer 0, refill ring slots 0..7 with the stage after next
+        load_stage<MT, WPL>(r0, src, base + D, ks0, ks_real, wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_groups<MT, WPL, D>(ring, 0, abuf0, srd0, src, base + D, true, acc, mask, bits, lane);
+        store_stage<MT, WPL>(r1, wbuf1, sbuf1, wave, lane);
+        __syncthreads();
+        // odd stage: buffer 1, refill ring slots 8..15
+        load_stage<MT, WPL>(r1, src, base + D + kSG, ks0, ks_real, wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_groups<MT, WPL, D>(ring, kSG, abuf1, srd1, src, base + D + kSG, true, acc, mask, bits,
+                                 lane);
+        store_stage<MT, WPL>(r0, wbuf0, sbuf0, wave, lane);
         __syncthreads();
     }
-    {
-        u32x4* cur = ((nst - 1) & 1) ? buf1 : buf0;
-#pragma unroll
-        for (int g = 0; g < kSG; ++g) compute_group<MT, WPL>(ring[g], cur + g * MT * 64 + lane, acc, mask, bits);
-    }
+    stage_groups<MT, WPL, D>(ring, 0, abuf0, srd0, src, 0, false, acc, mask, bits, lane);
+    store_stage<MT, WPL>(r1, wbuf1, sbuf1, wave, lane);
+    __syncthreads();
+    stage_groups<MT, WPL, D>(ring, kSG, abuf1, srd1, src, 0, false, acc, mask, bits, lane);
 }
 
 // One (row tile, 4 column chunks, K split) with MT active row blocks.
-template <int MT, int WPL>
+template <int MT, int WPL, int MTMAX>
 __device__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, int nrows, int chunk, int wave,
                              int lane, u32x4* lds) {
     const bool slot_rows = a.tile_src != TILE_MASKED;
@@ -229,7 +358,7 @@ __device__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, int nrows, int ch
 
     // activation row of each of this lane's MFMA A rows (rows past the tile
     // reuse its first row: MFMA rows are independent and are not stored)
-    const uint16_t* ap[MT];
+    Src<MT> src;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
         int r = 16 * t + (lane & 15);
@@ -242,18 +371,22 @@ __device__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, int nrows, int ch
             row = (a.arow == W4A16_AROW_TOKEN) ? f / a.top_k : f;
         }
         row = row < a.A_rows ? row : a.A_rows - 1;
-        ap[t] = a.A + row * a.K + 8 * (lane >> 4);
+        // A_rows * K * 2 < 2^32 is checked on the host
+        src.a_off[t] = static_cast<uint32_t>(row * a.K * 2 + 16 * (lane >> 4));
     }
+    src.x = make_rsrc(a.A, static_cast<uint64_t>(a.A_rows) * a.K * 2);
 
+    // K split s covers whole records [ks0, ks1)
     const int s = blockIdx.z;
-    const int ks0 = static_cast<int>(static_cast<int64_t>(s) * a.KS / a.split_k);
-    const int ks1 = static_cast<int>(static_cast<int64_t>(s + 1) * a.KS / a.split_k);
+    const int nrec = a.KSP / 8;
+    const int ks0 = 8 * static_cast<int>(static_cast<int64_t>(s) * nrec / a.split_k);
+    const int ks1 = 8 * static_cast<int>(static_cast<int64_t>(s + 1) * nrec / a.split_k);
     // a wavefront past the last chunk re-streams the last chunk (cache hits,
     // only when N / CW is not a multiple of 4) and stores nothing: the loop
     // stays free of wavefront-dependent branches
     const int64_t cbase = static_cast<int64_t>(e) * a.NC + (active ? chunk : a.NC - 1);
-    const uint32_t* cp = a.codes + (cbase * a.KS) * 64 * WPL + lane * WPL;
-    const uint16_t* sp = a.scales + (cbase * a.KS) * 16 * WPL + (lane & 15) * WPL;
+    src.w = make_rsrc(a.packed + cbase * a.chunk_words, static_cast<uint64_t>(a.chunk_words) * 4);
+    src.code_off = static_cast<uint32_t>(lane * WPL * 4);
 
     f32x4 acc[MT][WPL];
 #pragma unroll
@@ -265,7 +398,7 @@ __device__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, int nrows, int ch
     // only pins the register class and emits nothing
     uint32_t vbits = a.unpack_bits;
     asm volatile("" : "+v"(vbits));
-    stream_loop<MT, WPL>(cp, sp, ap, ks0, ks1, wave, lane, lds, acc, a.unpack_mask, vbits);
+    stream_loop<MT, WPL, MTMAX>(src, ks0, ks1, a.KS, wave, lane, lds, acc, a.unpack_mask, vbits);
     if (!active) return;
 
     // epilogue: lane holds rows 16t + 4*(lane/16) + i of column 16j + lane%16
@@ -297,23 +430,37 @@ __device__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, int nrows, int ch
 }
 
 template <int MT, int WPL>
+__device__ void gemm_tile_part(const GemmArgs& a, int e, int p0, int nrows, int chunk, int wave,
+                               int lane, u32x4* lds) {
+    const int mt_active = (nrows + 15) >> 4;
+    if (mt_active <= 1) gemm_tile_mt<1, WPL, MT>(a, e, p0, nrows, chunk, wave, lane, lds);
+    else if (MT >= 2 && mt_active == 2) gemm_tile_mt<(MT >= 2 ? 2 : 1), WPL, MT>(a, e, p0, nrows, chunk, wave, lane, lds);
+    else if (MT >= 3 && mt_active == 3) gemm_tile_mt<(MT >= 3 ? 3 : 1), WPL, MT>(a, e, p0, nrows, chunk, wave, lane, lds);
+    else if (MT >= 4) gemm_tile_mt<(MT >= 4 ? 4 : 1), WPL, MT>(a, e, p0, nrows, chunk, wave, lane, lds);
+}
+
+// A tile of more than 16 * MT rows (a variant whose registers hold fewer row
+// blocks than the tile) is processed in parts of 16 * MT rows; each part
+// re-streams the chunk.
+template <int MT, int WPL>
 __device__ void gemm_tile(const GemmArgs& a, int e, int p0, int nrows, int chunk, int wave,
                           int lane, u32x4* lds) {
-    const int mt_active = (nrows + 15) >> 4;
-    if (mt_active <= 1) gemm_tile_mt<1, WPL>(a, e, p0, nrows, chunk, wave, lane, lds);
-    else if (MT >= 2 && mt_active == 2) gemm_tile_mt<(MT >= 2 ? 2 : 1), WPL>(a, e, p0, nrows, chunk, wave, lane, lds);
-    else if (MT >= 3 && mt_active == 3) gemm_tile_mt<(MT >= 3 ? 3 : 1), WPL>(a, e, p0, nrows, chunk, wave, lane, lds);
-    else if (MT >= 4) gemm_tile_mt<(MT >= 4 ? 4 : 1), WPL>(a, e, p0, nrows, chunk, wave, lane, lds);
+    for (int r = 0; r < nrows; r += 16 * MT) {
+        if (r > 0) __syncthreads();  // the part reuses the staging buffers
+        gemm_tile_part<MT, WPL>(a, e, p0 + r, nrows - r < 16 * MT ? nrows - r : 16 * MT, chunk,
+                                wave, lane, lds);
+    }
 }
 
 // Tiles are walked grid-stride along grid.y, so any device-side tile count is
 // fully covered whatever the grid size; every wavefront leaves the loop once
-// its tile index passes the count.
+// its tile index passes the count.  The tile decision is uniform across the
+// workgroup, so every barrier inside is reached by all four wavefronts.
 template <int MT, int WPL>
 __global__ void __launch_bounds__(256) k_gemm_small(GemmArgs a) {
-    __shared__ u32x4 lds[2 * kSG * MT * 64];
+    __shared__ u32x4 lds[Lds<MT, WPL>::total];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int chunk = blockIdx.x * 4 + wave;
     for (int ty = blockIdx.y;; ty += gridDim.y) {
         int e, p0, nrows;
@@ -354,12 +501,9 @@ void launch_gemm_small(const GemmArgs& a, int mt, hipStream_t st) {
             default: k_gemm_small<4, 4><<<grid, block, 0, st>>>(a); break;
         }
     } else {
-        switch (mt) {
-            case 1: k_gemm_small<1, 8><<<grid, block, 0, st>>>(a); break;
-            case 2: k_gemm_small<2, 8><<<grid, block, 0, st>>>(a); break;
-            case 3: k_gemm_small<3, 8><<<grid, block, 0, st>>>(a); break;
-            default: k_gemm_small<4, 8><<<grid, block, 0, st>>>(a); break;
-        }
+        // 128-column chunks hold at most two row blocks in registers
+        if (mt <= 1) k_gemm_small<1, 8><<<grid, block, 0, st>>>(a);
+        else k_gemm_small<2, 8><<<grid, block, 0, st>>>(a);
     }
 }
 

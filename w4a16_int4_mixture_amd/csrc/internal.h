@@ -28,22 +28,24 @@ w4a16_status check_launch(const char* what);
 
 // ---- packed weight geometry ------------------------------------------------
 //
-// Codes: word (e, chunk, ks, lane, j) at index
-//   (((e * NC + chunk) * KS + ks) * 64 + lane) * WPL + j
-// holds the eight codes of column  chunk*CW + 16*j + lane%16  (packed column
-// order) for K = ks*32 + 8*(lane/16) + o, o = 0..7, with the code of offset o
-// in nibble  nib_of(o)  where the nibble order is
-//   nibble i holds offset 2*(i%4) + i/4   (i.e. 0,2,4,6,1,3,5,7)
-// so that (word >> 4p) & 0x000F000F selects offsets (2p, 2p+1) in the two
-// 16-bit halves, and (word >> 4b') & 0x0F0F0F0F gives four bytes.
-// Scales: bf16 (e, chunk, ks, c16, j) at index
-//   (((e * NC + chunk) * KS + ks) * 16 + c16) * WPL + j
-// holds the scale of column chunk*CW + 16*j + c16, group ks.
+// Per expert e and chunk c of CW packed columns, K/32 groups are padded to
+// KSP = round_up(K/32, 8) and cut into KSP/8 records ("stages") of 8 groups.
+// A record is contiguous: first the codes, then the scales of its 8 groups.
+//   codes : word (g8, lane, j) at  (g8 * 64 + lane) * WPL + j      (g8 < 8)
+//           = the eight codes of column c*CW + 16*j + lane%16 (packed order)
+//             for K = ks*32 + 8*(lane/16) + o, o = 0..7, with the code of
+//             offset o in nibble i where o = 2*(i%4) + i/4 (order
+//             0,2,4,6,1,3,5,7): (word >> 4p) & 0x000F000F then selects
+//             offsets (2p, 2p+1) in the two 16-bit halves
+//   scales: bf16 (g8, c16, j) at  512*WPL words + (g8 * 16 + c16) * WPL + j
+//           = the scale of column c*CW + 16*j + c16, group ks
+// Padding groups (ks >= K/32) hold zero codes and zero scales.
 // WPL = CW / 16 words (and scales) per lane per group.
 struct PackGeom {
-    int E, N, K, CW, NC, KS, WPL;
+    int E, N, K, CW, NC, KS, KSP, WPL;
     bool interleave;
-    uint64_t codes_bytes, scales_offset, scales_bytes, bytes;
+    uint64_t stage_words, chunk_words;   // 32-bit words per record / per chunk
+    uint64_t stage_bytes, chunk_bytes, bytes;
 };
 
 __host__ __device__ inline int nibble_k_offset(int i) { return 2 * (i & 3) + (i >> 2); }
@@ -95,10 +97,10 @@ struct GemmArgs {
     int max_m, chunks_per_expert;
     int grid_tiles;        // grid.y
     int grid_tiles_total;  // masked: experts * chunks_per_expert
-    // weights
-    const uint32_t* codes;
-    const uint16_t* scales;
-    int NC, KS, N, K, CW, E;
+    // weights (packed records, see PackGeom)
+    const uint32_t* packed;
+    int64_t chunk_words, stage_words;
+    int NC, KS, KSP, N, K, CW, E;
     int64_t A_rows;    // rows of A (row indices are clamped below it)
     int sorted_cap;    // entries of sorted_ids
     // output

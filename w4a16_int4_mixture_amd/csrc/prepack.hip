@@ -57,12 +57,14 @@ w4a16_status make_geom(int profile, uint32_t flags, int E, int N, int K, int gro
     g->CW = cw;
     g->NC = N / cw;
     g->KS = K / 32;
+    g->KSP = static_cast<int>(round_up(static_cast<uint64_t>(g->KS), 8));
     g->WPL = cw / 16;
     g->interleave = (flags & W4A16_PACK_GATE_UP_INTERLEAVE) != 0;
-    g->codes_bytes = static_cast<uint64_t>(E) * N * (K / 8) * 4;
-    g->scales_offset = round_up(g->codes_bytes, 256);
-    g->scales_bytes = static_cast<uint64_t>(E) * N * (K / 32) * 2;
-    g->bytes = g->scales_offset + round_up(g->scales_bytes, 256);
+    g->stage_words = 576ull * g->WPL;                    // 512 WPL code words + 64 WPL scale words
+    g->chunk_words = g->stage_words * (g->KSP / 8);
+    g->stage_bytes = g->stage_words * 4;
+    g->chunk_bytes = g->chunk_words * 4;
+    g->bytes = g->chunk_bytes * static_cast<uint64_t>(E) * g->NC;
     return W4A16_OK;
 }
 
@@ -79,7 +81,8 @@ w4a16_status check_desc(const w4a16_desc* d) {
     PackGeom g;
     w4a16_status st = make_geom(d->profile, d->flags, d->E, d->N, d->K, d->group, &g);
     if (st != W4A16_OK) return W4A16_ERR_MODE_MISMATCH;
-    if (g.CW != d->chunk_n || g.bytes != d->bytes || g.scales_offset != d->scales_offset) {
+    if (g.CW != d->chunk_n || g.KSP != d->k_groups || g.bytes != d->bytes ||
+        g.stage_bytes != d->stage_bytes || g.chunk_bytes != d->chunk_bytes) {
         set_error("weight descriptor is inconsistent with its profile/shape");
         return W4A16_ERR_MODE_MISMATCH;
     }
@@ -93,81 +96,60 @@ __host__ __device__ static inline uint32_t permute_word(uint32_t w) {
     return out;
 }
 
-__global__ void k_prepack_codes(const uint32_t* __restrict__ codes, uint32_t* __restrict__ out,
-                                int N, int K, int NC, int KS, int CW, int WPL, int interleave,
-                                int64_t total) {
-    int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (idx >= total) return;
-    int64_t r = idx;
-    int j = static_cast<int>(r % WPL);
-    r /= WPL;
-    int lane = static_cast<int>(r % 64);
-    r /= 64;
-    int ks = static_cast<int>(r % KS);
-    r /= KS;
-    int chunk = static_cast<int>(r % NC);
-    int64_t e = r / NC;
-    int nn = chunk * CW + 16 * j + (lane & 15);
-    int n = canonical_column(nn, N, CW, interleave != 0);
-    uint32_t w = codes[(e * N + n) * (K / 8) + ks * 4 + (lane >> 4)];
-    out[idx] = permute_word(w);
+// Word w of the packed buffer, from the canonical codes and scales.
+__host__ __device__ static inline uint32_t packed_word(const uint32_t* codes, const uint16_t* scales,
+                                                       const PackGeom& g, uint64_t w) {
+    const uint64_t chunk_id = w / g.chunk_words;        // e * NC + c
+    const int64_t e = static_cast<int64_t>(chunk_id / g.NC);
+    const int c = static_cast<int>(chunk_id % g.NC);
+    const uint64_t r = w % g.chunk_words;
+    const int stage = static_cast<int>(r / g.stage_words);
+    const int in = static_cast<int>(r % g.stage_words);
+    const int code_words = 512 * g.WPL;
+    if (in < code_words) {
+        const int j = in % g.WPL;
+        const int lane = (in / g.WPL) % 64;
+        const int ks = stage * 8 + in / (64 * g.WPL);
+        if (ks >= g.KS) return 0u;
+        const int n = canonical_column(c * g.CW + 16 * j + (lane & 15), g.N, g.CW, g.interleave);
+        return permute_word(codes[(e * g.N + n) * (g.K / 8) + ks * 4 + (lane >> 4)]);
+    }
+    uint32_t out = 0;
+    for (int h = 0; h < 2; ++h) {
+        const int b = 2 * (in - code_words) + h;         // bf16 index inside the scale block
+        const int j = b % g.WPL;
+        const int c16 = (b / g.WPL) % 16;
+        const int ks = stage * 8 + b / (16 * g.WPL);
+        uint32_t v = 0;
+        if (ks < g.KS) {
+            const int n = canonical_column(c * g.CW + 16 * j + c16, g.N, g.CW, g.interleave);
+            v = scales[(e * g.N + n) * g.KS + ks];
+        }
+        out |= v << (16 * h);
+    }
+    return out;
 }
 
-__global__ void k_prepack_scales(const uint16_t* __restrict__ scales, uint16_t* __restrict__ out,
-                                 int N, int NC, int KS, int CW, int WPL, int interleave,
-                                 int64_t total) {
-    int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (idx >= total) return;
-    int64_t r = idx;
-    int j = static_cast<int>(r % WPL);
-    r /= WPL;
-    int c16 = static_cast<int>(r % 16);
-    r /= 16;
-    int ks = static_cast<int>(r % KS);
-    r /= KS;
-    int chunk = static_cast<int>(r % NC);
-    int64_t e = r / NC;
-    int nn = chunk * CW + 16 * j + c16;
-    int n = canonical_column(nn, N, CW, interleave != 0);
-    out[idx] = scales[(e * N + n) * KS + ks];
+__global__ void k_prepack(const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+                          uint32_t* __restrict__ out, PackGeom g, uint64_t total) {
+    const uint64_t w = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (w >= total) return;
+    out[w] = packed_word(codes, scales, g, w);
 }
 
 void launch_prepack(const PackGeom& g, const uint32_t* codes, const uint16_t* scales,
                     void* packed, hipStream_t s) {
-    int64_t nw = static_cast<int64_t>(g.E) * g.N * (g.K / 8);
-    int64_t ns = static_cast<int64_t>(g.E) * g.N * (g.K / 32);
-    uint32_t* oc = static_cast<uint32_t*>(packed);
-    uint16_t* os = reinterpret_cast<uint16_t*>(static_cast<char*>(packed) + g.scales_offset);
-    k_prepack_codes<<<dim3(static_cast<unsigned>((nw + 255) / 256)), dim3(256), 0, s>>>(
-        codes, oc, g.N, g.K, g.NC, g.KS, g.CW, g.WPL, g.interleave, nw);
-    k_prepack_scales<<<dim3(static_cast<unsigned>((ns + 255) / 256)), dim3(256), 0, s>>>(
-        scales, os, g.N, g.NC, g.KS, g.CW, g.WPL, g.interleave, ns);
+    const uint64_t total = g.bytes / 4;
+    k_prepack<<<dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s>>>(
+        codes, scales, static_cast<uint32_t*>(packed), g, total);
 }
 
 // Host reference of the same permutation.
 static void prepack_host(const PackGeom& g, const uint32_t* codes, const uint16_t* scales,
                          void* packed) {
-    uint32_t* oc = static_cast<uint32_t*>(packed);
-    uint16_t* os = reinterpret_cast<uint16_t*>(static_cast<char*>(packed) + g.scales_offset);
-    int64_t idx = 0;
-    for (int64_t e = 0; e < g.E; ++e)
-        for (int chunk = 0; chunk < g.NC; ++chunk)
-            for (int ks = 0; ks < g.KS; ++ks)
-                for (int lane = 0; lane < 64; ++lane)
-                    for (int j = 0; j < g.WPL; ++j, ++idx) {
-                        int n = canonical_column(chunk * g.CW + 16 * j + (lane & 15), g.N, g.CW,
-                                                 g.interleave);
-                        oc[idx] = permute_word(codes[(e * g.N + n) * (g.K / 8) + ks * 4 + (lane >> 4)]);
-                    }
-    idx = 0;
-    for (int64_t e = 0; e < g.E; ++e)
-        for (int chunk = 0; chunk < g.NC; ++chunk)
-            for (int ks = 0; ks < g.KS; ++ks)
-                for (int c16 = 0; c16 < 16; ++c16)
-                    for (int j = 0; j < g.WPL; ++j, ++idx) {
-                        int n = canonical_column(chunk * g.CW + 16 * j + c16, g.N, g.CW, g.interleave);
-                        os[idx] = scales[(e * g.N + n) * g.KS + ks];
-                    }
+    uint32_t* out = static_cast<uint32_t*>(packed);
+    const uint64_t total = g.bytes / 4;
+    for (uint64_t w = 0; w < total; ++w) out[w] = packed_word(codes, scales, g, w);
 }
 
 static void fill_desc(const PackGeom& g, int profile, uint32_t flags, w4a16_desc* d) {
@@ -180,9 +162,9 @@ static void fill_desc(const PackGeom& g, int profile, uint32_t flags, w4a16_desc
     d->K = g.K;
     d->group = 32;
     d->chunk_n = g.CW;
-    d->reserved = 0;
-    d->codes_bytes = g.codes_bytes;
-    d->scales_offset = g.scales_offset;
+    d->k_groups = g.KSP;
+    d->stage_bytes = g.stage_bytes;
+    d->chunk_bytes = g.chunk_bytes;
     d->bytes = g.bytes;
 }
 
