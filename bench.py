@@ -3,9 +3,9 @@
     python bench.py [--steps K] [--warmup W] [--workload decode|prefill|tp8|masked|tiny]
 
 One step = one call of the whole path on one batch of seeded synthetic input
-already resident in HBM: routing sort (align) -> gate/up GEMM with SiLU*gate ->
-down GEMM -> top-k combine (for the masked workload: the two GEMMs and the
-combine).  W untimed warm-up steps, then exactly K timed steps between two
+already resident in HBM: routing sort (align) -> gate/up GEMM with SiLU*gate in
+its epilogue -> down GEMM -> top-k combine (for the masked workload: the two
+GEMMs and the combine).  W untimed warm-up steps, then exactly K timed steps between two
 device synchronisations.  Rank 0 prints one JSON line.
 
 The default workload is the decode share of a Kimi-K2-like layer on one GPU of
@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="run one plain device copy of this size before the warm-up (a known "
+                        "byte count for scaling HBM counters)")
     return p.parse_args()
 
 
@@ -108,7 +111,8 @@ def main():
     codes2, scales2 = to_dev(d["codes2"]), to_dev(d["scales2"])
     copies = []
     for _ in range(max(1, args.copies)):
-        copies.append((m.prepare_weight(codes13, scales13, profile),
+        # W13 with gate/up interleave: SiLU*gate runs in the gate/up epilogue
+        copies.append((m.prepare_weight(codes13, scales13, profile, m.PACK_GATE_UP_INTERLEAVE),
                        m.prepare_weight(codes2, scales2, profile)))
     del codes13, scales13, codes2, scales2
     torch.cuda.synchronize()
@@ -155,11 +159,15 @@ def main():
                  for (w13, w2) in copies]
 
         def stages(p):
-            return [("align", lambda: p.routing.align(ids, wl.E_global, em)),
-                    ("gate_up", lambda: m._capi.w4a16_moe_w4a16_gemm(p.gate_up_args(X))),
-                    ("down", lambda: m._capi.w4a16_moe_w4a16_gemm(p.down_args())),
-                    ("combine", lambda: m._capi.w4a16_moe_combine(
-                        p.Y2, p.Y2.shape[0], H, p.routing.row_of, tw, wl.T, wl.top_k, p.out))]
+            ga, da = p.stage_args(X)
+            st = [("align", lambda: p.routing.align(ids, wl.E_global, em)),
+                  ("gate_up", lambda: m._capi.w4a16_moe_w4a16_gemm(ga))]
+            if p.separate_act:
+                st.append(("act", lambda: p.act()))
+            return st + [("down", lambda: m._capi.w4a16_moe_w4a16_gemm(da)),
+                         ("combine", lambda: m._capi.w4a16_moe_combine(
+                             p.Y2, p.Y2.shape[0], H, p.routing.row_of, tw, wl.T, wl.top_k,
+                             p.out))]
 
     # pre-built argument structs: the timed loop only launches
     stage_lists = [stages(p) for p in paths]
@@ -167,9 +175,13 @@ def main():
         if masked:
             p.gate_up_args(a3, mm)
             p.down_args(mm)
-        else:
-            p.gate_up_args(X)
-            p.down_args()
+
+    if args.calib_copy_mib > 0:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(i, events=None):
         st = stage_lists[i % len(stage_lists)]
@@ -232,19 +244,28 @@ def main():
 
     gu, dn = stage_us["gate_up"], stage_us["down"]
     src_hash = kernel_source_hash()
+    # the dominant kernel is the gate/up GEMM; its algorithmic HBM bytes per
+    # launch are the active experts' codes + scales, the activations read once
+    # and the routed rows' outputs written once
+    x_bytes = (rows if masked else wl.T) * H * 2
+    out_bytes = rows * I * 2           # Z: SiLU*gate is applied in the epilogue
+    alg_bytes13 = bytes13 + x_bytes + out_bytes
     if args.workload == "prefill":
         bound, unit_rf = "mfma", "TFLOP/s"
         achieved = flops13 / (gu * 1e-6) / 1e12
         peak = BF16_PEAK_TFLOPS
     else:
         bound, unit_rf = "hbm", "GB/s"
-        achieved = bytes13 / (gu * 1e-6) / 1e9
+        achieved = alg_bytes13 / (gu * 1e-6) / 1e9
         peak = HBM_PEAK_GBS
+    plan13 = paths[0].plan if not masked else None
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit_rf,
                 "frac": round(achieved / peak, 4),
                 "traffic": traffic_from_profiles(args.workload, src_hash),
-                "kernel": "gate_up stage (w4a16_moe_w4a16_gemm)",
-                "algorithmic_per_launch": bytes13 if bound == "hbm" else flops13}
+                "kernel": "k_gemm_small (gate/up GEMM with SiLU*gate epilogue and in-kernel "
+                          "split-K fix-up: one launch per call)",
+                "algorithmic_per_launch": alg_bytes13 if bound == "hbm" else flops13,
+                "launch_us": round(gu, 2)}
 
     cpu = None
     if not args.no_cpu_baseline and args.workload in ("decode", "tiny", "masked"):
@@ -267,7 +288,9 @@ def main():
         "config": {"workload": workload_name(args.workload, wl), "tokens": wl.T,
                    "top_k": wl.top_k, "local_experts": wl.E_local, "hidden": H,
                    "intermediate": I, "routed_rows": rows, "active_experts": active,
-                   "weight_copies": len(paths)},
+                   "weight_copies": len(paths),
+                   "gate_up_tile_m": None if plan13 is None else plan13.tile_m,
+                   "gate_up_split_k": None if plan13 is None else plan13.split_k},
         "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
         "event_total_us": round(event_total, 2),
         "gate_up_plus_down_us": round(gu + dn, 2),

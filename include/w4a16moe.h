@@ -216,7 +216,11 @@ typedef enum {
 typedef enum {
     W4A16_EPI_STORE = 0,     /* store bf16(acc) */
     W4A16_EPI_SILU_MUL = 1   /* W13 only: store bf16(silu(bf16(gate)) * bf16(up)),
-                                out is [rows, N/2] */
+                                out is [rows, N/2].  With a W13 packed with
+                                GATE_UP_INTERLEAVE it is applied to the
+                                accumulators in the GEMM kernel; with a plain
+                                W13 the GEMM stages bf16 Y13 in the workspace
+                                and a second kernel applies it (same result) */
 } w4a16_epilogue;
 
 #define W4A16_GEMM_F32_OUT 0x1u  /* store the fp32 accumulator (float) instead of
@@ -259,8 +263,14 @@ typedef struct {
     /* output */
     void* out;                      /* device; bf16 (or float with F32_OUT) */
     int64_t out_rows;               /* rows available in out */
-    /* scratch */
-    void* workspace;                /* device, >= w4a16_gemm_workspace_bytes(...) */
+    /* scratch: device, 256-byte aligned, >= w4a16_gemm_workspace_bytes(...).
+       It starts with the split-K arrival counters, which must read zero when
+       a call starts: allocate it zeroed.  A completed call leaves the
+       counters it used at zero but may leave partial sums after them, so a
+       workspace reused for a call of another shape, split or tile capacity
+       must be zeroed again first.  Calls that share a workspace must not run
+       concurrently. */
+    void* workspace;
     uint64_t workspace_bytes;
 } w4a16_gemm_args;
 
@@ -269,11 +279,13 @@ w4a16_status w4a16_gemm_workspace_bytes(const w4a16_gemm_args* args, uint64_t* b
 
 /* Run one grouped GEMM stage.  Checks the descriptor (magic, version, shape,
  * flags vs epilogue) before launching: a weight packed with gate/up
- * interleave used with EPI_STORE, or a plain weight with EPI_SILU_MUL, is a
- * MODE_MISMATCH; so is any split_k override under MASKED (the grouped
- * dispatch owns its schedule).  Rows of padding, rows past masked_m and
- * experts with no rows are never stored; experts with masked_m == 0 read no
- * weights. */
+ * interleave used with EPI_STORE is a MODE_MISMATCH; so is any split_k
+ * override under MASKED (the grouped dispatch owns its schedule).  Rows of
+ * padding, rows past masked_m and experts with no rows are never stored;
+ * experts with masked_m == 0 read no weights.  With a K split, each split
+ * leaves an fp32 partial in the workspace and the split that finishes last
+ * adds them in split order, inside the same kernel: results do not depend on
+ * the order in which splits finish. */
 w4a16_status w4a16_moe_w4a16_gemm(const w4a16_gemm_args* args, void* stream);
 
 /* ------------------------------------------------------------------------ */

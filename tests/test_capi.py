@@ -176,6 +176,11 @@ def test_gemm_argument_checks():
     # interleaved W13 with a plain store: the columns would come out permuted
     di = host_desc(flags=capi.W4A16_PACK_GATE_UP_INTERLEAVE)
     assert ws_status(gemm_args(di)) == capi.W4A16_ERR_MODE_MISMATCH
+    # interleaved W13 with the SiLU epilogue: applied in the GEMM, no staging
+    assert capi.w4a16_gemm_workspace_bytes(gemm_args(di, epilogue=capi.W4A16_EPI_SILU_MUL)) == 0
+    # a plain W13 with the SiLU epilogue stages bf16 Y13 [sorted_cap, N]
+    assert capi.w4a16_gemm_workspace_bytes(gemm_args(d, epilogue=capi.W4A16_EPI_SILU_MUL)) == \
+        256 * 128 * 2
     # masked: expected_m must be positive; split_k overrides are refused
     m = dict(layout=capi.W4A16_LAYOUT_MASKED, masked_m=1 << 20, max_m=32, expected_m=32,
              A_rows=64, out_rows=64)
@@ -185,10 +190,13 @@ def test_gemm_argument_checks():
     assert ws_status(gemm_args(d, **{**m, "A_rows": 10})) == capi.W4A16_ERR_CAPACITY
     # K splits are whole 8-group records: one record cannot be split
     assert capi.w4a16_gemm_workspace_bytes(gemm_args(d, split_k=2)) == 0
-    # launching with a too-small workspace fails before the launch
+    # two splits: arrival counters (one per tile x part x column group of four
+    # 64-column chunks, 256-byte granular), then fp32 partials [2, sorted_cap, N]
     d512 = host_desc(K=512)
     a = gemm_args(d512, split_k=2)
-    assert capi.w4a16_gemm_workspace_bytes(a) == 2 * 256 * 128 * 4
+    counters = -(-8 * 4 * 1 * 4 // 256) * 256
+    assert capi.w4a16_gemm_workspace_bytes(a) == counters + 2 * 256 * 128 * 4
+    # launching with a too-small workspace fails before the launch
     assert capi.lib().w4a16_moe_w4a16_gemm(ctypes.byref(a), None) == capi.W4A16_ERR_CAPACITY
 
 

@@ -60,8 +60,9 @@ def check_close(gpu, ref, what, exact_frac=0.95):
     assert same >= exact_frac, f"{what}: only {same:.3f} bit-identical"
 
 
-def prepare(m, codes, scales, profile):
-    return m.prepare_weight(dev(codes), dev(scales), profile)
+def prepare(m, codes, scales, profile, interleave=False):
+    return m.prepare_weight(dev(codes), dev(scales), profile,
+                            m.PACK_GATE_UP_INTERLEAVE if interleave else 0)
 
 
 # ------------------------------------------------------------------ prepack ----
@@ -220,10 +221,12 @@ def test_pipelined_main_loop_exact(m, H, tile_m, profile):
 
 # --------------------------------------------------------- general inputs ----
 
-def run_indexed(m, d, E_global, profile, tile_m=0, split=0, rows_hint=None):
+def run_indexed(m, d, E_global, profile, tile_m=0, split=0, rows_hint=None, interleave=True):
+    """The whole indexed path; by default with the gate/up-interleaved W13, so
+    that SiLU*gate runs in the gate/up GEMM's epilogue."""
     wl_T, k = d["topk_ids"].shape
     E = d["codes13"].shape[0]
-    w13 = prepare(m, d["codes13"], d["scales13"], profile)
+    w13 = prepare(m, d["codes13"], d["scales13"], profile, interleave)
     w2 = prepare(m, d["codes2"], d["scales2"], profile)
     rows_hint = wl_T * k if rows_hint is None else rows_hint
     path = m.IndexedPath(w13, w2, wl_T, k, E_global, rows_hint=rows_hint, tile_m=tile_m,
@@ -245,7 +248,8 @@ def run_indexed(m, d, E_global, profile, tile_m=0, split=0, rows_hint=None):
 def test_stages_and_path_random(m, seed, E, H, I, T, k, Eg, tile_m, split, profile):
     print(f"random path seed={seed} E={E} H={H} I={I} T={T} k={k}", flush=True)
     d = synth.random_small(seed, E, H, I, T, k, E_global=Eg)
-    path, out = run_indexed(m, d, Eg, profile, tile_m, split)
+    # plain W13 (separate activation kernel) on even seeds, interleaved on odd
+    path, out = run_indexed(m, d, Eg, profile, tile_m, split, interleave=seed % 2 == 1)
     ref = oracle.moe_forward(d["X"], d["topk_ids"], d["topk_weights"], Eg, d["expert_map"],
                              d["codes13"], d["scales13"], d["codes2"], d["scales2"],
                              intermediates=True)
@@ -253,9 +257,11 @@ def test_stages_and_path_random(m, seed, E, H, I, T, k, Eg, tile_m, split, profi
     check_close(host(path.Z, np.uint16)[pos], ref["Z"][f], "Z")
     check_close(host(path.Y2, np.uint16)[pos], ref["Y2"][f], "Y2")
     check_close(out, ref["out"], "out")
-    # the separate activation kernel as well
+    # the separate activation kernel as well (on a plain W13)
+    w13p = prepare(m, d["codes13"], d["scales13"], profile)
     Y13 = torch.zeros((path.routing.sorted_cap, 2 * I), dtype=torch.int16, device="cuda")
-    m.run_gemm(path.gate_up_args(dev(d["X"]), out=Y13, epilogue=0), "cuda")
+    m.run_gemm(m.gemm_args_indexed(w13p, dev(d["X"]), path.routing, Y13, 0, split_k=split,
+                                   rows_hint=T * k), "cuda")
     check_close(host(Y13, np.uint16)[pos], ref["Y13"][f], "Y13")
     Z2 = torch.zeros((path.routing.sorted_cap, I), dtype=torch.int16, device="cuda")
     from w4a16_int4_mixture_amd import _capi
@@ -263,6 +269,69 @@ def test_stages_and_path_random(m, seed, E, H, I, T, k, Eg, tile_m, split, profi
     torch.cuda.synchronize()
     check_close(host(Z2, np.uint16)[pos], oracle.silu_mul(host(Y13, np.uint16)[pos]), "silu",
                 exact_frac=0.99)
+
+
+@pytest.mark.parametrize("split", [1, 2, 3])
+@pytest.mark.parametrize("profile", [1, 2])
+def test_fused_silu_epilogue_and_splitk_fixup(m, split, profile):
+    """SiLU*gate in the gate/up epilogue (interleaved W13) equals the stored
+    Y13 followed by the activation kernel, bit for bit (the accumulators are
+    the same and both round gate and up to bf16 first); the in-kernel split-K
+    fix-up adds partials in split order, so repeated calls are bit-identical
+    and leave every arrival counter at zero."""
+    from w4a16_int4_mixture_amd import _capi
+    E, H, I, T, k = 5, 768, 256, 60, 3          # K = 768: three 8-group records
+    d = synth.random_small(40 + split, E, H, I, T, k)
+    print(f"fused silu: split={split} profile={profile}", flush=True)
+    w13i = prepare(m, d["codes13"], d["scales13"], profile, interleave=True)
+    w13p = prepare(m, d["codes13"], d["scales13"], profile)
+    w2 = prepare(m, d["codes2"], d["scales2"], profile)
+    pi = m.IndexedPath(w13i, w2, T, k, E, rows_hint=T * k, split_k13=split, split_k2=split)
+    pp = m.IndexedPath(w13p, w2, T, k, E, rows_hint=T * k, split_k13=split, split_k2=split)
+    args = (dev(d["X"]), dev(d["topk_ids"]), dev(d["topk_weights"]))
+    pi.Z.fill_(0x7FC0)
+    out_i = host(pi(*args), np.uint16).copy()
+    out_p = host(pp(*args), np.uint16).copy()
+    torch.cuda.synchronize()
+    pos, f = slot_rows(pi.routing, T, k)
+    assert np.array_equal(host(pi.Z, np.uint16)[pos], host(pp.Z, np.uint16)[pos])
+    assert np.array_equal(out_i, out_p)
+    ref = oracle.moe_forward(d["X"], d["topk_ids"], d["topk_weights"], E, None, d["codes13"],
+                             d["scales13"], d["codes2"], d["scales2"], intermediates=True)
+    check_close(host(pi.Z, np.uint16)[pos], ref["Z"][f], "fused Z")
+    check_close(out_i, ref["out"], "fused out")
+    for _ in range(2):
+        assert np.array_equal(host(pi(*args), np.uint16), out_i)
+    torch.cuda.synchronize()
+    # arrival counters (the first bytes of each workspace) are back at zero
+    for key, buf in pi._ws.items():
+        w = w13i if key[0] == "g" else w2
+        ncount = pi.routing.tiles_cap * 4 * ((w.N // w.desc.chunk_n + 3) // 4)
+        assert not host(buf[: 4 * ncount]).any(), f"counters left non-zero in workspace {key}"
+
+
+def test_masked_fused_silu(m):
+    """The grouped masked layout with the interleaved W13 (SiLU in the
+    epilogue) against the plain W13 and the oracle; padding rows are NaN."""
+    d = synth.make_workload("masked")
+    wl = d["wl"]
+    G, max_m = wl.E_local, d["max_m"]
+    w13i = prepare(m, d["codes13"], d["scales13"], 1, interleave=True)
+    w13p = prepare(m, d["codes13"], d["scales13"], 1)
+    w2 = prepare(m, d["codes2"], d["scales2"], 1)
+    a3 = dev(d["a3"].reshape(G * max_m, wl.H))
+    mm = dev(d["masked_m"])
+    pi = m.MaskedPath(w13i, w2, max_m, wl.expected_m, wl.T, wl.top_k)
+    pp = m.MaskedPath(w13p, w2, max_m, wl.expected_m, wl.T, wl.top_k)
+    out_i = host(pi(a3, mm, dev(d["row_of"]), dev(d["topk_weights"])), np.uint16)
+    out_p = host(pp(a3, mm, dev(d["row_of"]), dev(d["topk_weights"])), np.uint16)
+    torch.cuda.synchronize()
+    valid = np.concatenate([g * max_m + np.arange(c) for g, c in enumerate(d["masked_m"])])
+    assert np.array_equal(host(pi.Z, np.uint16)[valid], host(pp.Z, np.uint16)[valid])
+    assert np.array_equal(out_i, out_p)
+    a3h = d["a3"].reshape(G * max_m, wl.H)
+    refZ = oracle.silu_mul(oracle.masked_gemm(a3h, d["masked_m"], d["codes13"], d["scales13"]))
+    check_close(host(pi.Z, np.uint16)[valid], refZ[valid], "masked fused Z")
 
 
 def test_tiny_workload_full_path(m):

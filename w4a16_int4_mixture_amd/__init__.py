@@ -32,6 +32,12 @@ def _dev_empty(shape, dtype, device):
     return torch.empty(shape, dtype=dtype, device=device)
 
 
+def _workspace(nbytes, device):
+    """GEMM workspace: 256-byte granular and zeroed (its split-K arrival
+    counters must start at zero; calls leave them zero)."""
+    return torch.zeros(((nbytes + 255) // 256 * 256,), dtype=torch.uint8, device=device)
+
+
 @dataclass
 class PreparedWeight:
     packed: torch.Tensor        # uint8 device buffer
@@ -150,7 +156,7 @@ def run_gemm(args: _capi.w4a16_gemm_args, device, keep=None, stream=None):
     need = _capi.w4a16_gemm_workspace_bytes(args)
     ws = None
     if need and not args.workspace:
-        ws = _dev_empty(((need + 15) // 16 * 16,), torch.uint8, device)
+        ws = _workspace(need, device)
         args.workspace = ws.data_ptr()
         args.workspace_bytes = ws.numel()
     _capi.w4a16_moe_w4a16_gemm(args, stream)
@@ -161,7 +167,11 @@ def run_gemm(args: _capi.w4a16_gemm_args, device, keep=None, stream=None):
 
 class IndexedPath:
     """The whole indexed path with every buffer allocated once:
-    align -> gate/up GEMM (+ SiLU*gate) -> down GEMM -> top-k combine."""
+    align -> gate/up GEMM -> SiLU*gate -> down GEMM -> top-k combine.
+
+    With a W13 packed with gate/up interleave, SiLU*gate runs inside the
+    gate/up GEMM (one launch that writes Z); with a plain W13 the gate/up GEMM
+    stores Y13 and SiLU*gate is a call of its own (act)."""
 
     def __init__(self, w13: PreparedWeight, w2: PreparedWeight, T: int, top_k: int,
                  E_global: int, rows_hint: int = 0, tile_m: int = 0, split_k13: int = 0,
@@ -175,6 +185,8 @@ class IndexedPath:
         self.plan = plan
         self.routing = Routing(T, top_k, self.E, plan.block_m, plan.tile_m, device)
         cap = self.routing.sorted_cap
+        self.separate_act = not (w13.desc.flags & PACK_GATE_UP_INTERLEAVE)
+        self.Y13 = _dev_empty((cap, 2 * self.I), BF16, device) if self.separate_act else None
         self.Z = _dev_empty((cap, self.I), BF16, device)
         self.Y2 = _dev_empty((cap, self.H), BF16, device)
         self.out = _dev_empty((max(T, 1), self.H), BF16, device)
@@ -188,7 +200,7 @@ class IndexedPath:
             return
         buf = self._ws.get(key)
         if buf is None or buf.numel() < need:
-            buf = _dev_empty(((need + 255) // 256 * 256,), torch.uint8, self.device)
+            buf = _workspace(need, self.device)
             self._ws[key] = buf
         args.workspace = buf.data_ptr()
         args.workspace_bytes = buf.numel()
@@ -209,10 +221,25 @@ class IndexedPath:
         self._ws_for(("d", flags), a)
         return a
 
+    def stage_args(self, X):
+        """Argument structs of the two GEMM stages as the path launches them."""
+        if self.separate_act:
+            return self.gate_up_args(X, out=self.Y13, epilogue=_capi.W4A16_EPI_STORE), self.down_args()
+        return self.gate_up_args(X), self.down_args()
+
+    def act(self, stream=None):
+        """SiLU*gate on the rows of the padded routed layout (separate_act)."""
+        r = self.routing
+        _capi.w4a16_moe_silu_mul(self.Y13, r.sorted_cap, r.num_tokens_padded, self.I, self.Z,
+                                 stream)
+
     def __call__(self, X, topk_ids, topk_weights, expert_map=None, stream=None):
         self.routing.align(topk_ids, self.E_global, expert_map, stream=stream)
-        _capi.w4a16_moe_w4a16_gemm(self.gate_up_args(X), stream)
-        _capi.w4a16_moe_w4a16_gemm(self.down_args(), stream)
+        ga, da = self.stage_args(X)
+        _capi.w4a16_moe_w4a16_gemm(ga, stream)
+        if self.separate_act:
+            self.act(stream)
+        _capi.w4a16_moe_w4a16_gemm(da, stream)
         _capi.w4a16_moe_combine(self.Y2, self.Y2.shape[0], self.H, self.routing.row_of,
                                 topk_weights, self.T, self.top_k, self.out, stream)
         return self.out
@@ -241,7 +268,7 @@ class MaskedPath:
             return
         buf = self._ws.get(key)
         if buf is None or buf.numel() < need:
-            buf = _dev_empty(((need + 255) // 256 * 256,), torch.uint8, self.device)
+            buf = _workspace(need, self.device)
             self._ws[key] = buf
         args.workspace = buf.data_ptr()
         args.workspace_bytes = buf.numel()

@@ -110,16 +110,23 @@ static w4a16_status plan_impl(const w4a16_desc* d, int layout, int rows_hint, in
 
 // ---- GEMM ------------------------------------------------------------------
 
+// Workspace: [arrival counters | fp32 split-K partials | bf16 gate/up staging],
+// each part 256-byte aligned.  The counters must be zero before the first
+// call; every call leaves them zero.
 struct Resolved {
     GemmArgs g;
     int mt;
     int split;
     int64_t rows_cap;        // rows of the position-indexed output space
-    uint64_t ws_partial;     // bytes of fp32 partials
+    int64_t tiles_bound;     // tile indices a launch can visit
+    uint64_t ws_counters;    // bytes of arrival counters (split > 1)
+    uint64_t ws_partial;     // bytes of fp32 partials (split > 1)
     uint64_t ws_y13;         // bytes of the bf16 gate/up staging (SiLU not fused)
-    bool reduce;             // run the split-K reduction
     bool silu_separate;      // run the SiLU kernel on staged Y13
+    uint64_t ws_total() const { return ws_counters + ws_partial + ws_y13; }
 };
+
+static uint64_t round256(uint64_t b) { return (b + 255) / 256 * 256; }
 
 static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
     W4A16_CHECK_ARG(a, "null GEMM arguments");
@@ -138,10 +145,8 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
         set_error("weight packed with gate/up interleave used with a plain store epilogue");
         return W4A16_ERR_MODE_MISMATCH;
     }
-    if (a->epilogue == W4A16_EPI_SILU_MUL && interleaved) {
-        set_error("the in-register SiLU epilogue is not available in this build");
-        return W4A16_ERR_UNSUPPORTED;
-    }
+    W4A16_CHECK_ARG(!interleaved || d->chunk_n == 64 || d->chunk_n == 128,
+                    "gate/up interleave needs 64- or 128-column chunks");
     W4A16_CHECK_ARG(!(f32_out && a->epilogue != W4A16_EPI_STORE), "F32_OUT needs EPI_STORE");
     W4A16_CHECK_ARG(a->epilogue != W4A16_EPI_SILU_MUL || d->N % 16 == 0,
                     "SiLU epilogue needs N %% 16 == 0");
@@ -230,6 +235,7 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
             g.grid_tiles = a->blocks_cap;
         }
         g.grid_tiles = std::min(g.grid_tiles, 65535);
+        r->tiles_bound = a->tiles ? a->tiles_cap : a->blocks_cap;
         r->mt = tile_m / 16;
         r->split = split;
         r->rows_cap = a->sorted_cap;
@@ -275,6 +281,7 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
         g.grid_tiles_total = d->E * g.chunks_per_expert;
         g.grid_tiles = std::min(g.grid_tiles_total, 65535);
         int split = f32_out ? 1 : plan.split_k;
+        r->tiles_bound = g.grid_tiles_total;
         r->mt = plan.tile_m / 16;
         r->split = std::max(1, std::min(split, g.KSP / 8));
         r->rows_cap = rows;
@@ -284,17 +291,22 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
     g.split_k = r->split;
     g.unpack_mask = 0x000F000Fu;
     g.unpack_bits = 0x43004300u;
-    r->reduce = r->split > 1;
-    r->silu_separate = a->epilogue == W4A16_EPI_SILU_MUL && !r->reduce;
-    r->ws_partial = r->reduce ? static_cast<uint64_t>(r->split) * r->rows_cap * d->N * 4 : 0;
-    r->ws_y13 = r->silu_separate ? static_cast<uint64_t>(r->rows_cap) * d->N * 2 : 0;
+    const bool split = r->split > 1;
+    r->silu_separate = a->epilogue == W4A16_EPI_SILU_MUL && !interleaved;
+    const int64_t gx = (g.NC + 3) / 4;
+    r->ws_counters = split ? round256(static_cast<uint64_t>(r->tiles_bound) * kMaxTileParts * gx * 4) : 0;
+    r->ws_partial = split ? round256(static_cast<uint64_t>(r->split) * r->rows_cap * d->N * 4) : 0;
+    r->ws_y13 = r->silu_separate ? round256(static_cast<uint64_t>(r->rows_cap) * d->N * 2) : 0;
     g.ws_stride = r->rows_cap * d->N;
-    if (r->reduce) {
-        g.out_kind = OUT_PARTIAL;
-        g.out = a->workspace;
+    char* ws = static_cast<char*>(a->workspace);
+    g.counters = split && ws ? reinterpret_cast<int32_t*>(ws) : nullptr;
+    g.partials = split && ws ? reinterpret_cast<float*>(ws + r->ws_counters) : nullptr;
+    if (a->epilogue == W4A16_EPI_SILU_MUL && interleaved) {
+        g.out_kind = OUT_SILU;
+        g.out = a->out;
     } else if (r->silu_separate) {
         g.out_kind = OUT_BF16;
-        g.out = a->workspace;
+        g.out = ws ? ws + r->ws_counters + r->ws_partial : nullptr;
     } else {
         g.out_kind = f32_out ? OUT_F32 : OUT_BF16;
         g.out = a->out;
@@ -419,7 +431,7 @@ w4a16_status w4a16_gemm_workspace_bytes(const w4a16_gemm_args* args, uint64_t* b
     Resolved r;
     w4a16_status st = resolve(args, &r);
     if (st != W4A16_OK) return st;
-    *bytes = r.ws_partial + r.ws_y13;
+    *bytes = r.ws_total();
     return W4A16_OK;
 }
 
@@ -428,10 +440,10 @@ w4a16_status w4a16_moe_w4a16_gemm(const w4a16_gemm_args* args, void* stream) {
     Resolved r;
     w4a16_status st = resolve(args, &r);
     if (st != W4A16_OK) return st;
-    const uint64_t need = r.ws_partial + r.ws_y13;
+    const uint64_t need = r.ws_total();
     if (need > 0) {
-        if (!args->workspace || args->workspace_bytes < need || !aligned(args->workspace, 16)) {
-            set_error("workspace too small or misaligned: %llu bytes needed",
+        if (!args->workspace || args->workspace_bytes < need || !aligned(args->workspace, 256)) {
+            set_error("workspace too small or not 256-byte aligned: %llu bytes needed",
                       static_cast<unsigned long long>(need));
             return W4A16_ERR_CAPACITY;
         }
@@ -440,18 +452,12 @@ w4a16_status w4a16_moe_w4a16_gemm(const w4a16_gemm_args* args, void* stream) {
     launch_gemm_small(r.g, r.mt, s);
     st = check_launch("w4a16 gemm");
     if (st != W4A16_OK) return st;
-    const bool masked = args->layout == W4A16_LAYOUT_MASKED;
-    const int32_t* rows_dev = masked ? nullptr : args->num_tokens_padded;
-    const int32_t* mm = masked ? args->masked_m : nullptr;
-    const bool silu = args->epilogue == W4A16_EPI_SILU_MUL;
-    if (r.reduce) {
-        launch_splitk_reduce(static_cast<const float*>(args->workspace), r.split, r.g.ws_stride,
-                             r.rows_cap, rows_dev, args->desc->N, silu, mm, args->max_m,
-                             static_cast<uint16_t*>(args->out), s);
-        st = check_launch("split-K reduce");
-    } else if (r.silu_separate) {
-        launch_silu_mul(static_cast<const uint16_t*>(args->workspace), r.rows_cap, rows_dev,
-                        args->desc->N / 2, mm, args->max_m, static_cast<uint16_t*>(args->out), s);
+    if (r.silu_separate) {
+        const bool masked = args->layout == W4A16_LAYOUT_MASKED;
+        launch_silu_mul(static_cast<const uint16_t*>(r.g.out), r.rows_cap,
+                        masked ? nullptr : args->num_tokens_padded, args->desc->N / 2,
+                        masked ? args->masked_m : nullptr, args->max_m,
+                        static_cast<uint16_t*>(args->out), s);
         st = check_launch("silu_mul");
     }
     return st;

@@ -1,6 +1,6 @@
-// Bandwidth-bound steps around the GEMMs: SiLU(gate) * up, the fixed-order
-// reduction of split-K partials (optionally fused with the activation) and
-// the top-k weighted combine.  Each thread moves 16 bytes per access.
+// Bandwidth-bound steps around the GEMMs: SiLU(gate) * up (for weights
+// packed without gate/up interleave) and the top-k weighted combine.  Each
+// thread moves 16 bytes per access.
 //
 // Chord page, "Measurements": routing and activation sit outside the timed
 // gate/up + down unit; the computation between and after the GEMMs is the
@@ -14,7 +14,6 @@ namespace w4a16 {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline float lo_f(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ inline float hi_f(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
@@ -24,7 +23,6 @@ __device__ inline uint32_t bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, h);
 }
 __device__ inline uint32_t pack2(float a, float b) { return bf16_bits(a) | (bf16_bits(b) << 16); }
-__device__ inline float round_bf16(float x) { return __uint_as_float(bf16_bits(x) << 16); }
 
 // silu(g) * u in fp32 from bf16-valued inputs
 __device__ inline float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
@@ -52,43 +50,6 @@ __global__ void k_silu_mul(const uint16_t* __restrict__ y13, int64_t rows,
         o.z = pack2(silu_mul(lo_f(g.z), lo_f(u.z)), silu_mul(hi_f(g.z), hi_f(u.z)));
         o.w = pack2(silu_mul(lo_f(g.w), lo_f(u.w)), silu_mul(hi_f(g.w), hi_f(u.w)));
         *reinterpret_cast<u32x4*>(z + r * I + j) = o;
-    }
-}
-
-// out[r, n] = bf16( sum_{s < S} ws[s, r, n] ), s ascending; with `silu`, the
-// gate (n < N/2) and up (n >= N/2) sums are each rounded to bf16 first and
-// Z[r, j] = bf16( silu(g) * u ) is written instead ([rows, N/2]).
-__global__ void k_splitk_reduce(const float* __restrict__ ws, int S, int64_t stride,
-                                int64_t rows, const int32_t* __restrict__ rows_dev, int N,
-                                int silu, const int32_t* __restrict__ masked_m, int max_m,
-                                uint16_t* __restrict__ out) {
-    const int64_t nrows = rows_dev ? static_cast<int64_t>(rows_dev[0]) : rows;
-    const int width = silu ? N / 2 : N;
-    const int per_row = width / 4;
-    const int64_t total = nrows * per_row;
-    for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
-         idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        const int64_t r = idx / per_row;
-        const int j = static_cast<int>(idx % per_row) * 4;
-        if (masked_m && (r % max_m) >= masked_m[r / max_m]) continue;  // row past its expert's count
-        f32x4 a = *reinterpret_cast<const f32x4*>(ws + r * N + j);
-        for (int s = 1; s < S; ++s) a += *reinterpret_cast<const f32x4*>(ws + s * stride + r * N + j);
-        uint32_t lo, hi;
-        if (silu) {
-            f32x4 b = *reinterpret_cast<const f32x4*>(ws + r * N + N / 2 + j);
-            for (int s = 1; s < S; ++s)
-                b += *reinterpret_cast<const f32x4*>(ws + s * stride + r * N + N / 2 + j);
-            lo = pack2(silu_mul(round_bf16(a.x), round_bf16(b.x)),
-                       silu_mul(round_bf16(a.y), round_bf16(b.y)));
-            hi = pack2(silu_mul(round_bf16(a.z), round_bf16(b.z)),
-                       silu_mul(round_bf16(a.w), round_bf16(b.w)));
-        } else {
-            lo = pack2(a.x, a.y);
-            hi = pack2(a.z, a.w);
-        }
-        uint32_t* o = reinterpret_cast<uint32_t*>(out + r * width + j);
-        o[0] = lo;
-        o[1] = hi;
     }
 }
 
@@ -133,14 +94,6 @@ void launch_silu_mul(const uint16_t* y13, int64_t rows, const int32_t* rows_dev,
                      const int32_t* masked_m, int max_m, uint16_t* z, hipStream_t s) {
     k_silu_mul<<<grid_for(rows * (I / 8), 256), 256, 0, s>>>(y13, rows, rows_dev, I, masked_m,
                                                              max_m, z);
-}
-
-void launch_splitk_reduce(const float* ws, int split_k, int64_t ws_stride, int64_t rows,
-                          const int32_t* rows_dev, int N, bool silu, const int32_t* masked_m,
-                          int max_m, uint16_t* out, hipStream_t s) {
-    const int width = silu ? N / 2 : N;
-    k_splitk_reduce<<<grid_for(rows * (width / 4), 256), 256, 0, s>>>(
-        ws, split_k, ws_stride, rows, rows_dev, N, silu ? 1 : 0, masked_m, max_m, out);
 }
 
 void launch_combine(const uint16_t* y, int64_t y_rows, int H, const int32_t* row_of,

@@ -294,9 +294,10 @@ struct Lds {
 // Iterations cover two stages (16 groups); the K range is padded at its start
 // by one virtual record (zero scales) when it holds an odd number of records.
 template <int MT, int WPL, int MTMAX>
-__device__ void stream_loop(const Src<MT>& src, int ks0, int ks1, int ks_real, int wave,
-                            int lane, u32x4* lds, f32x4 (&acc)[MT][WPL], uint32_t mask,
-                            uint32_t bits) {
+__device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1, int ks_real,
+                                            int wave, int lane, u32x4* lds,
+                                            f32x4 (&acc)[MT][WPL], uint32_t mask,
+                                            uint32_t bits) {
     constexpr int D = 2 * kSG;
     using L = Lds<MTMAX, WPL>;
     if (ks1 <= ks0) return;
@@ -349,10 +350,96 @@ __device__ void stream_loop(const Src<MT>& src, int ks0, int ks1, int ks_real, i
     stage_groups<MT, WPL, D>(ring, kSG, abuf1, srd1, src, 0, false, acc, mask, bits, lane);
 }
 
-// One (row tile, 4 column chunks, K split) with MT active row blocks.
+// silu(g) * u with g and u first rounded to bf16 (the rounding of a gate/up
+// output that is stored and then activated)
+__device__ inline float silu_mul_bf16(float g, float u) {
+    g = __uint_as_float(static_cast<uint32_t>(f32_to_bf16_rne(g)) << 16);
+    u = __uint_as_float(static_cast<uint32_t>(f32_to_bf16_rne(u)) << 16);
+    return g / (1.0f + __expf(-g)) * u;
+}
+
+constexpr int kDeviceScope = 16;  // cache-policy bits of a device-coherent access
+
+// Split-K fix-up.  Every split writes its fp32 partial of the tile part, then
+// one thread counts the arrival; the split that arrives last re-reads the
+// others' partials and adds all of them in split order (its own from
+// registers), so the sum does not depend on which split came last.  The last
+// one also resets the counter to zero for the next call.  Returns true in the
+// last split's workgroup, with acc holding the full sum.  No workgroup waits
+// for another one.
+//
+// Partials are stored and loaded with device-scope coherent accesses (the
+// splits of a tile may run on different XCDs, whose L2 caches are separate),
+// and each wavefront waits for its stores to complete before the arrival is
+// counted.  Device-scope fences are avoided on purpose: they write back and
+// invalidate the whole L2 of the XCD, which costs far more than the GEMM.
+template <int MT, int WPL>
+__device__ __forceinline__ bool splitk_fixup(const GemmArgs& a, int p0, int nrows, int chunk,
+                                             bool active, int lane, int32_t* counter,
+                                             f32x4 (&acc)[MT][WPL]) {
+    __shared__ int last_flag;
+    const int s = blockIdx.z;
+    // byte offsets inside one split's partial [rows, N]: a per-lane part and
+    // a uniform part per (t, i, j); a split's partial is below 4 GiB (host check)
+    const uint32_t voff =
+        static_cast<uint32_t>((static_cast<int64_t>(p0 + 4 * (lane >> 4)) * a.N + chunk * a.CW +
+                               (lane & 15)) * 4);
+    const uint64_t split_bytes = static_cast<uint64_t>(a.ws_stride) * 4;
+    if (active) {
+        const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.partials + s * a.ws_stride, split_bytes);
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (16 * t + 4 * (lane >> 4) + i >= nrows) continue;
+#pragma unroll
+                for (int j = 0; j < WPL; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[t][j][i]), ws, voff,
+                                                          ((16 * t + i) * a.N + 16 * j) * 4,
+                                                          kDeviceScope);
+            }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wavefront's partial has reached memory
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int prev = atomicAdd(counter, 1);
+        const bool last = prev == a.split_k - 1;
+        if (last) atomicExch(counter, 0);
+        last_flag = last;
+    }
+    __syncthreads();
+    const bool last = last_flag != 0;
+    if (!last) return false;
+    if (!active) return true;
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (16 * t + 4 * (lane >> 4) + i >= nrows) continue;
+#pragma unroll
+            for (int j = 0; j < WPL; ++j) {
+                const int soff = ((16 * t + i) * a.N + 16 * j) * 4;
+                float v = 0.0f;
+                for (int q = 0; q < a.split_k; ++q) {
+                    float pq = acc[t][j][i];
+                    if (q != s)
+                        pq = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                            make_rsrc(a.partials + q * a.ws_stride, split_bytes), voff, soff,
+                            kDeviceScope));
+                    v = q == 0 ? pq : v + pq;
+                }
+                acc[t][j][i] = v;
+            }
+        }
+    return true;
+}
+
+// One (row tile part, 4 column chunks, K split) with MT active row blocks.
+// `counter`: this part's arrival counter (split_k > 1).
 template <int MT, int WPL, int MTMAX>
-__device__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, int nrows, int chunk, int wave,
-                             int lane, u32x4* lds) {
+__device__ __forceinline__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, int nrows,
+                                             int chunk, int wave, int lane, u32x4* lds,
+                                             int32_t* counter) {
     const bool slot_rows = a.tile_src != TILE_MASKED;
     const bool active = chunk < a.NC;
 
@@ -399,10 +486,12 @@ __device__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, int nrows, int ch
     uint32_t vbits = a.unpack_bits;
     asm volatile("" : "+v"(vbits));
     stream_loop<MT, WPL, MTMAX>(src, ks0, ks1, a.KS, wave, lane, lds, acc, a.unpack_mask, vbits);
+
+    if (a.split_k > 1 && !splitk_fixup<MT, WPL>(a, p0, nrows, chunk, active, lane, counter, acc))
+        return;
     if (!active) return;
 
     // epilogue: lane holds rows 16t + 4*(lane/16) + i of column 16j + lane%16
-    const int col0 = chunk * a.CW + (lane & 15);
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
 #pragma unroll
@@ -413,15 +502,24 @@ __device__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, int nrows, int ch
             if (slot_rows && (a.tile_src == TILE_BLOCKS || a.orow == W4A16_OROW_SLOT)) {
                 int f = a.sorted_ids[p0 + r];
                 if (f < 0 || f >= a.num_slots) continue;
-                if (a.orow == W4A16_OROW_SLOT && a.out_kind != OUT_PARTIAL) orow = f;
+                if (a.orow == W4A16_OROW_SLOT) orow = f;
             }
-            if (a.out_kind == OUT_BF16) {
-                uint16_t* o = static_cast<uint16_t*>(a.out) + orow * a.N + col0;
+            if (a.out_kind == OUT_SILU) {
+                // gate/up interleave: columns 16j (j < WPL/2) of the chunk are
+                // gate columns, 16(j + WPL/2) the matching up columns
+                uint16_t* o = static_cast<uint16_t*>(a.out) + orow * (a.N / 2) +
+                              chunk * (a.CW / 2) + (lane & 15);
+#pragma unroll
+                for (int j = 0; j < WPL / 2; ++j)
+                    o[16 * j] =
+                        f32_to_bf16_rne(silu_mul_bf16(acc[t][j][i], acc[t][j + WPL / 2][i]));
+            } else if (a.out_kind == OUT_BF16) {
+                uint16_t* o =
+                    static_cast<uint16_t*>(a.out) + orow * a.N + chunk * a.CW + (lane & 15);
 #pragma unroll
                 for (int j = 0; j < WPL; ++j) o[16 * j] = f32_to_bf16_rne(acc[t][j][i]);
             } else {
-                float* o = static_cast<float*>(a.out) +
-                           (a.out_kind == OUT_PARTIAL ? s * a.ws_stride : 0) + orow * a.N + col0;
+                float* o = static_cast<float*>(a.out) + orow * a.N + chunk * a.CW + (lane & 15);
 #pragma unroll
                 for (int j = 0; j < WPL; ++j) o[16 * j] = acc[t][j][i];
             }
@@ -430,25 +528,32 @@ __device__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, int nrows, int ch
 }
 
 template <int MT, int WPL>
-__device__ void gemm_tile_part(const GemmArgs& a, int e, int p0, int nrows, int chunk, int wave,
-                               int lane, u32x4* lds) {
+__device__ __forceinline__ void gemm_tile_part(const GemmArgs& a, int e, int p0, int nrows,
+                                               int chunk, int wave, int lane, u32x4* lds,
+                                               int32_t* counter) {
     const int mt_active = (nrows + 15) >> 4;
-    if (mt_active <= 1) gemm_tile_mt<1, WPL, MT>(a, e, p0, nrows, chunk, wave, lane, lds);
-    else if (MT >= 2 && mt_active == 2) gemm_tile_mt<(MT >= 2 ? 2 : 1), WPL, MT>(a, e, p0, nrows, chunk, wave, lane, lds);
-    else if (MT >= 3 && mt_active == 3) gemm_tile_mt<(MT >= 3 ? 3 : 1), WPL, MT>(a, e, p0, nrows, chunk, wave, lane, lds);
-    else if (MT >= 4) gemm_tile_mt<(MT >= 4 ? 4 : 1), WPL, MT>(a, e, p0, nrows, chunk, wave, lane, lds);
+    if (mt_active <= 1)
+        gemm_tile_mt<1, WPL, MT>(a, e, p0, nrows, chunk, wave, lane, lds, counter);
+    else if (MT >= 2 && mt_active == 2)
+        gemm_tile_mt<(MT >= 2 ? 2 : 1), WPL, MT>(a, e, p0, nrows, chunk, wave, lane, lds, counter);
+    else if (MT >= 3 && mt_active == 3)
+        gemm_tile_mt<(MT >= 3 ? 3 : 1), WPL, MT>(a, e, p0, nrows, chunk, wave, lane, lds, counter);
+    else if (MT >= 4)
+        gemm_tile_mt<(MT >= 4 ? 4 : 1), WPL, MT>(a, e, p0, nrows, chunk, wave, lane, lds, counter);
 }
 
 // A tile of more than 16 * MT rows (a variant whose registers hold fewer row
 // blocks than the tile) is processed in parts of 16 * MT rows; each part
 // re-streams the chunk.
 template <int MT, int WPL>
-__device__ void gemm_tile(const GemmArgs& a, int e, int p0, int nrows, int chunk, int wave,
-                          int lane, u32x4* lds) {
-    for (int r = 0; r < nrows; r += 16 * MT) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, int ty, int e, int p0, int nrows,
+                                          int chunk, int wave, int lane, u32x4* lds) {
+    for (int r = 0, part = 0; r < nrows; r += 16 * MT, ++part) {
         if (r > 0) __syncthreads();  // the part reuses the staging buffers
+        int32_t* counter =
+            a.counters + (static_cast<int64_t>(ty) * kMaxTileParts + part) * gridDim.x + blockIdx.x;
         gemm_tile_part<MT, WPL>(a, e, p0 + r, nrows - r < 16 * MT ? nrows - r : 16 * MT, chunk,
-                                wave, lane, lds);
+                                wave, lane, lds, counter);
     }
 }
 
@@ -486,7 +591,7 @@ __global__ void __launch_bounds__(256) k_gemm_small(GemmArgs a) {
             nrows = cnt - r0 < a.tile_m ? cnt - r0 : a.tile_m;
         }
         if (e < 0 || e >= a.E || nrows <= 0) continue;
-        gemm_tile<MT, WPL>(a, e, p0, nrows, chunk, wave, lane, lds);
+        gemm_tile<MT, WPL>(a, ty, e, p0, nrows, chunk, wave, lane, lds);
         __syncthreads();  // the next tile reuses the staging buffers
     }
 }

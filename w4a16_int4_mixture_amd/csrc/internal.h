@@ -80,8 +80,12 @@ void launch_align(const AlignArgs& a, hipStream_t s);
 
 // How a GEMM block finds its rows.
 enum TileSrc { TILE_TABLE = 0, TILE_BLOCKS = 1, TILE_MASKED = 2 };
-// What the GEMM stores.
-enum OutKind { OUT_BF16 = 0, OUT_F32 = 1, OUT_PARTIAL = 2 };
+// What the GEMM stores: bf16 [rows, N], fp32 [rows, N], or SiLU(gate) * up
+// as bf16 [rows, N/2] from a gate/up-interleaved weight.
+enum OutKind { OUT_BF16 = 0, OUT_F32 = 1, OUT_SILU = 2 };
+
+// Row-tile parts per tile (a tile of up to 64 rows in parts of 16 * MT rows).
+constexpr int kMaxTileParts = 4;
 
 struct GemmArgs {
     // rows
@@ -107,7 +111,12 @@ struct GemmArgs {
     void* out;
     int out_kind;
     int split_k;
-    int64_t ws_stride;  // elements between split partials (OUT_PARTIAL)
+    // split-K (split_k > 1): fp32 partials [split_k][ws_stride] (rows of the
+    // position-indexed space x N) and one arrival counter per (tile, part,
+    // column group), zero between calls
+    float* partials;
+    int32_t* counters;
+    int64_t ws_stride;
     uint32_t unpack_mask;  // 0x000F000F: one code in each 16-bit half
     uint32_t unpack_bits;  // 0x43004300: bf16 exponent of 128 in each half
 };
@@ -116,9 +125,6 @@ void launch_gemm_small(const GemmArgs& a, int mt, hipStream_t s);
 // masked_m != nullptr: rows r with r % max_m >= masked_m[r / max_m] are skipped.
 void launch_silu_mul(const uint16_t* y13, int64_t rows, const int32_t* rows_dev, int I,
                      const int32_t* masked_m, int max_m, uint16_t* z, hipStream_t s);
-void launch_splitk_reduce(const float* ws, int split_k, int64_t ws_stride, int64_t rows,
-                          const int32_t* rows_dev, int N, bool silu, const int32_t* masked_m,
-                          int max_m, uint16_t* out, hipStream_t s);
 void launch_combine(const uint16_t* y, int64_t y_rows, int H, const int32_t* row_of,
                     const float* w, int T, int top_k, uint16_t* out, hipStream_t s);
 
