@@ -219,6 +219,115 @@ def test_pipelined_main_loop_exact(m, H, tile_m, profile):
     assert bad.size == 0, f"{bad.size} rows differ, first positions {pos[bad[:8]]}"
 
 
+# ------------------------------------------------------ large-M kernel ----
+
+@pytest.mark.parametrize("H", [1024, 1056, 1248])
+@pytest.mark.parametrize("tile_m", [128, 192, 256])
+def test_large_tile_kernel_exact(m, H, tile_m):
+    """The large-M kernel (prefill profile, tiles over 64 rows) under the
+    exactness invariant: power-of-two scales make every dequantised weight
+    exact in bf16, so gate/up, the fused SiLU path's inputs and down are
+    bit-identical to the oracle.  About 220 rows per expert: tiles of 256
+    rows use all 16 row blocks, tiles of 128 and 192 split experts."""
+    from w4a16_int4_mixture_amd import _capi
+    E, I, T, k = 3, 128, 330, 2
+    d = exact_problem(H + tile_m, E, H, I, T, k)
+    print(f"large tile: H={H} tile_m={tile_m}", flush=True)
+    w13 = prepare(m, d["codes13"], d["scales13"], 2)
+    plan = _capi.w4a16_plan_gemm(w13.desc, _capi.W4A16_LAYOUT_INDEXED, T * k, 0, tile_m)
+    assert plan.kernel == 2 and plan.split_k == 1
+    r = m.Routing(T, k, E, 16, tile_m, "cuda")
+    r.align(dev(d["topk_ids"]), E)
+    X = dev(d["X"])
+    Y13 = torch.full((r.sorted_cap, 2 * I), -1, dtype=torch.int16, device="cuda")
+    m.run_gemm(m.gemm_args_indexed(w13, X, r, Y13, _capi.W4A16_AROW_TOKEN, rows_hint=T * k),
+               "cuda")
+    Y13f = torch.zeros((r.sorted_cap, 2 * I), dtype=torch.float32, device="cuda")
+    m.run_gemm(m.gemm_args_indexed(w13, X, r, Y13f, _capi.W4A16_AROW_TOKEN, flags=1,
+                                   rows_hint=T * k), "cuda")
+    torch.cuda.synchronize()
+    pos, f = slot_rows(r, T, k)
+    ref13 = oracle.moe_gate_up(d["X"], d["topk_ids"], E, None, d["codes13"], d["scales13"])
+    got = host(Y13, np.uint16)[pos]
+    bad = np.nonzero(np.any(got != ref13[f], axis=1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first positions {pos[bad[:8]]}"
+    ref13f = oracle.grouped_gemm(d["X"], f // k, d["topk_ids"].ravel()[f], d["codes13"],
+                                 d["scales13"], 2 * I, H, out_f32=True)
+    assert np.array_equal(host(Y13f)[pos], ref13f)
+    if H % 128:
+        return          # H is the N of down: only multiples of the 128-column chunk
+    # down, K = I = 128: one record of padding groups past K
+    w2 = prepare(m, d["codes2"], d["scales2"], 2)
+    rng = np.random.default_rng(7)
+    Zi = synth.bf16_trunc(rng.integers(-4, 5, size=(r.sorted_cap, I)).astype(np.float32))
+    Y2 = torch.zeros((r.sorted_cap, H), dtype=torch.int16, device="cuda")
+    m.run_gemm(m.gemm_args_indexed(w2, dev(Zi), r, Y2, _capi.W4A16_AROW_POSITION,
+                                   rows_hint=T * k), "cuda")
+    torch.cuda.synchronize()
+    Zslot = np.zeros((T * k, I), np.uint16)
+    Zslot[f] = Zi[pos]
+    ref2 = oracle.moe_down(Zslot, d["topk_ids"], E, None, d["codes2"], d["scales2"])
+    assert np.array_equal(host(Y2, np.uint16)[pos], ref2[f])
+
+
+@pytest.mark.parametrize("interleave", [False, True])
+def test_large_tile_kernel_random(m, interleave):
+    """General inputs through the large-M kernel: it rounds each dequantised
+    weight to bf16 once, so it is held to the oracle with bf16-rounded weights
+    at the tight bar, and to the exact oracle within the tolerance; the fused
+    SiLU epilogue equals the stored-Y13 path bit for bit."""
+    E, H, I, T, k = 4, 1024, 256, 200, 4
+    d = synth.random_small(51, E, H, I, T, k)
+    print(f"large tile random: interleave={interleave}", flush=True)
+    path, out = run_indexed(m, d, E, 2, rows_hint=T * k, interleave=interleave)
+    assert path.plan.tile_m > 64 and path.plan.kernel == 2
+    pos, f = slot_rows(path.routing, T, k)
+    args = (d["X"], d["topk_ids"], d["topk_weights"], E, None, d["codes13"], d["scales13"],
+            d["codes2"], d["scales2"])
+    ref1 = oracle.moe_forward(*args, wmode=1, intermediates=True)
+    check_close(host(path.Z, np.uint16)[pos], ref1["Z"][f], "large Z (bf16 weights)")
+    check_close(host(path.Y2, np.uint16)[pos], ref1["Y2"][f], "large Y2 (bf16 weights)")
+    check_close(out, ref1["out"], "large out (bf16 weights)")
+    ref0 = oracle.moe_forward(*args)
+    check_close(out, ref0, "large out (exact weights)", exact_frac=0.0)
+    if interleave:
+        pp, out_p = run_indexed(m, d, E, 2, rows_hint=T * k, interleave=False)
+        assert np.array_equal(host(path.Z, np.uint16)[pos], host(pp.Z, np.uint16)[pos])
+        assert np.array_equal(out, out_p)
+
+
+def test_large_tile_block_mode_and_masked(m):
+    """The large-M kernel from vLLM-style blocks (block_m 128, slot rows) and
+    from the grouped masked layout (expected_m 96)."""
+    from w4a16_int4_mixture_amd import _capi
+    E, H, I, T, k = 3, 512, 128, 120, 2
+    d = synth.random_small(61, E, H, I, T, k)
+    w13 = prepare(m, d["codes13"], d["scales13"], 2)
+    r = m.Routing(T, k, E, 128, 0, "cuda")
+    r.align(dev(d["topk_ids"]), E)
+    out = torch.full((T * k, 2 * I), -1, dtype=torch.int16, device="cuda")
+    a = m.gemm_args_indexed(w13, dev(d["X"]), r, out, _capi.W4A16_AROW_TOKEN,
+                            orow=_capi.W4A16_OROW_SLOT, use_tiles=False)
+    m.run_gemm(a, "cuda")
+    torch.cuda.synchronize()
+    ref = oracle.moe_gate_up(d["X"], d["topk_ids"], E, None, d["codes13"], d["scales13"], wmode=1)
+    check_close(host(out, np.uint16), ref, "large blocks slot rows")
+    # masked: G = 3 experts, counts 100, 0, 37 in a [G * 128, H] layout with NaN padding
+    G, max_m = 3, 128
+    counts = np.array([100, 0, 37], np.int32)
+    rng = np.random.default_rng(62)
+    a3 = np.full((G * max_m, H), 0x7FC0, np.uint16)
+    for g, c in enumerate(counts):
+        a3[g * max_m: g * max_m + c] = synth.random_activations(rng, c, H)
+    out = torch.zeros((G * max_m, 2 * I), dtype=torch.int16, device="cuda")
+    a = m.gemm_args_masked(w13, dev(a3), dev(counts), max_m, 96, out)
+    m.run_gemm(a, "cuda")
+    torch.cuda.synchronize()
+    refm = oracle.masked_gemm(a3, counts, d["codes13"], d["scales13"], wmode=1)
+    valid = np.concatenate([g * max_m + np.arange(c) for g, c in enumerate(counts)])
+    check_close(host(out, np.uint16)[valid], refm[valid], "large masked")
+
+
 # --------------------------------------------------------- general inputs ----
 
 def run_indexed(m, d, E_global, profile, tile_m=0, split=0, rows_hint=None, interleave=True):
@@ -418,12 +527,12 @@ def test_decode_workload_full_parity(m, decode_data):
     check_close(out, ref["out"], "decode out")
 
 
-def sampled_reference(d, E_global, tokens):
+def sampled_reference(d, E_global, tokens, wmode=0):
     """Oracle output rows for a sample of tokens (computes only their slots)."""
     ids = d["topk_ids"][tokens]
     w = d["topk_weights"][tokens]
     return oracle.moe_forward(d["X"][tokens], ids, w, E_global, d["expert_map"], d["codes13"],
-                              d["scales13"], d["codes2"], d["scales2"])
+                              d["scales13"], d["codes2"], d["scales2"], wmode=wmode)
 
 
 @pytest.mark.parametrize("name", ["prefill", "tp8"])
@@ -437,8 +546,13 @@ def test_large_workloads_sampled_parity(m, name):
     path, out = run_indexed(m, d, wl.E_global, profile, rows_hint=rows_hint)
     rng = np.random.default_rng(5)
     tokens = np.sort(rng.choice(wl.T, size=24, replace=False))
-    ref = sampled_reference(d, wl.E_global, tokens)
-    check_close(out[tokens], ref, f"{name} out (24 sampled tokens)")
+    # the large-M kernel (prefill) rounds each dequantised weight to bf16 once
+    wmode = 1 if path.plan.kernel == 2 else 0
+    ref = sampled_reference(d, wl.E_global, tokens, wmode)
+    check_close(out[tokens], ref, f"{name} out (24 sampled tokens, wmode {wmode})")
+    if wmode:
+        check_close(out[tokens], sampled_reference(d, wl.E_global, tokens), f"{name} exact weights",
+                    exact_frac=0.0)
 
 
 def test_masked_workload_parity(m):

@@ -32,13 +32,17 @@ def hipcc() -> str:
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
+
+# Per-source extra flags.  The streaming GEMM keeps its MFMA accumulators in
+# VGPRs (no accumulator-register copies in its loop); the large-M GEMM holds
+# 256 accumulators per lane and needs the accumulator registers.
+EXTRA = {"gemm_small.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the device-only feature flag: drop that note
     noise = "is not a recognized feature for this target"

@@ -38,8 +38,18 @@ static bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
-// Largest tile height the streaming kernel supports (4 MFMA row blocks).
+// Largest tile height of the streaming kernel (4 MFMA row blocks) and of the
+// large-M kernel (prefill profile only).
 static constexpr int kSmallMaxTile = 64;
+static constexpr int kLargeMaxTile = 256;
+// Routed rows per expert from which a prefill-profile weight uses the large-M
+// kernel (the pages switch their prefill heuristic at 80 tokens per expert;
+// on CDNA4 the per-tile dequant pays off from about 4 row blocks).
+static constexpr int kLargeMinRows = 64;
+
+static int max_tile(const w4a16_desc* d) {
+    return d->profile == W4A16_PROFILE_PREFILL ? kLargeMaxTile : kSmallMaxTile;
+}
 
 __device__ int32_t g_routing_errors;
 
@@ -84,27 +94,36 @@ static w4a16_status plan_impl(const w4a16_desc* d, int layout, int rows_hint, in
         }
         const bool deep_k = d->K >= 4096;
         const int64_t want = deep_k ? ceil_div(13LL * expected_m, 10) : ceil_div(5LL * expected_m, 4);
-        tile_m = static_cast<int>(std::min<int64_t>(std::max<int64_t>(round_up(want, 16), 16), kSmallMaxTile));
+        const int cap = expected_m >= kLargeMinRows ? max_tile(d) : kSmallMaxTile;
+        tile_m = static_cast<int>(std::min<int64_t>(std::max<int64_t>(round_up(want, 16), 16), cap));
         tiles_est = E;
     } else {
         if (tile_m_in > 0) {
             tile_m = tile_m_in;
         } else {
             const double tok_e = rows_hint > 0 ? static_cast<double>(rows_hint) / E : 16.0;
-            tile_m = static_cast<int>(std::min<int64_t>(
-                std::max<int64_t>(round_up(static_cast<int64_t>(2.0 * tok_e + 0.999), 16), 16), kSmallMaxTile));
+            if (tok_e >= kLargeMinRows && max_tile(d) > kSmallMaxTile) {
+                // one tile holds an expert's rows up to ~1.4x the mean
+                // (Poisson-like tails), in 64-row steps
+                tile_m = static_cast<int>(std::min<int64_t>(
+                    round_up(static_cast<int64_t>(1.4 * tok_e + 0.999), 64), kLargeMaxTile));
+            } else {
+                tile_m = static_cast<int>(std::min<int64_t>(
+                    std::max<int64_t>(round_up(static_cast<int64_t>(2.0 * tok_e + 0.999), 16), 16),
+                    kSmallMaxTile));
+            }
         }
         tiles_est = rows_hint > 0 ? ceil_div(rows_hint, tile_m) + E / 2 : E;
     }
     p->block_m = 16;
     p->tile_m = tile_m;
-    p->kernel = 1;
+    p->kernel = tile_m > kSmallMaxTile ? 2 : 1;
     const int64_t rows_est = layout == W4A16_LAYOUT_MASKED
                                  ? static_cast<int64_t>(E) * expected_m
                                  : std::max<int64_t>(rows_hint, E);
     const int64_t active = std::min<int64_t>(E, std::max<int64_t>(tiles_est, 1));
     const int64_t weight_bytes = active * static_cast<int64_t>(d->N) * d->K * 18 / 32;
-    p->split_k = choose_split(tiles_est, rows_est, NC, stages, d->N, weight_bytes);
+    p->split_k = p->kernel == 2 ? 1 : choose_split(tiles_est, rows_est, NC, stages, d->N, weight_bytes);
     return W4A16_OK;
 }
 
@@ -115,6 +134,7 @@ static w4a16_status plan_impl(const w4a16_desc* d, int layout, int rows_hint, in
 // call; every call leaves them zero.
 struct Resolved {
     GemmArgs g;
+    int kernel;              // 1 streaming, 2 large-M
     int mt;
     int split;
     int64_t rows_cap;        // rows of the position-indexed output space
@@ -186,16 +206,16 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
             W4A16_CHECK_ARG(a->tile_count && aligned(a->tiles, 16), "tile table needs tile_count and 16-byte alignment");
             W4A16_CHECK_ARG(a->tiles_cap >= 1, "tiles_cap must be positive");
             W4A16_CHECK_ARG(a->tile_m >= 16 && a->tile_m % 16 == 0, "tile_m must be a positive multiple of 16");
-            if (a->tile_m > kSmallMaxTile) {
-                set_error("tile_m %d exceeds the supported %d", a->tile_m, kSmallMaxTile);
+            if (a->tile_m > max_tile(d)) {
+                set_error("tile_m %d exceeds the %d this weight profile supports", a->tile_m, max_tile(d));
                 return W4A16_ERR_UNSUPPORTED;
             }
             tile_m = a->tile_m;
         } else {
             W4A16_CHECK_ARG(a->expert_ids && a->blocks_cap >= 1, "indexed layout without tiles needs expert_ids");
             W4A16_CHECK_ARG(a->block_m >= 16 && a->block_m % 16 == 0, "block_m must be a positive multiple of 16");
-            if (a->block_m > kSmallMaxTile) {
-                set_error("block_m %d exceeds the supported %d", a->block_m, kSmallMaxTile);
+            if (a->block_m > max_tile(d)) {
+                set_error("block_m %d exceeds the %d this weight profile supports", a->block_m, max_tile(d));
                 return W4A16_ERR_UNSUPPORTED;
             }
             tile_m = a->block_m;
@@ -203,8 +223,10 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
         st = plan_impl(d, W4A16_LAYOUT_INDEXED, a->rows_hint, 0, tile_m, &plan);
         if (st != W4A16_OK) return st;
         int split = a->split_k > 0 ? a->split_k : plan.split_k;
-        if (a->orow == W4A16_OROW_SLOT || f32_out) split = 1;
+        // the large-M kernel runs unsplit: split_k applies to the streaming kernel
+        if (a->orow == W4A16_OROW_SLOT || f32_out || plan.kernel == 2) split = 1;
         split = std::max(1, std::min(split, g.KSP / 8));
+        r->kernel = plan.kernel;
         {
             const int64_t need_a = a->arow == W4A16_AROW_POSITION ? a->sorted_cap
                                    : a->arow == W4A16_AROW_SLOT   ? a->num_slots
@@ -280,7 +302,8 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
         g.chunks_per_expert = static_cast<int>(ceil_div(a->max_m, plan.tile_m));
         g.grid_tiles_total = d->E * g.chunks_per_expert;
         g.grid_tiles = std::min(g.grid_tiles_total, 65535);
-        int split = f32_out ? 1 : plan.split_k;
+        int split = f32_out || plan.kernel == 2 ? 1 : plan.split_k;
+        r->kernel = plan.kernel;
         r->tiles_bound = g.grid_tiles_total;
         r->mt = plan.tile_m / 16;
         r->split = std::max(1, std::min(split, g.KSP / 8));
@@ -331,8 +354,8 @@ w4a16_status w4a16_plan_gemm(const w4a16_desc* desc, int32_t layout, int32_t row
     w4a16_status st = check_desc(desc);
     if (st != W4A16_OK) return st;
     W4A16_CHECK_ARG(layout == W4A16_LAYOUT_INDEXED || layout == W4A16_LAYOUT_MASKED, "unknown layout %d", layout);
-    W4A16_CHECK_ARG(tile_m == 0 || (tile_m >= 16 && tile_m % 16 == 0 && tile_m <= kSmallMaxTile),
-                    "tile_m must be 0 or a multiple of 16 up to %d", kSmallMaxTile);
+    W4A16_CHECK_ARG(tile_m == 0 || (tile_m >= 16 && tile_m % 16 == 0 && tile_m <= max_tile(desc)),
+                    "tile_m must be 0 or a multiple of 16 up to %d for this profile", max_tile(desc));
     return plan_impl(desc, layout, rows_hint, expected_m, tile_m, plan);
 }
 
@@ -449,7 +472,10 @@ w4a16_status w4a16_moe_w4a16_gemm(const w4a16_gemm_args* args, void* stream) {
         }
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    launch_gemm_small(r.g, r.mt, s);
+    if (r.kernel == 2)
+        launch_gemm_large(r.g, s);
+    else
+        launch_gemm_small(r.g, r.mt, s);
     st = check_launch("w4a16 gemm");
     if (st != W4A16_OK) return st;
     if (r.silu_separate) {

@@ -32,23 +32,16 @@
 //     leading slots before the range re-read its first group with zeroed
 //     scales (they add exactly zero).
 
+#include "device_common.h"
 #include "internal.h"
 
 namespace w4a16 {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+using namespace dev;
 
 constexpr int kSG = 8;  // groups of K per LDS stage
-
-__device__ inline uint16_t f32_to_bf16_rne(float x) {
-    __bf16 h = static_cast<__bf16>(x);
-    return __builtin_bit_cast(uint16_t, h);
-}
 
 // (x & mask) | bits: mask and bits arrive as kernel arguments (bits pinned in
 // a VGPR), so the compiler emits one v_and_or_b32 per bf16 pair.
@@ -73,18 +66,6 @@ template <int WPL>
 struct Codes {
     u32x4 w[WPL / 4];
 };
-
-// Buffer loads address the packed chunk and the activations with a scalar
-// resource and a 32-bit per-lane offset; the K position goes into the scalar
-// offset, so the loop does no per-lane address arithmetic.  Reads past a
-// resource's size return zero.
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint64_t bytes) {
-    const uint32_t n = bytes < 0xFFFFFFFFull ? static_cast<uint32_t>(bytes) : 0xFFFFFFFFu;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(n),
-                                             0x00020000);
-}
-
-constexpr int kNonTemporal = 2;  // cache-policy bits of a streaming load
 
 // Where one wavefront reads: its packed chunk, the activations, and this
 // lane's byte offsets into them.
@@ -349,16 +330,6 @@ __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1
     __syncthreads();
     stage_groups<MT, WPL, D>(ring, kSG, abuf1, srd1, src, 0, false, acc, mask, bits, lane);
 }
-
-// silu(g) * u with g and u first rounded to bf16 (the rounding of a gate/up
-// output that is stored and then activated)
-__device__ inline float silu_mul_bf16(float g, float u) {
-    g = __uint_as_float(static_cast<uint32_t>(f32_to_bf16_rne(g)) << 16);
-    u = __uint_as_float(static_cast<uint32_t>(f32_to_bf16_rne(u)) << 16);
-    return g / (1.0f + __expf(-g)) * u;
-}
-
-constexpr int kDeviceScope = 16;  // cache-policy bits of a device-coherent access
 
 // Split-K fix-up.  Every split writes its fp32 partial of the tile part, then
 // one thread counts the arrival; the split that arrives last re-reads the

@@ -121,6 +121,8 @@ struct GemmArgs {
     uint32_t unpack_bits;  // 0x43004300: bf16 exponent of 128 in each half
 };
 void launch_gemm_small(const GemmArgs& a, int mt, hipStream_t s);
+// Large-M kernel (prefill profile, tiles of up to 256 rows, no K split).
+void launch_gemm_large(const GemmArgs& a, hipStream_t s);
 
 // masked_m != nullptr: rows r with r % max_m >= masked_m[r / max_m] are skipped.
 void launch_silu_mul(const uint16_t* y13, int64_t rows, const int32_t* rows_dev, int I,
