@@ -212,11 +212,36 @@ def test_combine_and_silu_checks():
 
 # ---- host prepack = documented layout -------------------------------------------
 
+def decode_packed_prefill(packed, desc):
+    """PREFILL layout (32x32x16 MFMA operands): per expert and 128-column
+    chunk, records of 8 groups = codes [8 groups][2 halves h][64 lanes][4
+    words v] then scales [8][2 h][32 columns][2] bf16.  Word (h, lane, v) holds
+    column 32*(h + 2*(v//2)) + lane%32, K offsets 16*(v%2) + 8*(lane//32) + o
+    in nibble o; scale (h, c32, jj) is column 32*(h + 2*jj) + c32."""
+    E, N, K = desc.E, desc.N, desc.K
+    NC, KS, KSP = N // 128, K // 32, desc.k_groups
+    R = KSP // 8
+    rec = packed.view(np.uint32).reshape(E, NC, R, 4608)
+    # axes: e, chunk, record, group, h, K octet (lane//32), c32, jj, step
+    w = rec[..., :4096].reshape(E, NC, R, 8, 2, 2, 32, 2, 2)
+    # -> e, chunk, jj, h, c32 (column 64 jj + 32 h + c32) | record, group, step, octet
+    w = w.transpose(0, 1, 7, 4, 6, 2, 3, 8, 5).reshape(E, N, KSP * 4)
+    assert not w[:, :, K // 8:].any()                       # padding codes are zero
+    codes = np.ascontiguousarray(w[:, :, : K // 8])
+    sc = np.ascontiguousarray(rec[..., 4096:]).view(np.uint16)
+    sc = sc.reshape(E, NC, R, 8, 2, 32, 2).transpose(0, 1, 6, 4, 5, 2, 3).reshape(E, N, KSP)
+    assert not sc[:, :, KS:].any()                          # padding scales are zero
+    return codes.view(np.int32), sc[:, :, :KS]
+
+
 def decode_packed(packed, desc):
     """Read the packed buffer back into canonical codes and scales, from the
-    layout as documented in the library: per expert and chunk, records of 8
-    groups, each = codes [8][64 lanes][CW/16 words] (nibble i holding K offset
-    2*(i%4) + i/4) followed by scales [8][16][CW/16] bf16; padding groups zero."""
+    layout as documented in the library.  DECODE: per expert and chunk,
+    records of 8 groups, each = codes [8][64 lanes][CW/16 words] (nibble i
+    holding K offset 2*(i%4) + i/4) followed by scales [8][16][CW/16] bf16;
+    padding groups zero.  PREFILL: decode_packed_prefill."""
+    if desc.profile == capi.W4A16_PROFILE_PREFILL:
+        return decode_packed_prefill(packed, desc)
     E, N, K, CW = desc.E, desc.N, desc.K, desc.chunk_n
     NC, KS, WPL, KSP = N // CW, K // 32, CW // 16, desc.k_groups
     rec = packed.view(np.uint32).reshape(E, NC, KSP // 8, 576 * WPL)

@@ -224,11 +224,11 @@ def test_pipelined_main_loop_exact(m, H, tile_m, profile):
 @pytest.mark.parametrize("H", [1024, 1056, 1248])
 @pytest.mark.parametrize("tile_m", [128, 192, 256])
 def test_large_tile_kernel_exact(m, H, tile_m):
-    """The large-M kernel (prefill profile, tiles over 64 rows) under the
-    exactness invariant: power-of-two scales make every dequantised weight
-    exact in bf16, so gate/up, the fused SiLU path's inputs and down are
-    bit-identical to the oracle.  About 220 rows per expert: tiles of 256
-    rows use all 16 row blocks, tiles of 128 and 192 split experts."""
+    """The large-M kernel (PREFILL profile) under the exactness invariant:
+    power-of-two scales make every dequantised weight exact in bf16, so
+    gate/up, the fused SiLU path's inputs and down are bit-identical to the
+    oracle.  About 220 rows per expert: tiles of 256 rows use all 8 row
+    blocks of 32, tiles of 128 and 192 split experts."""
     from w4a16_int4_mixture_amd import _capi
     E, I, T, k = 3, 128, 330, 2
     d = exact_problem(H + tile_m, E, H, I, T, k)
@@ -359,13 +359,19 @@ def test_stages_and_path_random(m, seed, E, H, I, T, k, Eg, tile_m, split, profi
     d = synth.random_small(seed, E, H, I, T, k, E_global=Eg)
     # plain W13 (separate activation kernel) on even seeds, interleaved on odd
     path, out = run_indexed(m, d, Eg, profile, tile_m, split, interleave=seed % 2 == 1)
+    # the PREFILL profile's kernel rounds each dequantised weight to bf16 once
+    wmode = 1 if profile == 2 else 0
     ref = oracle.moe_forward(d["X"], d["topk_ids"], d["topk_weights"], Eg, d["expert_map"],
                              d["codes13"], d["scales13"], d["codes2"], d["scales2"],
-                             intermediates=True)
+                             intermediates=True, wmode=wmode)
     pos, f = slot_rows(path.routing, T, k)
     check_close(host(path.Z, np.uint16)[pos], ref["Z"][f], "Z")
     check_close(host(path.Y2, np.uint16)[pos], ref["Y2"][f], "Y2")
     check_close(out, ref["out"], "out")
+    if wmode:
+        ref0 = oracle.moe_forward(d["X"], d["topk_ids"], d["topk_weights"], Eg, d["expert_map"],
+                                  d["codes13"], d["scales13"], d["codes2"], d["scales2"])
+        check_close(out, ref0, "out (exact weights)", exact_frac=0.0)
     # the separate activation kernel as well (on a plain W13)
     w13p = prepare(m, d["codes13"], d["scales13"], profile)
     Y13 = torch.zeros((path.routing.sorted_cap, 2 * I), dtype=torch.int16, device="cuda")
@@ -406,7 +412,8 @@ def test_fused_silu_epilogue_and_splitk_fixup(m, split, profile):
     assert np.array_equal(host(pi.Z, np.uint16)[pos], host(pp.Z, np.uint16)[pos])
     assert np.array_equal(out_i, out_p)
     ref = oracle.moe_forward(d["X"], d["topk_ids"], d["topk_weights"], E, None, d["codes13"],
-                             d["scales13"], d["codes2"], d["scales2"], intermediates=True)
+                             d["scales13"], d["codes2"], d["scales2"], intermediates=True,
+                             wmode=1 if profile == 2 else 0)
     check_close(host(pi.Z, np.uint16)[pos], ref["Z"][f], "fused Z")
     check_close(out_i, ref["out"], "fused out")
     for _ in range(2):

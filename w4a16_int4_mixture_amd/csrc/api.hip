@@ -38,14 +38,12 @@ static bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
-// Largest tile height of the streaming kernel (4 MFMA row blocks) and of the
-// large-M kernel (prefill profile only).
+// Largest tile height of the streaming kernel (DECODE profile, 4 MFMA row
+// blocks) and of the large-M kernel (PREFILL profile, 8 row blocks of 32).
+// The profile, fixed at load time, picks the kernel; the routed rows per
+// expert pick the tile height inside it.
 static constexpr int kSmallMaxTile = 64;
 static constexpr int kLargeMaxTile = 256;
-// Routed rows per expert from which a prefill-profile weight uses the large-M
-// kernel (the pages switch their prefill heuristic at 80 tokens per expert;
-// on CDNA4 the per-tile dequant pays off from about 4 row blocks).
-static constexpr int kLargeMinRows = 64;
 
 static int max_tile(const w4a16_desc* d) {
     return d->profile == W4A16_PROFILE_PREFILL ? kLargeMaxTile : kSmallMaxTile;
@@ -94,19 +92,22 @@ static w4a16_status plan_impl(const w4a16_desc* d, int layout, int rows_hint, in
         }
         const bool deep_k = d->K >= 4096;
         const int64_t want = deep_k ? ceil_div(13LL * expected_m, 10) : ceil_div(5LL * expected_m, 4);
-        const int cap = expected_m >= kLargeMinRows ? max_tile(d) : kSmallMaxTile;
-        tile_m = static_cast<int>(std::min<int64_t>(std::max<int64_t>(round_up(want, 16), 16), cap));
+        const int step = d->profile == W4A16_PROFILE_PREFILL ? 32 : 16;
+        tile_m = static_cast<int>(
+            std::min<int64_t>(std::max<int64_t>(round_up(want, step), step), max_tile(d)));
         tiles_est = E;
     } else {
         if (tile_m_in > 0) {
             tile_m = tile_m_in;
         } else {
             const double tok_e = rows_hint > 0 ? static_cast<double>(rows_hint) / E : 16.0;
-            if (tok_e >= kLargeMinRows && max_tile(d) > kSmallMaxTile) {
+            if (d->profile == W4A16_PROFILE_PREFILL) {
                 // one tile holds an expert's rows up to ~1.4x the mean
-                // (Poisson-like tails), in 64-row steps
+                // (Poisson-like tails), in 32-row steps; the kernel computes
+                // only the 32-row blocks a tile fills
                 tile_m = static_cast<int>(std::min<int64_t>(
-                    round_up(static_cast<int64_t>(1.4 * tok_e + 0.999), 64), kLargeMaxTile));
+                    std::max<int64_t>(round_up(static_cast<int64_t>(1.4 * tok_e + 0.999), 32), 32),
+                    kLargeMaxTile));
             } else {
                 tile_m = static_cast<int>(std::min<int64_t>(
                     std::max<int64_t>(round_up(static_cast<int64_t>(2.0 * tok_e + 0.999), 16), 16),
@@ -117,7 +118,7 @@ static w4a16_status plan_impl(const w4a16_desc* d, int layout, int rows_hint, in
     }
     p->block_m = 16;
     p->tile_m = tile_m;
-    p->kernel = tile_m > kSmallMaxTile ? 2 : 1;
+    p->kernel = d->profile == W4A16_PROFILE_PREFILL ? 2 : 1;
     const int64_t rows_est = layout == W4A16_LAYOUT_MASKED
                                  ? static_cast<int64_t>(E) * expected_m
                                  : std::max<int64_t>(rows_hint, E);
@@ -312,8 +313,10 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
         W4A16_CHECK_ARG(false, "unknown layout %d", a->layout);
     }
     g.split_k = r->split;
+    g.tiles_cap = static_cast<int>(std::min<int64_t>(r->tiles_bound, 0x7FFFFFFF));
     g.unpack_mask = 0x000F000Fu;
     g.unpack_bits = 0x43004300u;
+    g.nib_mask = 0x0F0F0F0Fu;
     const bool split = r->split > 1;
     r->silu_separate = a->epilogue == W4A16_EPI_SILU_MUL && !interleaved;
     const int64_t gx = (g.NC + 3) / 4;

@@ -4,28 +4,34 @@
 //   out[p, n] = sum_c A[row(p), c] * bf16((q[e,n,c] - 8) * s[e,n,c/32])
 //
 // Chord page, "H200 prefill and TP8": with many routed rows per expert the
-// path is bound by the matrix units and the dequant; the dequant (subtract,
-// then scale) is amortised over the rows of a tile, and block M follows the
-// routed rows per expert.
+// path is bound by the matrix units and by the dequant; the dequant (subtract,
+// then scale, rounded to BF16) is amortised over the rows of a tile, the main
+// loop keeps the next weights loading and dequantising while the current MMAs
+// run, and block M follows the routed rows per expert.
 //
-// CDNA4 design.  A workgroup is four wavefronts on a tile of up to 256 rows
-// (MB row blocks of 16) and 256 columns (two 128-column chunks of the prefill
-// profile).  Wavefront w works on chunk 2 * blockIdx.x + w / 2 and, inside
-// it, on the 16-column blocks {2h, 2h+1, 2h+4, 2h+5} (h = w % 2), for every
-// row of the tile; with the gate/up interleave those are two gate blocks and
-// their two up blocks, so SiLU * gate can run on the accumulators.
-//   * Weights: per K group each lane loads its four words (8 codes each) and
-//     four scales and dequantises them once for the whole tile: a code q
-//     becomes bf16 128 + q (one v_and_or_b32 per pair), then fp32, then
-//     (128 + q) * s - 136 * s in one exact FMA, then bf16 (one rounding of
-//     (q - 8) * s).  The B operands stay in registers; a ring keeps the
-//     weights of the next four groups in flight.
-//   * Activations: stages of two K groups (up to 256 rows x 64 K = 32 KB)
-//     go through LDS, double-buffered, one barrier per stage; each stage is
-//     loaded into registers one stage ahead and read back in MFMA A-operand
-//     order.
-//   * v_mfma_f32_16x16x32_bf16, one per (row block, column block, group);
-//     256 fp32 accumulators per lane live in the accumulation registers.
+// CDNA4 design.
+//   * Persistent: one workgroup of four wavefronts per CU walks work items
+//     (row tile, pair of 128-column chunks).  When there are more items than
+//     workgroups, each row tile stays on one XCD (workgroup w runs on XCD
+//     w % 8), so the activation rows of a tile are fetched into one L2 and
+//     reused there by all its column pairs.
+//   * v_mfma_f32_32x32x16_bf16.  Wavefront w works on chunk 2 * pair + w / 2
+//     and, inside it, on the 32-column blocks h and h + 2 (h = w % 2), for
+//     every row of the tile: with the gate/up interleave those are a gate
+//     block and its up block, so SiLU * gate runs on the accumulators.  Up to
+//     8 row blocks x 2 column blocks x 16 fp32 accumulators per lane (256) in
+//     the accumulation registers.
+//   * Activations go from HBM/L2 straight into LDS (buffer loads with the LDS
+//     bit: no staging registers), one 16 KB slot per K group (256 rows x 32 K,
+//     in MFMA A-operand order), kLead groups ahead in a ring of kLead + 1
+//     slots; one barrier per group.
+//   * Weights: per group each lane loads 16 bytes of codes (its two blocks,
+//     two K steps) and 4 bytes of scales into a register ring kLead groups
+//     ahead, and dequantises the next group while the MFMAs of the current
+//     group run: a code byte becomes fp32 (v_cvt_f32_ubyte), then (q - 8) * s
+//     in one exact FMA, then bf16 (one rounding).
+//   * The row count of a tile picks one of eight code paths (32-row blocks);
+//     all waves of a workgroup take the same path.
 
 #include "device_common.h"
 #include "internal.h"
@@ -37,293 +43,359 @@ namespace {
 using namespace dev;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWPL = 8;          // words per lane per group in a 128-column chunk
-constexpr int kRecWords = 576 * kWPL;
-constexpr int kBlocks = 4;       // 16-column blocks per wavefront
-constexpr int kRing = 4;         // groups of weights in flight
+constexpr int kRecWords = 4608;       // words per 8-group record (codes, then scales)
+constexpr int kLead = 8;              // groups of weights and activations in flight
+constexpr int kSlots = kLead + 1;     // LDS activation slots
+constexpr int kSlotBytes = 16 * 1024; // 8 row blocks x 2 K steps x 64 lanes x 16 bytes
 
-// The weights of one K group for one lane: words and scales of its four
-// column blocks (block order 2h, 2h+1, 2h+4, 2h+5).
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// The weights of one K group for one lane: codes of (block h, step 0),
+// (h, 1), (h + 2, 0), (h + 2, 1) and the bf16 scales of blocks h, h + 2.
 struct WGroup {
-    u32x2 w_lo, w_hi;   // words of blocks 2h, 2h+1 and 2h+4, 2h+5
-    uint32_t s_lo, s_hi;  // bf16 scale pairs of the same blocks
+    u32x4 w;
+    uint32_t s;
 };
 
 __device__ inline uint32_t pk_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
 }
 
-// B operand of one column block: the word's eight codes dequantised with the
-// scale s (c = -136 s), in MFMA K order (the packed nibble order puts K
-// offsets 2p and 2p+1 in the two 16-bit halves of (w >> 4p) & 0x000F000F).
-__device__ inline bf16x8 dequant_block(uint32_t w, float s, float c, uint32_t mask,
-                                       uint32_t bits) {
+// B operand of one (block, K step): the word's eight codes (nibble o = K
+// offset o) dequantised with the scale s (c = -8 s).  With nib = 0x0F0F0F0F
+// the bytes of w & nib hold offsets 0, 2, 4, 6 and those of (w >> 4) & nib
+// offsets 1, 3, 5, 7; each byte converts with one v_cvt_f32_ubyte (the mask
+// comes from a kernel argument so that the compiler cannot fold it into a
+// per-nibble bit-field extract, which would cost one more op per code).
+__device__ inline bf16x8 dequant_word(uint32_t w, uint32_t nib, float s, float c) {
+    const uint32_t m0 = w & nib;
+    const uint32_t m1 = (w >> 4) & nib;
     u32x4 d;
-    uint32_t x[4] = {w, w >> 4, w >> 8, w >> 12};
-    uint32_t o[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const uint32_t v = (x[p] & mask) | bits;            // bf16 (128 + q) pair
-        const float lo = __uint_as_float(v << 16);
-        const float hi = __uint_as_float(v & 0xFFFF0000u);
-        o[p] = pk_bf16(__builtin_fmaf(lo, s, c), __builtin_fmaf(hi, s, c));
-    }
-    d.x = o[0];
-    d.y = o[1];
-    d.z = o[2];
-    d.w = o[3];
+    d.x = pk_bf16(__builtin_fmaf(static_cast<float>(m0 & 0xFFu), s, c),
+                  __builtin_fmaf(static_cast<float>(m1 & 0xFFu), s, c));
+    d.y = pk_bf16(__builtin_fmaf(static_cast<float>((m0 >> 8) & 0xFFu), s, c),
+                  __builtin_fmaf(static_cast<float>((m1 >> 8) & 0xFFu), s, c));
+    d.z = pk_bf16(__builtin_fmaf(static_cast<float>((m0 >> 16) & 0xFFu), s, c),
+                  __builtin_fmaf(static_cast<float>((m1 >> 16) & 0xFFu), s, c));
+    d.w = pk_bf16(__builtin_fmaf(static_cast<float>(m0 >> 24), s, c),
+                  __builtin_fmaf(static_cast<float>(m1 >> 24), s, c));
     return __builtin_bit_cast(bf16x8, d);
 }
 
-__device__ inline void dequant_group(const WGroup& g, uint32_t mask, uint32_t bits,
-                                     bf16x8 (&b)[kBlocks]) {
-    const float s0 = __uint_as_float(g.s_lo << 16), s1 = __uint_as_float(g.s_lo & 0xFFFF0000u);
-    const float s2 = __uint_as_float(g.s_hi << 16), s3 = __uint_as_float(g.s_hi & 0xFFFF0000u);
-    b[0] = dequant_block(g.w_lo.x, s0, -136.0f * s0, mask, bits);
-    b[1] = dequant_block(g.w_lo.y, s1, -136.0f * s1, mask, bits);
-    b[2] = dequant_block(g.w_hi.x, s2, -136.0f * s2, mask, bits);
-    b[3] = dequant_block(g.w_hi.y, s3, -136.0f * s3, mask, bits);
+// b[jj][step]
+__device__ inline void dequant_group(const WGroup& g, uint32_t nib, bf16x8 (&b)[2][2]) {
+    const float s0 = __uint_as_float(g.s << 16), s1 = __uint_as_float(g.s & 0xFFFF0000u);
+    const float c0 = -8.0f * s0, c1 = -8.0f * s1;
+    b[0][0] = dequant_word(g.w.x, nib, s0, c0);
+    b[0][1] = dequant_word(g.w.y, nib, s0, c0);
+    b[1][0] = dequant_word(g.w.z, nib, s1, c1);
+    b[1][1] = dequant_word(g.w.w, nib, s1, c1);
 }
 
-// Loads group ks of the chunk for this lane: words at (slot * 64 + lane) * 8
-// + {2h, 2h+1} and + {2h+4, 2h+5}; scales (bf16) after the record's codes at
-// (slot * 16 + lane % 16) * 8 + the same block indices.
+// Loads group ks of the chunk for this lane (code_off, scale_off: the lane's
+// byte offsets inside a record's group).
 __device__ inline void load_wgroup(WGroup& g, __amdgpu_buffer_rsrc_t w, uint32_t code_off,
                                    uint32_t scale_off, int ks) {
-    const int soff = ((ks >> 3) * kRecWords + (ks & 7) * (64 * kWPL)) * 4;
-    const int ssoff = ((ks >> 3) * kRecWords + 512 * kWPL) * 4 + (ks & 7) * (16 * kWPL * 2);
-    g.w_lo = __builtin_bit_cast(
-        u32x2, __builtin_amdgcn_raw_buffer_load_b64(w, code_off, soff, kNonTemporal));
-    g.w_hi = __builtin_bit_cast(
-        u32x2, __builtin_amdgcn_raw_buffer_load_b64(w, code_off + 16, soff, kNonTemporal));
-    g.s_lo = __builtin_amdgcn_raw_buffer_load_b32(w, scale_off, ssoff, kNonTemporal);
-    g.s_hi = __builtin_amdgcn_raw_buffer_load_b32(w, scale_off + 8, ssoff, kNonTemporal);
+    const int rec = (ks >> 3) * kRecWords * 4;
+    const int soff = rec + (ks & 7) * 512 * 4;
+    const int ssoff = rec + 4096 * 4 + (ks & 7) * 128 * 2;
+    g.w = __builtin_bit_cast(u32x4,
+                             __builtin_amdgcn_raw_buffer_load_b128(w, code_off, soff, kNonTemporal));
+    g.s = __builtin_amdgcn_raw_buffer_load_b32(w, scale_off, ssoff, kNonTemporal);
 }
 
-// Activation stage: rows [0, 16 * MB) x 64 K (groups 2s, 2s+1), 8 x 16 bytes
-// per thread per 256 rows.  Thread i takes K chunk kc = i % 8 (group kc / 4,
-// K offset 8 * (kc % 4)) of rows i / 8 + 32 * pass.
-template <int MB>
-struct AStage {
-    u32x4 v[MB / 2];
+// s_waitcnt with only a vector-memory count (expcnt and lgkmcnt left free).
+template <int N>
+__device__ inline void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt field holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that also keeps the compiler from moving LDS accesses
+// across it.  The activation slots are written by buffer-to-LDS loads whose
+// completion each wave has already waited for (vmcnt), so no fence is needed
+// (a fence would wait for every weight load in flight as well).
+__device__ inline void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
+
+struct Item {
+    int e, p0, nrows, pair;
 };
-
-// soff = 128 s bytes (uniform); delta (<= 0, per lane) moves a K chunk of a
-// padding group back onto the last real group.
-template <int MB>
-__device__ inline void load_astage(AStage<MB>& st, __amdgpu_buffer_rsrc_t x,
-                                   const uint32_t (&row_off)[MB / 2], int soff, int delta) {
-#pragma unroll
-    for (int i = 0; i < MB / 2; ++i)
-        st.v[i] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(x, row_off[i] + delta, soff, 0));
-}
-
-// LDS layout of a stage: [group (2)][row block (16)][lane (64)] x 16 bytes,
-// lane = 16 * (K offset / 8) + row % 16 (the MFMA A-operand order).
-template <int MB>
-__device__ inline void store_astage(const AStage<MB>& st, u32x4* buf, int tid) {
-    const int kc = tid & 7;
-    const int g = kc >> 2;
-#pragma unroll
-    for (int i = 0; i < MB / 2; ++i) {
-        const int r = (tid >> 3) + 32 * i;
-        buf[(g * 16 + (r >> 4)) * 64 + (kc & 3) * 16 + (r & 15)] = st.v[i];
-    }
-}
-
-constexpr int kStageU4 = 2 * 16 * 64;  // u32x4 per LDS stage
 
 }  // namespace
 
-// One tile (expert e, positions [p0, p0 + nrows), nrows <= 16 * MB) for the
-// two chunks of blockIdx.x.
-template <int MB>
-__device__ __forceinline__ void large_tile(const GemmArgs& a, int e, int p0, int nrows,
-                                           int wave, int lane, u32x4* lds) {
-    const int tid = threadIdx.x;
-    const int chunk = blockIdx.x * 2 + (wave >> 1);
+// One work item with up to 32 * RB rows.
+template <int RB>
+__device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, int wave, int lane,
+                                           char* lds) {
+    // activation loads per group: one per (row block, K step), dealt to the
+    // four waves in turn; every wave issues kDma of them (a wave past the
+    // last one repeats it: same data to the same LDS bytes)
+    constexpr int kNA = 2 * RB;
+    constexpr int kDma = (kNA + 3) / 4;
+    // At the top of group g the activations of group g + 1 must have landed
+    // (they are read from LDS during group g); the kLead - 2 later groups of
+    // kDma + 2 operations may stay in flight.  (Group g + 1's own weight
+    // loads are not counted: the compiler may order them before its
+    // activation loads.  Scheduling barriers keep groups apart.)
+    constexpr int kWaitA = (kLead - 2) * (kDma + 2);
+
+    const int chunk = it.pair * 2 + (wave >> 1);
     const int h = wave & 1;
     const bool active = chunk < a.NC;
     const bool slot_rows = a.tile_src != TILE_MASKED;
+    const int KS = a.KS;
+    const int KSP = a.KSP;   // a multiple of 8 = kLead; groups >= KS have zero weights
 
-    // activation rows this thread stages: rows tid / 8 + 32 i (rows past the
-    // tile reuse its first row: they are computed, never stored)
-    uint32_t row_off[MB / 2];
+    // Activation load q covers row block q / 2, K step q % 2: lane l takes
+    // row 32 (q / 2) + l % 32, K 16 (q % 2) + 8 (l / 32) .. +7 of each group.
+    // Rows past the tile reuse its first row (computed, never stored).
+    uint32_t aoff[kDma];
+    uint32_t adst[kDma];
 #pragma unroll
-    for (int i = 0; i < MB / 2; ++i) {
-        const int r = (tid >> 3) + 32 * i;
-        const int rr = r < nrows ? r : 0;
-        int64_t row = p0 + rr;
+    for (int i = 0; i < kDma; ++i) {
+        const int q = wave + 4 * i < kNA ? wave + 4 * i : kNA - 1;
+        const int r = 32 * (q >> 1) + (lane & 31);
+        const int rr = r < it.nrows ? r : 0;
+        int64_t row = it.p0 + rr;
         if (slot_rows && a.arow != W4A16_AROW_POSITION) {
-            int f = a.sorted_ids[p0 + rr];
-            if (f < 0 || f >= a.num_slots) f = a.sorted_ids[p0];
+            int f = a.sorted_ids[it.p0 + rr];
+            if (f < 0 || f >= a.num_slots) f = a.sorted_ids[it.p0];
             if (f < 0 || f >= a.num_slots) f = 0;
             row = (a.arow == W4A16_AROW_TOKEN) ? f / a.top_k : f;
         }
         row = row < a.A_rows ? row : a.A_rows - 1;
         // A_rows * K * 2 < 2^32 is checked on the host
-        row_off[i] = static_cast<uint32_t>(row * a.K * 2 + (tid & 7) * 16);
+        aoff[i] = static_cast<uint32_t>(row * a.K * 2 + (q & 1) * 32 + (lane >> 5) * 16);
+        adst[i] = static_cast<uint32_t>(q * 1024);
     }
     const __amdgpu_buffer_rsrc_t x = make_rsrc(a.A, static_cast<uint64_t>(a.A_rows) * a.K * 2);
-    // K chunk kc of stage s lies in group 2s + kc / 4; in the stages that
-    // reach past K (padding groups, zero weights) such a chunk re-reads the
-    // last real group, so that nothing outside the row is read
-    const int kgrp_half = (tid & 7) >> 2;
-    auto a_delta = [&](int s) {
-        const int g = 2 * s + kgrp_half;
-        return g < a.KS ? 0 : (a.KS - 1 - g) * 64;
-    };
 
-    const int64_t cbase = static_cast<int64_t>(e) * a.NC + (active ? chunk : a.NC - 1);
+    const int64_t cbase = static_cast<int64_t>(it.e) * a.NC + (active ? chunk : a.NC - 1);
     const __amdgpu_buffer_rsrc_t w =
         make_rsrc(a.packed + cbase * a.chunk_words, static_cast<uint64_t>(a.chunk_words) * 4);
-    const uint32_t code_off = static_cast<uint32_t>((lane * kWPL + 2 * h) * 4);
-    const uint32_t scale_off = static_cast<uint32_t>(((lane & 15) * kWPL + 2 * h) * 2);
-    const uint32_t mask = a.unpack_mask;
-    const uint32_t bits = a.unpack_bits;
+    const uint32_t code_off = static_cast<uint32_t>((h * 64 + lane) * 16);
+    const uint32_t scale_off = static_cast<uint32_t>((h * 32 + (lane & 31)) * 4);
+    const uint32_t nib = a.nib_mask;
 
-    f32x4 acc[MB][kBlocks];
+    // Loads of group g into LDS slot byte offset `slot` and ring slot `r`.
+    // Padding groups (KS <= g < KSP) read zero weights and, for the
+    // activations, the last real group again (finite values times zero: a
+    // row's K range is never left); groups past KSP repeat the last ones and
+    // are never used.
+    auto issue = [&](int g, uint32_t slot, WGroup& r) {
+        const int ga = g < KS ? g : KS - 1;
+        const int gw = g < KSP ? g : KSP - 1;
 #pragma unroll
-    for (int t = 0; t < MB; ++t)
-#pragma unroll
-        for (int j = 0; j < kBlocks; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < kDma; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(x, LDS_PTR(lds + slot + adst[i]), 16,
+                                                     aoff[i], ga * 64, 0, 0);
+        load_wgroup(r, w, code_off, scale_off, gw);
+    };
 
-    const int ngroups = a.KSP;         // a multiple of 8
-    const int nst = ngroups / 2;       // a multiple of 4
-
-    WGroup ring[kRing];
+    f32x16 acc[RB][2];
 #pragma unroll
-    for (int i = 0; i < kRing; ++i) load_wgroup(ring[i], w, code_off, scale_off, i);
-    AStage<MB> ast;
-    load_astage<MB>(ast, x, row_off, 0, 2 * 0 + 1 < a.KS ? 0 : a_delta(0));
-    store_astage<MB>(ast, lds, tid);
-    __syncthreads();
-
-    // Two stages per iteration, so that ring slots and LDS buffers are static
-    // (nst is a multiple of 4).  The body has no branches: past the end, the
-    // last stage and the last group are loaded again and never used, so the
-    // compiler can count the loads in flight and wait only for the oldest.
-    for (int s = 0; s < nst; s += 2) {
+    for (int t = 0; t < RB; ++t)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int st = s + half;
-            const u32x4* cur = lds + half * kStageU4;
-            {
-                const int sn = st + 1 < nst ? st + 1 : nst - 1;
-                load_astage<MB>(ast, x, row_off, 128 * sn, 2 * sn + 1 < a.KS ? 0 : a_delta(sn));
+        for (int j = 0; j < 2; ++j) acc[t][j] = f32x16{};
+
+    WGroup ring[kLead];
+#pragma unroll
+    for (int i = 0; i < kLead; ++i) {
+        issue(i, i * kSlotBytes, ring[i]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // A fragments of one group (row block t, K step st), and B operands
+    // b[jj][st]; both double-buffered by group parity
+    bf16x8 av[2][RB][2];
+    bf16x8 b[2][2][2];
+    auto read_a = [&](uint32_t slot, bf16x8 (&dst)[RB][2]) {
+        const u32x4* As = reinterpret_cast<const u32x4*>(lds + slot);
+#pragma unroll
+        for (int t = 0; t < RB; ++t)
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+                dst[t][st] = __builtin_bit_cast(bf16x8, As[(2 * t + st) * 64 + lane]);
+    };
+    wait_vmcnt<(kLead - 1) * (kDma + 2)>();   // this wave's activations of group 0
+    barrier_lds();
+    read_a(0, av[0]);
+    dequant_group(ring[0], nib, b[0]);
+
+    // kLead groups per trip, so that ring slots and register buffers are
+    // static (kLead is even and divides KSP).  Group g: wait for this wave's
+    // activations of g + 1, barrier (all of them landed; every wave is done
+    // with the slot of group g - 1), load group g + kLead into that slot and
+    // ring slot u; then, while the MFMAs of group g run on registers, read
+    // the activations of group g + 1 from LDS and dequantise its weights.
+    uint32_t rslot = kSlotBytes;                 // LDS slot of group g + 1
+    uint32_t wslot = kLead * kSlotBytes;         // LDS slot of group g + kLead
+    for (int g0 = 0; g0 < KSP; g0 += kLead) {
+#pragma unroll
+        for (int u = 0; u < kLead; ++u) {
+            const int g = g0 + u;
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<kWaitA>();
+            barrier_lds();
+            __builtin_amdgcn_sched_barrier(0);
+            issue(g + kLead, wslot, ring[u]);
+            __builtin_amdgcn_sched_barrier(0);
+            read_a(rslot, av[(u + 1) & 1]);
+            dequant_group(ring[(u + 1) % kLead], nib, b[(u + 1) & 1]);
+#pragma unroll
+            for (int t = 0; t < RB; ++t)
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj)
+                        acc[t][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            av[u & 1][t][st], b[u & 1][jj][st], acc[t][jj], 0, 0, 0);
+            // each MFMA followed by about 96 / (4 RB) VALU ops of the next
+            // group's dequant and half an LDS read, which issue while it runs
+            constexpr int kV = (96 + 4 * RB - 1) / (4 * RB);
+#pragma unroll
+            for (int i = 0; i < 4 * RB; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
             }
-#pragma unroll
-            for (int gg = 0; gg < 2; ++gg) {
-                const int slot = 2 * half + gg;
-                const int g = 2 * st + gg;
-                bf16x8 b[kBlocks];
-                dequant_group(ring[slot], mask, bits, b);
-                load_wgroup(ring[slot], w, code_off, scale_off,
-                            g + kRing < ngroups ? g + kRing : ngroups - 1);
-#pragma unroll
-                for (int t = 0; t < MB; ++t) {
-                    const bf16x8 av = __builtin_bit_cast(bf16x8, cur[(gg * 16 + t) * 64 + lane]);
-#pragma unroll
-                    for (int j = 0; j < kBlocks; ++j)
-                        acc[t][j] =
-                            __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[j], acc[t][j], 0, 0, 0);
-                    // keep at most four row blocks of A fragments in registers
-                    if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-            store_astage<MB>(ast, lds + (1 - half) * kStageU4, tid);
-            __syncthreads();
+            rslot = rslot + kSlotBytes == kSlots * kSlotBytes ? 0 : rslot + kSlotBytes;
+            wslot = wslot + kSlotBytes == kSlots * kSlotBytes ? 0 : wslot + kSlotBytes;
         }
     }
+    // drain the loads past the end before the slots are reused
+    wait_vmcnt<0>();
+    barrier_lds();
     if (!active) return;
 
-    // epilogue: lane holds rows 16t + 4*(lane/16) + i of column 16 J[j] +
-    // lane%16, J = {2h, 2h+1, 2h+4, 2h+5}
+    // epilogue: acc[t][jj][i] holds row 32 t + 8 (i / 4) + 4 (lane / 32) +
+    // i % 4 of column 32 (h + 2 jj) + lane % 32 of the chunk
 #pragma unroll
-    for (int t = 0; t < MB; ++t) {
+    for (int t = 0; t < RB; ++t) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * t + 4 * (lane >> 4) + i;
-            if (r >= nrows) continue;
-            int64_t orow = p0 + r;
+        for (int i = 0; i < 16; ++i) {
+            const int r = 32 * t + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            if (r >= it.nrows) continue;
+            int64_t orow = it.p0 + r;
             if (slot_rows && (a.tile_src == TILE_BLOCKS || a.orow == W4A16_OROW_SLOT)) {
-                const int f = a.sorted_ids[p0 + r];
+                const int f = a.sorted_ids[it.p0 + r];
                 if (f < 0 || f >= a.num_slots) continue;
                 if (a.orow == W4A16_OROW_SLOT) orow = f;
             }
             if (a.out_kind == OUT_SILU) {
-                // blocks 2h, 2h+1 are gate columns, 2h+4, 2h+5 the matching up
+                // block h is a gate block, block h + 2 the matching up block
                 uint16_t* o = static_cast<uint16_t*>(a.out) + orow * (a.N / 2) + chunk * 64 +
-                              32 * h + (lane & 15);
-                o[0] = f32_to_bf16_rne(silu_mul_bf16(acc[t][0][i], acc[t][2][i]));
-                o[16] = f32_to_bf16_rne(silu_mul_bf16(acc[t][1][i], acc[t][3][i]));
+                              32 * h + (lane & 31);
+                o[0] = f32_to_bf16_rne(silu_mul_bf16(acc[t][0][i], acc[t][1][i]));
             } else {
-                const int64_t c0 = orow * a.N + chunk * 128 + 32 * h + (lane & 15);
+                const int64_t c0 = orow * a.N + chunk * 128 + 32 * h + (lane & 31);
                 if (a.out_kind == OUT_BF16) {
                     uint16_t* o = static_cast<uint16_t*>(a.out) + c0;
                     o[0] = f32_to_bf16_rne(acc[t][0][i]);
-                    o[16] = f32_to_bf16_rne(acc[t][1][i]);
-                    o[64] = f32_to_bf16_rne(acc[t][2][i]);
-                    o[80] = f32_to_bf16_rne(acc[t][3][i]);
+                    o[64] = f32_to_bf16_rne(acc[t][1][i]);
                 } else {
                     float* o = static_cast<float*>(a.out) + c0;
                     o[0] = acc[t][0][i];
-                    o[16] = acc[t][1][i];
-                    o[64] = acc[t][2][i];
-                    o[80] = acc[t][3][i];
+                    o[64] = acc[t][1][i];
                 }
             }
         }
     }
 }
 
-// Tiles are walked grid-stride along grid.y (the decision is uniform across
-// the workgroup, so every barrier is reached by all four wavefronts).  The
-// row-block count is rounded up to a multiple of 4 per tile.
+// Tile ty of the launch: expert, first position and rows (nrows <= 0: empty).
+__device__ inline Item tile_of(const GemmArgs& a, int ty) {
+    Item it{-1, 0, 0, 0};
+    if (a.tile_src == TILE_TABLE) {
+        const int4 t = reinterpret_cast<const int4*>(a.tiles)[ty];
+        it.e = t.x;
+        it.p0 = t.y;
+        it.nrows = t.z;
+    } else if (a.tile_src == TILE_BLOCKS) {
+        it.p0 = ty * a.block_m;
+        it.e = a.expert_ids[ty];
+        it.nrows = a.sorted_cap - it.p0 < a.block_m ? a.sorted_cap - it.p0 : a.block_m;
+    } else {
+        const int g = ty / a.chunks_per_expert;
+        const int r0 = (ty % a.chunks_per_expert) * a.tile_m;
+        const int cnt = a.masked_m[g];
+        it.e = g;
+        it.p0 = g * a.max_m + r0;
+        it.nrows = cnt - r0 < a.tile_m ? cnt - r0 : a.tile_m;
+    }
+    if (it.e < 0 || it.e >= a.E) it.nrows = 0;
+    it.nrows = it.nrows < 256 ? it.nrows : 256;
+    return it;
+}
+
 __global__ void __launch_bounds__(256) k_gemm_large(GemmArgs a) {
-    __shared__ u32x4 lds[2 * kStageU4];
+    __shared__ __attribute__((aligned(1024))) char lds[kSlots * kSlotBytes];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    for (int ty = blockIdx.y;; ty += gridDim.y) {
-        int e, p0, nrows;
-        if (a.tile_src == TILE_TABLE) {
-            if (ty >= a.tile_count[0]) return;
-            const int4 t = reinterpret_cast<const int4*>(a.tiles)[ty];
-            e = t.x;
-            p0 = t.y;
-            nrows = t.z;
-        } else if (a.tile_src == TILE_BLOCKS) {
-            p0 = ty * a.block_m;
-            if (p0 >= a.ntp[0]) return;
-            e = a.expert_ids[ty];
-            nrows = a.sorted_cap - p0 < a.block_m ? a.sorted_cap - p0 : a.block_m;
+
+    int n_tiles;
+    if (a.tile_src == TILE_TABLE) {
+        n_tiles = a.tile_count[0];
+        n_tiles = n_tiles < a.tiles_cap ? n_tiles : a.tiles_cap;
+    } else if (a.tile_src == TILE_BLOCKS) {
+        n_tiles = a.ntp[0] / a.block_m;
+        n_tiles = n_tiles < a.tiles_cap ? n_tiles : a.tiles_cap;
+    } else {
+        n_tiles = a.grid_tiles_total;
+    }
+    const int CP = (a.NC + 1) / 2;
+    const int nwg = gridDim.x;
+    // more items than workgroups and a whole number of workgroups per XCD:
+    // tile ty runs on XCD ty % 8; otherwise items are dealt out in order
+    const bool by_xcd = static_cast<int64_t>(n_tiles) * CP > nwg && (nwg & 7) == 0;
+    const int xcd = blockIdx.x & 7;
+    const int per_xcd = nwg >> 3;
+    for (int j = by_xcd ? (blockIdx.x >> 3) : blockIdx.x;; j += by_xcd ? per_xcd : nwg) {
+        int ty, pair;
+        if (by_xcd) {
+            ty = 8 * (j / CP) + xcd;
+            pair = j % CP;
+            if (j / CP * 8 >= n_tiles) return;
+            if (ty >= n_tiles) continue;
         } else {
-            if (ty >= a.grid_tiles_total) return;
-            const int g = ty / a.chunks_per_expert;
-            const int r0 = (ty % a.chunks_per_expert) * a.tile_m;
-            const int cnt = a.masked_m[g];
-            if (r0 >= cnt) continue;
-            e = g;
-            p0 = g * a.max_m + r0;
-            nrows = cnt - r0 < a.tile_m ? cnt - r0 : a.tile_m;
+            ty = j / CP;
+            pair = j % CP;
+            if (ty >= n_tiles) return;
         }
-        if (e < 0 || e >= a.E || nrows <= 0) continue;
-        nrows = nrows < 256 ? nrows : 256;
-        const int mb = (nrows + 63) >> 6;   // quarters of 256 rows
-        if (mb <= 1) large_tile<4>(a, e, p0, nrows, wave, lane, lds);
-        else if (mb == 2) large_tile<8>(a, e, p0, nrows, wave, lane, lds);
-        else if (mb == 3) large_tile<12>(a, e, p0, nrows, wave, lane, lds);
-        else large_tile<16>(a, e, p0, nrows, wave, lane, lds);
-        __syncthreads();  // the next tile reuses the staging buffers
+        Item it = tile_of(a, ty);
+        if (it.nrows <= 0) continue;
+        it.pair = pair;
+        switch ((it.nrows + 31) >> 5) {
+            case 1: large_item<1>(a, it, wave, lane, lds); break;
+            case 2: large_item<2>(a, it, wave, lane, lds); break;
+            case 3: large_item<3>(a, it, wave, lane, lds); break;
+            case 4: large_item<4>(a, it, wave, lane, lds); break;
+            case 5: large_item<5>(a, it, wave, lane, lds); break;
+            case 6: large_item<6>(a, it, wave, lane, lds); break;
+            case 7: large_item<7>(a, it, wave, lane, lds); break;
+            default: large_item<8>(a, it, wave, lane, lds); break;
+        }
     }
 }
 
+static int g_num_cus = 0;
+
 void launch_gemm_large(const GemmArgs& a, hipStream_t st) {
-    const dim3 grid((a.NC + 1) / 2, a.grid_tiles, 1), block(256);
-    k_gemm_large<<<grid, block, 0, st>>>(a);
+    if (g_num_cus <= 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            n > 0)
+            g_num_cus = n;
+        else
+            g_num_cus = 256;
+    }
+    const int64_t items = static_cast<int64_t>(a.grid_tiles) * ((a.NC + 1) / 2);
+    const int grid = static_cast<int>(items < g_num_cus ? items : g_num_cus);
+    k_gemm_large<<<dim3(grid), dim3(256), 0, st>>>(a);
 }
 
 }  // namespace w4a16

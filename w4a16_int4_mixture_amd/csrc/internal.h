@@ -31,6 +31,9 @@ w4a16_status check_launch(const char* what);
 // Per expert e and chunk c of CW packed columns, K/32 groups are padded to
 // KSP = round_up(K/32, 8) and cut into KSP/8 records ("stages") of 8 groups.
 // A record is contiguous: first the codes, then the scales of its 8 groups.
+// Both profiles use 576 * WPL words per record.
+//
+// DECODE (CW = 64, operands of v_mfma_f32_16x16x32_bf16):
 //   codes : word (g8, lane, j) at  (g8 * 64 + lane) * WPL + j      (g8 < 8)
 //           = the eight codes of column c*CW + 16*j + lane%16 (packed order)
 //             for K = ks*32 + 8*(lane/16) + o, o = 0..7, with the code of
@@ -39,6 +42,14 @@ w4a16_status check_launch(const char* what);
 //             offsets (2p, 2p+1) in the two 16-bit halves
 //   scales: bf16 (g8, c16, j) at  512*WPL words + (g8 * 16 + c16) * WPL + j
 //           = the scale of column c*CW + 16*j + c16, group ks
+// PREFILL (CW = 128, operands of v_mfma_f32_32x32x16_bf16; 32-column blocks
+// j = 0..3, half h = 0, 1 owns blocks h and h + 2):
+//   codes : word (g8, h, lane, v) at ((g8 * 2 + h) * 64 + lane) * 4 + v
+//           = the eight codes of column c*CW + 32*(h + 2*(v/2)) + lane%32 for
+//             K = ks*32 + 16*(v%2) + 8*(lane/32) + o, o = 0..7, in the
+//             canonical nibble order (nibble o = offset o)
+//   scales: bf16 (g8, h, c32, jj) at 4096 words + ((g8 * 2 + h) * 32 + c32) * 2 + jj
+//           = the scale of column c*CW + 32*(h + 2*jj) + c32, group ks
 // Padding groups (ks >= K/32) hold zero codes and zero scales.
 // WPL = CW / 16 words (and scales) per lane per group.
 struct PackGeom {
@@ -100,6 +111,7 @@ struct GemmArgs {
     const int32_t* masked_m;
     int max_m, chunks_per_expert;
     int grid_tiles;        // grid.y
+    int tiles_cap;         // tile indices that may hold work (bound of the device count)
     int grid_tiles_total;  // masked: experts * chunks_per_expert
     // weights (packed records, see PackGeom)
     const uint32_t* packed;
@@ -119,9 +131,10 @@ struct GemmArgs {
     int64_t ws_stride;
     uint32_t unpack_mask;  // 0x000F000F: one code in each 16-bit half
     uint32_t unpack_bits;  // 0x43004300: bf16 exponent of 128 in each half
+    uint32_t nib_mask;     // 0x0F0F0F0F: one code in each byte
 };
 void launch_gemm_small(const GemmArgs& a, int mt, hipStream_t s);
-// Large-M kernel (prefill profile, tiles of up to 256 rows, no K split).
+// Large-M kernel (PREFILL profile only, tiles of up to 256 rows, no K split).
 void launch_gemm_large(const GemmArgs& a, hipStream_t s);
 
 // masked_m != nullptr: rows r with r % max_m >= masked_m[r / max_m] are skipped.

@@ -96,6 +96,34 @@ __host__ __device__ static inline uint32_t permute_word(uint32_t w) {
     return out;
 }
 
+// PREFILL record word `in` (see the layout in internal.h): codes in their
+// canonical nibble order, one 16-byte group per (group, half, lane).
+__host__ __device__ static inline uint32_t prefill_word(const uint32_t* codes,
+                                                        const uint16_t* scales, const PackGeom& g,
+                                                        int64_t e, int c, int stage, int in) {
+    if (in < 4096) {
+        const int v = in & 3, lane = (in >> 2) & 63, h = (in >> 8) & 1;
+        const int ks = stage * 8 + (in >> 9);
+        if (ks >= g.KS) return 0u;
+        const int j = h + 2 * (v >> 1), s = v & 1;
+        const int n = canonical_column(c * 128 + 32 * j + (lane & 31), g.N, 128, g.interleave);
+        return codes[(e * g.N + n) * (g.K / 8) + ks * 4 + 2 * s + (lane >> 5)];
+    }
+    uint32_t out = 0;
+    for (int hh = 0; hh < 2; ++hh) {
+        const int b = 2 * (in - 4096) + hh;   // bf16 index inside the scale block
+        const int jj = b & 1, c32 = (b >> 1) & 31, h = (b >> 6) & 1;
+        const int ks = stage * 8 + (b >> 7);
+        uint32_t v = 0;
+        if (ks < g.KS) {
+            const int n = canonical_column(c * 128 + 32 * (h + 2 * jj) + c32, g.N, 128, g.interleave);
+            v = scales[(e * g.N + n) * g.KS + ks];
+        }
+        out |= v << (16 * hh);
+    }
+    return out;
+}
+
 // Word w of the packed buffer, from the canonical codes and scales.
 __host__ __device__ static inline uint32_t packed_word(const uint32_t* codes, const uint16_t* scales,
                                                        const PackGeom& g, uint64_t w) {
@@ -105,6 +133,7 @@ __host__ __device__ static inline uint32_t packed_word(const uint32_t* codes, co
     const uint64_t r = w % g.chunk_words;
     const int stage = static_cast<int>(r / g.stage_words);
     const int in = static_cast<int>(r % g.stage_words);
+    if (g.CW == 128) return prefill_word(codes, scales, g, e, c, stage, in);
     const int code_words = 512 * g.WPL;
     if (in < code_words) {
         const int j = in % g.WPL;
