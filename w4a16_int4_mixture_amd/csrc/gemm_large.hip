@@ -126,6 +126,51 @@ struct Item {
 
 }  // namespace
 
+// Stores rows [r0, r1) of a work item from the fp32 staging tile in LDS
+// ([128 rows][256 columns], row r at (r - r0) * 256): 32 lanes per row,
+// 8 staged values each; bf16 or fp32 rows, or SiLU(gate) * up of the
+// interleaved gate/up pairs (4 outputs per lane).
+__device__ __forceinline__ void store_rows(const GemmArgs& a, const Item& it, const float* stg,
+                                        int r0, int r1) {
+    const bool silu = a.out_kind == OUT_SILU;
+    const bool slot_rows = a.tile_src != TILE_MASKED;
+    const bool row_map = slot_rows && (a.tile_src == TILE_BLOCKS || a.orow == W4A16_OROW_SLOT);
+    const int nout = silu ? a.N / 2 : a.N;             // output row length
+    const int width = silu ? 128 : 256;                // output columns of the tile
+    const int col0 = it.pair * width;
+    const int cvalid = nout - col0 < width ? nout - col0 : width;
+    const int q = threadIdx.x & 31;                    // 8 staged values: 8 columns or 4 pairs
+    const int cc = silu ? 4 * q : 8 * q;               // first output column of this lane
+    for (int r = r0 + (threadIdx.x >> 5); r < r1; r += 8) {
+        int64_t orow = it.p0 + r;
+        if (row_map) {
+            const int f = a.sorted_ids[it.p0 + r];
+            if (f < 0 || f >= a.num_slots) continue;
+            if (a.orow == W4A16_OROW_SLOT) orow = f;
+        }
+        if (cc >= cvalid) continue;
+        const f32x4* src = reinterpret_cast<const f32x4*>(stg + (r - r0) * 256 + 8 * q);
+        const f32x4 v0 = src[0], v1 = src[1];
+        if (silu) {
+            u32x2 o;
+            o.x = pk_bf16(silu_mul_bf16(v0.x, v0.y), silu_mul_bf16(v0.z, v0.w));
+            o.y = pk_bf16(silu_mul_bf16(v1.x, v1.y), silu_mul_bf16(v1.z, v1.w));
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + orow * nout + col0 + cc) = o;
+        } else if (a.out_kind == OUT_BF16) {
+            u32x4 o;
+            o.x = pk_bf16(v0.x, v0.y);
+            o.y = pk_bf16(v0.z, v0.w);
+            o.z = pk_bf16(v1.x, v1.y);
+            o.w = pk_bf16(v1.z, v1.w);
+            *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + orow * nout + col0 + cc) = o;
+        } else {
+            f32x4* o = reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + orow * nout + col0 + cc);
+            o[0] = v0;
+            o[1] = v1;
+        }
+    }
+}
+
 // One work item with up to 32 * RB rows.
 template <int RB>
 __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, int wave, int lane,
@@ -269,40 +314,32 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
     // drain the loads past the end before the slots are reused
     wait_vmcnt<0>();
     barrier_lds();
-    if (!active) return;
 
-    // epilogue: acc[t][jj][i] holds row 32 t + 8 (i / 4) + 4 (lane / 32) +
-    // i % 4 of column 32 (h + 2 jj) + lane % 32 of the chunk
+    // Epilogue, in passes of 128 rows: the fp32 accumulators of the pass go
+    // to LDS as a [128 rows][256 columns] tile of the workgroup (the two
+    // chunks side by side; for SiLU * gate, gate and up interleaved per
+    // output column), then all threads store whole row segments.
+    // acc[t][jj][i] holds row 32 t + 8 (i / 4) + 4 (lane / 32) + i % 4 of
+    // column 32 (h + 2 jj) + lane % 32 of the chunk.
+    float* stg = reinterpret_cast<float*>(lds);
+    const bool silu = a.out_kind == OUT_SILU;
+    const int zc = (wave >> 1) * 64 + 32 * h + (lane & 31);          // SiLU output column
+    const int c0 = (wave >> 1) * 128 + 32 * h + (lane & 31);         // plain output column
+    const int s0 = silu ? 2 * zc : c0, s1 = silu ? 2 * zc + 1 : c0 + 64;
 #pragma unroll
-    for (int t = 0; t < RB; ++t) {
+    for (int p = 0; p < (RB + 3) / 4; ++p) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = 32 * t + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-            if (r >= it.nrows) continue;
-            int64_t orow = it.p0 + r;
-            if (slot_rows && (a.tile_src == TILE_BLOCKS || a.orow == W4A16_OROW_SLOT)) {
-                const int f = a.sorted_ids[it.p0 + r];
-                if (f < 0 || f >= a.num_slots) continue;
-                if (a.orow == W4A16_OROW_SLOT) orow = f;
-            }
-            if (a.out_kind == OUT_SILU) {
-                // block h is a gate block, block h + 2 the matching up block
-                uint16_t* o = static_cast<uint16_t*>(a.out) + orow * (a.N / 2) + chunk * 64 +
-                              32 * h + (lane & 31);
-                o[0] = f32_to_bf16_rne(silu_mul_bf16(acc[t][0][i], acc[t][1][i]));
-            } else {
-                const int64_t c0 = orow * a.N + chunk * 128 + 32 * h + (lane & 31);
-                if (a.out_kind == OUT_BF16) {
-                    uint16_t* o = static_cast<uint16_t*>(a.out) + c0;
-                    o[0] = f32_to_bf16_rne(acc[t][0][i]);
-                    o[64] = f32_to_bf16_rne(acc[t][1][i]);
-                } else {
-                    float* o = static_cast<float*>(a.out) + c0;
-                    o[0] = acc[t][0][i];
-                    o[64] = acc[t][1][i];
-                }
+        for (int t = 4 * p; t < RB && t < 4 * p + 4; ++t) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = 32 * (t - 4 * p) + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                stg[r * 256 + s0] = acc[t][0][i];
+                stg[r * 256 + s1] = acc[t][1][i];
             }
         }
+        barrier_lds();
+        store_rows(a, it, stg, 128 * p, it.nrows < 128 * p + 128 ? it.nrows : 128 * p + 128);
+        barrier_lds();   // the staging bytes are reused (next pass, next item's loads)
     }
 }
 
