@@ -31,15 +31,35 @@ __device__ inline void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ inline int local_expert(const AlignArgs& a, int64_t f, int* bad) {
-    int g = a.topk_ids[f];
-    if (g < 0 || g >= a.E_global) {
-        *bad = 1;
-        return -1;
+
+// Chunks of 64 slots whose routing ids one wavefront loads at once.
+constexpr int kBatch = 16;
+
+// Local experts of slots c0*64 + lane .. for kBatch chunks (-1: none or past
+// the end); all loads of the batch are issued before any is used.
+__device__ inline void load_batch(const AlignArgs& a, int64_t c0, int64_t c_end, int64_t S,
+                                  int lane, int (&eb)[kBatch], int* bad) {
+    int g[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+        const int64_t f = (c0 + j) * 64 + lane;
+        g[j] = (c0 + j < c_end && f < S) ? a.topk_ids[f] : 0;
     }
-    int e = a.expert_map ? a.expert_map[g] : g;
-    if (e < -1 || e >= a.E_local) *bad = 1;
-    return (e >= 0 && e < a.E_local) ? e : -1;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+        const int64_t f = (c0 + j) * 64 + lane;
+        int e = -1;
+        if (c0 + j < c_end && f < S) {
+            if (g[j] < 0 || g[j] >= a.E_global) {
+                *bad = 1;
+            } else {
+                e = a.expert_map ? a.expert_map[g[j]] : g[j];
+                if (e < -1 || e >= a.E_local) *bad = 1;
+                if (e < 0 || e >= a.E_local) e = -1;
+            }
+        }
+        eb[j] = e;
+    }
 }
 
 // In-place exclusive prefix sum of v[0..n) by one wavefront; returns the total.
@@ -86,17 +106,22 @@ __global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int bad = 0;
 
-    // ---- pass 1: counts per (wave, expert)
+    // ---- pass 1: counts per (wave, expert).  The routing ids of kBatch
+    // chunks are loaded together, so that one memory latency covers them.
     for (int e = lane; e < E; e += 64) my_cnt[e] = 0;
-    for (int64_t c = c_begin; c < c_end; ++c) {
-        for (int e = lane; e < E; e += 64) my_mask[e] = 0;
-        wave_sync();
-        int64_t f = c * 64 + lane;
-        int e = f < S ? local_expert(a, f, &bad) : -1;
-        if (e >= 0) atomicOr(reinterpret_cast<unsigned long long*>(&my_mask[e]), 1ull << lane);
-        wave_sync();
-        for (int ee = lane; ee < E; ee += 64) my_cnt[ee] += __popcll(my_mask[ee]);
-        wave_sync();
+    for (int64_t c0 = c_begin; c0 < c_end; c0 += kBatch) {
+        int eb[kBatch];
+        load_batch(a, c0, c_end, S, lane, eb, &bad);
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            if (c0 + j >= c_end) break;
+            for (int e = lane; e < E; e += 64) my_mask[e] = 0;
+            wave_sync();
+            if (eb[j] >= 0) atomicOr(reinterpret_cast<unsigned long long*>(&my_mask[eb[j]]), 1ull << lane);
+            wave_sync();
+            for (int ee = lane; ee < E; ee += 64) my_cnt[ee] += __popcll(my_mask[ee]);
+            wave_sync();
+        }
     }
     if (bad && a.err_flag) atomicAdd(a.err_flag, 1);
     __syncthreads();
@@ -157,24 +182,30 @@ __global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
     __syncthreads();
 
     // ---- pass 3: scatter
-    for (int64_t c = c_begin; c < c_end; ++c) {
-        for (int e = lane; e < E; e += 64) my_mask[e] = 0;
-        wave_sync();
-        int64_t f = c * 64 + lane;
-        int e = f < S ? local_expert(a, f, &bad) : -1;
-        if (e >= 0) atomicOr(reinterpret_cast<unsigned long long*>(&my_mask[e]), 1ull << lane);
-        wave_sync();
-        if (f < S) {
-            int pos = -1;
-            if (e >= 0) {
-                pos = my_cnt[e] + __popcll(my_mask[e] & below);
-                a.r.sorted_ids[pos] = static_cast<int32_t>(f);
+    for (int64_t c0 = c_begin; c0 < c_end; c0 += kBatch) {
+        int eb[kBatch];
+        load_batch(a, c0, c_end, S, lane, eb, &bad);
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            if (c0 + j >= c_end) break;
+            for (int e = lane; e < E; e += 64) my_mask[e] = 0;
+            wave_sync();
+            const int e = eb[j];
+            const int64_t f = (c0 + j) * 64 + lane;
+            if (e >= 0) atomicOr(reinterpret_cast<unsigned long long*>(&my_mask[e]), 1ull << lane);
+            wave_sync();
+            if (f < S) {
+                int pos = -1;
+                if (e >= 0) {
+                    pos = my_cnt[e] + __popcll(my_mask[e] & below);
+                    a.r.sorted_ids[pos] = static_cast<int32_t>(f);
+                }
+                if (a.r.row_of) a.r.row_of[f] = pos;
             }
-            if (a.r.row_of) a.r.row_of[f] = pos;
+            wave_sync();
+            for (int ee = lane; ee < E; ee += 64) my_cnt[ee] += __popcll(my_mask[ee]);
+            wave_sync();
         }
-        wave_sync();
-        for (int ee = lane; ee < E; ee += 64) my_cnt[ee] += __popcll(my_mask[ee]);
-        wave_sync();
     }
 }
 

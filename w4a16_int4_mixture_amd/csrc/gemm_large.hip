@@ -290,10 +290,12 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
             __builtin_amdgcn_sched_barrier(0);
             read_a(rslot, av[(u + 1) & 1]);
             dequant_group(ring[(u + 1) % kLead], nib, b[(u + 1) & 1]);
+            // K step outermost: the two MFMAs on one accumulator are 2 RB
+            // MFMAs apart, so none waits for the result of the one before
 #pragma unroll
-            for (int t = 0; t < RB; ++t)
+            for (int st = 0; st < 2; ++st)
 #pragma unroll
-                for (int st = 0; st < 2; ++st)
+                for (int t = 0; t < RB; ++t)
 #pragma unroll
                     for (int jj = 0; jj < 2; ++jj)
                         acc[t][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
