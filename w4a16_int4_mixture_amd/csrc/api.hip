@@ -64,17 +64,22 @@ __device__ int32_t g_routing_errors;
 // but never below 8 groups of K per split.
 
 // K splits are whole 8-group records; every split keeps at least 2 records.
+// The streaming kernel runs four wavefronts per workgroup and (by its
+// registers) four workgroups per CU; a launch larger than one round of
+// resident workgroups ends with a partly idle machine, so K splits are added
+// only while the launch still fits in one round.  Every extra split also
+// writes and reads one fp32 [rows, N] partial: keep that under a quarter of
+// the weight stream.
+static constexpr int64_t kResidentWorkgroups = 1024;   // 256 CUs x 4
+
 static int choose_split(int64_t tiles_est, int64_t rows_est, int NC, int stages, int N,
                         int64_t weight_bytes) {
-    const int64_t target_waves = 4096;       // ~1.3 rounds of 3 wavefronts per SIMD
-    const int64_t waves = tiles_est * NC;
-    // every extra split writes and reads one fp32 [rows, N] partial: keep that
-    // under a quarter of the weight stream
+    const int64_t wgs = std::max<int64_t>(tiles_est, 1) * ((NC + 3) / 4);
     const int64_t partial_bytes = std::max<int64_t>(rows_est, 1) * N * 8;
     int split = 1;
-    while (waves * split < target_waves && stages / (split * 2) >= 2 &&
-           partial_bytes * (split * 2) <= weight_bytes / 4)
-        split *= 2;
+    while (wgs * (split + 1) <= kResidentWorkgroups && stages / (split + 1) >= 2 &&
+           partial_bytes * (split + 1) <= weight_bytes / 4)
+        ++split;
     return split;
 }
 
@@ -109,8 +114,11 @@ static w4a16_status plan_impl(const w4a16_desc* d, int layout, int rows_hint, in
                     std::max<int64_t>(round_up(static_cast<int64_t>(1.4 * tok_e + 0.999), 32), 32),
                     kLargeMaxTile));
             } else {
+                // the streaming kernel's work per K group grows with the row
+                // blocks of a tile, while an expert cut into two tiles streams
+                // its weights twice: tiles of ~1.25x the mean, in 16-row steps
                 tile_m = static_cast<int>(std::min<int64_t>(
-                    std::max<int64_t>(round_up(static_cast<int64_t>(2.0 * tok_e + 0.999), 16), 16),
+                    std::max<int64_t>(round_up(static_cast<int64_t>(1.25 * tok_e + 0.999), 16), 16),
                     kSmallMaxTile));
             }
         }
