@@ -296,7 +296,7 @@ def test_plan_rules():
     d2 = host_desc(E=48, N=7168, K=2048)
     p = capi.w4a16_plan_gemm(d13, capi.W4A16_LAYOUT_INDEXED, 512)       # ~10.7 rows/expert
     assert p.tile_m == 16 and p.block_m == 16 and p.split_k >= 1
-    # 56 tiles x 16 column quads fill one round of resident workgroups: no K split
+    # 56 tiles x 16 column quads already exceed one round of resident workgroups: no K split
     assert p.split_k == 1
     p_small = capi.w4a16_plan_gemm(d13, capi.W4A16_LAYOUT_INDEXED, 96)
     assert p_small.tile_m == 16

@@ -65,12 +65,13 @@ __device__ int32_t g_routing_errors;
 
 // K splits are whole 8-group records; every split keeps at least 2 records.
 // The streaming kernel runs four wavefronts per workgroup and (by its
-// registers) four workgroups per CU; a launch larger than one round of
-// resident workgroups ends with a partly idle machine, so K splits are added
-// only while the launch still fits in one round.  Every extra split also
-// writes and reads one fp32 [rows, N] partial: keep that under a quarter of
-// the weight stream.
-static constexpr int64_t kResidentWorkgroups = 1024;   // 256 CUs x 4
+// registers) two workgroups per CU for tiles of up to 32 rows; K splits are
+// added only while the items still fit in one round of resident workgroups
+// (more items are dealt evenly over several rounds by the persistent grid,
+// and need no split to fill the machine).  Every extra split also writes and
+// reads one fp32 [rows, N] partial: keep that under a quarter of the weight
+// stream.
+static constexpr int64_t kResidentWorkgroups = 512;   // 256 CUs x 2
 
 static int choose_split(int64_t tiles_est, int64_t rows_est, int NC, int stages, int N,
                         int64_t weight_bytes) {
@@ -265,7 +266,6 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
         } else {
             g.grid_tiles = a->blocks_cap;
         }
-        g.grid_tiles = std::min(g.grid_tiles, 65535);
         r->tiles_bound = a->tiles ? a->tiles_cap : a->blocks_cap;
         r->mt = tile_m / 16;
         r->split = split;
@@ -310,7 +310,7 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
         g.tile_m = plan.tile_m;
         g.chunks_per_expert = static_cast<int>(ceil_div(a->max_m, plan.tile_m));
         g.grid_tiles_total = d->E * g.chunks_per_expert;
-        g.grid_tiles = std::min(g.grid_tiles_total, 65535);
+        g.grid_tiles = g.grid_tiles_total;
         int split = f32_out || plan.kernel == 2 ? 1 : plan.split_k;
         r->kernel = plan.kernel;
         r->tiles_bound = g.grid_tiles_total;

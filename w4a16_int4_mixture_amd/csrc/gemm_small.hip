@@ -346,10 +346,9 @@ __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1
 // invalidate the whole L2 of the XCD, which costs far more than the GEMM.
 template <int MT, int WPL>
 __device__ __forceinline__ bool splitk_fixup(const GemmArgs& a, int p0, int nrows, int chunk,
-                                             bool active, int lane, int32_t* counter,
+                                             int s, bool active, int lane, int32_t* counter,
                                              f32x4 (&acc)[MT][WPL]) {
     __shared__ int last_flag;
-    const int s = blockIdx.z;
     // byte offsets inside one split's partial [rows, N]: a per-lane part and
     // a uniform part per (t, i, j); a split's partial is below 4 GiB (host check)
     const uint32_t voff =
@@ -409,7 +408,7 @@ __device__ __forceinline__ bool splitk_fixup(const GemmArgs& a, int p0, int nrow
 // `counter`: this part's arrival counter (split_k > 1).
 template <int MT, int WPL, int MTMAX>
 __device__ __forceinline__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, int nrows,
-                                             int chunk, int wave, int lane, u32x4* lds,
+                                             int chunk, int s, int wave, int lane, u32x4* lds,
                                              int32_t* counter) {
     const bool slot_rows = a.tile_src != TILE_MASKED;
     const bool active = chunk < a.NC;
@@ -435,7 +434,6 @@ __device__ __forceinline__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, i
     src.x = make_rsrc(a.A, static_cast<uint64_t>(a.A_rows) * a.K * 2);
 
     // K split s covers whole records [ks0, ks1)
-    const int s = blockIdx.z;
     const int nrec = a.KSP / 8;
     const int ks0 = 8 * static_cast<int>(static_cast<int64_t>(s) * nrec / a.split_k);
     const int ks1 = 8 * static_cast<int>(static_cast<int64_t>(s + 1) * nrec / a.split_k);
@@ -458,7 +456,7 @@ __device__ __forceinline__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, i
     asm volatile("" : "+v"(vbits));
     stream_loop<MT, WPL, MTMAX>(src, ks0, ks1, a.KS, wave, lane, lds, acc, a.unpack_mask, vbits);
 
-    if (a.split_k > 1 && !splitk_fixup<MT, WPL>(a, p0, nrows, chunk, active, lane, counter, acc))
+    if (a.split_k > 1 && !splitk_fixup<MT, WPL>(a, p0, nrows, chunk, s, active, lane, counter, acc))
         return;
     if (!active) return;
 
@@ -500,86 +498,125 @@ __device__ __forceinline__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, i
 
 template <int MT, int WPL>
 __device__ __forceinline__ void gemm_tile_part(const GemmArgs& a, int e, int p0, int nrows,
-                                               int chunk, int wave, int lane, u32x4* lds,
+                                               int chunk, int s, int wave, int lane, u32x4* lds,
                                                int32_t* counter) {
     const int mt_active = (nrows + 15) >> 4;
     if (mt_active <= 1)
-        gemm_tile_mt<1, WPL, MT>(a, e, p0, nrows, chunk, wave, lane, lds, counter);
+        gemm_tile_mt<1, WPL, MT>(a, e, p0, nrows, chunk, s, wave, lane, lds, counter);
     else if (MT >= 2 && mt_active == 2)
-        gemm_tile_mt<(MT >= 2 ? 2 : 1), WPL, MT>(a, e, p0, nrows, chunk, wave, lane, lds, counter);
+        gemm_tile_mt<(MT >= 2 ? 2 : 1), WPL, MT>(a, e, p0, nrows, chunk, s, wave, lane, lds, counter);
     else if (MT >= 3 && mt_active == 3)
-        gemm_tile_mt<(MT >= 3 ? 3 : 1), WPL, MT>(a, e, p0, nrows, chunk, wave, lane, lds, counter);
+        gemm_tile_mt<(MT >= 3 ? 3 : 1), WPL, MT>(a, e, p0, nrows, chunk, s, wave, lane, lds, counter);
     else if (MT >= 4)
-        gemm_tile_mt<(MT >= 4 ? 4 : 1), WPL, MT>(a, e, p0, nrows, chunk, wave, lane, lds, counter);
+        gemm_tile_mt<(MT >= 4 ? 4 : 1), WPL, MT>(a, e, p0, nrows, chunk, s, wave, lane, lds, counter);
 }
 
 // A tile of more than 16 * MT rows (a variant whose registers hold fewer row
 // blocks than the tile) is processed in parts of 16 * MT rows; each part
-// re-streams the chunk.
+// re-streams the chunk.  `quad`: the tile's group of four chunks; `s`: the
+// K split.
 template <int MT, int WPL>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int ty, int e, int p0, int nrows,
-                                          int chunk, int wave, int lane, u32x4* lds) {
+                                          int quad, int s, int wave, int lane, u32x4* lds) {
+    const int nquads = (a.NC + 3) / 4;
     for (int r = 0, part = 0; r < nrows; r += 16 * MT, ++part) {
         if (r > 0) __syncthreads();  // the part reuses the staging buffers
         int32_t* counter =
-            a.counters + (static_cast<int64_t>(ty) * kMaxTileParts + part) * gridDim.x + blockIdx.x;
-        gemm_tile_part<MT, WPL>(a, e, p0 + r, nrows - r < 16 * MT ? nrows - r : 16 * MT, chunk,
-                                wave, lane, lds, counter);
+            a.counters + (static_cast<int64_t>(ty) * kMaxTileParts + part) * nquads + quad;
+        gemm_tile_part<MT, WPL>(a, e, p0 + r, nrows - r < 16 * MT ? nrows - r : 16 * MT,
+                                quad * 4 + wave, s, wave, lane, lds, counter);
     }
 }
 
-// Tiles are walked grid-stride along grid.y, so any device-side tile count is
-// fully covered whatever the grid size; every wavefront leaves the loop once
-// its tile index passes the count.  The tile decision is uniform across the
-// workgroup, so every barrier inside is reached by all four wavefronts.
+// Workgroup w runs work items w, w + G, ... (G = the grid), an item being
+// (tile, group of four chunks, K split), splits of one chunk group adjacent;
+// the loop covers any device-side tile count whatever the grid.  The item
+// decision is uniform across the workgroup, so every barrier inside is
+// reached by all four wavefronts.
 template <int MT, int WPL>
 __global__ void __launch_bounds__(256) k_gemm_small(GemmArgs a) {
     __shared__ u32x4 lds[Lds<MT, WPL>::total];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int chunk = blockIdx.x * 4 + wave;
-    for (int ty = blockIdx.y;; ty += gridDim.y) {
+    int n_tiles;
+    if (a.tile_src == TILE_TABLE) {
+        n_tiles = a.tile_count[0];
+    } else if (a.tile_src == TILE_BLOCKS) {
+        n_tiles = a.ntp[0] / a.block_m;
+    } else {
+        n_tiles = a.grid_tiles_total;
+    }
+    n_tiles = n_tiles < a.tiles_cap ? n_tiles : a.tiles_cap;
+    const int qs = ((a.NC + 3) / 4) * a.split_k;   // items per tile
+    const int64_t n_items = static_cast<int64_t>(n_tiles) * qs;
+    for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+        const int ty = static_cast<int>(item / qs);
+        const int rem = static_cast<int>(item % qs);
+        const int quad = rem / a.split_k, s = rem % a.split_k;
         int e, p0, nrows;
         if (a.tile_src == TILE_TABLE) {
-            if (ty >= a.tile_count[0]) return;
             const int4 t = reinterpret_cast<const int4*>(a.tiles)[ty];
             e = t.x;
             p0 = t.y;
             nrows = t.z;
         } else if (a.tile_src == TILE_BLOCKS) {
             p0 = ty * a.block_m;
-            if (p0 >= a.ntp[0]) return;
             e = a.expert_ids[ty];
             nrows = a.sorted_cap - p0 < a.block_m ? a.sorted_cap - p0 : a.block_m;
         } else {
-            if (ty >= a.grid_tiles_total) return;
             const int g = ty / a.chunks_per_expert;
             const int r0 = (ty % a.chunks_per_expert) * a.tile_m;
             const int cnt = a.masked_m[g];
-            if (r0 >= cnt) continue;
             e = g;
             p0 = g * a.max_m + r0;
             nrows = cnt - r0 < a.tile_m ? cnt - r0 : a.tile_m;
         }
         if (e < 0 || e >= a.E || nrows <= 0) continue;
-        gemm_tile<MT, WPL>(a, ty, e, p0, nrows, chunk, wave, lane, lds);
-        __syncthreads();  // the next tile reuses the staging buffers
+        gemm_tile<MT, WPL>(a, ty, e, p0, nrows, quad, s, wave, lane, lds);
+        __syncthreads();  // the next item reuses the staging buffers
     }
 }
 
+// Workgroups of one kernel variant resident on the device at once (from the
+// runtime's occupancy calculation: registers and LDS), cached per variant.
+static int g_resident[5] = {0, 0, 0, 0, 0};
+
+template <int MT>
+static int resident_wgs() {
+    if (g_resident[MT] <= 0) {
+        int dev = 0, ncu = 0, per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            ncu = 256;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemm_small<MT, 4>, 256, 0) !=
+                hipSuccess ||
+            per_cu <= 0)
+            per_cu = 1;
+        g_resident[MT] = ncu * per_cu;
+    }
+    return g_resident[MT];
+}
+
+template <int MT>
+static void launch_mt(const GemmArgs& a, hipStream_t st) {
+    // One workgroup per item (from the host's tile estimate) while they fit
+    // in four rounds of resident workgroups: the hardware then hands items to
+    // CUs as they free up, which balances items of unequal cost (empty
+    // masked tiles, parts).  Beyond that, items are dealt evenly to that many
+    // workgroups, which saves the start-up of very short items (short K).
+    const int64_t cap = 4 * static_cast<int64_t>(resident_wgs<MT>());
+    const int64_t items = static_cast<int64_t>(a.grid_tiles) * ((a.NC + 3) / 4) * a.split_k;
+    const int64_t rounds = (items + cap - 1) / cap;
+    const int64_t g = rounds > 0 ? (items + rounds - 1) / rounds : 1;
+    k_gemm_small<MT, 4><<<dim3(static_cast<unsigned>(g < 1 ? 1 : g)), dim3(256), 0, st>>>(a);
+}
+
 void launch_gemm_small(const GemmArgs& a, int mt, hipStream_t st) {
-    const dim3 grid((a.NC + 3) / 4, a.grid_tiles, a.split_k), block(256);
-    if (a.CW == 64) {
-        switch (mt) {
-            case 1: k_gemm_small<1, 4><<<grid, block, 0, st>>>(a); break;
-            case 2: k_gemm_small<2, 4><<<grid, block, 0, st>>>(a); break;
-            case 3: k_gemm_small<3, 4><<<grid, block, 0, st>>>(a); break;
-            default: k_gemm_small<4, 4><<<grid, block, 0, st>>>(a); break;
-        }
-    } else {
-        // 128-column chunks hold at most two row blocks in registers
-        if (mt <= 1) k_gemm_small<1, 8><<<grid, block, 0, st>>>(a);
-        else k_gemm_small<2, 8><<<grid, block, 0, st>>>(a);
+    switch (mt) {
+        case 1: launch_mt<1>(a, st); break;
+        case 2: launch_mt<2>(a, st); break;
+        case 3: launch_mt<3>(a, st); break;
+        default: launch_mt<4>(a, st); break;
     }
 }
 

@@ -110,7 +110,7 @@ struct GemmArgs {
     int block_m, tile_m;
     const int32_t* masked_m;
     int max_m, chunks_per_expert;
-    int grid_tiles;        // grid.y
+    int grid_tiles;        // tiles the host expects (sizes the persistent grids)
     int tiles_cap;         // tile indices that may hold work (bound of the device count)
     int grid_tiles_total;  // masked: experts * chunks_per_expert
     // weights (packed records, see PackGeom)
