@@ -262,8 +262,10 @@ def main():
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit_rf,
                 "frac": round(achieved / peak, 4),
                 "traffic": traffic_from_profiles(args.workload, src_hash),
-                "kernel": "k_gemm_small (gate/up GEMM with SiLU*gate epilogue and in-kernel "
-                          "split-K fix-up: one launch per call)",
+                "kernel": ("k_gemm_large (gate/up GEMM of the PREFILL profile, SiLU*gate in its "
+                           "epilogue: one launch per call)" if args.workload == "prefill" else
+                           "k_gemm_small (gate/up GEMM with SiLU*gate epilogue and in-kernel "
+                           "split-K fix-up: one launch per call)"),
                 "algorithmic_per_launch": alg_bytes13 if bound == "hbm" else flops13,
                 "launch_us": round(gu, 2)}
 
