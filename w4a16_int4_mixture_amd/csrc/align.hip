@@ -7,17 +7,25 @@
 // path stays graph-capturable; Figure 3: activations are not padded, the
 // routing indices carry the padding sentinels.
 //
-// One workgroup of W wavefronts.  Wavefront w owns a contiguous range of
-// 64-slot chunks (flat slot f = t*k + j, ascending).  For one chunk, lane l
-// holds slot f = 64*c + l and sets bit l of mask[w][e] (64-bit LDS OR) for
-// its local expert e.  Then popcount(mask[w][e]) counts the chunk's slots of
-// expert e and popcount(mask[w][e] & lanes_below_l) is the rank of lane l's
-// slot among them: both are independent of the order in which the ORs land,
-// so the sort is stable and bit-reproducible without ordered atomics.
-//   pass 1: per (wave, expert) counts
-//   pass 2: per-expert totals, padded offsets (wave prefix scan), per-wave
-//           bases, expert_ids, padding sentinels, GEMM tile table, tails
+// B workgroups of W wavefronts; workgroup b owns a contiguous range of
+// 64-slot chunks (flat slot f = t*k + j, ascending), wavefront w a contiguous
+// piece of it.
+//   pass 0: every workgroup counts the local slots of each expert over all
+//           slots, and separately those before its own range (LDS atomics:
+//           counts do not depend on order); so every workgroup derives the
+//           same padded offsets, and its own bases, without exchanging
+//           anything with the others
+//   pass 1: per (wave, expert) counts over the workgroup's range
+//   pass 2: padded offsets (wave prefix scan), per-wave bases; workgroup 0
+//           writes expert_ids, padding sentinels, the GEMM tile table and
+//           the counts, all workgroups the tails
 //   pass 3: scatter each local slot to base + rank, record row_of
+// In passes 1 and 3, for one chunk, lane l holds slot f = 64*c + l and sets
+// bit l of mask[w][e] (64-bit LDS OR) for its local expert e.  Then
+// popcount(mask[w][e]) counts the chunk's slots of expert e and
+// popcount(mask[w][e] & lanes_below_l) is the rank of lane l's slot among
+// them: both are independent of the order in which the ORs land, so the sort
+// is stable and bit-reproducible without ordered atomics.
 
 #include "internal.h"
 
@@ -34,6 +42,8 @@ __device__ inline void wave_sync() {
 
 // Chunks of 64 slots whose routing ids one wavefront loads at once.
 constexpr int kBatch = 16;
+// Largest expert map kept in LDS.
+constexpr int kMapLds = 4096;
 
 // Local experts of slots c0*64 + lane .. for kBatch chunks (-1: none or past
 // the end); all loads of the batch are issued before any is used.
@@ -50,6 +60,35 @@ __device__ inline void load_batch(const AlignArgs& a, int64_t c0, int64_t c_end,
         const int64_t f = (c0 + j) * 64 + lane;
         int e = -1;
         if (c0 + j < c_end && f < S) {
+            if (g[j] < 0 || g[j] >= a.E_global) {
+                *bad = 1;
+            } else {
+                e = a.expert_map ? a.expert_map[g[j]] : g[j];
+                if (e < -1 || e >= a.E_local) *bad = 1;
+                if (e < 0 || e >= a.E_local) e = -1;
+            }
+        }
+        eb[j] = e;
+    }
+}
+
+// Local experts of slots (c0 + j * stride) * 64 + lane for kBatch chunks
+// (-1: none or past the end); all loads are issued before any is used.
+__device__ inline void load_strided(const AlignArgs& a, int64_t c0, int stride, int64_t chunks,
+                                    int64_t S, int lane, int (&eb)[kBatch], int* bad) {
+    int g[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+        const int64_t c = c0 + static_cast<int64_t>(j) * stride;
+        const int64_t f = c * 64 + lane;
+        g[j] = (c < chunks && f < S) ? a.topk_ids[f] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+        const int64_t c = c0 + static_cast<int64_t>(j) * stride;
+        const int64_t f = c * 64 + lane;
+        int e = -1;
+        if (c < chunks && f < S) {
             if (g[j] < 0 || g[j] >= a.E_global) {
                 *bad = 1;
             } else {
@@ -93,18 +132,82 @@ __global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
     int* pad = cnt + W * E;                                       // [E] padded counts -> offsets
     int* ntile = pad + E;                                         // [E] tiles -> tile offsets
     int* tot = ntile + E;                                         // [E] slot counts
-    int* red = tot + E;                                           // [4] totals
+    int* pre = tot + E;                                           // [E] counts before this range
+    int* red = pre + E;                                           // [4] totals
     uint64_t* my_mask = masks + w * E;
     int* my_cnt = cnt + w * E;
 
     const int64_t S = static_cast<int64_t>(a.T) * a.top_k;
     const int32_t sentinel = static_cast<int32_t>(S);
     const int64_t chunks = (S + 63) / 64;
-    const int64_t cpw = (chunks + W - 1) / W;
-    const int64_t c_begin = w * cpw;
-    const int64_t c_end = c_begin + cpw < chunks ? c_begin + cpw : chunks;
+    // this workgroup's chunks, then this wave's part of them
+    const int64_t cpb = (chunks + gridDim.x - 1) / gridDim.x;
+    const int64_t b_begin = blockIdx.x * cpb < chunks ? blockIdx.x * cpb : chunks;
+    const int64_t b_end = b_begin + cpb < chunks ? b_begin + cpb : chunks;
+    const int64_t cpw = (b_end - b_begin + W - 1) / W;
+    const int64_t c_begin = b_begin + w * cpw < b_end ? b_begin + w * cpw : b_end;
+    const int64_t c_end = c_begin + cpw < b_end ? c_begin + cpw : b_end;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int bad = 0;
+
+    // ---- pass 0: per-expert totals over all slots and counts before the
+    // range.  The expert map is cached in LDS (when it fits) and the routing
+    // ids are read 16 bytes at a time, all of a thread's loads issued first.
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        tot[e] = 0;
+        pre[e] = 0;
+    }
+    int* lmap = red + 4;                                          // [E_global] if cached
+    const bool map_lds = a.E_global <= kMapLds;
+    if (map_lds)
+        for (int i = threadIdx.x; i < a.E_global; i += blockDim.x)
+            lmap[i] = a.expert_map ? a.expert_map[i] : i;
+    __syncthreads();
+    auto local_of = [&](int g) {
+        if (g < 0 || g >= a.E_global) {
+            bad = 1;
+            return -1;
+        }
+        int e = map_lds ? lmap[g] : (a.expert_map ? a.expert_map[g] : g);
+        if (e < -1 || e >= E) bad = 1;
+        return (e >= 0 && e < E) ? e : -1;
+    };
+    const int64_t pre_end = b_begin * 64;                         // slots before the range
+    const bool vec = (reinterpret_cast<uintptr_t>(a.topk_ids) & 15) == 0;
+    // (a single workgroup takes its totals from pass 1 instead)
+    const bool multi = gridDim.x > 1;
+    const int64_t n4 = multi && vec ? S / 4 : 0;                  // 4-id groups read as int4
+    for (int64_t i0 = threadIdx.x; i0 < n4; i0 += static_cast<int64_t>(blockDim.x) * kBatch) {
+        int4 v[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int64_t i = i0 + static_cast<int64_t>(j) * blockDim.x;
+            v[j] = i < n4 ? reinterpret_cast<const int4*>(a.topk_ids)[i] : int4{-1, -1, -1, -1};
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int64_t i = i0 + static_cast<int64_t>(j) * blockDim.x;
+            if (i >= n4) break;
+            const int gs[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int e = local_of(gs[q]);
+                if (e < 0) continue;
+                atomicAdd(&tot[e], 1);
+                if (4 * i + q < pre_end) atomicAdd(&pre[e], 1);
+            }
+        }
+    }
+    for (int64_t f = 4 * n4 + threadIdx.x; multi && f < S; f += blockDim.x) {
+        const int e = local_of(a.topk_ids[f]);
+        if (e < 0) continue;
+        atomicAdd(&tot[e], 1);
+        if (f < pre_end) atomicAdd(&pre[e], 1);
+    }
+    // one workgroup reports out-of-range ids
+    if (multi && bad && a.err_flag && blockIdx.x == 0) atomicAdd(a.err_flag, 1);
+    bad = 0;
+    __syncthreads();
 
     // ---- pass 1: counts per (wave, expert).  The routing ids of kBatch
     // chunks are loaded together, so that one memory latency covers them.
@@ -123,16 +226,19 @@ __global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
             wave_sync();
         }
     }
-    if (bad && a.err_flag) atomicAdd(a.err_flag, 1);
+    if (!multi && bad && a.err_flag) atomicAdd(a.err_flag, 1);
     __syncthreads();
 
-    // ---- pass 2: totals, offsets, metadata
+    // ---- pass 2: offsets, metadata
     const int bm = a.block_m;
     const int tm = a.r.tile_m > 0 ? a.r.tile_m : 1;
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        int c = 0;
-        for (int ww = 0; ww < W; ++ww) c += cnt[ww * E + e];
-        tot[e] = c;
+        if (!multi) {
+            int c = 0;
+            for (int ww = 0; ww < W; ++ww) c += cnt[ww * E + e];
+            tot[e] = c;
+        }
+        const int c = tot[e];
         pad[e] = (c + bm - 1) / bm * bm;
         ntile[e] = (c + tm - 1) / tm;
     }
@@ -149,12 +255,13 @@ __global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
     const int total = red[0];
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         const int off = pad[e];
-        int run = off;
+        int run = off + pre[e];
         for (int ww = 0; ww < W; ++ww) {
             int b = cnt[ww * E + e];
             cnt[ww * E + e] = run;
             run += b;
         }
+        if (blockIdx.x != 0) continue;
         const int c = tot[e];
         const int p = (c + bm - 1) / bm * bm;
         for (int j = c; j < p; ++j) a.r.sorted_ids[off + j] = sentinel;
@@ -171,14 +278,14 @@ __global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
             }
         }
     }
-    if (threadIdx.x == 0) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
         a.r.num_tokens_padded[0] = total;
         if (a.r.tiles) a.r.tile_count[0] = red[1];
     }
-    for (int i = total + threadIdx.x; i < a.r.sorted_cap; i += blockDim.x)
-        a.r.sorted_ids[i] = sentinel;
-    for (int b = total / bm + threadIdx.x; b < a.r.blocks_cap; b += blockDim.x)
-        a.r.expert_ids[b] = -1;
+    const int64_t gtid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t gsize = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = total + gtid; i < a.r.sorted_cap; i += gsize) a.r.sorted_ids[i] = sentinel;
+    for (int64_t b = total / bm + gtid; b < a.r.blocks_cap; b += gsize) a.r.expert_ids[b] = -1;
     __syncthreads();
 
     // ---- pass 3: scatter
@@ -212,17 +319,27 @@ __global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
 int align_waves(int E_local) {
     // keep the LDS footprint (12 bytes per wave and expert) under 60 KiB
     int w = 16;
-    while (w > 1 && static_cast<int64_t>(w) * E_local * 12 + E_local * 12 + 64 > 60 * 1024) w >>= 1;
+    // (plus 16 per expert and the cached expert map, at most 16 KiB)
+    while (w > 1 && static_cast<int64_t>(w) * E_local * 12 + E_local * 16 + 64 + 4 * kMapLds >
+                        60 * 1024)
+        w >>= 1;
     return w;
 }
 
-size_t align_lds_bytes(int W, int E_local) {
-    return static_cast<size_t>(W) * E_local * 12 + static_cast<size_t>(E_local) * 12 + 16;
+size_t align_lds_bytes(int W, int E_local, int E_global) {
+    return static_cast<size_t>(W) * E_local * 12 + static_cast<size_t>(E_local) * 16 + 16 +
+           (E_global <= kMapLds ? static_cast<size_t>(E_global) * 4 : 0);
 }
 
 void launch_align(const AlignArgs& a, hipStream_t s) {
     int W = align_waves(a.E_local);
-    k_align<<<dim3(1), dim3(64 * W), align_lds_bytes(W, a.E_local), s>>>(a);
+    // about one chunk of 64 slots per wavefront in each workgroup's range;
+    // every workgroup also counts all slots once (pass 0)
+    const int64_t chunks = (static_cast<int64_t>(a.T) * a.top_k + 63) / 64;
+    int64_t nb = chunks / W;
+    nb = nb < 1 ? 1 : (nb > 64 ? 64 : nb);
+    k_align<<<dim3(static_cast<unsigned>(nb)), dim3(64 * W),
+              align_lds_bytes(W, a.E_local, a.E_global), s>>>(a);
 }
 
 }  // namespace w4a16
