@@ -264,11 +264,12 @@ typedef struct {
     void* out;                      /* device; bf16 (or float with F32_OUT) */
     int64_t out_rows;               /* rows available in out */
     /* scratch: device, 256-byte aligned, >= w4a16_gemm_workspace_bytes(...).
-       It starts with the split-K arrival counters, which must read zero when
-       a call starts: allocate it zeroed.  A completed call leaves the
-       counters it used at zero but may leave partial sums after them, so a
-       workspace reused for a call of another shape, split or tile capacity
-       must be zeroed again first.  Calls that share a workspace must not run
+       It starts with counters (split-K arrival counters; with a PREFILL
+       weight, the 256-byte work-queue block), which must read zero when a
+       call starts: allocate it zeroed.  A completed call leaves the counters
+       it used at zero but may leave partial sums after them, so a workspace
+       reused for a call of another shape, split or tile capacity must be
+       zeroed again first.  Calls that share a workspace must not run
        concurrently. */
     void* workspace;
     uint64_t workspace_bytes;

@@ -181,6 +181,12 @@ def test_gemm_argument_checks():
     # a plain W13 with the SiLU epilogue stages bf16 Y13 [sorted_cap, N]
     assert capi.w4a16_gemm_workspace_bytes(gemm_args(d, epilogue=capi.W4A16_EPI_SILU_MUL)) == \
         256 * 128 * 2
+    # a PREFILL weight: the large-M kernel's work-queue counters, one 256-byte
+    # block before the Y13 staging
+    dp = host_desc(profile=capi.W4A16_PROFILE_PREFILL)
+    assert capi.w4a16_gemm_workspace_bytes(gemm_args(dp)) == 256
+    assert capi.w4a16_gemm_workspace_bytes(gemm_args(dp, epilogue=capi.W4A16_EPI_SILU_MUL)) == \
+        256 + 256 * 128 * 2
     # masked: expected_m must be positive; split_k overrides are refused
     m = dict(layout=capi.W4A16_LAYOUT_MASKED, masked_m=1 << 20, max_m=32, expected_m=32,
              A_rows=64, out_rows=64)

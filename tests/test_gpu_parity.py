@@ -270,6 +270,48 @@ def test_large_tile_kernel_exact(m, H, tile_m):
     assert np.array_equal(host(Y2, np.uint16)[pos], ref2[f])
 
 
+def test_large_tile_work_queue_exact(m):
+    """A launch with more column-pair items than workgroups takes its items
+    from per-XCD counters, largest tile first.  Skewed routing gives tiles of
+    many sizes (ragged last tiles of split experts, three experts with no
+    rows); under the exactness invariant gate/up is bit-identical to the oracle
+    on every row, on three calls in a row (the last workgroup of a call clears
+    the counters for the next), and the counters read zero afterwards."""
+    from w4a16_int4_mixture_amd import _capi
+    E, H, I, T, k = 40, 512, 1024, 1200, 4
+    d = exact_problem(77, E, H, I, T, k)
+    rng = np.random.default_rng(78)
+    p = 1.0 / np.arange(1, E + 1) ** 0.8
+    p[[5, 17, 31]] = 0
+    p /= p.sum()
+    d["topk_ids"] = np.stack([rng.choice(E, size=k, replace=False, p=p)
+                              for _ in range(T)]).astype(np.int32)
+    print("large tile work queue: 40 experts, skewed", flush=True)
+    w13 = prepare(m, d["codes13"], d["scales13"], 2)
+    plan = _capi.w4a16_plan_gemm(w13.desc, _capi.W4A16_LAYOUT_INDEXED, T * k, 0, 0)
+    assert plan.kernel == 2
+    r = m.Routing(T, k, E, 16, plan.tile_m, "cuda")
+    r.align(dev(d["topk_ids"]), E)
+    n_tiles = int(host(r.tile_count)[0])
+    sizes = host(r.tiles)[:n_tiles, 2]
+    assert n_tiles * (2 * I // 256) > 256 and len(set(sizes.tolist())) > 8
+    X = dev(d["X"])
+    Y13 = torch.empty((r.sorted_cap, 2 * I), dtype=torch.int16, device="cuda")
+    a = m.gemm_args_indexed(w13, X, r, Y13, _capi.W4A16_AROW_TOKEN, rows_hint=T * k)
+    ws = m._workspace(_capi.w4a16_gemm_workspace_bytes(a), "cuda")
+    pos, f = slot_rows(r, T, k)
+    ref13 = oracle.moe_gate_up(d["X"], d["topk_ids"], E, None, d["codes13"], d["scales13"])
+    for call in range(3):
+        Y13.fill_(-1)
+        m.run_gemm(m.gemm_args_indexed(w13, X, r, Y13, _capi.W4A16_AROW_TOKEN, rows_hint=T * k,
+                                       workspace=ws), "cuda")
+        torch.cuda.synchronize()
+        got = host(Y13, np.uint16)[pos]
+        bad = np.nonzero(np.any(got != ref13[f], axis=1))[0]
+        assert bad.size == 0, f"call {call}: {bad.size} rows differ, first positions {pos[bad[:8]]}"
+        assert not host(ws[:36]).any(), f"call {call}: queue counters left non-zero"
+
+
 @pytest.mark.parametrize("interleave", [False, True])
 def test_large_tile_kernel_random(m, interleave):
     """General inputs through the large-M kernel: it rounds each dequantised

@@ -127,6 +127,10 @@ def gemm_args_indexed(w: PreparedWeight, A, routing: Routing, out, arow, epilogu
     if workspace is not None:
         a.workspace = workspace.data_ptr()
         a.workspace_bytes = workspace.numel() * workspace.element_size()
+    # the struct holds raw pointers: keep the tensors alive with it, so that a
+    # temporary passed in is not freed (and its memory handed out again)
+    # before the launch
+    a._refs = (w, A, routing, out, workspace)
     return a
 
 
@@ -148,6 +152,10 @@ def gemm_args_masked(w: PreparedWeight, A, masked_m, max_m, expected_m, out, epi
     if workspace is not None:
         a.workspace = workspace.data_ptr()
         a.workspace_bytes = workspace.numel() * workspace.element_size()
+    # the struct holds raw pointers: keep the tensors alive with it, so that a
+    # temporary passed in is not freed (and its memory handed out again)
+    # before the launch
+    a._refs = (w, A, out, workspace, masked_m)
     return a
 
 
@@ -159,6 +167,8 @@ def run_gemm(args: _capi.w4a16_gemm_args, device, keep=None, stream=None):
         ws = _workspace(need, device)
         args.workspace = ws.data_ptr()
         args.workspace_bytes = ws.numel()
+        if stream is not None:
+            ws.record_stream(stream)    # not reused before the launch on `stream` ends
     _capi.w4a16_moe_w4a16_gemm(args, stream)
     if keep is not None and ws is not None:
         keep.append(ws)

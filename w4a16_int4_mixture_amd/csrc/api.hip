@@ -149,7 +149,7 @@ struct Resolved {
     int split;
     int64_t rows_cap;        // rows of the position-indexed output space
     int64_t tiles_bound;     // tile indices a launch can visit
-    uint64_t ws_counters;    // bytes of arrival counters (split > 1)
+    uint64_t ws_counters;    // bytes of arrival counters (split > 1) or work-queue counters
     uint64_t ws_partial;     // bytes of fp32 partials (split > 1)
     uint64_t ws_y13;         // bytes of the bf16 gate/up staging (SiLU not fused)
     bool silu_separate;      // run the SiLU kernel on staged Y13
@@ -328,12 +328,14 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
     const bool split = r->split > 1;
     r->silu_separate = a->epilogue == W4A16_EPI_SILU_MUL && !interleaved;
     const int64_t gx = (g.NC + 3) / 4;
-    r->ws_counters = split ? round256(static_cast<uint64_t>(r->tiles_bound) * kMaxTileParts * gx * 4) : 0;
+    // split-K arrival counters; the PREFILL kernel's work-queue counters (nine ints)
+    r->ws_counters = split ? round256(static_cast<uint64_t>(r->tiles_bound) * kMaxTileParts * gx * 4)
+                     : r->kernel == 2 ? 256 : 0;
     r->ws_partial = split ? round256(static_cast<uint64_t>(r->split) * r->rows_cap * d->N * 4) : 0;
     r->ws_y13 = r->silu_separate ? round256(static_cast<uint64_t>(r->rows_cap) * d->N * 2) : 0;
     g.ws_stride = r->rows_cap * d->N;
     char* ws = static_cast<char*>(a->workspace);
-    g.counters = split && ws ? reinterpret_cast<int32_t*>(ws) : nullptr;
+    g.counters = r->ws_counters && ws ? reinterpret_cast<int32_t*>(ws) : nullptr;
     g.partials = split && ws ? reinterpret_cast<float*>(ws + r->ws_counters) : nullptr;
     if (a->epilogue == W4A16_EPI_SILU_MUL && interleaved) {
         g.out_kind = OUT_SILU;

@@ -46,10 +46,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kRecWords = 4608;       // words per 8-group record (codes, then scales)
-constexpr int kLead = 8;              // groups of weights and activations in flight
-constexpr int kSlots = kLead + 1;     // LDS activation slots
-constexpr int kSlotBytes = 16 * 1024; // 8 row blocks x 2 K steps x 64 lanes x 16 bytes
+constexpr int kRecWords = 4608;        // words per 8-group record (codes, then scales)
+constexpr uint32_t kSlot = 32 * 1024;  // LDS bytes of one stage: 256 rows x 64 K x 2 bytes
+constexpr int kSlots = 4;              // stages of activations in LDS
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -120,6 +119,12 @@ __device__ inline void wait_vmcnt() {
 // (a fence would wait for every weight load in flight as well).
 __device__ inline void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
 
+// Workgroup barrier after LDS reads or writes made with ds_ instructions: the
+// compiler does not wait for them before an s_barrier it did not place, so
+// this one waits for all of this wave's LDS operations first (the epilogue's
+// staging writes must have landed before other waves read them).
+__device__ inline void barrier_ds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 struct Item {
     int e, p0, nrows, pair;
 };
@@ -172,37 +177,41 @@ __device__ __forceinline__ void store_rows(const GemmArgs& a, const Item& it, co
 }
 
 // One work item with up to 32 * RB rows.
+//
+// The K loop runs in stages of two groups (64 K).  The activations of a stage
+// sit in an LDS slot as [32 RB rows][128 bytes], row-major; the 16-byte chunk
+// c of row r is stored at chunk position c ^ f(r), f(r) = (r & 7) ^ ((r >> 3)
+// & 1), so that the A-operand reads (eight or sixteen consecutive rows, one
+// chunk each) fall in distinct LDS banks.  Each buffer-to-LDS load brings
+// eight whole rows of a stage (eight lanes per 128-byte line), which the
+// vector L1 serves as eight line requests.  Four slots: while stage s is read,
+// s + 1 has landed and s + 2, s + 3 are in flight.  Weights of stages s .. s +
+// 3 sit in a register ring.  One barrier per stage.
 template <int RB>
 __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, int wave, int lane,
                                            char* lds) {
-    // activation loads per group: one per (row block, K step), dealt to the
-    // four waves in turn; every wave issues kDma of them (a wave past the
-    // last one repeats it: same data to the same LDS bytes)
-    constexpr int kNA = 2 * RB;
-    constexpr int kDma = (kNA + 3) / 4;
-    // At the top of group g the activations of group g + 1 must have landed
-    // (they are read from LDS during group g); the kLead - 2 later groups of
-    // kDma + 2 operations may stay in flight.  (Group g + 1's own weight
-    // loads are not counted: the compiler may order them before its
-    // activation loads.  Scheduling barriers keep groups apart.)
-    constexpr int kWaitA = (kLead - 2) * (kDma + 2);
+    // buffer-to-LDS loads per wave and stage: 4 RB of 8 rows, dealt to the
+    // four waves; then the weights of the stage's two groups (codes, scales)
+    constexpr int kDma = RB;
+    constexpr int kStageOps = kDma + 4;
 
     const int chunk = it.pair * 2 + (wave >> 1);
     const int h = wave & 1;
     const bool active = chunk < a.NC;
     const bool slot_rows = a.tile_src != TILE_MASKED;
     const int KS = a.KS;
-    const int KSP = a.KSP;   // a multiple of 8 = kLead; groups >= KS have zero weights
+    const int KSP = a.KSP;          // a multiple of 8; groups >= KS have zero weights
+    const int SA = (KS + 1) >> 1;   // stages holding real activations
 
-    // Activation load q covers row block q / 2, K step q % 2: lane l takes
-    // row 32 (q / 2) + l % 32, K 16 (q % 2) + 8 (l / 32) .. +7 of each group.
-    // Rows past the tile reuse its first row (computed, never stored).
+    // Activation load i of this wave covers rows 8 j .. 8 j + 7, j = wave + 4 i:
+    // lane l takes row 8 j + l / 8 and global chunk (l % 8) ^ f(row).  Rows
+    // past the tile reuse its first row (computed, never stored).
+    const uint32_t cl = static_cast<uint32_t>((lane & 7) ^ (lane >> 3));
     uint32_t aoff[kDma];
-    uint32_t adst[kDma];
 #pragma unroll
     for (int i = 0; i < kDma; ++i) {
-        const int q = wave + 4 * i < kNA ? wave + 4 * i : kNA - 1;
-        const int r = 32 * (q >> 1) + (lane & 31);
+        const int j = wave + 4 * i;
+        const int r = 8 * j + (lane >> 3);
         const int rr = r < it.nrows ? r : 0;
         int64_t row = it.p0 + rr;
         if (slot_rows && a.arow != W4A16_AROW_POSITION) {
@@ -213,9 +222,12 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
         }
         row = row < a.A_rows ? row : a.A_rows - 1;
         // A_rows * K * 2 < 2^32 is checked on the host
-        aoff[i] = static_cast<uint32_t>(row * a.K * 2 + (q & 1) * 32 + (lane >> 5) * 16);
-        adst[i] = static_cast<uint32_t>(q * 1024);
+        aoff[i] = static_cast<uint32_t>(row * a.K * 2) + 16 * (cl ^ static_cast<uint32_t>(j & 1));
     }
+    // In the last stage of an odd group count, the chunks of the missing
+    // second group (chunk >= 4) repeat the first group's (a row's K range is
+    // never left; those products meet zero weights).
+    const uint32_t dpart = (cl & 4) ? 64u : 0u;
     const __amdgpu_buffer_rsrc_t x = make_rsrc(a.A, static_cast<uint64_t>(a.A_rows) * a.K * 2);
 
     const int64_t cbase = static_cast<int64_t>(it.e) * a.NC + (active ? chunk : a.NC - 1);
@@ -225,19 +237,22 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
     const uint32_t scale_off = static_cast<uint32_t>((h * 32 + (lane & 31)) * 4);
     const uint32_t nib = a.nib_mask;
 
-    // Loads of group g into LDS slot byte offset `slot` and ring slot `r`.
-    // Padding groups (KS <= g < KSP) read zero weights and, for the
-    // activations, the last real group again (finite values times zero: a
-    // row's K range is never left); groups past KSP repeat the last ones and
-    // are never used.
-    auto issue = [&](int g, uint32_t slot, WGroup& r) {
-        const int ga = g < KS ? g : KS - 1;
-        const int gw = g < KSP ? g : KSP - 1;
+    // One batch of loads: the activations of stage sa into LDS slot `slot`,
+    // then the weights of stage sw into ring entry r (in this order: the
+    // waits count on it).  Stages past the activations repeat the last one;
+    // weight groups past KSP repeat the last (never used).
+    auto issue = [&](int sa, uint32_t slot, int sw, WGroup (&r)[2]) {
+        const bool part = (KS & 1) && sa >= SA - 1;
+        sa = sa < SA ? sa : SA - 1;
 #pragma unroll
         for (int i = 0; i < kDma; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(x, LDS_PTR(lds + slot + adst[i]), 16,
-                                                     aoff[i], ga * 64, 0, 0);
-        load_wgroup(r, w, code_off, scale_off, gw);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(x, LDS_PTR(lds + slot + (wave + 4 * i) * 1024), 16,
+                                                     part ? aoff[i] - dpart : aoff[i], sa * 128, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        const int g0 = 2 * sw < KSP ? 2 * sw : KSP - 1;
+        const int g1 = 2 * sw + 1 < KSP ? 2 * sw + 1 : KSP - 1;
+        load_wgroup(r[0], w, code_off, scale_off, g0);
+        load_wgroup(r[1], w, code_off, scale_off, g1);
     };
 
     f32x16 acc[RB][2];
@@ -246,76 +261,102 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[t][j] = f32x16{};
 
-    WGroup ring[kLead];
+    // A operand of (row block t, group half hh, K step st): lane l reads row
+    // 32 t + l % 32, chunk 4 hh + 2 st + l / 32, at its swizzled position
+    const uint32_t fl = static_cast<uint32_t>((lane & 7) ^ ((lane >> 3) & 1));
+    uint32_t aread[2][2];
 #pragma unroll
-    for (int i = 0; i < kLead; ++i) {
-        issue(i, i * kSlotBytes, ring[i]);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+            aread[hh][st] = static_cast<uint32_t>((lane & 31) * 128) +
+                            16 * ((static_cast<uint32_t>(4 * hh + 2 * st + (lane >> 5))) ^ fl);
 
-    // A fragments of one group (row block t, K step st), and B operands
-    // b[jj][st]; both double-buffered by group parity
     bf16x8 av[2][RB][2];
     bf16x8 b[2][2][2];
-    auto read_a = [&](uint32_t slot, bf16x8 (&dst)[RB][2]) {
-        const u32x4* As = reinterpret_cast<const u32x4*>(lds + slot);
+    auto read_a = [&](uint32_t slot, int hh, bf16x8 (&dst)[RB][2]) {
 #pragma unroll
         for (int t = 0; t < RB; ++t)
 #pragma unroll
             for (int st = 0; st < 2; ++st)
-                dst[t][st] = __builtin_bit_cast(bf16x8, As[(2 * t + st) * 64 + lane]);
+                dst[t][st] = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4*>(lds + slot + t * 4096 + aread[hh][st]));
     };
-    wait_vmcnt<(kLead - 1) * (kDma + 2)>();   // this wave's activations of group 0
-    barrier_lds();
-    read_a(0, av[0]);
-    dequant_group(ring[0], nib, b[0]);
-
-    // kLead groups per trip, so that ring slots and register buffers are
-    // static (kLead is even and divides KSP).  Group g: wait for this wave's
-    // activations of g + 1, barrier (all of them landed; every wave is done
-    // with the slot of group g - 1), load group g + kLead into that slot and
-    // ring slot u; then, while the MFMAs of group g run on registers, read
-    // the activations of group g + 1 from LDS and dequantise its weights.
-    uint32_t rslot = kSlotBytes;                 // LDS slot of group g + 1
-    uint32_t wslot = kLead * kSlotBytes;         // LDS slot of group g + kLead
-    for (int g0 = 0; g0 < KSP; g0 += kLead) {
+    auto mfmas = [&](const bf16x8 (&av_)[RB][2], const bf16x8 (&b_)[2][2]) {
+        // K step outermost: the two MFMAs on one accumulator are 2 RB MFMAs
+        // apart, so none waits for the result of the one before
 #pragma unroll
-        for (int u = 0; u < kLead; ++u) {
-            const int g = g0 + u;
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int t = 0; t < RB; ++t)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+                    acc[t][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av_[t][st], b_[jj][st],
+                                                                         acc[t][jj], 0, 0, 0);
+        // each MFMA followed by about 96 / (4 RB) VALU ops of the next
+        // group's dequant and half an LDS read, which issue while it runs
+        constexpr int kV = (96 + 4 * RB - 1) / (4 * RB);
+#pragma unroll
+        for (int i = 0; i < 4 * RB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
+        }
+    };
+
+    // Prologue: weights of stage 0, then (activations of s, weights of s + 1)
+    // for s = 0, 1, 2: the same order as the loop's batches.
+    WGroup ring[4][2];
+    {
+        load_wgroup(ring[0][0], w, code_off, scale_off, 0);
+        load_wgroup(ring[0][1], w, code_off, scale_off, 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+            issue(s, s * kSlot, s + 1, ring[s + 1]);
             __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt<kWaitA>();
+        }
+    }
+    // activations of stage 0 (the weights of stage 1 and two batches may stay
+    // in flight)
+    wait_vmcnt<4 + 2 * kStageOps>();
+    barrier_lds();
+    read_a(0, 0, av[0]);
+    dequant_group(ring[0][0], nib, b[0]);
+
+    // Four stages per trip (slot and ring indices static; KSP / 2 is even).
+    // Even group 2 s: read the activations of group 2 s + 1 (same stage) and
+    // dequantise its weights while the MFMAs of group 2 s run.  Odd group
+    // 2 s + 1: wait for this wave's activations of stage s + 1 (the weights
+    // of s + 2 and the batch of stage s - 1 may stay in flight), barrier (they
+    // all landed; every wave is done with the slot of stage s - 1), load the
+    // activations of stage s + 3 into that slot and the weights of stage s + 4
+    // into ring entry s % 4, then read the activations of group 2 s + 2.
+    const int NST = KSP >> 1;
+    for (int s0 = 0; s0 < NST; s0 += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int s = s0 + u;
+            __builtin_amdgcn_sched_barrier(0);
+            read_a(u * kSlot, 1, av[1]);
+            dequant_group(ring[u][1], nib, b[1]);
+            mfmas(av[0], b[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<4 + kStageOps>();
             barrier_lds();
             __builtin_amdgcn_sched_barrier(0);
-            issue(g + kLead, wslot, ring[u]);
+            issue(s + 3, ((u + 3) & 3) * kSlot, s + 4, ring[u]);
+            // (the next batch's weights go to ring[u], whose last group was
+            // dequantised above)
             __builtin_amdgcn_sched_barrier(0);
-            read_a(rslot, av[(u + 1) & 1]);
-            dequant_group(ring[(u + 1) % kLead], nib, b[(u + 1) & 1]);
-            // K step outermost: the two MFMAs on one accumulator are 2 RB
-            // MFMAs apart, so none waits for the result of the one before
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int t = 0; t < RB; ++t)
-#pragma unroll
-                    for (int jj = 0; jj < 2; ++jj)
-                        acc[t][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            av[u & 1][t][st], b[u & 1][jj][st], acc[t][jj], 0, 0, 0);
-            // each MFMA followed by about 96 / (4 RB) VALU ops of the next
-            // group's dequant and half an LDS read, which issue while it runs
-            constexpr int kV = (96 + 4 * RB - 1) / (4 * RB);
-#pragma unroll
-            for (int i = 0; i < 4 * RB; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
-            }
-            rslot = rslot + kSlotBytes == kSlots * kSlotBytes ? 0 : rslot + kSlotBytes;
-            wslot = wslot + kSlotBytes == kSlots * kSlotBytes ? 0 : wslot + kSlotBytes;
+            read_a(((u + 1) & 3) * kSlot, 0, av[0]);
+            dequant_group(ring[(u + 1) & 3][0], nib, b[0]);
+            mfmas(av[1], b[1]);
         }
     }
     // drain the loads past the end before the slots are reused
     wait_vmcnt<0>();
-    barrier_lds();
+    barrier_ds();
 
     // Epilogue, in passes of 128 rows: the fp32 accumulators of the pass go
     // to LDS as a [128 rows][256 columns] tile of the workgroup (the two
@@ -339,9 +380,9 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
                 stg[r * 256 + s1] = acc[t][1][i];
             }
         }
-        barrier_lds();
+        barrier_ds();
         store_rows(a, it, stg, 128 * p, it.nrows < 128 * p + 128 ? it.nrows : 128 * p + 128);
-        barrier_lds();   // the staging bytes are reused (next pass, next item's loads)
+        barrier_ds();    // the staging bytes are reused (next pass, next item's loads)
     }
 }
 
@@ -370,8 +411,66 @@ __device__ inline Item tile_of(const GemmArgs& a, int ty) {
     return it;
 }
 
+// Tiles the work queue can order (more run in the static order).
+constexpr int kMaxOrder = 256;
+
+// Dynamic schedule for launches with more items than workgroups.  Every
+// workgroup ranks the tiles by 32-row block count, largest first (ties by
+// index, so the order is the same everywhere), and deals them to the eight
+// XCDs in snake order (ranks x, 15-x, 16+x, 31-x, ... go to XCD x), which
+// evens out the row blocks per XCD.  The items of XCD x (its tiles in that
+// order, each tile's column pairs in turn) are handed out by counter q[x]:
+// the column pairs of one tile run close together in time on the XCD whose
+// L2 holds that tile's activation rows, and the largest items go first so
+// that the last round is made of the smallest.  A workgroup whose XCD has no
+// items left takes them from the other XCDs' counters.  q[8] counts the
+// workgroups that found every counter spent; the last of them clears all
+// nine, so the next launch finds them at zero.
+__device__ inline void rank_tiles(const GemmArgs& a, int n_tiles, int* s_cost, int* s_order) {
+    const int t = threadIdx.x;
+    int cost = 0;
+    if (t < n_tiles) {
+        const Item it = tile_of(a, t);
+        cost = it.nrows > 0 ? (it.nrows + 31) >> 5 : 0;
+    }
+    s_cost[t] = cost;
+    __syncthreads();
+    if (t < n_tiles) {
+        int rank = 0;
+        for (int u = 0; u < n_tiles; ++u) {
+            const int c = s_cost[u];
+            rank += c > cost || (c == cost && u < t);
+        }
+        s_order[rank] = t;
+    }
+    __syncthreads();
+}
+
+// Thread 0: the next item (tile * CP + pair) from the XCD's counter, then
+// from the others'; -1 once all are spent.  `spent` marks counters found past
+// their last item (they never come back).
+__device__ inline int pull_item(int* q, int xcd, int n_tiles, int CP, const int* s_cost,
+                                const int* s_order, unsigned& spent) {
+    for (int k = 0; k < 8; ++k) {
+        const int x = (xcd + k) & 7;
+        if (spent & (1u << x)) continue;
+        const int j = atomicAdd(q + x, 1);
+        const int i = j / CP;
+        const int r = 16 * (i >> 1) + ((i & 1) ? 15 - x : x);
+        if (r < n_tiles && s_cost[s_order[r]] > 0) return s_order[r] * CP + j % CP;
+        spent |= 1u << x;
+    }
+    return -1;
+}
+
 __global__ void __launch_bounds__(256) k_gemm_large(GemmArgs a) {
-    __shared__ __attribute__((aligned(1024))) char lds[kSlots * kSlotBytes];
+    // one LDS object: the staging slots, then the work queue's tile order
+    // (a second __shared__ object makes the compiler wait for every LDS DMA
+    // load before each read of the slots)
+    __shared__ __attribute__((aligned(1024))) char lds[kSlots * kSlot + (2 * kMaxOrder + 4) * 4];
+    int* s_cost = reinterpret_cast<int*>(lds + kSlots * kSlot);
+    int* s_order = s_cost + kMaxOrder;
+    int& s_pick = s_order[kMaxOrder];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -387,22 +486,35 @@ __global__ void __launch_bounds__(256) k_gemm_large(GemmArgs a) {
     }
     const int CP = (a.NC + 1) / 2;
     const int nwg = gridDim.x;
-    // more items than workgroups and a whole number of workgroups per XCD:
-    // tile ty runs on XCD ty % 8; otherwise items are dealt out in order
-    const bool by_xcd = static_cast<int64_t>(n_tiles) * CP > nwg && (nwg & 7) == 0;
     const int xcd = blockIdx.x & 7;
+    const bool many = static_cast<int64_t>(n_tiles) * CP > nwg;
+    const bool queued = many && a.counters && n_tiles <= kMaxOrder;
+    // static order: with a whole number of workgroups per XCD, tile ty runs on
+    // XCD ty % 8; otherwise items are dealt out in order
+    const bool by_xcd = many && (nwg & 7) == 0;
     const int per_xcd = nwg >> 3;
+    if (queued) rank_tiles(a, n_tiles, s_cost, s_order);
+    unsigned spent = 0;
     for (int j = by_xcd ? (blockIdx.x >> 3) : blockIdx.x;; j += by_xcd ? per_xcd : nwg) {
         int ty, pair;
-        if (by_xcd) {
+        if (queued) {
+            if (threadIdx.x == 0) s_pick = pull_item(a.counters, xcd, n_tiles, CP, s_cost, s_order, spent);
+            __syncthreads();
+            // every wave reads s_pick before the item's first barrier, so the
+            // next write cannot overtake a read
+            const int pick = __builtin_amdgcn_readfirstlane(s_pick);
+            if (pick < 0) break;
+            ty = pick / CP;
+            pair = pick % CP;
+        } else if (by_xcd) {
             ty = 8 * (j / CP) + xcd;
             pair = j % CP;
-            if (j / CP * 8 >= n_tiles) return;
+            if (j / CP * 8 >= n_tiles) break;
             if (ty >= n_tiles) continue;
         } else {
             ty = j / CP;
             pair = j % CP;
-            if (ty >= n_tiles) return;
+            if (ty >= n_tiles) break;
         }
         Item it = tile_of(a, ty);
         if (it.nrows <= 0) continue;
@@ -417,6 +529,11 @@ __global__ void __launch_bounds__(256) k_gemm_large(GemmArgs a) {
             case 7: large_item<7>(a, it, wave, lane, lds); break;
             default: large_item<8>(a, it, wave, lane, lds); break;
         }
+    }
+    if (queued && threadIdx.x == 0) {
+        __threadfence();
+        if (atomicAdd(a.counters + 8, 1) == nwg - 1)
+            for (int x = 0; x < 9; ++x) atomicExch(a.counters + x, 0);
     }
 }
 
