@@ -48,7 +48,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kRecWords = 4608;        // words per 8-group record (codes, then scales)
 constexpr uint32_t kSlot = 32 * 1024;  // LDS bytes of one stage: 256 rows x 64 K x 2 bytes
-constexpr int kSlots = 4;              // stages of activations in LDS
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -129,13 +128,20 @@ struct Item {
     int e, p0, nrows, pair;
 };
 
+// The four activation slots (separate LDS objects, so that the compiler can
+// tell a slot being read from one being loaded); the epilogue stages 32 rows
+// of fp32 results in each.
+struct Slots {
+    char* p[4];
+};
+
 }  // namespace
 
 // Stores rows [r0, r1) of a work item from the fp32 staging tile in LDS
-// ([128 rows][256 columns], row r at (r - r0) * 256): 32 lanes per row,
-// 8 staged values each; bf16 or fp32 rows, or SiLU(gate) * up of the
-// interleaved gate/up pairs (4 outputs per lane).
-__device__ __forceinline__ void store_rows(const GemmArgs& a, const Item& it, const float* stg,
+// ([128 rows][256 columns]; rows 32 k .. 32 k + 31 of the pass in slot k):
+// 32 lanes per row, 8 staged values each; bf16 or fp32 rows, or SiLU(gate) *
+// up of the interleaved gate/up pairs (4 outputs per lane).
+__device__ __forceinline__ void store_rows(const GemmArgs& a, const Item& it, const Slots& sl,
                                         int r0, int r1) {
     const bool silu = a.out_kind == OUT_SILU;
     const bool slot_rows = a.tile_src != TILE_MASKED;
@@ -154,7 +160,7 @@ __device__ __forceinline__ void store_rows(const GemmArgs& a, const Item& it, co
             if (a.orow == W4A16_OROW_SLOT) orow = f;
         }
         if (cc >= cvalid) continue;
-        const f32x4* src = reinterpret_cast<const f32x4*>(stg + (r - r0) * 256 + 8 * q);
+        const f32x4* src = reinterpret_cast<const f32x4*>(sl.p[(r - r0) >> 5]) + ((r - r0) & 31) * 64 + 2 * q;
         const f32x4 v0 = src[0], v1 = src[1];
         if (silu) {
             u32x2 o;
@@ -189,7 +195,7 @@ __device__ __forceinline__ void store_rows(const GemmArgs& a, const Item& it, co
 // 3 sit in a register ring.  One barrier per stage.
 template <int RB>
 __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, int wave, int lane,
-                                           char* lds) {
+                                           const Slots& sl) {
     // buffer-to-LDS loads per wave and stage: 4 RB of 8 rows, dealt to the
     // four waves; then the weights of the stage's two groups (codes, scales)
     constexpr int kDma = RB;
@@ -237,18 +243,18 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
     const uint32_t scale_off = static_cast<uint32_t>((h * 32 + (lane & 31)) * 4);
     const uint32_t nib = a.nib_mask;
 
-    // One batch of loads: the activations of stage sa into LDS slot `slot`,
-    // then the weights of stage sw into ring entry r (in this order: the
-    // waits count on it).  Stages past the activations repeat the last one;
-    // weight groups past KSP repeat the last (never used).
-    auto issue = [&](int sa, uint32_t slot, int sw, WGroup (&r)[2]) {
+    // One batch of loads: the activations of stage sa into LDS slot `slot`
+    // and the weights of stage sw into ring entry r (the waits count whole
+    // batches, so their order inside a batch is free).  Stages past the
+    // activations repeat the last one; weight groups past KSP repeat the last
+    // (never used).
+    auto issue = [&](int sa, int slot, int sw, WGroup (&r)[2]) {
         const bool part = (KS & 1) && sa >= SA - 1;
         sa = sa < SA ? sa : SA - 1;
 #pragma unroll
         for (int i = 0; i < kDma; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(x, LDS_PTR(lds + slot + (wave + 4 * i) * 1024), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(x, LDS_PTR(sl.p[slot] + (wave + 4 * i) * 1024), 16,
                                                      part ? aoff[i] - dpart : aoff[i], sa * 128, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
         const int g0 = 2 * sw < KSP ? 2 * sw : KSP - 1;
         const int g1 = 2 * sw + 1 < KSP ? 2 * sw + 1 : KSP - 1;
         load_wgroup(r[0], w, code_off, scale_off, g0);
@@ -274,15 +280,17 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
 
     bf16x8 av[2][RB][2];
     bf16x8 b[2][2][2];
-    auto read_a = [&](uint32_t slot, int hh, bf16x8 (&dst)[RB][2]) {
+    auto read_a = [&](int slot, int hh, bf16x8 (&dst)[RB][2]) {
 #pragma unroll
         for (int t = 0; t < RB; ++t)
 #pragma unroll
             for (int st = 0; st < 2; ++st)
                 dst[t][st] = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4*>(lds + slot + t * 4096 + aread[hh][st]));
+                    bf16x8, *reinterpret_cast<const u32x4*>(sl.p[slot] + t * 4096 + aread[hh][st]));
     };
-    auto mfmas = [&](const bf16x8 (&av_)[RB][2], const bf16x8 (&b_)[2][2]) {
+    // nvm: buffer loads of a batch to spread over the MFMAs (one after every
+    // other MFMA), so that no burst of them holds up the wave's issue
+    auto mfmas = [&](const bf16x8 (&av_)[RB][2], const bf16x8 (&b_)[2][2], int nvm) {
         // K step outermost: the two MFMAs on one accumulator are 2 RB MFMAs
         // apart, so none waits for the result of the one before
 #pragma unroll
@@ -300,6 +308,7 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
         for (int i = 0; i < 4 * RB; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (i % 2 == 1 && i / 2 < nvm) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
         }
     };
@@ -313,13 +322,12 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < 3; ++s) {
-            issue(s, s * kSlot, s + 1, ring[s + 1]);
+            issue(s, s, s + 1, ring[s + 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // activations of stage 0 (the weights of stage 1 and two batches may stay
-    // in flight)
-    wait_vmcnt<4 + 2 * kStageOps>();
+    // activations of stage 0 (the two later batches may stay in flight)
+    wait_vmcnt<2 * kStageOps>();
     barrier_lds();
     read_a(0, 0, av[0]);
     dequant_group(ring[0][0], nib, b[0]);
@@ -327,31 +335,31 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
     // Four stages per trip (slot and ring indices static; KSP / 2 is even).
     // Even group 2 s: read the activations of group 2 s + 1 (same stage) and
     // dequantise its weights while the MFMAs of group 2 s run.  Odd group
-    // 2 s + 1: wait for this wave's activations of stage s + 1 (the weights
-    // of s + 2 and the batch of stage s - 1 may stay in flight), barrier (they
-    // all landed; every wave is done with the slot of stage s - 1), load the
-    // activations of stage s + 3 into that slot and the weights of stage s + 4
-    // into ring entry s % 4, then read the activations of group 2 s + 2.
+    // 2 s + 1: wait for this wave's batch of stage s - 2 (activations of s + 1;
+    // the batch of s - 1 may stay in flight), barrier (they all landed; every
+    // wave is done with the slot of stage s - 1), then, spread over the MFMAs
+    // of group 2 s + 1, load the activations of stage s + 3 into that slot and
+    // the weights of stage s + 4 into ring entry s % 4, and read the
+    // activations of group 2 s + 2.
     const int NST = KSP >> 1;
     for (int s0 = 0; s0 < NST; s0 += 4) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int s = s0 + u;
             __builtin_amdgcn_sched_barrier(0);
-            read_a(u * kSlot, 1, av[1]);
+            read_a(u, 1, av[1]);
             dequant_group(ring[u][1], nib, b[1]);
-            mfmas(av[0], b[0]);
+            mfmas(av[0], b[0], 0);
             __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt<4 + kStageOps>();
+            wait_vmcnt<kStageOps>();
             barrier_lds();
             __builtin_amdgcn_sched_barrier(0);
-            issue(s + 3, ((u + 3) & 3) * kSlot, s + 4, ring[u]);
-            // (the next batch's weights go to ring[u], whose last group was
+            // (the batch's weights go to ring[u], whose last group was
             // dequantised above)
-            __builtin_amdgcn_sched_barrier(0);
-            read_a(((u + 1) & 3) * kSlot, 0, av[0]);
+            issue(s + 3, (u + 3) & 3, s + 4, ring[u]);
+            read_a((u + 1) & 3, 0, av[0]);
             dequant_group(ring[(u + 1) & 3][0], nib, b[0]);
-            mfmas(av[1], b[1]);
+            mfmas(av[1], b[1], kStageOps);
         }
     }
     // drain the loads past the end before the slots are reused
@@ -364,7 +372,6 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
     // output column), then all threads store whole row segments.
     // acc[t][jj][i] holds row 32 t + 8 (i / 4) + 4 (lane / 32) + i % 4 of
     // column 32 (h + 2 jj) + lane % 32 of the chunk.
-    float* stg = reinterpret_cast<float*>(lds);
     const bool silu = a.out_kind == OUT_SILU;
     const int zc = (wave >> 1) * 64 + 32 * h + (lane & 31);          // SiLU output column
     const int c0 = (wave >> 1) * 128 + 32 * h + (lane & 31);         // plain output column
@@ -375,13 +382,14 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
         for (int t = 4 * p; t < RB && t < 4 * p + 4; ++t) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int r = 32 * (t - 4 * p) + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                const int r = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                float* stg = reinterpret_cast<float*>(sl.p[t - 4 * p]);
                 stg[r * 256 + s0] = acc[t][0][i];
                 stg[r * 256 + s1] = acc[t][1][i];
             }
         }
         barrier_ds();
-        store_rows(a, it, stg, 128 * p, it.nrows < 128 * p + 128 ? it.nrows : 128 * p + 128);
+        store_rows(a, it, sl, 128 * p, it.nrows < 128 * p + 128 ? it.nrows : 128 * p + 128);
         barrier_ds();    // the staging bytes are reused (next pass, next item's loads)
     }
 }
@@ -464,13 +472,18 @@ __device__ inline int pull_item(int* q, int xcd, int n_tiles, int CP, const int*
 }
 
 __global__ void __launch_bounds__(256) k_gemm_large(GemmArgs a) {
-    // one LDS object: the staging slots, then the work queue's tile order
-    // (a second __shared__ object makes the compiler wait for every LDS DMA
-    // load before each read of the slots)
-    __shared__ __attribute__((aligned(1024))) char lds[kSlots * kSlot + (2 * kMaxOrder + 4) * 4];
-    int* s_cost = reinterpret_cast<int*>(lds + kSlots * kSlot);
-    int* s_order = s_cost + kMaxOrder;
-    int& s_pick = s_order[kMaxOrder];
+    __shared__ __attribute__((aligned(1024))) char slot0[kSlot];
+    __shared__ __attribute__((aligned(1024))) char slot1[kSlot];
+    __shared__ __attribute__((aligned(1024))) char slot2[kSlot];
+    __shared__ __attribute__((aligned(1024))) char slot3[kSlot];
+    __shared__ int s_cost[kMaxOrder];
+    __shared__ int s_order[kMaxOrder];
+    __shared__ int s_pick;
+    Slots sl;
+    sl.p[0] = slot0;
+    sl.p[1] = slot1;
+    sl.p[2] = slot2;
+    sl.p[3] = slot3;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -520,14 +533,14 @@ __global__ void __launch_bounds__(256) k_gemm_large(GemmArgs a) {
         if (it.nrows <= 0) continue;
         it.pair = pair;
         switch ((it.nrows + 31) >> 5) {
-            case 1: large_item<1>(a, it, wave, lane, lds); break;
-            case 2: large_item<2>(a, it, wave, lane, lds); break;
-            case 3: large_item<3>(a, it, wave, lane, lds); break;
-            case 4: large_item<4>(a, it, wave, lane, lds); break;
-            case 5: large_item<5>(a, it, wave, lane, lds); break;
-            case 6: large_item<6>(a, it, wave, lane, lds); break;
-            case 7: large_item<7>(a, it, wave, lane, lds); break;
-            default: large_item<8>(a, it, wave, lane, lds); break;
+            case 1: large_item<1>(a, it, wave, lane, sl); break;
+            case 2: large_item<2>(a, it, wave, lane, sl); break;
+            case 3: large_item<3>(a, it, wave, lane, sl); break;
+            case 4: large_item<4>(a, it, wave, lane, sl); break;
+            case 5: large_item<5>(a, it, wave, lane, sl); break;
+            case 6: large_item<6>(a, it, wave, lane, sl); break;
+            case 7: large_item<7>(a, it, wave, lane, sl); break;
+            default: large_item<8>(a, it, wave, lane, sl); break;
         }
     }
     if (queued && threadIdx.x == 0) {
