@@ -221,9 +221,10 @@ def test_combine_and_silu_checks():
 def decode_packed_prefill(packed, desc):
     """PREFILL layout (32x32x16 MFMA operands): per expert and 128-column
     chunk, records of 8 groups = codes [8 groups][2 halves h][64 lanes][4
-    words v] then scales [8][2 h][32 columns][2] bf16.  Word (h, lane, v) holds
-    column 32*(h + 2*(v//2)) + lane%32, K offsets 16*(v%2) + 8*(lane//32) + o
-    in nibble o; scale (h, c32, jj) is column 32*(h + 2*jj) + c32."""
+    words v] then scales [2 h][32 columns][8 groups][2] bf16.  Word (h, lane,
+    v) holds column 32*(h + 2*(v//2)) + lane%32, K offsets 16*(v%2) +
+    8*(lane//32) + o in nibble o; scale (h, c32, group, jj) is column
+    32*(h + 2*jj) + c32."""
     E, N, K = desc.E, desc.N, desc.K
     NC, KS, KSP = N // 128, K // 32, desc.k_groups
     R = KSP // 8
@@ -235,7 +236,8 @@ def decode_packed_prefill(packed, desc):
     assert not w[:, :, K // 8:].any()                       # padding codes are zero
     codes = np.ascontiguousarray(w[:, :, : K // 8])
     sc = np.ascontiguousarray(rec[..., 4096:]).view(np.uint16)
-    sc = sc.reshape(E, NC, R, 8, 2, 32, 2).transpose(0, 1, 6, 4, 5, 2, 3).reshape(E, N, KSP)
+    # axes: e, chunk, record, h, c32, group, jj -> e, chunk, jj, h, c32 | record, group
+    sc = sc.reshape(E, NC, R, 2, 32, 8, 2).transpose(0, 1, 6, 3, 4, 2, 5).reshape(E, N, KSP)
     assert not sc[:, :, KS:].any()                          # padding scales are zero
     return codes.view(np.int32), sc[:, :, :KS]
 

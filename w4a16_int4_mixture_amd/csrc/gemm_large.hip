@@ -12,9 +12,10 @@
 // CDNA4 design.
 //   * Persistent: one workgroup of four wavefronts per CU walks work items
 //     (row tile, pair of 128-column chunks).  When there are more items than
-//     workgroups, each row tile stays on one XCD (workgroup w runs on XCD
-//     w % 8), so the activation rows of a tile are fetched into one L2 and
-//     reused there by all its column pairs.
+//     workgroups, items come from per-XCD counters, largest tile first, each
+//     row tile dealt to one XCD (workgroup w runs on XCD w % 8), so that the
+//     activation rows of a tile are fetched into one L2 and reused there by
+//     all its column pairs.
 //   * v_mfma_f32_32x32x16_bf16.  Wavefront w works on chunk 2 * pair + w / 2
 //     and, inside it, on the 32-column blocks h and h + 2 (h = w % 2), for
 //     every row of the tile: with the gate/up interleave those are a gate
@@ -22,14 +23,16 @@
 //     8 row blocks x 2 column blocks x 16 fp32 accumulators per lane (256) in
 //     the accumulation registers.
 //   * Activations go from HBM/L2 straight into LDS (buffer loads with the LDS
-//     bit: no staging registers), one 16 KB slot per K group (256 rows x 32 K,
-//     in MFMA A-operand order), kLead groups ahead in a ring of kLead + 1
-//     slots; one barrier per group.
+//     bit: no staging registers), whole 128-byte lines of eight rows per
+//     load, one 32 KB slot per stage of two K groups (256 rows x 64 K, rows
+//     contiguous, 16-byte chunks XOR-swizzled against LDS bank conflicts),
+//     four slots (stages s .. s + 3); one barrier per stage.
 //   * Weights: per group each lane loads 16 bytes of codes (its two blocks,
-//     two K steps) and 4 bytes of scales into a register ring kLead groups
-//     ahead, and dequantises the next group while the MFMAs of the current
-//     group run: a code byte becomes fp32 (v_cvt_f32_ubyte), then (q - 8) * s
-//     in one exact FMA, then bf16 (one rounding).
+//     two K steps) into a register ring four stages ahead, and per record
+//     (8 groups) 32 bytes of scales; it dequantises the next group while the
+//     MFMAs of the current group run: a code byte becomes fp32
+//     (v_cvt_f32_ubyte), then (q - 8) * s in one exact FMA, then bf16 (one
+//     rounding).
 //   * The row count of a tile picks one of eight code paths (32-row blocks);
 //     all waves of a workgroup take the same path.
 
@@ -51,11 +54,10 @@ constexpr uint32_t kSlot = 32 * 1024;  // LDS bytes of one stage: 256 rows x 64 
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-// The weights of one K group for one lane: codes of (block h, step 0),
-// (h, 1), (h + 2, 0), (h + 2, 1) and the bf16 scales of blocks h, h + 2.
+// The codes of one K group for one lane: (block h, step 0), (h, 1),
+// (h + 2, 0), (h + 2, 1).
 struct WGroup {
     u32x4 w;
-    uint32_t s;
 };
 
 __device__ inline uint32_t pk_bf16(float a, float b) {
@@ -83,9 +85,9 @@ __device__ inline bf16x8 dequant_word(uint32_t w, uint32_t nib, float s, float c
     return __builtin_bit_cast(bf16x8, d);
 }
 
-// b[jj][step]
-__device__ inline void dequant_group(const WGroup& g, uint32_t nib, bf16x8 (&b)[2][2]) {
-    const float s0 = __uint_as_float(g.s << 16), s1 = __uint_as_float(g.s & 0xFFFF0000u);
+// b[jj][step]; sw: the group's bf16 scales of blocks h (low half), h + 2
+__device__ inline void dequant_group(const WGroup& g, uint32_t sw, uint32_t nib, bf16x8 (&b)[2][2]) {
+    const float s0 = __uint_as_float(sw << 16), s1 = __uint_as_float(sw & 0xFFFF0000u);
     const float c0 = -8.0f * s0, c1 = -8.0f * s1;
     b[0][0] = dequant_word(g.w.x, nib, s0, c0);
     b[0][1] = dequant_word(g.w.y, nib, s0, c0);
@@ -93,16 +95,29 @@ __device__ inline void dequant_group(const WGroup& g, uint32_t nib, bf16x8 (&b)[
     b[1][1] = dequant_word(g.w.w, nib, s1, c1);
 }
 
-// Loads group ks of the chunk for this lane (code_off, scale_off: the lane's
-// byte offsets inside a record's group).
-__device__ inline void load_wgroup(WGroup& g, __amdgpu_buffer_rsrc_t w, uint32_t code_off,
-                                   uint32_t scale_off, int ks) {
-    const int rec = (ks >> 3) * kRecWords * 4;
-    const int soff = rec + (ks & 7) * 512 * 4;
-    const int ssoff = rec + 4096 * 4 + (ks & 7) * 128 * 2;
+// Loads the codes of group ks of the chunk for this lane (code_off: the
+// lane's byte offset inside a record's group).
+__device__ inline void load_wgroup(WGroup& g, __amdgpu_buffer_rsrc_t w, uint32_t code_off, int ks) {
+    const int soff = (ks >> 3) * kRecWords * 4 + (ks & 7) * 512 * 4;
     g.w = __builtin_bit_cast(u32x4,
                              __builtin_amdgcn_raw_buffer_load_b128(w, code_off, soff, kNonTemporal));
-    g.s = __builtin_amdgcn_raw_buffer_load_b32(w, scale_off, ssoff, kNonTemporal);
+}
+
+// Loads this lane's scales of record rec (its 8 groups, one 32-bit word per
+// group; scale_off: the lane's byte offset inside a record's scale block).
+__device__ inline void load_rscales(u32x4 (&sc)[2], __amdgpu_buffer_rsrc_t w, uint32_t scale_off,
+                                    int rec) {
+    const int soff = rec * kRecWords * 4 + 4096 * 4;
+    sc[0] = __builtin_bit_cast(u32x4,
+                               __builtin_amdgcn_raw_buffer_load_b128(w, scale_off, soff, kNonTemporal));
+    sc[1] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(w, scale_off + 16, soff, kNonTemporal));
+}
+
+// Scale word of group gi (0..7) of a record's scales.
+__device__ inline uint32_t rscale(const u32x4 (&sc)[2], int gi) {
+    const u32x4& v = sc[gi >> 2];
+    return (gi & 3) == 0 ? v.x : (gi & 3) == 1 ? v.y : (gi & 3) == 2 ? v.z : v.w;
 }
 
 // s_waitcnt with only a vector-memory count (expcnt and lgkmcnt left free).
@@ -196,10 +211,10 @@ __device__ __forceinline__ void store_rows(const GemmArgs& a, const Item& it, co
 template <int RB>
 __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, int wave, int lane,
                                            const Slots& sl) {
-    // buffer-to-LDS loads per wave and stage: 4 RB of 8 rows, dealt to the
-    // four waves; then the weights of the stage's two groups (codes, scales)
+    // loads per wave and stage: 4 RB buffer-to-LDS loads of 8 rows, dealt
+    // to the four waves, and the codes of the stage's two groups
     constexpr int kDma = RB;
-    constexpr int kStageOps = kDma + 4;
+    constexpr int kStageOps = kDma + 2;
 
     const int chunk = it.pair * 2 + (wave >> 1);
     const int h = wave & 1;
@@ -240,11 +255,12 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
     const __amdgpu_buffer_rsrc_t w =
         make_rsrc(a.packed + cbase * a.chunk_words, static_cast<uint64_t>(a.chunk_words) * 4);
     const uint32_t code_off = static_cast<uint32_t>((h * 64 + lane) * 16);
-    const uint32_t scale_off = static_cast<uint32_t>((h * 32 + (lane & 31)) * 4);
+    const uint32_t scale_off = static_cast<uint32_t>((h * 32 + (lane & 31)) * 32);
     const uint32_t nib = a.nib_mask;
+    const int NREC = KSP >> 3;
 
     // One batch of loads: the activations of stage sa into LDS slot `slot`
-    // and the weights of stage sw into ring entry r (the waits count whole
+    // and the codes of stage sw into ring entry r (the waits count whole
     // batches, so their order inside a batch is free).  Stages past the
     // activations repeat the last one; weight groups past KSP repeat the last
     // (never used).
@@ -257,8 +273,8 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
                                                      part ? aoff[i] - dpart : aoff[i], sa * 128, 0, 0);
         const int g0 = 2 * sw < KSP ? 2 * sw : KSP - 1;
         const int g1 = 2 * sw + 1 < KSP ? 2 * sw + 1 : KSP - 1;
-        load_wgroup(r[0], w, code_off, scale_off, g0);
-        load_wgroup(r[1], w, code_off, scale_off, g1);
+        load_wgroup(r[0], w, code_off, g0);
+        load_wgroup(r[1], w, code_off, g1);
     };
 
     f32x16 acc[RB][2];
@@ -313,12 +329,16 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
         }
     };
 
-    // Prologue: weights of stage 0, then (activations of s, weights of s + 1)
-    // for s = 0, 1, 2: the same order as the loop's batches.
+    // Prologue: codes of stage 0 and the scales of record 0, then
+    // (activations of s, codes of s + 1) for s = 0, 1, 2: the same order as
+    // the loop's batches.  Scales: one record (four stages) per pair of loads,
+    // the next record's loaded with the first batch of a trip.
     WGroup ring[4][2];
+    u32x4 sc_cur[2], sc_nxt[2];
     {
-        load_wgroup(ring[0][0], w, code_off, scale_off, 0);
-        load_wgroup(ring[0][1], w, code_off, scale_off, 1);
+        load_wgroup(ring[0][0], w, code_off, 0);
+        load_wgroup(ring[0][1], w, code_off, 1);
+        load_rscales(sc_cur, w, scale_off, 0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < 3; ++s) {
@@ -330,7 +350,7 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
     wait_vmcnt<2 * kStageOps>();
     barrier_lds();
     read_a(0, 0, av[0]);
-    dequant_group(ring[0][0], nib, b[0]);
+    dequant_group(ring[0][0], rscale(sc_cur, 0), nib, b[0]);
 
     // Four stages per trip (slot and ring indices static; KSP / 2 is even).
     // Even group 2 s: read the activations of group 2 s + 1 (same stage) and
@@ -348,19 +368,31 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
             const int s = s0 + u;
             __builtin_amdgcn_sched_barrier(0);
             read_a(u, 1, av[1]);
-            dequant_group(ring[u][1], nib, b[1]);
+            dequant_group(ring[u][1], rscale(sc_cur, 2 * u + 1), nib, b[1]);
             mfmas(av[0], b[0], 0);
             __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt<kStageOps>();
+            // the batch of stage s - 1 may stay in flight; the first batch of
+            // a trip also holds the next record's scales
+            if (u == 1)
+                wait_vmcnt<kStageOps + 2>();
+            else
+                wait_vmcnt<kStageOps>();
             barrier_lds();
             __builtin_amdgcn_sched_barrier(0);
-            // (the batch's weights go to ring[u], whose last group was
+            // (the batch's codes go to ring[u], whose last group was
             // dequantised above)
             issue(s + 3, (u + 3) & 3, s + 4, ring[u]);
+            if (u == 0) {
+                const int rn = (s0 >> 2) + 1;
+                load_rscales(sc_nxt, w, scale_off, rn < NREC ? rn : NREC - 1);
+            }
             read_a((u + 1) & 3, 0, av[0]);
-            dequant_group(ring[(u + 1) & 3][0], nib, b[0]);
-            mfmas(av[1], b[1], kStageOps);
+            dequant_group(ring[(u + 1) & 3][0], u < 3 ? rscale(sc_cur, 2 * u + 2) : rscale(sc_nxt, 0),
+                          nib, b[0]);
+            mfmas(av[1], b[1], u == 0 ? kStageOps + 2 : kStageOps);
         }
+        sc_cur[0] = sc_nxt[0];
+        sc_cur[1] = sc_nxt[1];
     }
     // drain the loads past the end before the slots are reused
     wait_vmcnt<0>();

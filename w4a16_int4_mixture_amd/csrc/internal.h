@@ -48,8 +48,9 @@ w4a16_status check_launch(const char* what);
 //           = the eight codes of column c*CW + 32*(h + 2*(v/2)) + lane%32 for
 //             K = ks*32 + 16*(v%2) + 8*(lane/32) + o, o = 0..7, in the
 //             canonical nibble order (nibble o = offset o)
-//   scales: bf16 (g8, h, c32, jj) at 4096 words + ((g8 * 2 + h) * 32 + c32) * 2 + jj
-//           = the scale of column c*CW + 32*(h + 2*jj) + c32, group ks
+//   scales: bf16 (h, c32, g8, jj) at 4096 words + ((h * 32 + c32) * 8 + g8) * 2 + jj
+//           = the scale of column c*CW + 32*(h + 2*jj) + c32, group ks (a
+//           lane's scales of the record's 8 groups are 32 contiguous bytes)
 // Padding groups (ks >= K/32) hold zero codes and zero scales.
 // WPL = CW / 16 words (and scales) per lane per group.
 struct PackGeom {

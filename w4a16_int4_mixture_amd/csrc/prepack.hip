@@ -112,8 +112,8 @@ __host__ __device__ static inline uint32_t prefill_word(const uint32_t* codes,
     uint32_t out = 0;
     for (int hh = 0; hh < 2; ++hh) {
         const int b = 2 * (in - 4096) + hh;   // bf16 index inside the scale block
-        const int jj = b & 1, c32 = (b >> 1) & 31, h = (b >> 6) & 1;
-        const int ks = stage * 8 + (b >> 7);
+        const int jj = b & 1, c32 = (b >> 4) & 31, h = (b >> 9) & 1;
+        const int ks = stage * 8 + ((b >> 1) & 7);
         uint32_t v = 0;
         if (ks < g.KS) {
             const int n = canonical_column(c * 128 + 32 * (h + 2 * jj) + c32, g.N, 128, g.interleave);
