@@ -155,34 +155,43 @@ struct Slots {
 // Stores rows [r0, r1) of a work item from the fp32 staging tile in LDS
 // ([128 rows][256 columns]; rows 32 k .. 32 k + 31 of the pass in slot k):
 // 32 lanes per row, 8 staged values each; bf16 or fp32 rows, or SiLU(gate) *
-// up of the interleaved gate/up pairs (4 outputs per lane).
-__device__ __forceinline__ void store_rows(const GemmArgs& a, const Item& it, const Slots& sl,
-                                        int r0, int r1) {
-    const bool silu = a.out_kind == OUT_SILU;
-    const bool slot_rows = a.tile_src != TILE_MASKED;
-    const bool row_map = slot_rows && (a.tile_src == TILE_BLOCKS || a.orow == W4A16_OROW_SLOT);
+// up of the interleaved gate/up pairs (4 outputs per lane).  KIND and ROWMAP
+// (output row from sorted_ids) are template parameters so that each variant
+// is a straight loop: with the variants merged, the compiler could no longer
+// tell which registers came from memory and waited for every store in flight
+// before each new one.
+template <int KIND, bool ROWMAP>
+__device__ __forceinline__ void store_rows_k(const GemmArgs& a, const Item& it, const Slots& sl,
+                                          int r0, int r1) {
+    constexpr bool silu = KIND == OUT_SILU;
     const int nout = silu ? a.N / 2 : a.N;             // output row length
     const int width = silu ? 128 : 256;                // output columns of the tile
     const int col0 = it.pair * width;
     const int cvalid = nout - col0 < width ? nout - col0 : width;
     const int q = threadIdx.x & 31;                    // 8 staged values: 8 columns or 4 pairs
     const int cc = silu ? 4 * q : 8 * q;               // first output column of this lane
-    for (int r = r0 + (threadIdx.x >> 5); r < r1; r += 8) {
+    if (cc >= cvalid) return;
+    // slot k (a compile-time index: the reads stay LDS reads) holds rows
+    // r0 + 32 k .. r0 + 32 k + 31
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+    for (int rr = (threadIdx.x >> 5); rr < 32; rr += 8) {
+        const int r = r0 + 32 * k + rr;
+        if (r >= r1) break;
         int64_t orow = it.p0 + r;
-        if (row_map) {
+        if (ROWMAP) {
             const int f = a.sorted_ids[it.p0 + r];
             if (f < 0 || f >= a.num_slots) continue;
             if (a.orow == W4A16_OROW_SLOT) orow = f;
         }
-        if (cc >= cvalid) continue;
-        const f32x4* src = reinterpret_cast<const f32x4*>(sl.p[(r - r0) >> 5]) + ((r - r0) & 31) * 64 + 2 * q;
+        const f32x4* src = reinterpret_cast<const f32x4*>(sl.p[k]) + rr * 64 + 2 * q;
         const f32x4 v0 = src[0], v1 = src[1];
-        if (silu) {
+        if (KIND == OUT_SILU) {
             u32x2 o;
             o.x = pk_bf16(silu_mul_bf16(v0.x, v0.y), silu_mul_bf16(v0.z, v0.w));
             o.y = pk_bf16(silu_mul_bf16(v1.x, v1.y), silu_mul_bf16(v1.z, v1.w));
             *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + orow * nout + col0 + cc) = o;
-        } else if (a.out_kind == OUT_BF16) {
+        } else if (KIND == OUT_BF16) {
             u32x4 o;
             o.x = pk_bf16(v0.x, v0.y);
             o.y = pk_bf16(v0.z, v0.w);
@@ -194,6 +203,21 @@ __device__ __forceinline__ void store_rows(const GemmArgs& a, const Item& it, co
             o[0] = v0;
             o[1] = v1;
         }
+    }
+}
+
+__device__ __forceinline__ void store_rows(const GemmArgs& a, const Item& it, const Slots& sl,
+                                        int r0, int r1) {
+    const bool row_map = a.tile_src != TILE_MASKED &&
+                         (a.tile_src == TILE_BLOCKS || a.orow == W4A16_OROW_SLOT);
+    if (row_map) {
+        if (a.out_kind == OUT_SILU) store_rows_k<OUT_SILU, true>(a, it, sl, r0, r1);
+        else if (a.out_kind == OUT_BF16) store_rows_k<OUT_BF16, true>(a, it, sl, r0, r1);
+        else store_rows_k<OUT_F32, true>(a, it, sl, r0, r1);
+    } else {
+        if (a.out_kind == OUT_SILU) store_rows_k<OUT_SILU, false>(a, it, sl, r0, r1);
+        else if (a.out_kind == OUT_BF16) store_rows_k<OUT_BF16, false>(a, it, sl, r0, r1);
+        else store_rows_k<OUT_F32, false>(a, it, sl, r0, r1);
     }
 }
 
