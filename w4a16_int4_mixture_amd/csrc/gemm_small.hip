@@ -264,7 +264,10 @@ struct Lds {
 // The K loop of one workgroup tile with MT active 16-row blocks (MTMAX sizes
 // the LDS layout).
 //
-// Codes: a ring of D = 16 groups in registers, refilled as consumed.
+// Codes: a ring of D groups in registers, refilled as consumed: one stage (D
+// = 8) in the one-block variant, so that three of its workgroups fit on a CU
+// (the HBM stream needs about eight wavefronts per CU in flight, and a
+// decode-sized grid then runs in one round); two stages (D = 16) otherwise.
 // Activation fragments and scales: LDS double buffer, one barrier per stage;
 // each stage's global loads are issued two stages ahead into one of two
 // register sets.  Issue order matters because vector-memory completions are
@@ -274,12 +277,16 @@ struct Lds {
 //
 // Iterations cover two stages (16 groups); the K range is padded at its start
 // by one virtual record (zero scales) when it holds an odd number of records.
+// Ring slot r0 + g of a stage holds its group g: r0 = 0 for the even stage,
+// and for the odd one kSG (D = 16) or 0 (D = 8).
 template <int MT, int WPL, int MTMAX>
 __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1, int ks_real,
                                             int wave, int lane, u32x4* lds,
                                             f32x4 (&acc)[MT][WPL], uint32_t mask,
                                             uint32_t bits) {
-    constexpr int D = 2 * kSG;
+    constexpr int D = MTMAX == 1 ? kSG : 2 * kSG;
+    constexpr int IT = 2 * kSG;          // groups per iteration
+    constexpr int RO = D == IT ? kSG : 0;  // ring slot of the odd stage's first group
     using L = Lds<MTMAX, WPL>;
     if (ks1 <= ks0) return;
     const u32x4* abuf0 = lds;
@@ -294,9 +301,9 @@ __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1
 
     // ks0 and ks1 are multiples of 8: the ring starts pad (0 or 8) groups early
     // on a virtual record that adds zero
-    const int pad = (D - (ks1 - ks0) % D) % D;
+    const int pad = (IT - (ks1 - ks0) % IT) % IT;
     const int kb = ks0 - pad;
-    const int nit = (ks1 - kb) / D;             // iterations of two stages
+    const int nit = (ks1 - kb) / IT;            // iterations of two stages
 
     Codes<WPL> ring[D];
     Stage<MT, WPL> r0, r1;
@@ -310,25 +317,28 @@ __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1
     __syncthreads();
 
     for (int it = 0; it < nit - 1; ++it) {
-        const int base = kb + it * D;
-        // even stage: buffer 0, refill ring slots 0..7 with the stage after next
-        load_stage<MT, WPL>(r0, src, base + D, ks0, ks_real, wave, lane);
+        const int base = kb + it * IT;
+        // even stage: buffer 0; its ring slots take groups D ahead
+        load_stage<MT, WPL>(r0, src, base + IT, ks0, ks_real, wave, lane);
         __builtin_amdgcn_sched_barrier(0);
         stage_groups<MT, WPL, D>(ring, 0, abuf0, srd0, src, base + D, true, acc, mask, bits, lane);
         store_stage<MT, WPL>(r1, wbuf1, sbuf1, wave, lane);
         __syncthreads();
-        // odd stage: buffer 1, refill ring slots 8..15
-        load_stage<MT, WPL>(r1, src, base + D + kSG, ks0, ks_real, wave, lane);
+        // odd stage: buffer 1
+        load_stage<MT, WPL>(r1, src, base + IT + kSG, ks0, ks_real, wave, lane);
         __builtin_amdgcn_sched_barrier(0);
-        stage_groups<MT, WPL, D>(ring, kSG, abuf1, srd1, src, base + D + kSG, true, acc, mask, bits,
+        stage_groups<MT, WPL, D>(ring, RO, abuf1, srd1, src, base + D + kSG, true, acc, mask, bits,
                                  lane);
         store_stage<MT, WPL>(r0, wbuf0, sbuf0, wave, lane);
         __syncthreads();
     }
-    stage_groups<MT, WPL, D>(ring, 0, abuf0, srd0, src, 0, false, acc, mask, bits, lane);
+    // last iteration: with a one-stage ring the even stage still refills it
+    // with the odd stage's groups
+    const int last = kb + (nit - 1) * IT;
+    stage_groups<MT, WPL, D>(ring, 0, abuf0, srd0, src, last + kSG, D < IT, acc, mask, bits, lane);
     store_stage<MT, WPL>(r1, wbuf1, sbuf1, wave, lane);
     __syncthreads();
-    stage_groups<MT, WPL, D>(ring, kSG, abuf1, srd1, src, 0, false, acc, mask, bits, lane);
+    stage_groups<MT, WPL, D>(ring, RO, abuf1, srd1, src, 0, false, acc, mask, bits, lane);
 }
 
 // Split-K fix-up.  Every split writes its fp32 partial of the tile part, then
