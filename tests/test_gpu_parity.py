@@ -428,6 +428,45 @@ def test_stages_and_path_random(m, seed, E, H, I, T, k, Eg, tile_m, split, profi
                 exact_frac=0.99)
 
 
+def _bf16_order(bits):
+    """bf16 bit patterns as integers in numeric order (+0 and -0 both 0)."""
+    b = bits.astype(np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+@pytest.mark.parametrize("up", [0x3F80, 0xC060])  # up = 1.0 and up = -3.5
+def test_silu_mul_every_bf16_gate(m, up):
+    """SiLU(g) * u on every finite bf16 gate value g: each result within one bf16
+    ulp of the fp64 oracle (or 1e-37 apart, where results are subnormal), at
+    least 99% bit-identical."""
+    from w4a16_int4_mixture_amd import _capi
+    I = 256
+    g = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    g = np.where((g & 0x7F80) != 0x7F80, g, 0).astype(np.uint16).reshape(256, I)
+    Y13 = np.empty((256, 2 * I), np.uint16)
+    Y13[:, :I] = g
+    Y13[:, I:] = up
+    print(f"silu every gate: up=0x{up:04x}", flush=True)
+    Z = torch.zeros((256, I), dtype=torch.int16, device="cuda")
+    rows = torch.tensor([256], dtype=torch.int32, device="cuda")
+    Yd = dev(Y13)
+    _capi.w4a16_moe_silu_mul(Yd, 256, rows, I, Z)
+    torch.cuda.synchronize()
+    got = host(Z, np.uint16)
+    ref = oracle.silu_mul(Y13)
+    ulps = np.abs(_bf16_order(got) - _bf16_order(ref))
+    near = np.abs(bf(got) - bf(ref)) <= 1e-37
+    same = np.mean(got == ref)
+    print(f"  max ulps {ulps.max()}, outside one ulp and 1e-37 {np.sum((ulps > 1) & ~near)},"
+          f" bit-identical {same:.4f}", flush=True)
+    bad = np.nonzero(((ulps > 1) & ~near).ravel())[0]
+    for i in bad[:8]:
+        print(f"  gate 0x{g.ravel()[i]:04x} ({bf(g.ravel()[i:i + 1])[0]:.6g}): gpu 0x{got.ravel()[i]:04x}"
+              f" oracle 0x{ref.ravel()[i]:04x}", flush=True)
+    assert bad.size == 0
+    assert same >= 0.99
+
+
 @pytest.mark.parametrize("split", [1, 2, 3])
 @pytest.mark.parametrize("profile", [1, 2])
 def test_fused_silu_epilogue_and_splitk_fixup(m, split, profile):

@@ -23,13 +23,19 @@ __device__ inline float bf16_round(float x) {
 }
 
 // silu(g) * u with g and u first rounded to bf16 (the rounding of a gate/up
-// output that is stored and then activated); the logistic factor with the
-// hardware exp2 and reciprocal (about 1 ulp of fp32 each, far below the bf16
-// rounding of the result)
+// output that is stored and then activated).  silu(g) = g / (1 + e^-g) is
+// evaluated as g / (1 + t) for g >= 0 and g t / (1 + t) for g < 0, with t =
+// e^-|g|, so nothing overflows (e^-g would below g = -88.7, where g e^g is
+// still a normal bf16).  The hardware exp2 flushes subnormal results, so t is
+// formed as 2^64 t (normal down to g = -131) and the 2^-64 is applied after
+// the correctly rounded division, by an exact power-of-two multiply.
 __device__ inline float silu_mul_bf16(float g, float u) {
     g = bf16_round(g);
     u = bf16_round(u);
-    return g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+    const float ts = __builtin_amdgcn_exp2f(64.0f - __builtin_fabsf(g) * 1.44269504088896341f);
+    const float den = 1.0f + ts * 0x1p-64f;
+    const float s = g >= 0.0f ? g / den : g * ts / den * 0x1p-64f;
+    return s * u;
 }
 
 // Buffer loads address the packed weights and the activations with a scalar

@@ -7,6 +7,7 @@
 // plain SiLU(gate) * up of the MoE FFN and the top-k weighted sum of the
 // expert outputs.
 
+#include "device_common.h"
 #include "internal.h"
 
 namespace w4a16 {
@@ -24,12 +25,9 @@ __device__ inline uint32_t bf16_bits(float x) {
 }
 __device__ inline uint32_t pack2(float a, float b) { return bf16_bits(a) | (bf16_bits(b) << 16); }
 
-// silu(g) * u in fp32 from bf16-valued inputs, evaluated as the GEMM
-// epilogues do (g * u times the hardware reciprocal of 1 + exp(-g)), so the
-// fused and the separate activation agree bit for bit
-__device__ inline float silu_mul(float g, float u) {
-    return g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-}
+// silu(g) * u in fp32 from bf16-valued inputs: the GEMM epilogues' own
+// function, so the fused and the separate activation agree bit for bit
+__device__ inline float silu_mul(float g, float u) { return dev::silu_mul_bf16(g, u); }
 
 }  // namespace
 
