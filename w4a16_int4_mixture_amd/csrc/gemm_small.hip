@@ -299,6 +299,22 @@ __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1
     const uint16_t* srd0 = reinterpret_cast<const uint16_t*>(sbuf0) + (lane & 15) * WPL;
     const uint16_t* srd1 = reinterpret_cast<const uint16_t*>(sbuf1) + (lane & 15) * WPL;
 
+    // a K range of one stage (K = 256, or a split of one record) runs alone,
+    // without the virtual stage that pads other odd stage counts
+    if (ks1 - ks0 == kSG) {
+        Codes<WPL> one[kSG];
+        Stage<MT, WPL> r;
+        load_stage<MT, WPL>(r, src, ks0, ks0, ks_real, wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kSG; ++i) load_codes<WPL>(one[i], src.w, src.code_off, ks0 + i);
+        __builtin_amdgcn_sched_barrier(0);
+        store_stage<MT, WPL>(r, wbuf0, sbuf0, wave, lane);
+        __syncthreads();
+        stage_groups<MT, WPL, kSG>(one, 0, abuf0, srd0, src, 0, false, acc, mask, bits, lane);
+        return;
+    }
+
     // ks0 and ks1 are multiples of 8: the ring starts pad (0 or 8) groups early
     // on a virtual record that adds zero
     const int pad = (IT - (ks1 - ks0) % IT) % IT;
