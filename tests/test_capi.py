@@ -310,10 +310,11 @@ def test_plan_rules():
     assert p_small.tile_m == 16
     assert p_small.split_k >= p.split_k                                   # fewer tiles -> more splits
     assert capi.w4a16_plan_gemm(d13, capi.W4A16_LAYOUT_INDEXED, 0, tile_m=48).tile_m == 48
-    # masked: ~1.3 x expected_m for deep-K gate/up, ~1.25 x for short-K down
-    assert capi.w4a16_plan_gemm(d13, capi.W4A16_LAYOUT_MASKED, 0, 32).tile_m == 48
-    assert capi.w4a16_plan_gemm(d2, capi.W4A16_LAYOUT_MASKED, 0, 32).tile_m == 48
-    assert capi.w4a16_plan_gemm(d2, capi.W4A16_LAYOUT_MASKED, 0, 16).tile_m == 32
+    # masked: tiles of expected_m rows, in 16-row steps
+    assert capi.w4a16_plan_gemm(d13, capi.W4A16_LAYOUT_MASKED, 0, 32).tile_m == 32
+    assert capi.w4a16_plan_gemm(d2, capi.W4A16_LAYOUT_MASKED, 0, 32).tile_m == 32
+    assert capi.w4a16_plan_gemm(d2, capi.W4A16_LAYOUT_MASKED, 0, 20).tile_m == 32
+    assert capi.w4a16_plan_gemm(d2, capi.W4A16_LAYOUT_MASKED, 0, 16).tile_m == 16
     assert status_of(capi.w4a16_plan_gemm, d13, capi.W4A16_LAYOUT_MASKED, 0, 0) == \
         capi.W4A16_ERR_INVALID_ARG
     for pl in (p, p_small):

@@ -58,8 +58,10 @@ __device__ int32_t g_routing_errors;
 // the tile is sized to hold an expert's rows in one pass (about twice the mean
 // so that Poisson-like tails rarely spill into a second pass, which would
 // stream the expert's weights again), in 16-row MFMA steps.  The masked rule
-// sizes tiles from expected_m: ~1.3x for deep-K gate/up (a spill re-reads the
-// whole K), ~1.25x for short-K down.  K splits are added until the grid holds
+// sizes tiles to expected_m itself: a tile of up to 32 rows keeps two
+// streaming workgroups per CU (three at 16), which is worth more than the
+// extra weight pass of an expert above expected_m (on the Zipf EP32 share,
+// 1.0x tiles beat 1.3x / 1.25x ones by a quarter on both GEMMs).  K splits are added until the grid holds
 // enough wavefronts to keep every CU streaming (shape-aware split-K gating),
 // but never below 8 groups of K per split.
 
@@ -96,8 +98,7 @@ static w4a16_status plan_impl(const w4a16_desc* d, int layout, int rows_hint, in
             set_error("expected_m must be a positive integer (got %d)", expected_m);
             return W4A16_ERR_INVALID_ARG;
         }
-        const bool deep_k = d->K >= 4096;
-        const int64_t want = deep_k ? ceil_div(13LL * expected_m, 10) : ceil_div(5LL * expected_m, 4);
+        const int64_t want = expected_m;
         const int step = d->profile == W4A16_PROFILE_PREFILL ? 32 : 16;
         tile_m = static_cast<int>(
             std::min<int64_t>(std::max<int64_t>(round_up(want, step), step), max_tile(d)));
