@@ -28,14 +28,21 @@ __device__ inline float bf16_round(float x) {
 // e^-|g|, so nothing overflows (e^-g would below g = -88.7, where g e^g is
 // still a normal bf16).  The hardware exp2 flushes subnormal results, so t is
 // formed as 2^64 t (normal down to g = -131) and the 2^-64 is applied after
-// the correctly rounded division, by an exact power-of-two multiply.
+// the division, by an exact power-of-two multiply.  The divisor lies in
+// [1, 2]: the quotient is the hardware reciprocal's product refined by one
+// Newton step (within an ulp of fp32, far below the bf16 rounding after),
+// with the dividend's sign.
 __device__ inline float silu_mul_bf16(float g, float u) {
     g = bf16_round(g);
     u = bf16_round(u);
     const float ts = __builtin_amdgcn_exp2f(64.0f - __builtin_fabsf(g) * 1.44269504088896341f);
     const float den = 1.0f + ts * 0x1p-64f;
-    const float s = g >= 0.0f ? g / den : g * ts / den * 0x1p-64f;
-    return s * u;
+    const float num = g >= 0.0f ? g : g * ts;
+    const float r = __builtin_amdgcn_rcpf(den);
+    float q = num * r;
+    q = __builtin_fmaf(__builtin_fmaf(-den, q, num), r, q);
+    q = __builtin_copysignf(q, num);   // the refinement would turn -0 into +0
+    return (g >= 0.0f ? q : q * 0x1p-64f) * u;
 }
 
 // Buffer loads address the packed weights and the activations with a scalar
