@@ -198,23 +198,34 @@ __device__ inline void stage_groups(Codes<WPL> (&ring)[D], int r0, const u32x4* 
     }
 }
 
-// One LDS stage held in registers between its loads and its store.
-//   a: the activation fragments this wavefront loads (groups g = 4i + wave)
-//   s: this wavefront's scales for the stage (WPL/4 x 16 bytes per lane)
-template <int MT, int WPL>
-struct Stage {
-    u32x4 a[kSG / 4][MT];
-    u32x4 s[WPL / 4];
-};
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-// Stage starting at group `base` (a multiple of 8).  A record before ks_min
-// (a virtual one ahead of the K range) reads record ks_min / 8 with zeroed
-// scales (only the first stage of a K range can be virtual, so only that load
-// site carries the check); activation columns past K (padding groups, whose
-// scales are zero) are clamped to the last real group.
-template <int MT, int WPL, bool MAYBE_VIRTUAL = false>
-__device__ inline void load_stage(Stage<MT, WPL>& st, const Src<MT>& src, int base, int ks_min,
-                                  int ks_real, int wave, int lane) {
+// s_waitcnt with only a vector-memory count (expcnt and lgkmcnt left free).
+template <int N>
+__device__ inline void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt field holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier after this wavefront's LDS accesses have completed.  No
+// fence: the staging buffers are written by buffer-to-LDS loads, whose
+// completion each wavefront has waited for (vmcnt) before the barrier, and a
+// fence would also wait for every code load in flight.
+__device__ inline void barrier_ds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// The stage starting at group `base` (a multiple of 8) goes straight into LDS
+// buffer `buf` (activations, then the four wavefronts' scales) with buffer
+// loads carrying the LDS bit; lane l of each load writes 16 bytes at l * 16.
+// This wavefront loads the activation fragments of groups 4 i + wave and its
+// own scales: kSG / 4 * MT + WPL / 4 loads.  A virtual stage (base < ks_min,
+// ahead of the K range; only the first stage of a range can be one) reads the
+// activations of group ks_min and writes zero scales instead of loading them
+// (one LDS store per 16 bytes); activation columns past K (padding groups,
+// whose scales are zero) are clamped to the last real group.
+template <int MT, int WPL, int MTMAX, bool MAYBE_VIRTUAL = false>
+__device__ inline void dma_stage(const Src<MT>& src, u32x4* buf, int base, int ks_min, int ks_real,
+                                 int wave, int lane) {
+    constexpr int kAStage = kSG * MTMAX * 64;   // u32x4 of activations per buffer
 #pragma unroll
     for (int i = 0; i < kSG / 4; ++i) {
         int g = base + 4 * i + wave;
@@ -222,43 +233,40 @@ __device__ inline void load_stage(Stage<MT, WPL>& st, const Src<MT>& src, int ba
         g = g < ks_real ? g : ks_real - 1;
 #pragma unroll
         for (int t = 0; t < MT; ++t)
-            st.a[i][t] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(src.x, src.a_off[t], g * 64, 0));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(src.x, LDS_PTR(buf + ((4 * i + wave) * MT + t) * 64),
+                                                     16, src.a_off[t], g * 64, 0, 0);
     }
     // the record's scale block (8 groups x 16 x WPL bf16) follows its codes;
     // lane l takes 16-byte pieces l, 64 + l, ...
-    const bool virt = MAYBE_VIRTUAL && base < ks_min;
-    const int rec = (virt ? ks_min : base) >> 3;
-    const int soff = (rec * (576 * WPL) + 512 * WPL) * 4;
+    u32x4* sb = buf + kAStage + wave * (WPL / 4 * 64);
+    if (MAYBE_VIRTUAL && base < ks_min) {
 #pragma unroll
-    for (int v = 0; v < WPL / 4; ++v) {
-        const u32x4 x = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(src.w, (64 * v + lane) * 16, soff, 0));
-        st.s[v] = virt ? u32x4{0u, 0u, 0u, 0u} : x;
+        for (int v = 0; v < WPL / 4; ++v) sb[64 * v + lane] = u32x4{0u, 0u, 0u, 0u};
+    } else {
+        const int soff = ((base >> 3) * (576 * WPL) + 512 * WPL) * 4;
+#pragma unroll
+        for (int v = 0; v < WPL / 4; ++v)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(src.w, LDS_PTR(sb + 64 * v), 16,
+                                                     (64 * v + lane) * 16, soff, 0, 0);
     }
-}
-
-template <int MT, int WPL>
-__device__ inline void store_stage(const Stage<MT, WPL>& st, u32x4* abuf, u32x4* sbuf, int wave,
-                                   int lane) {
-#pragma unroll
-    for (int i = 0; i < kSG / 4; ++i)
-#pragma unroll
-        for (int t = 0; t < MT; ++t) abuf[((4 * i + wave) * MT + t) * 64 + lane] = st.a[i][t];
-#pragma unroll
-    for (int v = 0; v < WPL / 4; ++v) sbuf[64 * v + lane] = st.s[v];
 }
 
 }  // namespace
 
-// LDS per workgroup: activation stages [2][kSG][MT][64] x 16 B and scale
-// stages [2][4 wavefronts][WPL/4 x 64] x 16 B.
+// LDS per workgroup: two staging buffers, each the activation fragments of a
+// stage [kSG][MT][64] x 16 B, then the scales [4 wavefronts][WPL/4 x 64] x
+// 16 B.  The buffers are separate LDS objects, so that the compiler tells
+// reads of one from buffer-to-LDS loads into the other.
 template <int MT, int WPL>
 struct Lds {
     static constexpr int a_stage = kSG * MT * 64;   // u32x4 per activation stage
     static constexpr int s_wave = WPL / 4 * 64;     // u32x4 per wavefront scale stage
     static constexpr int s_stage = 4 * s_wave;
-    static constexpr int total = 2 * a_stage + 2 * s_stage;
+    static constexpr int buf = a_stage + s_stage;   // u32x4 per buffer
+};
+
+struct Stg {
+    u32x4* b[2];
 };
 
 // The K loop of one workgroup tile with MT active 16-row blocks (MTMAX sizes
@@ -268,12 +276,11 @@ struct Lds {
 // = 8) in the one-block variant, so that three of its workgroups fit on a CU
 // (the HBM stream needs about eight wavefronts per CU in flight, and a
 // decode-sized grid then runs in one round); two stages (D = 16) otherwise.
-// Activation fragments and scales: LDS double buffer, one barrier per stage;
-// each stage's global loads are issued two stages ahead into one of two
-// register sets.  Issue order matters because vector-memory completions are
-// waited for in order: storing a stage to LDS waits only for loads issued
-// before it, i.e. ring refills that are due at that point anyway, so the
-// ring keeps its full depth.
+// Activation fragments and scales: two LDS buffers filled by buffer-to-LDS
+// loads one stage ahead.  A stage ends with a wait for this wavefront's loads
+// into the other buffer (vector-memory completions are counted in order, so
+// the count is the stage's ring refills, which may stay in flight) and one
+// barrier, after which the buffer just read is free for the stage after next.
 //
 // Iterations cover two stages (16 groups); the K range is padded at its start
 // by one virtual record (zero scales) when it holds an odd number of records.
@@ -281,36 +288,35 @@ struct Lds {
 // and for the odd one kSG (D = 16) or 0 (D = 8).
 template <int MT, int WPL, int MTMAX>
 __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1, int ks_real,
-                                            int wave, int lane, u32x4* lds,
+                                            int wave, int lane, const Stg& stg,
                                             f32x4 (&acc)[MT][WPL], uint32_t mask,
                                             uint32_t bits) {
     constexpr int D = MTMAX == 1 ? kSG : 2 * kSG;
-    constexpr int IT = 2 * kSG;          // groups per iteration
-    constexpr int RO = D == IT ? kSG : 0;  // ring slot of the odd stage's first group
+    constexpr int IT = 2 * kSG;                    // groups per iteration
+    constexpr int RO = D == IT ? kSG : 0;          // ring slot of the odd stage's first group
+    constexpr int kRefill = kSG * (WPL / 4);       // code loads of one stage's refills
+    constexpr int kStage = kSG / 4 * MT + WPL / 4; // staging loads per stage and wavefront
     using L = Lds<MTMAX, WPL>;
     if (ks1 <= ks0) return;
-    const u32x4* abuf0 = lds;
-    const u32x4* abuf1 = lds + L::a_stage;
-    u32x4* wbuf0 = lds;
-    u32x4* wbuf1 = lds + L::a_stage;
-    u32x4* sbuf0 = lds + 2 * L::a_stage + wave * L::s_wave;
-    u32x4* sbuf1 = sbuf0 + L::s_stage;
+    const u32x4* abuf0 = stg.b[0];
+    const u32x4* abuf1 = stg.b[1];
     // this lane's scales of group g in a stage: bf16 (16 g + lane % 16) * WPL
-    const uint16_t* srd0 = reinterpret_cast<const uint16_t*>(sbuf0) + (lane & 15) * WPL;
-    const uint16_t* srd1 = reinterpret_cast<const uint16_t*>(sbuf1) + (lane & 15) * WPL;
+    const uint16_t* srd0 = reinterpret_cast<const uint16_t*>(stg.b[0] + L::a_stage + wave * L::s_wave) +
+                           (lane & 15) * WPL;
+    const uint16_t* srd1 = reinterpret_cast<const uint16_t*>(stg.b[1] + L::a_stage + wave * L::s_wave) +
+                           (lane & 15) * WPL;
 
     // a K range of one stage (K = 256, or a split of one record) runs alone,
     // without the virtual stage that pads other odd stage counts
     if (ks1 - ks0 == kSG) {
         Codes<WPL> one[kSG];
-        Stage<MT, WPL> r;
-        load_stage<MT, WPL>(r, src, ks0, ks0, ks_real, wave, lane);
+        dma_stage<MT, WPL, MTMAX>(src, stg.b[0], ks0, ks0, ks_real, wave, lane);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < kSG; ++i) load_codes<WPL>(one[i], src.w, src.code_off, ks0 + i);
         __builtin_amdgcn_sched_barrier(0);
-        store_stage<MT, WPL>(r, wbuf0, sbuf0, wave, lane);
-        __syncthreads();
+        wait_vmcnt<kRefill>();                   // the stage's buffer has landed
+        barrier_ds();
         stage_groups<MT, WPL, kSG>(one, 0, abuf0, srd0, src, 0, false, acc, mask, bits, lane);
         return;
     }
@@ -321,39 +327,39 @@ __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1
     const int kb = ks0 - pad;
     const int nit = (ks1 - kb) / IT;            // iterations of two stages
 
+    // buffer 1's loads after the ring's, as in the loop (where a stage's loads
+    // follow the refills), so that the waits for ring slots match on both paths
     Codes<WPL> ring[D];
-    Stage<MT, WPL> r0, r1;
-    load_stage<MT, WPL, true>(r0, src, kb, ks0, ks_real, wave, lane);
-    load_stage<MT, WPL>(r1, src, kb + kSG, ks0, ks_real, wave, lane);
-    __builtin_amdgcn_sched_barrier(0);          // stage loads ahead of the ring
+    dma_stage<MT, WPL, MTMAX, true>(src, stg.b[0], kb, ks0, ks_real, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < D; ++i) load_codes<WPL>(ring[i], src.w, src.code_off, kb + i < ks0 ? ks0 : kb + i);
     __builtin_amdgcn_sched_barrier(0);
-    store_stage<MT, WPL>(r0, wbuf0, sbuf0, wave, lane);
-    __syncthreads();
+    dma_stage<MT, WPL, MTMAX>(src, stg.b[1], kb + kSG, ks0, ks_real, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<kStage + D * (WPL / 4)>();        // buffer 0 has landed
+    barrier_ds();
 
     for (int it = 0; it < nit - 1; ++it) {
         const int base = kb + it * IT;
         // even stage: buffer 0; its ring slots take groups D ahead
-        load_stage<MT, WPL>(r0, src, base + IT, ks0, ks_real, wave, lane);
-        __builtin_amdgcn_sched_barrier(0);
         stage_groups<MT, WPL, D>(ring, 0, abuf0, srd0, src, base + D, true, acc, mask, bits, lane);
-        store_stage<MT, WPL>(r1, wbuf1, sbuf1, wave, lane);
-        __syncthreads();
+        wait_vmcnt<kRefill>();                   // buffer 1 has landed
+        barrier_ds();                            // (for every wavefront); buffer 0 is free
+        dma_stage<MT, WPL, MTMAX>(src, stg.b[0], base + IT, ks0, ks_real, wave, lane);
         // odd stage: buffer 1
-        load_stage<MT, WPL>(r1, src, base + IT + kSG, ks0, ks_real, wave, lane);
-        __builtin_amdgcn_sched_barrier(0);
         stage_groups<MT, WPL, D>(ring, RO, abuf1, srd1, src, base + D + kSG, true, acc, mask, bits,
                                  lane);
-        store_stage<MT, WPL>(r0, wbuf0, sbuf0, wave, lane);
-        __syncthreads();
+        wait_vmcnt<kRefill>();                   // buffer 0 has landed
+        barrier_ds();                            // buffer 1 is free
+        dma_stage<MT, WPL, MTMAX>(src, stg.b[1], base + IT + kSG, ks0, ks_real, wave, lane);
     }
     // last iteration: with a one-stage ring the even stage still refills it
     // with the odd stage's groups
     const int last = kb + (nit - 1) * IT;
     stage_groups<MT, WPL, D>(ring, 0, abuf0, srd0, src, last + kSG, D < IT, acc, mask, bits, lane);
-    store_stage<MT, WPL>(r1, wbuf1, sbuf1, wave, lane);
-    __syncthreads();
+    wait_vmcnt<(D < IT ? kRefill : 0)>();        // buffer 1 has landed
+    barrier_ds();
     stage_groups<MT, WPL, D>(ring, RO, abuf1, srd1, src, 0, false, acc, mask, bits, lane);
 }
 
@@ -434,7 +440,7 @@ __device__ __forceinline__ bool splitk_fixup(const GemmArgs& a, int p0, int nrow
 // `counter`: this part's arrival counter (split_k > 1).
 template <int MT, int WPL, int MTMAX>
 __device__ __forceinline__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, int nrows,
-                                             int chunk, int s, int wave, int lane, u32x4* lds,
+                                             int chunk, int s, int wave, int lane, const Stg& stg,
                                              int32_t* counter) {
     const bool slot_rows = a.tile_src != TILE_MASKED;
     const bool active = chunk < a.NC;
@@ -480,7 +486,7 @@ __device__ __forceinline__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, i
     // only pins the register class and emits nothing
     uint32_t vbits = a.unpack_bits;
     asm volatile("" : "+v"(vbits));
-    stream_loop<MT, WPL, MTMAX>(src, ks0, ks1, a.KS, wave, lane, lds, acc, a.unpack_mask, vbits);
+    stream_loop<MT, WPL, MTMAX>(src, ks0, ks1, a.KS, wave, lane, stg, acc, a.unpack_mask, vbits);
 
     if (a.split_k > 1 && !splitk_fixup<MT, WPL>(a, p0, nrows, chunk, s, active, lane, counter, acc))
         return;
@@ -524,17 +530,17 @@ __device__ __forceinline__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, i
 
 template <int MT, int WPL>
 __device__ __forceinline__ void gemm_tile_part(const GemmArgs& a, int e, int p0, int nrows,
-                                               int chunk, int s, int wave, int lane, u32x4* lds,
+                                               int chunk, int s, int wave, int lane, const Stg& stg,
                                                int32_t* counter) {
     const int mt_active = (nrows + 15) >> 4;
     if (mt_active <= 1)
-        gemm_tile_mt<1, WPL, MT>(a, e, p0, nrows, chunk, s, wave, lane, lds, counter);
+        gemm_tile_mt<1, WPL, MT>(a, e, p0, nrows, chunk, s, wave, lane, stg, counter);
     else if (MT >= 2 && mt_active == 2)
-        gemm_tile_mt<(MT >= 2 ? 2 : 1), WPL, MT>(a, e, p0, nrows, chunk, s, wave, lane, lds, counter);
+        gemm_tile_mt<(MT >= 2 ? 2 : 1), WPL, MT>(a, e, p0, nrows, chunk, s, wave, lane, stg, counter);
     else if (MT >= 3 && mt_active == 3)
-        gemm_tile_mt<(MT >= 3 ? 3 : 1), WPL, MT>(a, e, p0, nrows, chunk, s, wave, lane, lds, counter);
+        gemm_tile_mt<(MT >= 3 ? 3 : 1), WPL, MT>(a, e, p0, nrows, chunk, s, wave, lane, stg, counter);
     else if (MT >= 4)
-        gemm_tile_mt<(MT >= 4 ? 4 : 1), WPL, MT>(a, e, p0, nrows, chunk, s, wave, lane, lds, counter);
+        gemm_tile_mt<(MT >= 4 ? 4 : 1), WPL, MT>(a, e, p0, nrows, chunk, s, wave, lane, stg, counter);
 }
 
 // A tile of more than 16 * MT rows (a variant whose registers hold fewer row
@@ -543,14 +549,14 @@ __device__ __forceinline__ void gemm_tile_part(const GemmArgs& a, int e, int p0,
 // K split.
 template <int MT, int WPL>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int ty, int e, int p0, int nrows,
-                                          int quad, int s, int wave, int lane, u32x4* lds) {
+                                          int quad, int s, int wave, int lane, const Stg& stg) {
     const int nquads = (a.NC + 3) / 4;
     for (int r = 0, part = 0; r < nrows; r += 16 * MT, ++part) {
         if (r > 0) __syncthreads();  // the part reuses the staging buffers
         int32_t* counter =
             a.counters + (static_cast<int64_t>(ty) * kMaxTileParts + part) * nquads + quad;
         gemm_tile_part<MT, WPL>(a, e, p0 + r, nrows - r < 16 * MT ? nrows - r : 16 * MT,
-                                quad * 4 + wave, s, wave, lane, lds, counter);
+                                quad * 4 + wave, s, wave, lane, stg, counter);
     }
 }
 
@@ -561,7 +567,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int ty, int e, int 
 // reached by all four wavefronts.
 template <int MT, int WPL>
 __global__ void __launch_bounds__(256) k_gemm_small(GemmArgs a) {
-    __shared__ u32x4 lds[Lds<MT, WPL>::total];
+    __shared__ u32x4 stage0[Lds<MT, WPL>::buf];
+    __shared__ u32x4 stage1[Lds<MT, WPL>::buf];
+    Stg stg;
+    stg.b[0] = stage0;
+    stg.b[1] = stage1;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int n_tiles;
@@ -598,7 +608,7 @@ __global__ void __launch_bounds__(256) k_gemm_small(GemmArgs a) {
             nrows = cnt - r0 < a.tile_m ? cnt - r0 : a.tile_m;
         }
         if (e < 0 || e >= a.E || nrows <= 0) continue;
-        gemm_tile<MT, WPL>(a, ty, e, p0, nrows, quad, s, wave, lane, lds);
+        gemm_tile<MT, WPL>(a, ty, e, p0, nrows, quad, s, wave, lane, stg);
         __syncthreads();  // the next item reuses the staging buffers
     }
 }
