@@ -14,13 +14,14 @@
 // chunks of CW output columns of one row tile, over one K range.
 //   * Codes: every lane fetches its CW/16 words of a K group with 16-byte
 //     non-temporal loads; the packed layout makes each wavefront's stream
-//     contiguous.  A register ring keeps D groups of codes in flight (64
-//     VGPRs), refilled as each group is consumed.
+//     contiguous.  A register ring keeps D groups of codes in flight (8 or
+//     16 groups: 32 or 64 VGPRs), refilled as each group is consumed.
 //   * Activations and scales are staged through LDS, one stage (8 groups)
 //     ahead, double-buffered, one barrier per stage: each wavefront loads a
 //     quarter of the stage's activation fragments (shared by all four) and
-//     its own chunk's scales for the stage (one 16-byte load per lane); the
-//     fragments are read back in MFMA A-operand order (conflict-free).
+//     its own chunk's scales for the stage (one 16-byte load per lane), with
+//     buffer loads that write LDS directly; the fragments are read back in
+//     MFMA A-operand order (conflict-free).
 //   * A code q becomes the bf16 value 128 + q by OR-ing the exponent pattern
 //     0x43 above it, two codes per v_and_or_b32; v_mfma_f32_16x16x32_bf16 (K
 //     = 32 = one scale group) yields sum x (128 + q); the offset -136 sum x is
@@ -30,7 +31,7 @@
 //     accumulator element.  Weights are never rounded.
 //   * The loop is branch-free: K ranges are aligned to the end of the ring;
 //     leading slots before the range re-read its first group with zeroed
-//     scales (they add exactly zero).
+//     scales (they add exactly zero).  A range of a single stage runs alone.
 
 #include "device_common.h"
 #include "internal.h"
