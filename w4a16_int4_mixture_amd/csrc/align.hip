@@ -46,9 +46,10 @@ constexpr int kBatch = 16;
 constexpr int kMapLds = 4096;
 
 // Local experts of slots c0*64 + lane .. for kBatch chunks (-1: none or past
-// the end); all loads of the batch are issued before any is used.
-__device__ inline void load_batch(const AlignArgs& a, int64_t c0, int64_t c_end, int64_t S,
-                                  int lane, int (&eb)[kBatch], int* bad) {
+// the end); all loads of the batch are issued before any is used.  lmap: the
+// expert map cached in LDS, or null (then read from global memory).
+__device__ inline void load_batch(const AlignArgs& a, const int* lmap, int64_t c0, int64_t c_end,
+                                  int64_t S, int lane, int (&eb)[kBatch], int* bad) {
     int g[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
@@ -63,36 +64,7 @@ __device__ inline void load_batch(const AlignArgs& a, int64_t c0, int64_t c_end,
             if (g[j] < 0 || g[j] >= a.E_global) {
                 *bad = 1;
             } else {
-                e = a.expert_map ? a.expert_map[g[j]] : g[j];
-                if (e < -1 || e >= a.E_local) *bad = 1;
-                if (e < 0 || e >= a.E_local) e = -1;
-            }
-        }
-        eb[j] = e;
-    }
-}
-
-// Local experts of slots (c0 + j * stride) * 64 + lane for kBatch chunks
-// (-1: none or past the end); all loads are issued before any is used.
-__device__ inline void load_strided(const AlignArgs& a, int64_t c0, int stride, int64_t chunks,
-                                    int64_t S, int lane, int (&eb)[kBatch], int* bad) {
-    int g[kBatch];
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-        const int64_t c = c0 + static_cast<int64_t>(j) * stride;
-        const int64_t f = c * 64 + lane;
-        g[j] = (c < chunks && f < S) ? a.topk_ids[f] : 0;
-    }
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-        const int64_t c = c0 + static_cast<int64_t>(j) * stride;
-        const int64_t f = c * 64 + lane;
-        int e = -1;
-        if (c < chunks && f < S) {
-            if (g[j] < 0 || g[j] >= a.E_global) {
-                *bad = 1;
-            } else {
-                e = a.expert_map ? a.expert_map[g[j]] : g[j];
+                e = lmap ? lmap[g[j]] : a.expert_map ? a.expert_map[g[j]] : g[j];
                 if (e < -1 || e >= a.E_local) *bad = 1;
                 if (e < 0 || e >= a.E_local) e = -1;
             }
@@ -210,11 +182,19 @@ __global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
     __syncthreads();
 
     // ---- pass 1: counts per (wave, expert).  The routing ids of kBatch
-    // chunks are loaded together, so that one memory latency covers them.
+    // chunks are loaded together, so that one memory latency covers them;
+    // when one batch covers all of this wave's chunks, pass 3 reuses it.
+    const int* lm = map_lds ? lmap : nullptr;
+    const bool one_batch = c_end - c_begin <= kBatch;
+    int kept[kBatch];
     for (int e = lane; e < E; e += 64) my_cnt[e] = 0;
     for (int64_t c0 = c_begin; c0 < c_end; c0 += kBatch) {
         int eb[kBatch];
-        load_batch(a, c0, c_end, S, lane, eb, &bad);
+        load_batch(a, lm, c0, c_end, S, lane, eb, &bad);
+        if (one_batch) {
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) kept[j] = eb[j];
+        }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             if (c0 + j >= c_end) break;
@@ -291,7 +271,12 @@ __global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
     // ---- pass 3: scatter
     for (int64_t c0 = c_begin; c0 < c_end; c0 += kBatch) {
         int eb[kBatch];
-        load_batch(a, c0, c_end, S, lane, eb, &bad);
+        if (one_batch) {
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) eb[j] = kept[j];
+        } else {
+            load_batch(a, lm, c0, c_end, S, lane, eb, &bad);
+        }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             if (c0 + j >= c_end) break;
