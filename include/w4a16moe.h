@@ -291,7 +291,9 @@ w4a16_status w4a16_moe_w4a16_gemm(const w4a16_gemm_args* args, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Activation between the GEMMs: Z[r, j] = bf16( silu(g) * u ), g = Y13[r, j],
- * u = Y13[r, I + j], silu(g) = g / (1 + exp(-g)), evaluated in fp32.
+ * u = Y13[r, I + j], silu(g) = g / (1 + exp(-g)), evaluated in fp32 without
+ * overflow: within one bf16 ulp of the exact value for every finite bf16 g,
+ * and the same function as the fused SILU_MUL epilogue.
  * Rows [0, *rows_dev) when rows_dev != NULL (device count, e.g.
  * num_tokens_padded), else [0, rows).                                       */
 /* ------------------------------------------------------------------------ */
