@@ -131,6 +131,20 @@ def test_align_edge_cases(m, T, k, Eg, El, bm, tm):
     check_align(m, ids.reshape(T, k), Eg, El, em, bm, tm)
 
 
+@pytest.mark.parametrize("T,k,Eg,El", [(140000, 8, 384, 48), (2000, 4, 5000, 100)])
+def test_align_large_slot_counts_and_maps(m, T, k, Eg, El):
+    """Over a million slots (each wavefront then takes several batches of
+    routing ids, loaded again for the scatter), and an expert map too large
+    for the kernel's LDS copy (looked up in global memory)."""
+    print(f"align large: T={T} k={k} Eg={Eg} El={El}", flush=True)
+    rng = np.random.default_rng(T + k)
+    ids = rng.integers(0, Eg, size=(T, k), dtype=np.int32)
+    em = np.full(Eg, -1, np.int32)
+    sel = rng.permutation(Eg)[:El]
+    em[sel] = np.arange(El, dtype=np.int32)
+    check_align(m, ids, Eg, El, em, 16, 32)
+
+
 def test_align_validate_reports_bad_ids(m):
     from w4a16_int4_mixture_amd import _capi
     ids = np.array([[0, 1], [2, 9]], np.int32)
