@@ -220,7 +220,10 @@ typedef enum {
                                 GATE_UP_INTERLEAVE it is applied to the
                                 accumulators in the GEMM kernel; with a plain
                                 W13 the GEMM stages bf16 Y13 in the workspace
-                                and a second kernel applies it (same result) */
+                                at the rows it would store (positions, or
+                                slots with OROW_SLOT) and a second kernel
+                                applies it to those rows (same result; padding
+                                rows are skipped in both) */
 } w4a16_epilogue;
 
 #define W4A16_GEMM_F32_OUT 0x1u  /* store the fp32 accumulator (float) instead of
@@ -231,7 +234,13 @@ typedef struct {
     int32_t epilogue;               /* w4a16_epilogue */
     uint32_t flags;                 /* W4A16_GEMM_* */
     int32_t split_k;                /* 0 = automatic; >1 forces K splits (INDEXED
-                                       only: MASKED rejects it, MODE_MISMATCH) */
+                                       only: MASKED rejects it, MODE_MISMATCH).
+                                       Each split keeps an fp32 partial of
+                                       sorted_cap x N; a forced split whose
+                                       partial reaches 4 GiB is UNSUPPORTED (the
+                                       automatic choice then runs unsplit).
+                                       Ignored (no split) with OROW_SLOT or
+                                       F32_OUT and with a PREFILL weight */
     const uint16_t* A;              /* device bf16 activations, [A_rows, K];
                                        A_rows * K * 2 bytes must stay below
                                        4 GiB (else UNSUPPORTED) */
@@ -250,11 +259,17 @@ typedef struct {
     const int32_t* tiles;           /* device [tiles_cap][4] from w4a16_moe_align, or NULL */
     int32_t tiles_cap;
     const int32_t* tile_count;      /* device [1] */
-    int32_t tile_m;                 /* rows per tile of the tile table */
+    int32_t tile_m;                 /* rows per tile: the tile_m the table was
+                                       written with (w4a16_routing.tile_m).  A
+                                       table entry with more rows than this is
+                                       cut to tile_m rows; the rows past it are
+                                       neither computed nor stored */
     int32_t rows_hint;              /* host: expected routed rows on this GPU (launch
                                        choice only; 0 = unknown) */
     /* MASKED */
-    const int32_t* masked_m;        /* device int32 [G]: valid rows of each expert */
+    const int32_t* masked_m;        /* device int32 [G]: valid rows of each expert;
+                                       a count above max_m counts as max_m, one
+                                       <= 0 as no rows */
     int32_t max_m;                  /* rows reserved per expert; A is [G*max_m, K] */
     int32_t expected_m;             /* host hint > 0, launch choice only */
     /* weights */
@@ -290,22 +305,32 @@ w4a16_status w4a16_gemm_workspace_bytes(const w4a16_gemm_args* args, uint64_t* b
 w4a16_status w4a16_moe_w4a16_gemm(const w4a16_gemm_args* args, void* stream);
 
 /* ------------------------------------------------------------------------ */
-/* Activation between the GEMMs: Z[r, j] = bf16( silu(g) * u ), g = Y13[r, j],
- * u = Y13[r, I + j], silu(g) = g / (1 + exp(-g)), evaluated in fp32 without
- * overflow: within one bf16 ulp of the exact value for every finite bf16 g,
- * and the same function as the fused SILU_MUL epilogue.
- * Rows [0, *rows_dev) when rows_dev != NULL (device count, e.g.
- * num_tokens_padded), else [0, rows).                                       */
+/* Activation between the GEMMs (Chord page, "Measurements": the activation  */
+/* is the step between the timed gate/up and down GEMMs; the path's          */
+/* activation is SiLU of the gate half times the up half of the gate/up      */
+/* output).                                                                  */
+/*   Z[r, j] = bf16( silu(g) * u ), g = Y13[r, j], u = Y13[r, I + j],        */
+/* silu(g) = g / (1 + exp(-g)), evaluated in fp32 without overflow: within  */
+/* one bf16 ulp of the exact value for every finite bf16 g, and the same     */
+/* function as the fused SILU_MUL epilogue.                                  */
+/*   y13: device bf16 [rows, 2I]; z: device bf16 [rows, I]; I % 8 == 0.      */
+/* Rows [0, min(*rows_dev, rows)) when rows_dev != NULL (device count, e.g.  */
+/* num_tokens_padded), else [0, rows).  INVALID_ARG on null or misaligned    */
+/* buffers (16 bytes) or a bad I.                                            */
 /* ------------------------------------------------------------------------ */
 w4a16_status w4a16_moe_silu_mul(const uint16_t* y13, int64_t rows, const int32_t* rows_dev,
                                 int32_t I, uint16_t* z, void* stream);
 
 /* ------------------------------------------------------------------------ */
-/* Top-k weighted combine:                                                   */
+/* Top-k weighted combine (Chord page, "Measurements": the expert outputs of */
+/* the timed GEMMs are merged per token after the down GEMM, outside the     */
+/* timed unit; the merge is the router's top-k weighted sum):                */
 /*   out[t, h] = bf16( sum_{j<k, row_of[t*k+j] >= 0} w[t, j] * y[row_of[t*k+j], h] ) */
 /* fp32, j ascending, each product and sum rounded separately; a token with */
 /* no local slot gives +0.  y: device bf16 [y_rows, H]; row_of: device       */
-/* int32 [T*k]; topk_weights: device float [T, k]; out: device bf16 [T, H].  */
+/* int32 [T*k] (entries outside [0, y_rows) are skipped); topk_weights:      */
+/* device float [T, k]; out: device bf16 [T, H].  INVALID_ARG on null or     */
+/* misaligned buffers (16 bytes) or H not a positive multiple of 8.          */
 /* ------------------------------------------------------------------------ */
 w4a16_status w4a16_moe_combine(const uint16_t* y, int64_t y_rows, int32_t H,
                                const int32_t* row_of, const float* topk_weights, int32_t T,

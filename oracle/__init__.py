@@ -59,6 +59,11 @@ def num_threads() -> int:
     return int(_load().oracle_num_threads())
 
 
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP loops from now on (n >= 1)."""
+    _load().oracle_set_num_threads(ctypes.c_int(int(n)))
+
+
 # ---- element helpers -------------------------------------------------------
 
 def bf16_from_f64(x) -> np.ndarray:

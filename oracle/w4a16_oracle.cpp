@@ -132,6 +132,16 @@ extern "C" {
 
 int oracle_version(void) { return 1; }
 
+// Threads the OpenMP loops below use (set_num_threads: n >= 1; the
+// benchmark's single-thread leg).
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

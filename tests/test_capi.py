@@ -206,6 +206,37 @@ def test_gemm_argument_checks():
     assert capi.lib().w4a16_moe_w4a16_gemm(ctypes.byref(a), None) == capi.W4A16_ERR_CAPACITY
 
 
+def test_split_k_partials_stay_below_4gib():
+    """A split's fp32 partial [sorted_cap, N] is addressed with 32-bit byte
+    offsets: a forced split whose partial reaches 4 GiB is refused before any
+    launch, and the automatic choice runs unsplit instead (no partials in the
+    workspace)."""
+    d = host_desc(E=8, N=4096, K=1024)
+    big = dict(sorted_cap=300000, out_rows=300000, tiles_cap=20000, num_slots=262144, top_k=8,
+               A_rows=32768)
+    assert 300000 * 4096 * 4 >= 1 << 32
+    assert ws_status(gemm_args(d, split_k=2, **big)) == capi.W4A16_ERR_UNSUPPORTED
+    assert "4 GiB" in capi.w4a16_last_error()
+    # automatic: no split, so no counters and no partials
+    assert capi.w4a16_gemm_workspace_bytes(gemm_args(d, **big)) == 0
+    # the same forced split on a partial below 4 GiB is accepted
+    small = dict(big, sorted_cap=200000, out_rows=200000)
+    assert capi.w4a16_gemm_workspace_bytes(gemm_args(d, split_k=2, **small)) >= 2 * 200000 * 4096 * 4
+
+
+def test_split_sizing_without_row_hint_uses_sorted_cap():
+    """With no rows_hint the automatic split sizes its partials from the
+    routing capacity (every split writes an fp32 partial of sorted_cap rows),
+    not from one row per expert: a large capacity gets fewer splits."""
+    d = host_desc(E=8, N=256, K=4096)
+    ws_small = capi.w4a16_gemm_workspace_bytes(gemm_args(d, sorted_cap=64, out_rows=64))
+    ws_large = capi.w4a16_gemm_workspace_bytes(gemm_args(d, sorted_cap=65536, out_rows=65536))
+    # small capacity: split (partials present); large: the partials would
+    # exceed a quarter of the weight stream, so it runs unsplit
+    assert ws_small > 0
+    assert ws_large == 0
+
+
 def test_combine_and_silu_checks():
     fake = 1 << 20
     assert capi.lib().w4a16_moe_combine(fake, 4, 12, fake, fake, 1, 1, fake, None) == \

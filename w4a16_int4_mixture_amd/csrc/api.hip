@@ -86,8 +86,11 @@ static int choose_split(int64_t tiles_est, int64_t rows_est, int NC, int stages,
     return split;
 }
 
+// rows_cap: rows of the position-indexed output space when the caller's
+// buffers are known (0 = unknown); with no rows_hint it sizes the split-K
+// partials.
 static w4a16_status plan_impl(const w4a16_desc* d, int layout, int rows_hint, int expected_m,
-                              int tile_m_in, w4a16_plan* p) {
+                              int tile_m_in, int64_t rows_cap, w4a16_plan* p) {
     const int E = d->E;
     const int stages = d->k_groups / 8;
     const int NC = d->N / d->chunk_n;
@@ -129,9 +132,10 @@ static w4a16_status plan_impl(const w4a16_desc* d, int layout, int rows_hint, in
     p->block_m = 16;
     p->tile_m = tile_m;
     p->kernel = d->profile == W4A16_PROFILE_PREFILL ? 2 : 1;
-    const int64_t rows_est = layout == W4A16_LAYOUT_MASKED
-                                 ? static_cast<int64_t>(E) * expected_m
-                                 : std::max<int64_t>(rows_hint, E);
+    const int64_t rows_est = layout == W4A16_LAYOUT_MASKED ? static_cast<int64_t>(E) * expected_m
+                             : rows_hint > 0                ? std::max<int64_t>(rows_hint, E)
+                             : rows_cap > 0                 ? rows_cap
+                                                            : E;
     const int64_t active = std::min<int64_t>(E, std::max<int64_t>(tiles_est, 1));
     const int64_t weight_bytes = active * static_cast<int64_t>(d->N) * d->K * 18 / 32;
     p->split_k = p->kernel == 2 ? 1 : choose_split(tiles_est, rows_est, NC, stages, d->N, weight_bytes);
@@ -231,7 +235,7 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
             }
             tile_m = a->block_m;
         }
-        st = plan_impl(d, W4A16_LAYOUT_INDEXED, a->rows_hint, 0, tile_m, &plan);
+        st = plan_impl(d, W4A16_LAYOUT_INDEXED, a->rows_hint, 0, tile_m, a->sorted_cap, &plan);
         if (st != W4A16_OK) return st;
         int split = a->split_k > 0 ? a->split_k : plan.split_k;
         // the large-M kernel runs unsplit: split_k applies to the streaming kernel
@@ -290,7 +294,8 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
             set_error("the grouped masked dispatch chooses its own schedule: split_k override refused");
             return W4A16_ERR_MODE_MISMATCH;
         }
-        st = plan_impl(d, W4A16_LAYOUT_MASKED, 0, a->expected_m, 0, &plan);
+        st = plan_impl(d, W4A16_LAYOUT_MASKED, 0, a->expected_m, 0,
+                       static_cast<int64_t>(d->E) * a->max_m, &plan);
         if (st != W4A16_OK) return st;
         const int64_t rows = static_cast<int64_t>(d->E) * a->max_m;
         if (a->A_rows < rows) {
@@ -321,6 +326,16 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
     } else {
         W4A16_CHECK_ARG(false, "unknown layout %d", a->layout);
     }
+    // a split's fp32 partial [rows_cap, N] is addressed with 32-bit byte
+    // offsets: below 4 GiB or no split (an explicit override is refused)
+    if (r->split > 1 && static_cast<uint64_t>(r->rows_cap) * d->N * 4 >= 0xFFFFFFFFull) {
+        if (a->layout == W4A16_LAYOUT_INDEXED && a->split_k > 1) {
+            set_error("split_k %d: a split's fp32 partial of %lld x %d exceeds 4 GiB", a->split_k,
+                      static_cast<long long>(r->rows_cap), d->N);
+            return W4A16_ERR_UNSUPPORTED;
+        }
+        r->split = 1;
+    }
     g.split_k = r->split;
     g.tiles_cap = static_cast<int>(std::min<int64_t>(r->tiles_bound, 0x7FFFFFFF));
     g.unpack_mask = 0x000F000Fu;
@@ -329,8 +344,9 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
     const bool split = r->split > 1;
     r->silu_separate = a->epilogue == W4A16_EPI_SILU_MUL && !interleaved;
     const int64_t gx = (g.NC + 3) / 4;
-    // split-K arrival counters; the PREFILL kernel's work-queue counters (nine ints)
-    r->ws_counters = split ? round256(static_cast<uint64_t>(r->tiles_bound) * kMaxTileParts * gx * 4)
+    // split-K arrival counters (one per tile and group of four chunks); the
+    // PREFILL kernel's work-queue counters (nine ints)
+    r->ws_counters = split ? round256(static_cast<uint64_t>(r->tiles_bound) * gx * 4)
                      : r->kernel == 2 ? 256 : 0;
     r->ws_partial = split ? round256(static_cast<uint64_t>(r->split) * r->rows_cap * d->N * 4) : 0;
     r->ws_y13 = r->silu_separate ? round256(static_cast<uint64_t>(r->rows_cap) * d->N * 2) : 0;
@@ -370,7 +386,7 @@ w4a16_status w4a16_plan_gemm(const w4a16_desc* desc, int32_t layout, int32_t row
     W4A16_CHECK_ARG(layout == W4A16_LAYOUT_INDEXED || layout == W4A16_LAYOUT_MASKED, "unknown layout %d", layout);
     W4A16_CHECK_ARG(tile_m == 0 || (tile_m >= 16 && tile_m % 16 == 0 && tile_m <= max_tile(desc)),
                     "tile_m must be 0 or a multiple of 16 up to %d for this profile", max_tile(desc));
-    return plan_impl(desc, layout, rows_hint, expected_m, tile_m, plan);
+    return plan_impl(desc, layout, rows_hint, expected_m, tile_m, 0, plan);
 }
 
 w4a16_status w4a16_moe_align_capacity(int32_t T, int32_t top_k, int32_t E_local, int32_t block_m,
@@ -493,10 +509,16 @@ w4a16_status w4a16_moe_w4a16_gemm(const w4a16_gemm_args* args, void* stream) {
     st = check_launch("w4a16 gemm");
     if (st != W4A16_OK) return st;
     if (r.silu_separate) {
+        // the GEMM staged Y13 in the workspace at the rows it would have
+        // written (positions, or slots with OROW_SLOT); the activation visits
+        // the same rows and skips padding, so it writes only rows the caller's
+        // output holds
         const bool masked = args->layout == W4A16_LAYOUT_MASKED;
         launch_silu_mul(static_cast<const uint16_t*>(r.g.out), r.rows_cap,
                         masked ? nullptr : args->num_tokens_padded, args->desc->N / 2,
                         masked ? args->masked_m : nullptr, args->max_m,
+                        masked ? nullptr : args->sorted_ids, args->num_slots,
+                        !masked && args->orow == W4A16_OROW_SLOT,
                         static_cast<uint16_t*>(args->out), s);
         st = check_launch("silu_mul");
     }
@@ -508,7 +530,8 @@ w4a16_status w4a16_moe_silu_mul(const uint16_t* y13, int64_t rows, const int32_t
     clear_error();
     W4A16_CHECK_ARG(y13 && z && aligned(y13, 16) && aligned(z, 16), "null or misaligned buffers");
     W4A16_CHECK_ARG(rows >= 0 && I >= 8 && I % 8 == 0, "rows must be >= 0 and I a multiple of 8");
-    launch_silu_mul(y13, rows, rows_dev, I, nullptr, 1, z, static_cast<hipStream_t>(stream));
+    launch_silu_mul(y13, rows, rows_dev, I, nullptr, 1, nullptr, 0, false, z,
+                    static_cast<hipStream_t>(stream));
     return check_launch("silu_mul");
 }
 

@@ -31,19 +31,38 @@ __device__ inline float silu_mul(float g, float u) { return dev::silu_mul_bf16(g
 
 }  // namespace
 
-// Z[r, j..j+7] from Y13[r, j..j+7] (gate) and Y13[r, I+j..] (up).
+// Z[r, j..j+7] from Y13[r, j..j+7] (gate) and Y13[r, I+j..] (up), over the
+// positions p < min(*rows_dev, rows) (or p < rows):
+//   masked_m != nullptr: p = g * max_m + i is skipped when i >= masked_m[g]
+//                        (a count above max_m covers the expert's max_m rows);
+//   sorted_ids != nullptr: p is skipped when f = sorted_ids[p] is not a slot
+//                        (padding sentinel); the row is f if slot_rows, else p.
 __global__ void k_silu_mul(const uint16_t* __restrict__ y13, int64_t rows,
                            const int32_t* __restrict__ rows_dev, int I,
                            const int32_t* __restrict__ masked_m, int max_m,
+                           const int32_t* __restrict__ sorted_ids, int num_slots, int slot_rows,
                            uint16_t* __restrict__ z) {
-    const int64_t nrows = rows_dev ? static_cast<int64_t>(rows_dev[0]) : rows;
+    int64_t nrows = rows;
+    if (rows_dev) {
+        const int64_t d = rows_dev[0];
+        nrows = d < rows ? (d > 0 ? d : 0) : rows;
+    }
     const int per_row = I / 8;
     const int64_t total = nrows * per_row;
     for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
          idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        const int64_t r = idx / per_row;
+        const int64_t p = idx / per_row;
         const int j = static_cast<int>(idx % per_row) * 8;
-        if (masked_m && (r % max_m) >= masked_m[r / max_m]) continue;
+        if (masked_m) {
+            const int mg = masked_m[p / max_m];
+            if ((p % max_m) >= (mg < max_m ? mg : max_m)) continue;
+        }
+        int64_t r = p;
+        if (sorted_ids) {
+            const int f = sorted_ids[p];
+            if (f < 0 || f >= num_slots) continue;
+            if (slot_rows) r = f;
+        }
         const u32x4 g = *reinterpret_cast<const u32x4*>(y13 + r * 2 * I + j);
         const u32x4 u = *reinterpret_cast<const u32x4*>(y13 + r * 2 * I + I + j);
         u32x4 o;
@@ -93,9 +112,11 @@ static unsigned grid_for(int64_t items, int block) {
 }
 
 void launch_silu_mul(const uint16_t* y13, int64_t rows, const int32_t* rows_dev, int I,
-                     const int32_t* masked_m, int max_m, uint16_t* z, hipStream_t s) {
+                     const int32_t* masked_m, int max_m, const int32_t* sorted_ids, int num_slots,
+                     bool slot_rows, uint16_t* z, hipStream_t s) {
     k_silu_mul<<<grid_for(rows * (I / 8), 256), 256, 0, s>>>(y13, rows, rows_dev, I, masked_m,
-                                                             max_m, z);
+                                                             max_m, sorted_ids, num_slots,
+                                                             slot_rows ? 1 : 0, z);
 }
 
 void launch_combine(const uint16_t* y, int64_t y_rows, int H, const int32_t* row_of,

@@ -95,8 +95,14 @@ __device__ inline void dequant_group(const WGroup& g, uint32_t sw, uint32_t nib,
     b[1][1] = dequant_word(g.w.w, nib, s1, c1);
 }
 
+// Vector-memory instructions one wavefront issues per helper call; the K
+// loop's waits (s_waitcnt vmcnt, completions counted in issue order) are
+// written in these counts.
+constexpr int kWGroupLoads = 1;   // load_wgroup: one K group of codes
+constexpr int kRScaleLoads = 2;   // load_rscales: one record's scales
+
 // Loads the codes of group ks of the chunk for this lane (code_off: the
-// lane's byte offset inside a record's group).
+// lane's byte offset inside a record's group).  Issues kWGroupLoads loads.
 __device__ inline void load_wgroup(WGroup& g, __amdgpu_buffer_rsrc_t w, uint32_t code_off, int ks) {
     const int soff = (ks >> 3) * kRecWords * 4 + (ks & 7) * 512 * 4;
     g.w = __builtin_bit_cast(u32x4,
@@ -105,6 +111,7 @@ __device__ inline void load_wgroup(WGroup& g, __amdgpu_buffer_rsrc_t w, uint32_t
 
 // Loads this lane's scales of record rec (its 8 groups, one 32-bit word per
 // group; scale_off: the lane's byte offset inside a record's scale block).
+// Issues kRScaleLoads loads.
 __device__ inline void load_rscales(u32x4 (&sc)[2], __amdgpu_buffer_rsrc_t w, uint32_t scale_off,
                                     int rec) {
     const int soff = rec * kRecWords * 4 + 4096 * 4;
@@ -235,10 +242,13 @@ __device__ __forceinline__ void store_rows(const GemmArgs& a, const Item& it, co
 template <int RB>
 __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, int wave, int lane,
                                            const Slots& sl) {
-    // loads per wave and stage: 4 RB buffer-to-LDS loads of 8 rows, dealt
-    // to the four waves, and the codes of the stage's two groups
+    // loads per wave and stage (one batch, `issue` below): 4 RB
+    // buffer-to-LDS loads of 8 rows, dealt to the four waves, and the codes
+    // of the stage's two groups
     constexpr int kDma = RB;
-    constexpr int kStageOps = kDma + 2;
+    constexpr int kStageOps = kDma + 2 * kWGroupLoads;
+    static_assert(3 * kStageOps + 2 * kWGroupLoads + kRScaleLoads < 64,
+                  "everything the prologue issues fits the 6-bit vmcnt field");
 
     const int chunk = it.pair * 2 + (wave >> 1);
     const int h = wave & 1;
@@ -370,7 +380,9 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // activations of stage 0 (the two later batches may stay in flight)
+    // issued: codes of stage 0 and the scales of record 0, then three
+    // batches; the batches of stages 1 and 2 may stay in flight, so the
+    // activations of stage 0 have landed
     wait_vmcnt<2 * kStageOps>();
     barrier_lds();
     read_a(0, 0, av[0]);
@@ -395,10 +407,11 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
             dequant_group(ring[u][1], rscale(sc_cur, 2 * u + 1), nib, b[1]);
             mfmas(av[0], b[0], 0);
             __builtin_amdgcn_sched_barrier(0);
-            // the batch of stage s - 1 may stay in flight; the first batch of
-            // a trip also holds the next record's scales
+            // issued since the batch that holds the activations of stage s + 1:
+            // the batch of the previous step (kStageOps), which may stay in
+            // flight, followed at u == 0 by the next record's scales
             if (u == 1)
-                wait_vmcnt<kStageOps + 2>();
+                wait_vmcnt<kStageOps + kRScaleLoads>();
             else
                 wait_vmcnt<kStageOps>();
             barrier_lds();
@@ -463,9 +476,12 @@ __device__ inline Item tile_of(const GemmArgs& a, int ty) {
         it.e = a.expert_ids[ty];
         it.nrows = a.sorted_cap - it.p0 < a.block_m ? a.sorted_cap - it.p0 : a.block_m;
     } else {
+        // masked_m is the valid count of each expert; a count above max_m is
+        // cut to max_m, so no tile reaches past the expert's rows
         const int g = ty / a.chunks_per_expert;
         const int r0 = (ty % a.chunks_per_expert) * a.tile_m;
-        const int cnt = a.masked_m[g];
+        const int mg = a.masked_m[g];
+        const int cnt = mg < a.max_m ? mg : a.max_m;
         it.e = g;
         it.p0 = g * a.max_m + r0;
         it.nrows = cnt - r0 < a.tile_m ? cnt - r0 : a.tile_m;

@@ -78,14 +78,28 @@ struct Src {
     uint32_t a_off[MT];        // row of MFMA A row block t, K offset 8 * (lane / 16)
 };
 
+// Vector-memory instructions one wavefront issues per helper call.  The K
+// loop's waits (s_waitcnt vmcnt) are written in these counts: completions of
+// loads are counted in issue order, so "at most N outstanding" names exactly
+// which batches have landed.
+template <int WPL>
+constexpr int kCodeLoads = WPL / 4;                       // load_codes: one K group
+template <int MT, int WPL>
+constexpr int kStageActLoads = (kSG / 4) * MT;            // dma_stage: activation fragments
+template <int WPL>
+constexpr int kStageScaleLoads = WPL / 4;                 // dma_stage: this wavefront's scales
+template <int MT, int WPL>
+constexpr int kStageLoads = kStageActLoads<MT, WPL> + kStageScaleLoads<WPL>;
+
 // Codes of group ks (record ks / 8, slot ks % 8) for this lane; lane_off =
-// lane * WPL words, in bytes.
+// lane * WPL words, in bytes.  Issues kCodeLoads<WPL> loads.
 template <int WPL>
 __device__ inline void load_codes(Codes<WPL>& c, __amdgpu_buffer_rsrc_t w, uint32_t lane_off,
                                   int ks) {
     const int soff = ((ks >> 3) * (576 * WPL) + (ks & 7) * (64 * WPL)) * 4;
+    static_assert(sizeof(c.w) / sizeof(c.w[0]) == kCodeLoads<WPL>, "one load per 16 bytes");
 #pragma unroll
-    for (int i = 0; i < WPL / 4; ++i)
+    for (int i = 0; i < kCodeLoads<WPL>; ++i)
         c.w[i] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(w, lane_off + 16 * i, soff, kNonTemporal));
 }
@@ -218,15 +232,18 @@ __device__ inline void barrier_ds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_ba
 // buffer `buf` (activations, then the four wavefronts' scales) with buffer
 // loads carrying the LDS bit; lane l of each load writes 16 bytes at l * 16.
 // This wavefront loads the activation fragments of groups 4 i + wave and its
-// own scales: kSG / 4 * MT + WPL / 4 loads.  A virtual stage (base < ks_min,
+// own scales: kStageLoads<MT, WPL> loads.  A virtual stage (base < ks_min,
 // ahead of the K range; only the first stage of a range can be one) reads the
 // activations of group ks_min and writes zero scales instead of loading them
-// (one LDS store per 16 bytes); activation columns past K (padding groups,
-// whose scales are zero) are clamped to the last real group.
+// (one LDS store per 16 bytes, so it issues kStageScaleLoads fewer loads; a
+// wait written for the full count then waits at least as long); activation
+// columns past K (padding groups, whose scales are zero) are clamped to the
+// last real group.
 template <int MT, int WPL, int MTMAX, bool MAYBE_VIRTUAL = false>
 __device__ inline void dma_stage(const Src<MT>& src, u32x4* buf, int base, int ks_min, int ks_real,
                                  int wave, int lane) {
     constexpr int kAStage = kSG * MTMAX * 64;   // u32x4 of activations per buffer
+    static_assert((kSG / 4) * MT == kStageActLoads<MT, WPL>, "activation loads per stage");
 #pragma unroll
     for (int i = 0; i < kSG / 4; ++i) {
         int g = base + 4 * i + wave;
@@ -246,7 +263,7 @@ __device__ inline void dma_stage(const Src<MT>& src, u32x4* buf, int base, int k
     } else {
         const int soff = ((base >> 3) * (576 * WPL) + 512 * WPL) * 4;
 #pragma unroll
-        for (int v = 0; v < WPL / 4; ++v)
+        for (int v = 0; v < kStageScaleLoads<WPL>; ++v)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(src.w, LDS_PTR(sb + 64 * v), 16,
                                                      (64 * v + lane) * 16, soff, 0, 0);
     }
@@ -295,8 +312,10 @@ __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1
     constexpr int D = MTMAX == 1 ? kSG : 2 * kSG;
     constexpr int IT = 2 * kSG;                    // groups per iteration
     constexpr int RO = D == IT ? kSG : 0;          // ring slot of the odd stage's first group
-    constexpr int kRefill = kSG * (WPL / 4);       // code loads of one stage's refills
-    constexpr int kStage = kSG / 4 * MT + WPL / 4; // staging loads per stage and wavefront
+    constexpr int kRefill = kSG * kCodeLoads<WPL>;  // code loads of one stage's refills
+    constexpr int kStage = kStageLoads<MT, WPL>;     // staging loads per stage and wavefront
+    constexpr int kRing = D * kCodeLoads<WPL>;       // code loads that fill the ring
+    static_assert(kStage + kRing < 64 && kRefill < 64, "waits fit the 6-bit vmcnt field");
     using L = Lds<MTMAX, WPL>;
     if (ks1 <= ks0) return;
     const u32x4* abuf0 = stg.b[0];
@@ -316,6 +335,8 @@ __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1
 #pragma unroll
         for (int i = 0; i < kSG; ++i) load_codes<WPL>(one[i], src.w, src.code_off, ks0 + i);
         __builtin_amdgcn_sched_barrier(0);
+        // issued: the stage's buffer, then kSG groups of codes (= kRefill
+        // loads) that may stay in flight
         wait_vmcnt<kRefill>();                   // the stage's buffer has landed
         barrier_ds();
         stage_groups<MT, WPL, kSG>(one, 0, abuf0, srd0, src, 0, false, acc, mask, bits, lane);
@@ -338,19 +359,23 @@ __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1
     __builtin_amdgcn_sched_barrier(0);
     dma_stage<MT, WPL, MTMAX>(src, stg.b[1], kb + kSG, ks0, ks_real, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<kStage + D * (WPL / 4)>();        // buffer 0 has landed
+    // issued: buffer 0, the ring (kRing), buffer 1 (kStage); the last two may
+    // stay in flight
+    wait_vmcnt<kStage + kRing>();                // buffer 0 has landed
     barrier_ds();
 
     for (int it = 0; it < nit - 1; ++it) {
         const int base = kb + it * IT;
         // even stage: buffer 0; its ring slots take groups D ahead
         stage_groups<MT, WPL, D>(ring, 0, abuf0, srd0, src, base + D, true, acc, mask, bits, lane);
+        // issued since buffer 1's loads: this stage's ring refills (kRefill)
         wait_vmcnt<kRefill>();                   // buffer 1 has landed
         barrier_ds();                            // (for every wavefront); buffer 0 is free
         dma_stage<MT, WPL, MTMAX>(src, stg.b[0], base + IT, ks0, ks_real, wave, lane);
         // odd stage: buffer 1
         stage_groups<MT, WPL, D>(ring, RO, abuf1, srd1, src, base + D + kSG, true, acc, mask, bits,
                                  lane);
+        // issued since buffer 0's loads: this stage's ring refills (kRefill)
         wait_vmcnt<kRefill>();                   // buffer 0 has landed
         barrier_ds();                            // buffer 1 is free
         dma_stage<MT, WPL, MTMAX>(src, stg.b[1], base + IT + kSG, ks0, ks_real, wave, lane);
@@ -359,6 +384,7 @@ __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1
     // with the odd stage's groups
     const int last = kb + (nit - 1) * IT;
     stage_groups<MT, WPL, D>(ring, 0, abuf0, srd0, src, last + kSG, D < IT, acc, mask, bits, lane);
+    // issued since buffer 1's loads: the refills of this stage, if any
     wait_vmcnt<(D < IT ? kRefill : 0)>();        // buffer 1 has landed
     barrier_ds();
     stage_groups<MT, WPL, D>(ring, RO, abuf1, srd1, src, 0, false, acc, mask, bits, lane);
@@ -544,21 +570,14 @@ __device__ __forceinline__ void gemm_tile_part(const GemmArgs& a, int e, int p0,
         gemm_tile_mt<(MT >= 4 ? 4 : 1), WPL, MT>(a, e, p0, nrows, chunk, s, wave, lane, stg, counter);
 }
 
-// A tile of more than 16 * MT rows (a variant whose registers hold fewer row
-// blocks than the tile) is processed in parts of 16 * MT rows; each part
-// re-streams the chunk.  `quad`: the tile's group of four chunks; `s`: the
-// K split.
+// One tile of at most 16 * MT rows: `quad` is its group of four chunks, `s`
+// its K split; the split-K arrival counter is the (tile, quad) one.
 template <int MT, int WPL>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int ty, int e, int p0, int nrows,
                                           int quad, int s, int wave, int lane, const Stg& stg) {
     const int nquads = (a.NC + 3) / 4;
-    for (int r = 0, part = 0; r < nrows; r += 16 * MT, ++part) {
-        if (r > 0) __syncthreads();  // the part reuses the staging buffers
-        int32_t* counter =
-            a.counters + (static_cast<int64_t>(ty) * kMaxTileParts + part) * nquads + quad;
-        gemm_tile_part<MT, WPL>(a, e, p0 + r, nrows - r < 16 * MT ? nrows - r : 16 * MT,
-                                quad * 4 + wave, s, wave, lane, stg, counter);
-    }
+    int32_t* counter = a.counters + static_cast<int64_t>(ty) * nquads + quad;
+    gemm_tile_part<MT, WPL>(a, e, p0, nrows, quad * 4 + wave, s, wave, lane, stg, counter);
 }
 
 // Workgroup w runs work items w, w + G, ... (G = the grid), an item being
@@ -601,13 +620,20 @@ __global__ void __launch_bounds__(256) k_gemm_small(GemmArgs a) {
             e = a.expert_ids[ty];
             nrows = a.sorted_cap - p0 < a.block_m ? a.sorted_cap - p0 : a.block_m;
         } else {
+            // masked_m is the valid count of each expert; a count above max_m
+            // is cut to max_m, so no tile reaches past the expert's rows
             const int g = ty / a.chunks_per_expert;
             const int r0 = (ty % a.chunks_per_expert) * a.tile_m;
-            const int cnt = a.masked_m[g];
+            const int mg = a.masked_m[g];
+            const int cnt = mg < a.max_m ? mg : a.max_m;
             e = g;
             p0 = g * a.max_m + r0;
             nrows = cnt - r0 < a.tile_m ? cnt - r0 : a.tile_m;
         }
+        // a tile-table entry taller than the launch's tile height (a table
+        // written for another tile_m) is cut to it: its rows past 16 * MT are
+        // not computed, and nothing is stored outside the tile
+        nrows = nrows < 16 * MT ? nrows : 16 * MT;
         if (e < 0 || e >= a.E || nrows <= 0) continue;
         gemm_tile<MT, WPL>(a, ty, e, p0, nrows, quad, s, wave, lane, stg);
         __syncthreads();  // the next item reuses the staging buffers

@@ -96,9 +96,6 @@ enum TileSrc { TILE_TABLE = 0, TILE_BLOCKS = 1, TILE_MASKED = 2 };
 // as bf16 [rows, N/2] from a gate/up-interleaved weight.
 enum OutKind { OUT_BF16 = 0, OUT_F32 = 1, OUT_SILU = 2 };
 
-// Row-tile parts per tile (a tile of up to 64 rows in parts of 16 * MT rows).
-constexpr int kMaxTileParts = 4;
-
 struct GemmArgs {
     // rows
     int tile_src, arow, orow, top_k, num_slots;
@@ -125,8 +122,9 @@ struct GemmArgs {
     int out_kind;
     int split_k;
     // split-K (split_k > 1): fp32 partials [split_k][ws_stride] (rows of the
-    // position-indexed space x N) and one arrival counter per (tile, part,
-    // column group), zero between calls
+    // position-indexed space x N; ws_stride * 4 bytes < 4 GiB, checked on the
+    // host) and one arrival counter per (tile, column group), zero between
+    // calls
     float* partials;
     int32_t* counters;
     int64_t ws_stride;
@@ -138,9 +136,14 @@ void launch_gemm_small(const GemmArgs& a, int mt, hipStream_t s);
 // Large-M kernel (PREFILL profile only, tiles of up to 256 rows, no K split).
 void launch_gemm_large(const GemmArgs& a, hipStream_t s);
 
-// masked_m != nullptr: rows r with r % max_m >= masked_m[r / max_m] are skipped.
+// SiLU(gate) * up over positions p < rows (p < min(*rows_dev, rows) when
+// rows_dev is given).  masked_m != nullptr: p is skipped when p % max_m >=
+// masked_m[p / max_m] (counts cut to max_m).  sorted_ids != nullptr: p is
+// skipped unless f = sorted_ids[p] is in [0, num_slots); its row is f when
+// slot_rows, else p.
 void launch_silu_mul(const uint16_t* y13, int64_t rows, const int32_t* rows_dev, int I,
-                     const int32_t* masked_m, int max_m, uint16_t* z, hipStream_t s);
+                     const int32_t* masked_m, int max_m, const int32_t* sorted_ids, int num_slots,
+                     bool slot_rows, uint16_t* z, hipStream_t s);
 void launch_combine(const uint16_t* y, int64_t y_rows, int H, const int32_t* row_of,
                     const float* w, int T, int top_k, uint16_t* out, hipStream_t s);
 
