@@ -304,6 +304,21 @@ w4a16_status w4a16_gemm_workspace_bytes(const w4a16_gemm_args* args, uint64_t* b
  * the order in which splits finish. */
 w4a16_status w4a16_moe_w4a16_gemm(const w4a16_gemm_args* args, void* stream);
 
+/* Allocation-free variant of w4a16_moe_w4a16_gemm, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, checks, kernels and
+ * results; args->workspace and args->workspace_bytes are ignored.  Instead,
+ * the call uses a static scratch array of the library (32 MiB per GPU, held
+ * from the library's load until the process ends), whose device address is
+ * looked up once per device on that device's first call.  A call whose
+ * workspace (w4a16_gemm_workspace_bytes) exceeds 32 MiB returns CAPACITY
+ * before anything is launched.  The call allocates and frees nothing.
+ * Every call on one GPU shares that GPU's array: the call clears the part
+ * that must start at zero (its counters) with a kernel on `stream`, and calls
+ * that may overlap on one GPU (different streams, or different threads
+ * without ordering) race on it and must be serialised by the caller. */
+w4a16_status w4a16_moe_w4a16_gemm_noalloc(const w4a16_gemm_args* args, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Activation between the GEMMs (Chord page, "Measurements": the activation  */
 /* is the step between the timed gate/up and down GEMMs; the path's          */

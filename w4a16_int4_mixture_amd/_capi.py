@@ -113,6 +113,8 @@ SIGNATURES = {
     "w4a16_gemm_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(w4a16_gemm_args),
                                                   ctypes.POINTER(ctypes.c_uint64)]),
     "w4a16_moe_w4a16_gemm": (ctypes.c_int, [ctypes.POINTER(w4a16_gemm_args), ctypes.c_void_p]),
+    "w4a16_moe_w4a16_gemm_noalloc": (ctypes.c_int, [ctypes.POINTER(w4a16_gemm_args),
+                                                    ctypes.c_void_p]),
     "w4a16_moe_silu_mul": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
     "w4a16_moe_combine": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
@@ -221,6 +223,10 @@ def w4a16_gemm_workspace_bytes(args: w4a16_gemm_args) -> int:
 
 def w4a16_moe_w4a16_gemm(args: w4a16_gemm_args, stream=None) -> None:
     check(lib().w4a16_moe_w4a16_gemm(ctypes.byref(args), stream_handle(stream)))
+
+
+def w4a16_moe_w4a16_gemm_noalloc(args: w4a16_gemm_args, stream=None) -> None:
+    check(lib().w4a16_moe_w4a16_gemm_noalloc(ctypes.byref(args), stream_handle(stream)))
 
 
 def w4a16_moe_silu_mul(y13, rows, rows_dev, I, z, stream=None) -> None:

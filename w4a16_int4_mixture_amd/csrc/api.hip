@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "internal.h"
 
@@ -367,6 +368,67 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
     return W4A16_OK;
 }
 
+// Launches of one resolved GEMM call; the workspace pointers inside r.g are
+// already set.
+static w4a16_status run_resolved(const w4a16_gemm_args* args, const Resolved& r, hipStream_t s) {
+    if (r.kernel == 2)
+        launch_gemm_large(r.g, s);
+    else
+        launch_gemm_small(r.g, r.mt, s);
+    w4a16_status st = check_launch("w4a16 gemm");
+    if (st != W4A16_OK) return st;
+    if (r.silu_separate) {
+        // the GEMM staged Y13 in the workspace at the rows it would have
+        // written (positions, or slots with OROW_SLOT); the activation visits
+        // the same rows and skips padding, so it writes only rows the caller's
+        // output holds
+        const bool masked = args->layout == W4A16_LAYOUT_MASKED;
+        launch_silu_mul(static_cast<const uint16_t*>(r.g.out), r.rows_cap,
+                        masked ? nullptr : args->num_tokens_padded, args->desc->N / 2,
+                        masked ? args->masked_m : nullptr, args->max_m,
+                        masked ? nullptr : args->sorted_ids, args->num_slots,
+                        !masked && args->orow == W4A16_OROW_SLOT,
+                        static_cast<uint16_t*>(args->out), s);
+        st = check_launch("silu_mul");
+    }
+    return st;
+}
+
+// ---- static device scratch of the allocation-free GEMM entry point ----------
+//
+// One array per GPU, held from module load until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: the device
+// address of each GPU's copy comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address is passed to
+// kernels.
+constexpr uint64_t kScratchBytes = 32ull << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+static w4a16_status scratch_for_current_device(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        set_error("no current HIP device below %d for the static scratch", kMaxDevices);
+        return W4A16_ERR_HIP;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            set_error("hipGetSymbolAddress of the static scratch failed on device %d: %s", dev,
+                      hipGetErrorString(e));
+            return W4A16_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return W4A16_OK;
+}
+
 }  // namespace w4a16
 
 using namespace w4a16;
@@ -501,28 +563,46 @@ w4a16_status w4a16_moe_w4a16_gemm(const w4a16_gemm_args* args, void* stream) {
             return W4A16_ERR_CAPACITY;
         }
     }
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (r.kernel == 2)
-        launch_gemm_large(r.g, s);
-    else
-        launch_gemm_small(r.g, r.mt, s);
-    st = check_launch("w4a16 gemm");
+    return run_resolved(args, r, static_cast<hipStream_t>(stream));
+}
+
+w4a16_status w4a16_moe_w4a16_gemm_noalloc(const w4a16_gemm_args* args, void* stream) {
+    clear_error();
+    W4A16_CHECK_ARG(args, "null GEMM arguments");
+    // size the call with no workspace first: a call that needs more than the
+    // static scratch is refused before anything touches the device
+    w4a16_gemm_args a = *args;
+    a.workspace = nullptr;
+    a.workspace_bytes = 0;
+    Resolved r;
+    w4a16_status st = resolve(&a, &r);
     if (st != W4A16_OK) return st;
-    if (r.silu_separate) {
-        // the GEMM staged Y13 in the workspace at the rows it would have
-        // written (positions, or slots with OROW_SLOT); the activation visits
-        // the same rows and skips padding, so it writes only rows the caller's
-        // output holds
-        const bool masked = args->layout == W4A16_LAYOUT_MASKED;
-        launch_silu_mul(static_cast<const uint16_t*>(r.g.out), r.rows_cap,
-                        masked ? nullptr : args->num_tokens_padded, args->desc->N / 2,
-                        masked ? args->masked_m : nullptr, args->max_m,
-                        masked ? nullptr : args->sorted_ids, args->num_slots,
-                        !masked && args->orow == W4A16_OROW_SLOT,
-                        static_cast<uint16_t*>(args->out), s);
-        st = check_launch("silu_mul");
+    const uint64_t need = r.ws_total();
+    if (need > kScratchBytes) {
+        set_error("this call needs %llu bytes of scratch; the allocation-free entry point "
+                  "holds %llu (use w4a16_moe_w4a16_gemm with a workspace)",
+                  static_cast<unsigned long long>(need),
+                  static_cast<unsigned long long>(kScratchBytes));
+        return W4A16_ERR_CAPACITY;
     }
-    return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (need > 0) {
+        void* ptr = nullptr;
+        st = scratch_for_current_device(&ptr);
+        if (st != W4A16_OK) return st;
+        a.workspace = ptr;
+        a.workspace_bytes = kScratchBytes;
+        st = resolve(&a, &r);
+        if (st != W4A16_OK) return st;
+        // the array keeps the previous call's bytes: the counters at its
+        // start must read zero when the kernels begin
+        if (r.ws_counters > 0) {
+            launch_zero(ptr, r.ws_counters, s);
+            st = check_launch("scratch counters");
+            if (st != W4A16_OK) return st;
+        }
+    }
+    return run_resolved(&a, r, s);
 }
 
 w4a16_status w4a16_moe_silu_mul(const uint16_t* y13, int64_t rows, const int32_t* rows_dev,

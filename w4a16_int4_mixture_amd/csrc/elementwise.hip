@@ -104,6 +104,14 @@ __global__ void __launch_bounds__(64) k_combine(const uint16_t* __restrict__ y, 
     }
 }
 
+// Zero n 16-byte words (a kernel rather than a memset, so that it can sit in
+// a captured HIP graph).
+__global__ void k_zero16(u32x4* __restrict__ p, int64_t n) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
 static unsigned grid_for(int64_t items, int block) {
     int64_t g = (items + block - 1) / block;
     if (g > 8192) g = 8192;
@@ -122,6 +130,11 @@ void launch_silu_mul(const uint16_t* y13, int64_t rows, const int32_t* rows_dev,
 void launch_combine(const uint16_t* y, int64_t y_rows, int H, const int32_t* row_of,
                     const float* w, int T, int top_k, uint16_t* out, hipStream_t s) {
     k_combine<<<dim3(T, (H + 511) / 512), dim3(64), 0, s>>>(y, y_rows, H, row_of, w, top_k, out);
+}
+
+void launch_zero(void* p, uint64_t bytes, hipStream_t s) {
+    const int64_t n = static_cast<int64_t>(bytes / 16);
+    if (n > 0) k_zero16<<<grid_for(n, 256), 256, 0, s>>>(static_cast<u32x4*>(p), n);
 }
 
 }  // namespace w4a16

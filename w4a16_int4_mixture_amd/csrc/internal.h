@@ -144,6 +144,8 @@ void launch_gemm_large(const GemmArgs& a, hipStream_t s);
 void launch_silu_mul(const uint16_t* y13, int64_t rows, const int32_t* rows_dev, int I,
                      const int32_t* masked_m, int max_m, const int32_t* sorted_ids, int num_slots,
                      bool slot_rows, uint16_t* z, hipStream_t s);
+// Zero `bytes` (a multiple of 16) at p, 16-byte aligned, with a kernel.
+void launch_zero(void* p, uint64_t bytes, hipStream_t s);
 void launch_combine(const uint16_t* y, int64_t y_rows, int H, const int32_t* row_of,
                     const float* w, int T, int top_k, uint16_t* out, hipStream_t s);
 
