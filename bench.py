@@ -1,24 +1,28 @@
 """Benchmark of the W4A16 INT4 MoE expert path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload decode|prefill|tp8|masked|tiny]
+                    [--no-prefill] [--no-cpu-baseline] [--no-graph]
 
 One step = one call of the whole path on one batch of seeded synthetic input
 already resident in HBM: routing sort (align) -> gate/up GEMM with SiLU*gate in
 its epilogue -> down GEMM -> top-k combine (for the masked workload: the two
-GEMMs and the combine).  W untimed warm-up steps, then exactly K timed steps between two
-device synchronisations.  Rank 0 prints one JSON line.
+GEMMs and the combine).  W untimed warm-up steps, then exactly K timed steps
+between two device synchronisations.  One JSON line is printed.
 
-The default workload is the decode share of a Kimi-K2-like layer on one GPU of
-an EP8 deployment (48 local experts, hidden 7168, intermediate 2048, 64 tokens
-x top-8, about 9-15 routed rows per local expert): a weight-streaming problem,
-so its roofline is HBM bandwidth on the algorithmic weight bytes.  Two
-prepacked copies of the weights are used alternately so that no call finds the
-previous call's weights in the 256 MB last-level cache.
+The headline workload (default) is the decode share of a Kimi-K2-like layer on
+one GPU of an EP8 deployment (48 local experts, hidden 7168, intermediate 2048,
+64 tokens x top-8, about 9-15 routed rows per local expert): a weight-streaming
+problem, so its roofline is HBM bandwidth on the algorithmic weight bytes.
+Unless --no-prefill is given, the same run then measures the EP8 prefill share
+(8192 tokens over 384 experts, 48 local; MFMA-bound) and reports it in a
+"prefill" sub-object with its own roofline (bf16 MFMA TFLOP/s) and CPU
+baseline.  Two prepacked copies of the weights are used alternately so that no
+call finds the previous call's weights in the 256 MB last-level cache.
 
 Extra figures in the line: per-stage microseconds (HIP events on the stream the
-kernels run on), the page's unit (gate/up + down), the HIP-graph replay time of
+kernels run on), the pages' unit (gate/up + down), the HIP-graph replay time of
 the same step, the roofline object of the dominant kernel and the CPU oracle's
-time on the host cores.
+time on the host cores (all threads, and one thread).
 """
 from __future__ import annotations
 
@@ -26,6 +30,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -46,9 +51,12 @@ def parse():
     p.add_argument("--workload", default="decode",
                    choices=["decode", "prefill", "tp8", "masked", "tiny"])
     p.add_argument("--copies", type=int, default=2, help="prepacked weight copies rotated per call")
+    p.add_argument("--no-prefill", action="store_true",
+                   help="do not add the prefill sub-object to the decode line")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true")
-    p.add_argument("--cpu-budget-s", type=float, default=20.0)
+    p.add_argument("--cpu-budget-s", type=float, default=12.0,
+                   help="target seconds of oracle work per CPU leg")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run one plain device copy of this size before the warm-up (a known "
                         "byte count for scaling HBM counters)")
@@ -78,22 +86,36 @@ def traffic_from_profiles(workload: str, src_hash: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py: this path runs on one GPU; multi-GPU sharding (EP all-to-all, TP "
-              "reduce-scatter) is described in DESIGN.md but not built. Run with --gpus 1.",
-              file=sys.stderr)
-        sys.exit(2)
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
 
+
+def workload_name(name, wl):
+    return {
+        "decode": "EP8 decode share: 48 local experts, H7168 I2048, 64 tokens x top-8 (~10.7 rows/expert)",
+        "prefill": "EP8 prefill share: 48 local experts, H7168 I2048, 8192 tokens x top-8 over 384",
+        "tp8": "TP8 share: 384 experts, H7168 I256, 1024 tokens x top-8",
+        "masked": "grouped masked EP32 share: 12 experts, 256 rows Zipf(1.2), expected_m 32",
+        "tiny": "tiny: 8 experts, top-2, H256 I128, 16 tokens",
+    }[name]
+
+
+def run_workload(name, args, src_hash, cpu_legs=True):
+    """Prepare one workload on the GPU, time `args.steps` calls of the path
+    (after `args.warmup`), and return its figures as a dict."""
     import numpy as np
     import torch
 
     import synth
     import w4a16_int4_mixture_amd as m
 
-    torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
 
     def to_dev(a):
@@ -101,10 +123,10 @@ def main():
         return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
 
     t0 = time.time()
-    d = synth.make_workload(args.workload, seed=0)
+    d = synth.make_workload(name, seed=0)
     wl = d["wl"]
-    profile = m.PROFILE_PREFILL if args.workload == "prefill" else m.PROFILE_DECODE
-    print(f"[bench] workload {args.workload}: generated inputs in {time.time() - t0:.1f}s",
+    profile = m.PROFILE_PREFILL if name == "prefill" else m.PROFILE_DECODE
+    print(f"[bench] workload {name}: generated inputs in {time.time() - t0:.1f}s",
           file=sys.stderr, flush=True)
 
     codes13, scales13 = to_dev(d["codes13"]), to_dev(d["scales13"])
@@ -121,7 +143,7 @@ def main():
     ids = to_dev(d["topk_ids"])
     tw = to_dev(d["topk_weights"])
     em = None if d["expert_map"] is None else to_dev(d["expert_map"])
-    masked = args.workload == "masked"
+    masked = name == "masked"
 
     # local routed rows and active experts (host-side knowledge of the draw)
     if masked:
@@ -150,8 +172,9 @@ def main():
         row_of = to_dev(d["row_of"])
 
         def stages(p):
-            return [("gate_up", lambda: m._capi.w4a16_moe_w4a16_gemm(p.gate_up_args(a3, mm))),
-                    ("down", lambda: m._capi.w4a16_moe_w4a16_gemm(p.down_args(mm))),
+            ga, da = p.gate_up_args(a3, mm), p.down_args(mm)
+            return [("gate_up", lambda: m._capi.w4a16_moe_w4a16_gemm(ga)),
+                    ("down", lambda: m._capi.w4a16_moe_w4a16_gemm(da)),
                     ("combine", lambda: m._capi.w4a16_moe_combine(
                         p.Y2, p.Y2.shape[0], H, row_of, tw, wl.T, wl.top_k, p.out))]
     else:
@@ -169,12 +192,9 @@ def main():
                              p.Y2, p.Y2.shape[0], H, p.routing.row_of, tw, wl.T, wl.top_k,
                              p.out))]
 
-    # pre-built argument structs: the timed loop only launches
+    # pre-built argument structs (workspaces resolved once): the timed loop
+    # only launches
     stage_lists = [stages(p) for p in paths]
-    for p in paths:  # resolve workspaces once
-        if masked:
-            p.gate_up_args(a3, mm)
-            p.down_args(mm)
 
     if args.calib_copy_mib > 0:
         src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -196,7 +216,8 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # timed steps (wall clock between synchronisations), stage events per step
+    # timed steps (wall clock between synchronisations), stage events per step;
+    # every launch goes to torch's current stream, where the events are recorded
     n_st = len(stage_lists[0])
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_st + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -206,9 +227,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     stage_us = {}
-    for j, (name, _) in enumerate(stage_lists[0]):
+    for j, (sname, _) in enumerate(stage_lists[0]):
         vals = [ev[i][j].elapsed_time(ev[i][j + 1]) * 1000.0 for i in range(args.steps)]
-        stage_us[name] = float(np.median(vals))
+        stage_us[sname] = float(np.median(vals))
     event_total = float(np.median([ev[i][0].elapsed_time(ev[i][n_st]) * 1000.0
                                    for i in range(args.steps)]))
     ms_per_step = wall * 1000.0 / args.steps
@@ -243,14 +264,13 @@ def main():
             print(f"[bench] graph capture failed: {exc}", file=sys.stderr)
 
     gu, dn = stage_us["gate_up"], stage_us["down"]
-    src_hash = kernel_source_hash()
     # the dominant kernel is the gate/up GEMM; its algorithmic HBM bytes per
     # launch are the active experts' codes + scales, the activations read once
     # and the routed rows' outputs written once
     x_bytes = (rows if masked else wl.T) * H * 2
     out_bytes = rows * I * 2           # Z: SiLU*gate is applied in the epilogue
     alg_bytes13 = bytes13 + x_bytes + out_bytes
-    if args.workload == "prefill":
+    if name == "prefill":
         bound, unit_rf = "mfma", "TFLOP/s"
         achieved = flops13 / (gu * 1e-6) / 1e12
         peak = BF16_PEAK_TFLOPS
@@ -261,19 +281,48 @@ def main():
     plan13 = paths[0].plan if not masked else None
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit_rf,
                 "frac": round(achieved / peak, 4),
-                "traffic": traffic_from_profiles(args.workload, src_hash),
+                "traffic": traffic_from_profiles(name, src_hash),
                 "kernel": ("k_gemm_large (gate/up GEMM of the PREFILL profile, SiLU*gate in its "
-                           "epilogue: one launch per call)" if args.workload == "prefill" else
+                           "epilogue: one launch per call)" if name == "prefill" else
                            "k_gemm_small (gate/up GEMM with SiLU*gate epilogue and in-kernel "
                            "split-K fix-up: one launch per call)"),
                 "algorithmic_per_launch": alg_bytes13 if bound == "hbm" else flops13,
                 "launch_us": round(gu, 2)}
 
+    del paths, stage_lists, copies
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
     cpu = None
-    if not args.no_cpu_baseline and args.workload in ("decode", "tiny", "masked"):
-        cpu = cpu_baseline(d, wl, args.workload, args.cpu_budget_s)
+    if cpu_legs and not args.no_cpu_baseline:
+        cpu = cpu_baseline(d, wl, name, args.cpu_budget_s)
 
     weight_bytes = bytes13 + bytes2
+    return {
+        "wl": wl, "rows": rows, "active": active, "us_call": us_call, "ms_per_step": ms_per_step,
+        "stage_us": stage_us, "event_total": event_total, "graph_us": graph_us,
+        "gu": gu, "dn": dn, "roofline": roofline, "cpu": cpu, "plan13": plan13,
+        "weight_bytes": weight_bytes, "flops": flops13 + flops2, "copies": args.copies,
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this path runs on one GPU; multi-GPU sharding (EP all-to-all, TP "
+              "reduce-scatter) is described in DESIGN.md but not built. Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    torch.cuda.set_device(0)
+    src_hash = kernel_source_hash()
+
+    r = run_workload(args.workload, args, src_hash)
+    wl = r["wl"]
+    plan13 = r["plan13"]
+    gu, dn, us_call = r["gu"], r["dn"], r["us_call"]
     line = {
         "metric": METRIC,
         "value": round(us_call, 2),
@@ -281,76 +330,115 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(r["ms_per_step"], 4),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16 activations x int4 weights (fp32 accumulate)",
         "data": "synthetic (seeded, random-init weights)",
         "config": {"workload": workload_name(args.workload, wl), "tokens": wl.T,
-                   "top_k": wl.top_k, "local_experts": wl.E_local, "hidden": H,
-                   "intermediate": I, "routed_rows": rows, "active_experts": active,
-                   "weight_copies": len(paths),
+                   "top_k": wl.top_k, "local_experts": wl.E_local, "hidden": wl.H,
+                   "intermediate": wl.I, "routed_rows": r["rows"],
+                   "active_experts": r["active"], "weight_copies": r["copies"],
                    "gate_up_tile_m": None if plan13 is None else plan13.tile_m,
                    "gate_up_split_k": None if plan13 is None else plan13.split_k},
-        "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
-        "event_total_us": round(event_total, 2),
+        "stages_us": {k: round(v, 2) for k, v in r["stage_us"].items()},
+        "event_total_us": round(r["event_total"], 2),
         "gate_up_plus_down_us": round(gu + dn, 2),
-        "graph_us_per_call": None if graph_us is None else round(graph_us, 2),
-        "weight_GBps_path": round(weight_bytes / (us_call * 1e-6) / 1e9, 1),
-        "weight_GBps_gate_up_plus_down": round(weight_bytes / ((gu + dn) * 1e-6) / 1e9, 1),
-        "tflops_gate_up_plus_down": round((flops13 + flops2) / ((gu + dn) * 1e-6) / 1e12, 2),
-        "roofline": roofline,
-        "cpu_baseline": cpu,
+        "graph_us_per_call": None if r["graph_us"] is None else round(r["graph_us"], 2),
+        "weight_GBps_path": round(r["weight_bytes"] / (us_call * 1e-6) / 1e9, 1),
+        "weight_GBps_gate_up_plus_down": round(r["weight_bytes"] / ((gu + dn) * 1e-6) / 1e9, 1),
+        "frac_hbm_gate_up_plus_down": round(r["weight_bytes"] / ((gu + dn) * 1e-6) / 1e9
+                                            / HBM_PEAK_GBS, 4),
+        "tflops_gate_up_plus_down": round(r["flops"] / ((gu + dn) * 1e-6) / 1e12, 2),
+        "roofline": r["roofline"],
+        "cpu_baseline": r["cpu"],
         "kernel_source_hash": src_hash,
     }
+
+    if args.workload == "decode" and not args.no_prefill:
+        p = run_workload("prefill", args, src_hash)
+        pg, pd, pu = p["gu"], p["dn"], p["us_call"]
+        line["prefill"] = {
+            "workload": workload_name("prefill", p["wl"]),
+            "routed_rows": p["rows"],
+            "us_per_call": round(pu, 2),
+            "stages_us": {k: round(v, 2) for k, v in p["stage_us"].items()},
+            "gate_up_plus_down_us": round(pg + pd, 2),
+            "tflops_gate_up_plus_down": round(p["flops"] / ((pg + pd) * 1e-6) / 1e12, 2),
+            "frac_mfma_gate_up_plus_down": round(p["flops"] / ((pg + pd) * 1e-6) / 1e12
+                                                 / BF16_PEAK_TFLOPS, 4),
+            "tflops_path": round(p["flops"] / (pu * 1e-6) / 1e12, 2),
+            "graph_us_per_call": None if p["graph_us"] is None else round(p["graph_us"], 2),
+            "gate_up_tile_m": p["plan13"].tile_m,
+            "roofline": p["roofline"],
+            "cpu_baseline": p["cpu"],
+        }
     print(json.dumps(line), flush=True)
 
 
-def workload_name(name, wl):
-    return {
-        "decode": "EP8 decode share: 48 local experts, H7168 I2048, 64 tokens x top-8 (~10.7 rows/expert)",
-        "prefill": "EP8 prefill share: 48 local experts, H7168 I2048, 8192 tokens x top-8 over 384",
-        "tp8": "TP8 share: 384 experts, H7168 I256, 1024 tokens x top-8",
-        "masked": "grouped masked EP32 share: 12 experts, 256 rows Zipf(1.2), expected_m 32",
-        "tiny": "tiny: 8 experts, top-2, H256 I128, 16 tokens",
-    }[name]
-
-
-def cpu_baseline(d, wl, workload, budget_s):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
-    import numpy as np
-
-    import oracle
-    oracle.build(force=False)
-    threads = oracle.num_threads()
+def _oracle_call(oracle, d, wl, workload, tokens):
+    """The oracle's whole path on the first `tokens` tokens (or, masked, the
+    whole workload)."""
     if workload == "masked":
         G, max_m = wl.E_local, d["max_m"]
         a3 = d["a3"].reshape(G * max_m, wl.H)
-        t0 = time.perf_counter()
         Z = oracle.silu_mul(oracle.masked_gemm(a3, d["masked_m"], d["codes13"], d["scales13"]))
         Y2 = oracle.masked_gemm(Z, d["masked_m"], d["codes2"], d["scales2"])
         oracle.combine(Y2, d["row_of"], d["topk_weights"])
-        dt = time.perf_counter() - t0
-        return {"value": round(dt * 1e6, 1), "unit": "us/call", "cores": threads, "kind": "oracle",
-                "sample": "the full masked workload, one call"}
-    # tokens sampled so that the run stays inside the time budget (full when it fits)
-    T = wl.T
-    probe = max(1, min(T, 4))
-    t0 = time.perf_counter()
-    oracle.moe_forward(d["X"][:probe], d["topk_ids"][:probe], d["topk_weights"][:probe],
-                       wl.E_global, d["expert_map"], d["codes13"], d["scales13"], d["codes2"],
-                       d["scales2"])
-    per_tok = (time.perf_counter() - t0) / probe
-    n = int(max(probe, min(T, budget_s / max(per_tok, 1e-9))))
-    t0 = time.perf_counter()
+        return
+    # the PREFILL profile's kernel rounds each dequantised weight to bf16 once:
+    # its oracle is the one with bf16-rounded weights (same cost)
+    wmode = 1 if workload == "prefill" else 0
+    n = tokens
     oracle.moe_forward(d["X"][:n], d["topk_ids"][:n], d["topk_weights"][:n], wl.E_global,
-                       d["expert_map"], d["codes13"], d["scales13"], d["codes2"], d["scales2"])
-    dt = time.perf_counter() - t0
-    return {"value": round(dt * 1e6 * T / n, 1), "unit": "us/call", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{n} of {T} tokens of the same workload (time scaled to the full call)",
-            "measured_s": round(dt, 2)}
+                       d["expert_map"], d["codes13"], d["scales13"], d["codes2"], d["scales2"],
+                       wmode=wmode)
+
+
+def _timed_leg(oracle, d, wl, workload, budget_s):
+    """Oracle seconds for as many tokens as fit in about budget_s (the whole
+    call when it fits), scaled to one call."""
+    T = wl.T
+    if workload == "masked":
+        t0 = time.perf_counter()
+        _oracle_call(oracle, d, wl, workload, T)
+        dt = time.perf_counter() - t0
+        return dt * 1e6, "the full masked workload, one call", dt
+    # grow the sample until it takes about the budget (or covers the call):
+    # a short probe overestimates the time per token (fixed costs)
+    n = max(1, min(T, 4))
+    while True:
+        t0 = time.perf_counter()
+        _oracle_call(oracle, d, wl, workload, n)
+        dt = time.perf_counter() - t0
+        if n >= T or dt >= 0.5 * budget_s:
+            break
+        n = int(min(T, max(n + 1, n * budget_s / max(dt, 1e-6))))
+    return dt * 1e6 * T / n, f"first {n} of {T} tokens of the same workload (time scaled to the full call)", dt
+
+
+def cpu_baseline(d, wl, workload, budget_s):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    once on all the threads OpenMP gives it, once on one thread."""
+    import oracle
+    oracle.build(force=False)
+    threads = oracle.num_threads()
+    try:
+        host_cpus = len(os.sched_getaffinity(0))
+    except AttributeError:
+        host_cpus = os.cpu_count()
+    value, sample, dt = _timed_leg(oracle, d, wl, workload, budget_s)
+    oracle.set_num_threads(1)
+    try:
+        value1, sample1, dt1 = _timed_leg(oracle, d, wl, workload, budget_s / 3)
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": round(value, 1), "unit": "us/call", "cores": threads, "kind": "oracle",
+            "sample": sample, "measured_s": round(dt, 2), "cpu_model": cpu_model(),
+            "host_cpus": host_cpus,
+            "single_thread": {"value": round(value1, 1), "unit": "us/call", "cores": 1,
+                              "sample": sample1, "measured_s": round(dt1, 2)}}
 
 
 if __name__ == "__main__":
