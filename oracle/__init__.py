@@ -222,6 +222,23 @@ def masked_gemm(a3, masked_m, codes, scales, wmode=0, out=None):
     return out
 
 
+def contiguous_gemm(a2, m_indices, codes, scales, wmode=0, out=None):
+    """Grouped contiguous layout: a2 [m, K] bf16, m_indices int32 [m] (expert
+    of each row, -1 on padding) -> out [m, N]; rows whose index is not an
+    expert are left as they are in `out` (zeros when out is None)."""
+    a2 = _c(a2, np.uint16)
+    mi = _c(m_indices, np.int32)
+    G, N, _ = codes.shape
+    m, K = a2.shape
+    assert mi.shape == (m,)
+    if out is None:
+        out = np.zeros((m, N), dtype=np.uint16)
+    _load().oracle_contiguous_gemm(_p(a2), _p(mi), ctypes.c_int64(m), G,
+                                   _p(_c(codes, np.int32)), _p(_c(scales, np.uint16)), N, K,
+                                   wmode, _p(out))
+    return out
+
+
 def moe_forward(X, topk_ids, topk_weights, E_global, expert_map, codes13, scales13,
                 codes2, scales2, wmode=0, intermediates=False):
     X = _c(X, np.uint16)

@@ -372,6 +372,26 @@ void oracle_masked_gemm(const uint16_t* a3, const int32_t* masked_m, int G, int 
                         0, 0, out);
 }
 
+// Grouped contiguous layout (Chord page, "Grouped SM90 kernels": the
+// contiguous prefill entry takes a2 [m, K] with rows concatenated per expert,
+// each expert's rows padded to a 128-row boundary, and m_indices int32 [m]
+// naming each row's expert, -1 on padding rows; the output is [m, N]; Figure
+// 3 shows where that padding lives).  For every row r with
+// 0 <= m_indices[r] < G: out[r, :] = bf16( A[r, :] . w[m_indices[r]]^T ) in
+// fp32 ascending K; every other row is left untouched.
+void oracle_contiguous_gemm(const uint16_t* a2, const int32_t* m_indices, int64_t m, int G,
+                            const uint32_t* codes, const uint16_t* scales, int N, int K,
+                            int wmode, uint16_t* out) {
+    std::vector<int32_t> a_row(m), expert(m);
+    for (int64_t r = 0; r < m; ++r) {
+        a_row[r] = static_cast<int32_t>(r);
+        const int32_t e = m_indices[r];
+        expert[r] = (e >= 0 && e < G) ? e : -1;
+    }
+    oracle_grouped_gemm(a2, a_row.data(), expert.data(), m, codes, scales, G, N, K, wmode, 0, 0,
+                        out);
+}
+
 // Whole indexed path O4 -> O5 -> O6 -> O7 in the slot-indexed layout.
 // Intermediates may be NULL; when given they are [T*k, 2I], [T*k, I], [T*k, H]
 // (rows of non-local slots are zero).

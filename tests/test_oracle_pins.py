@@ -450,3 +450,68 @@ def test_tiles_cover_each_expert_segment_in_order(T, k, Eg, El, bm, tm):
             want.append([e, piece[0], len(piece), 0])
         p = seg_end
     assert tiles.tolist() == want
+
+
+# ------------------------------------------------ grouped contiguous layout ----
+
+def _contiguous_layout(counts, align=128):
+    """m_indices of the contiguous layout: each expert's rows concatenated,
+    padded to a multiple of `align` with -1 (experts with no rows take no
+    space)."""
+    mi = []
+    for e, c in enumerate(counts):
+        if c == 0:
+            continue
+        p = -(-c // align) * align
+        mi += [e] * c + [-1] * (p - c)
+    return np.array(mi, np.int32)
+
+
+def test_contiguous_exactness_invariant_and_padding_rows_untouched():
+    """Integer activations and power-of-two scales make every product and sum
+    exact, so each valid row is the exact integer-arithmetic product rounded
+    once to bf16; padding rows (NaN-poisoned activations, index -1) keep the
+    output's previous contents."""
+    rng = np.random.default_rng(21)
+    G, K, N = 4, 128, 32
+    counts = [5, 0, 130, 17]
+    mi = _contiguous_layout(counts)
+    m = mi.size
+    assert m == 128 + 256 + 128
+    Ai = rng.integers(-4, 5, size=(m, K))
+    A = synth.bf16_trunc(Ai.astype(np.float32))
+    A[mi < 0] = 0x7FC0
+    codes = rng.integers(0, 2**32, size=(G, N, K // 8), dtype=np.uint32).view(np.int32)
+    scales = synth.bf16_trunc(np.exp2(-rng.integers(6, 9, size=(G, N, K // 32))).astype(np.float32))
+    out = oracle.contiguous_gemm(A, mi, codes, scales, out=np.full((m, N), 0xABCD, np.uint16))
+    for r in range(m):
+        e = mi[r]
+        if e < 0:
+            assert np.all(out[r] == 0xABCD)
+            continue
+        want = _exact_gemm(Ai[r][None], codes[e], scales[e], K)[0]
+        assert np.array_equal(out[r], np.array([bf16_of_exact(v) for v in want], np.uint16))
+
+
+@pytest.mark.parametrize("c", [0, 9, 32, 63])
+def test_contiguous_one_hot_rows_read_their_own_expert(c):
+    """A row that is the unit vector e_c reads out column c of its own
+    expert's dequantised matrix: (q[e, n, c] - 8) * s[e, n, c / 32], rounded
+    to bf16 (rows of three experts, and of an index past the experts, which is
+    treated as padding)."""
+    rng = np.random.default_rng(30 + c)
+    G, K, N = 3, 64, 16
+    mi = np.array([2, 2, 0, 1, 1, 1, -1, 7], np.int32)
+    A = np.zeros((mi.size, K), np.uint16)
+    A[:, c] = 0x3F80
+    codes = rng.integers(0, 2**32, size=(G, N, K // 8), dtype=np.uint32).view(np.int32)
+    scales = synth.random_scales(rng, G, N, K)
+    out = oracle.contiguous_gemm(A, mi, codes, scales, out=np.full((mi.size, N), 0x1111, np.uint16))
+    q = signed_q(codes, K)[:, :, c]
+    s = f32_of_bf16(scales[:, :, c // 32]).astype(np.float64)
+    for r, e in enumerate(mi):
+        if e < 0 or e >= G:
+            assert np.all(out[r] == 0x1111)
+        else:
+            want = np.array([bf16_of_exact(v) for v in q[e] * s[e]], np.uint16)
+            assert np.array_equal(out[r], want)
