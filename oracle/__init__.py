@@ -239,6 +239,37 @@ def contiguous_gemm(a2, m_indices, codes, scales, wmode=0, out=None):
     return out
 
 
+def router_topk(logits, k):
+    """Router logits float32 [T, E] -> (topk_ids int32 [T, k], weights float32
+    [T, k]): largest logits first (ties: lower id first), softmax over the k
+    selected logits."""
+    lg = _c(logits, np.float32)
+    T, E = lg.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float32)
+    _load().oracle_router_topk(_p(lg), T, E, k, _p(ids), _p(w))
+    return ids, w
+
+
+def indexed_to_masked(X, topk_ids, E_global, expert_map, E_local, max_m, a3=None):
+    """Place each local slot's activation row into the grouped masked layout.
+    Returns (a3 [E_local * max_m, H], masked_m [E_local], row_of [T*k],
+    dropped); rows of a3 not written keep their contents (zeros when a3 is
+    None)."""
+    X = _c(X, np.uint16)
+    ids = _c(topk_ids, np.int32)
+    T, k = ids.shape
+    H = X.shape[1]
+    if a3 is None:
+        a3 = np.zeros((E_local * max_m, H), dtype=np.uint16)
+    mm = np.empty(E_local, dtype=np.int32)
+    row_of = np.empty(T * k, dtype=np.int32)
+    dropped = _load().oracle_indexed_to_masked(_p(X), H, _p(ids), T, k, E_global,
+                                               _p(_c(expert_map, np.int32)), E_local, max_m,
+                                               _p(a3), _p(mm), _p(row_of))
+    return a3, mm, row_of, int(dropped)
+
+
 def moe_forward(X, topk_ids, topk_weights, E_global, expert_map, codes13, scales13,
                 codes2, scales2, wmode=0, intermediates=False):
     X = _c(X, np.uint16)

@@ -38,9 +38,11 @@
 // Build: g++ -O2 -std=c++17 -fopenmp -ffp-contract=off -shared -fPIC
 // (-ffp-contract=off keeps every multiply and add a separate rounding step.)
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <numeric>
 #include <vector>
 
 #ifdef _OPENMP
@@ -390,6 +392,64 @@ void oracle_contiguous_gemm(const uint16_t* a2, const int32_t* m_indices, int64_
     }
     oracle_grouped_gemm(a2, a_row.data(), expert.data(), m, codes, scales, G, N, K, wmode, 0, 0,
                         out);
+}
+
+// ---- the step before the expert GEMMs: routing ----------------------------
+//
+// Router top-k (the pages name an optimised expert routing step ahead of the
+// grouped GEMMs and keep it outside their timed unit; the path's weights are
+// the softmax of the selected experts' router logits).  For each token t: the
+// k experts with the largest logits, largest first, equal logits taken in
+// ascending expert id (a stable sort of the ids by decreasing logit); weight j
+// = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k selected logits, in fp64,
+// rounded once to fp32.  This equals a softmax over all experts followed by
+// top-k and renormalisation over the k kept.  Logits are finite.
+void oracle_router_topk(const float* logits, int T, int E, int k, int32_t* ids, float* weights) {
+    std::vector<int> order(E);
+    for (int t = 0; t < T; ++t) {
+        const float* l = logits + static_cast<int64_t>(t) * E;
+        std::iota(order.begin(), order.end(), 0);
+        std::stable_sort(order.begin(), order.end(), [l](int a, int b) { return l[a] > l[b]; });
+        const double top = l[order[0]];
+        double den = 0.0;
+        for (int j = 0; j < k; ++j) den += std::exp(static_cast<double>(l[order[j]]) - top);
+        for (int j = 0; j < k; ++j) {
+            ids[static_cast<int64_t>(t) * k + j] = order[j];
+            weights[static_cast<int64_t>(t) * k + j] =
+                static_cast<float>(std::exp(static_cast<double>(l[order[j]]) - top) / den);
+        }
+    }
+}
+
+// Indexed routing -> grouped masked layout (the pages' masked dispatch takes
+// rows already placed per expert, [G, max_m, K] with the valid count of each
+// expert in masked_m; this is the placement, from topk_ids).  Slots f = t*k +
+// j in ascending order; the i-th local slot of expert e goes to row e*max_m +
+// i when i < max_m: a3 row = X[f / k], row_of[f] = e*max_m + i.  Non-local
+// slots and slots of rank i >= max_m get row_of[f] = -1 (the latter are
+// dropped); masked_m[e] = min(count_e, max_m).  Rows of a3 not written keep
+// their contents.  Returns the number of dropped local slots.
+int oracle_indexed_to_masked(const uint16_t* X, int H, const int32_t* topk_ids, int T, int top_k,
+                             int E_global, const int32_t* expert_map, int E_local, int max_m,
+                             uint16_t* a3, int32_t* masked_m, int32_t* row_of) {
+    const int64_t slots = static_cast<int64_t>(T) * top_k;
+    std::vector<int32_t> count(E_local, 0);
+    int dropped = 0;
+    for (int64_t f = 0; f < slots; ++f) {
+        row_of[f] = -1;
+        const int e = local_expert(topk_ids, f, E_global, expert_map, E_local);
+        if (e < 0) continue;
+        const int i = count[e]++;
+        if (i >= max_m) {
+            ++dropped;
+            continue;
+        }
+        const int64_t r = static_cast<int64_t>(e) * max_m + i;
+        row_of[f] = static_cast<int32_t>(r);
+        std::memcpy(a3 + r * H, X + (f / top_k) * H, sizeof(uint16_t) * H);
+    }
+    for (int e = 0; e < E_local; ++e) masked_m[e] = count[e] < max_m ? count[e] : max_m;
+    return dropped;
 }
 
 // Whole indexed path O4 -> O5 -> O6 -> O7 in the slot-indexed layout.

@@ -515,3 +515,83 @@ def test_contiguous_one_hot_rows_read_their_own_expert(c):
         else:
             want = np.array([bf16_of_exact(v) for v in q[e] * s[e]], np.uint16)
             assert np.array_equal(out[r], want)
+
+
+# ------------------------------------------------------------- routing step ----
+
+def test_router_equal_logits_give_lowest_ids_and_equal_weights():
+    """All logits equal: the k lowest expert ids, each weight exactly 1/k (k a
+    power of two)."""
+    ids, w = oracle.router_topk(np.full((3, 12), 0.75, np.float32), 4)
+    assert ids.tolist() == [[0, 1, 2, 3]] * 3
+    assert np.all(w == np.float32(0.25))
+
+
+def test_router_two_experts_closed_form():
+    """Two selected logits ln 3 apart: weights 3/4 and 1/4 (to fp32 rounding of
+    the logits), largest first; the unselected logits play no part."""
+    lg = np.array([[-5.0, np.log(3.0), 0.0, -7.0]], np.float32)
+    ids, w = oracle.router_topk(lg, 2)
+    assert ids.tolist() == [[1, 2]]
+    assert abs(float(w[0, 0]) - 0.75) < 1e-6 and abs(float(w[0, 1]) - 0.25) < 1e-6
+
+
+def test_router_matches_full_softmax_then_topk_then_renormalise():
+    """Softmax over all experts, keep the k largest probabilities (stable by
+    id), renormalise: the same experts in the same order and the same weights
+    within fp32 rounding (numpy fp64 as the second formulation)."""
+    rng = np.random.default_rng(40)
+    T, E, k = 50, 384, 8
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    lg[0, 10] = lg[0, 20] = lg[0, 5] = 9.0                 # a tie among the largest
+    ids, w = oracle.router_topk(lg, k)
+    p = np.exp(lg.astype(np.float64) - lg.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    want = np.stack([np.lexsort((np.arange(E), -p[t]))[:k] for t in range(T)])
+    assert np.array_equal(ids, want)
+    assert ids[0, :3].tolist() == [5, 10, 20]
+    sel = np.take_along_axis(p, want, 1)
+    assert np.allclose(w, sel / sel.sum(1, keepdims=True), rtol=2e-7, atol=0)
+    assert np.allclose(w.sum(1), 1.0, atol=1e-6)
+
+
+def _place_brute_force(X, ids, em, E, max_m):
+    """Independent placement: local slots grouped by expert with a stable
+    argsort, rank within the expert from the sorted order."""
+    T, k = ids.shape
+    g = ids.ravel()
+    loc = np.where((g >= 0) & (g < len(em)), em[np.clip(g, 0, len(em) - 1)], -1)
+    f_local = np.nonzero(loc >= 0)[0]
+    order = f_local[np.argsort(loc[f_local], kind="stable")]
+    row_of = np.full(T * k, -1, np.int64)
+    a3 = np.full((E * max_m, X.shape[1]), 0xDEAD, np.uint16)
+    mm = np.zeros(E, np.int64)
+    dropped = 0
+    for e in range(E):
+        fs = order[loc[order] == e]
+        mm[e] = min(fs.size, max_m)
+        dropped += max(0, fs.size - max_m)
+        for i, f in enumerate(fs[:max_m]):
+            row_of[f] = e * max_m + i
+            a3[e * max_m + i] = X[f // k]
+    return a3, mm, row_of, dropped
+
+
+@pytest.mark.parametrize("T,k,Eg,E,max_m", [(20, 3, 10, 4, 32), (64, 8, 40, 12, 16), (5, 2, 6, 6, 1)])
+def test_indexed_to_masked_matches_brute_force(T, k, Eg, E, max_m):
+    """Every local slot lands in its expert's rows in ascending slot order;
+    slots past max_m are dropped and counted; non-local and out-of-range ids
+    map to -1; rows never written keep their contents."""
+    rng = np.random.default_rng(T + max_m)
+    ids = np.argsort(rng.random((T, Eg)), axis=1)[:, :k].astype(np.int32)
+    ids[0, 0] = -3
+    em = np.full(Eg, -1, np.int32)
+    em[rng.permutation(Eg)[:E]] = rng.permutation(E).astype(np.int32)
+    X = synth.random_activations(rng, T, 64)
+    a3, mm, row_of, dropped = oracle.indexed_to_masked(
+        X, ids, Eg, em, E, max_m, a3=np.full((E * max_m, 64), 0xDEAD, np.uint16))
+    wa3, wmm, wrow, wdrop = _place_brute_force(X, ids, em, E, max_m)
+    assert np.array_equal(a3, wa3) and np.array_equal(mm, wmm)
+    assert np.array_equal(row_of, wrow) and dropped == wdrop
+    if max_m == 1:
+        assert dropped > 0
