@@ -5,8 +5,9 @@
 
 One step = one call of the whole path on one batch of seeded synthetic input
 already resident in HBM: routing sort (align) -> gate/up GEMM with SiLU*gate in
-its epilogue -> down GEMM -> top-k combine (for the masked workload: the two
-GEMMs and the combine).  W untimed warm-up steps, then exactly K timed steps
+its epilogue -> down GEMM -> top-k combine (for the masked and contiguous
+workloads: the two GEMMs, then the combine).  With --combine fused the
+combine runs in the down GEMM's epilogue.  W untimed warm-up steps, then exactly K timed steps
 between two device synchronisations.  One JSON line is printed.
 
 The headline workload (default) is the decode share of a Kimi-K2-like layer on
@@ -49,10 +50,13 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode",
-                   choices=["decode", "prefill", "tp8", "masked", "tiny"])
+                   choices=["decode", "prefill", "tp8", "masked", "contiguous", "tiny"])
     p.add_argument("--copies", type=int, default=2, help="prepacked weight copies rotated per call")
     p.add_argument("--no-prefill", action="store_true",
                    help="do not add the prefill sub-object to the decode line")
+    p.add_argument("--combine", choices=["separate", "fused"], default="separate",
+                   help="indexed path: top-k combine as its own kernel or in the down GEMM's "
+                        "epilogue (streaming kernel only)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=12.0,
@@ -103,6 +107,7 @@ def workload_name(name, wl):
         "prefill": "EP8 prefill share: 48 local experts, H7168 I2048, 8192 tokens x top-8 over 384",
         "tp8": "TP8 share: 384 experts, H7168 I256, 1024 tokens x top-8",
         "masked": "grouped masked EP32 share: 12 experts, 256 rows Zipf(1.2), expected_m 32",
+        "contiguous": "grouped contiguous EP8 prefill share: 48 experts x 128 rows, H7168 I2048",
         "tiny": "tiny: 8 experts, top-2, H256 I128, 16 tokens",
     }[name]
 
@@ -125,7 +130,8 @@ def run_workload(name, args, src_hash, cpu_legs=True):
     t0 = time.time()
     d = synth.make_workload(name, seed=0)
     wl = d["wl"]
-    profile = m.PROFILE_PREFILL if name == "prefill" else m.PROFILE_DECODE
+    mfma_bound = name in ("prefill", "contiguous")
+    profile = m.PROFILE_PREFILL if mfma_bound else m.PROFILE_DECODE
     print(f"[bench] workload {name}: generated inputs in {time.time() - t0:.1f}s",
           file=sys.stderr, flush=True)
 
@@ -144,10 +150,14 @@ def run_workload(name, args, src_hash, cpu_legs=True):
     tw = to_dev(d["topk_weights"])
     em = None if d["expert_map"] is None else to_dev(d["expert_map"])
     masked = name == "masked"
+    contig = name == "contiguous"
 
     # local routed rows and active experts (host-side knowledge of the draw)
     if masked:
         counts = d["masked_m"].astype(np.int64)
+    elif contig:
+        mi_h = d["m_indices"]
+        counts = np.bincount(mi_h[mi_h >= 0], minlength=wl.E_local).astype(np.int64)
     else:
         flat = d["topk_ids"].ravel()
         loc = flat if d["expert_map"] is None else d["expert_map"][flat]
@@ -177,20 +187,35 @@ def run_workload(name, args, src_hash, cpu_legs=True):
                     ("down", lambda: m._capi.w4a16_moe_w4a16_gemm(da)),
                     ("combine", lambda: m._capi.w4a16_moe_combine(
                         p.Y2, p.Y2.shape[0], H, row_of, tw, wl.T, wl.top_k, p.out))]
-    else:
-        paths = [m.IndexedPath(w13, w2, wl.T, wl.top_k, wl.E_global, rows_hint=rows, device=dev)
+    elif contig:
+        a2 = to_dev(d["a2"])
+        mi = to_dev(d["m_indices"])
+        row_of = to_dev(d["row_of"])
+        paths = [m.ContiguousPath(w13, w2, d["m_indices"].size, wl.T, wl.top_k, device=dev)
                  for (w13, w2) in copies]
 
         def stages(p):
-            ga, da = p.stage_args(X)
+            ga, da = p.gate_up_args(a2, mi), p.down_args(mi)
+            return [("gate_up", lambda: m._capi.w4a16_moe_w4a16_gemm(ga)),
+                    ("down", lambda: m._capi.w4a16_moe_w4a16_gemm(da)),
+                    ("combine", lambda: m._capi.w4a16_moe_combine(
+                        p.Y2, p.Y2.shape[0], H, row_of, tw, wl.T, wl.top_k, p.out))]
+    else:
+        fused = args.combine == "fused" and profile == m.PROFILE_DECODE
+        paths = [m.IndexedPath(w13, w2, wl.T, wl.top_k, wl.E_global, rows_hint=rows, device=dev,
+                               fuse_combine=fused)
+                 for (w13, w2) in copies]
+
+        def stages(p):
+            ga, da = p.stage_args(X, tw)
             st = [("align", lambda: p.routing.align(ids, wl.E_global, em)),
                   ("gate_up", lambda: m._capi.w4a16_moe_w4a16_gemm(ga))]
             if p.separate_act:
                 st.append(("act", lambda: p.act()))
-            return st + [("down", lambda: m._capi.w4a16_moe_w4a16_gemm(da)),
-                         ("combine", lambda: m._capi.w4a16_moe_combine(
-                             p.Y2, p.Y2.shape[0], H, p.routing.row_of, tw, wl.T, wl.top_k,
-                             p.out))]
+            st.append(("down", lambda: m._capi.w4a16_moe_w4a16_gemm(da)))
+            if not p.fuse_combine:
+                st.append(("combine", lambda: p.combine(tw)))
+            return st
 
     # pre-built argument structs (workspaces resolved once): the timed loop
     # only launches
@@ -267,10 +292,10 @@ def run_workload(name, args, src_hash, cpu_legs=True):
     # the dominant kernel is the gate/up GEMM; its algorithmic HBM bytes per
     # launch are the active experts' codes + scales, the activations read once
     # and the routed rows' outputs written once
-    x_bytes = (rows if masked else wl.T) * H * 2
+    x_bytes = (rows if masked or contig else wl.T) * H * 2
     out_bytes = rows * I * 2           # Z: SiLU*gate is applied in the epilogue
     alg_bytes13 = bytes13 + x_bytes + out_bytes
-    if name == "prefill":
+    if mfma_bound:
         bound, unit_rf = "mfma", "TFLOP/s"
         achieved = flops13 / (gu * 1e-6) / 1e12
         peak = BF16_PEAK_TFLOPS
@@ -279,13 +304,16 @@ def run_workload(name, args, src_hash, cpu_legs=True):
         achieved = alg_bytes13 / (gu * 1e-6) / 1e9
         peak = HBM_PEAK_GBS
     plan13 = paths[0].plan if not masked else None
+    kname = {"prefill": "k_gemm_large (gate/up GEMM of the PREFILL profile, SiLU*gate in its "
+                        "epilogue: one launch per call)",
+             "contiguous": "k_gemm_large (gate/up GEMM, grouped contiguous layout, SiLU*gate in "
+                           "its epilogue: one launch per call)"}.get(
+        name, "k_gemm_small (gate/up GEMM with SiLU*gate epilogue and in-kernel split-K fix-up: "
+              "one launch per call)")
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit_rf,
                 "frac": round(achieved / peak, 4),
                 "traffic": traffic_from_profiles(name, src_hash),
-                "kernel": ("k_gemm_large (gate/up GEMM of the PREFILL profile, SiLU*gate in its "
-                           "epilogue: one launch per call)" if name == "prefill" else
-                           "k_gemm_small (gate/up GEMM with SiLU*gate epilogue and in-kernel "
-                           "split-K fix-up: one launch per call)"),
+                "kernel": kname,
                 "algorithmic_per_launch": alg_bytes13 if bound == "hbm" else flops13,
                 "launch_us": round(gu, 2)}
 
@@ -388,8 +416,9 @@ def _oracle_call(oracle, d, wl, workload, tokens):
         oracle.combine(Y2, d["row_of"], d["topk_weights"])
         return
     # the PREFILL profile's kernel rounds each dequantised weight to bf16 once:
-    # its oracle is the one with bf16-rounded weights (same cost)
-    wmode = 1 if workload == "prefill" else 0
+    # its oracle is the one with bf16-rounded weights (same cost); the
+    # contiguous workload computes the same rows as the indexed path
+    wmode = 1 if workload in ("prefill", "contiguous") else 0
     n = tokens
     oracle.moe_forward(d["X"][:n], d["topk_ids"][:n], d["topk_weights"][:n], wl.E_global,
                        d["expert_map"], d["codes13"], d["scales13"], d["codes2"], d["scales2"],

@@ -169,6 +169,9 @@ typedef struct {
     int32_t tiles_cap;
     int32_t* tile_count;        /* [1] (required when tiles != NULL) */
     int32_t tile_m;             /* rows per tile, multiple of 16, <= 256 */
+    int32_t* expert_offsets;    /* [E_local + 1] or NULL: start of each local
+                                   expert's padded segment in sorted_ids, then
+                                   num_tokens_padded */
 } w4a16_routing;
 
 #define W4A16_ALIGN_VALIDATE 0x1u  /* read routing back and report ROUTING for
@@ -192,13 +195,73 @@ w4a16_status w4a16_moe_align(const int32_t* topk_ids, int32_t T, int32_t top_k,
                              void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* The step before the expert GEMMs: router top-k (the pages list an        */
+/* optimised expert routing step ahead of the grouped GEMMs, outside their   */
+/* timed unit; news.ainew.jp, "vLLM publishes Kimi K3 production support",   */
+/* TL;DR), fused with the routing sort when the sort runs as one workgroup.  */
+/*   logits : device float [T, E_global], finite                            */
+/*   topk_ids [T, top_k] (written): the top_k experts with the largest        */
+/*            logits, largest first, equal logits in ascending expert id     */
+/*   topk_weights [T, top_k] (written): softmax over the selected logits,     */
+/*            e^(l_j - l_0) / sum_i e^(l_i - l_0) in fp32, summed in j order  */
+/* 1 <= E_global <= 1024, 1 <= top_k <= min(64, E_global); INVALID_ARG else. */
+/* ------------------------------------------------------------------------ */
+w4a16_status w4a16_moe_router_topk(const float* logits, int32_t T, int32_t E_global,
+                                   int32_t top_k, int32_t* topk_ids, float* topk_weights,
+                                   void* stream);
+
+/* Router top-k, then w4a16_moe_align on its ids (same arguments, outputs
+ * and errors).  One launch when the sort runs as one workgroup (up to 2047
+ * routed slots at 16 wavefronts: decode sizes), else the router kernel then
+ * the sort. */
+w4a16_status w4a16_moe_route_align(const float* logits, int32_t T, int32_t E_global,
+                                   int32_t top_k, const int32_t* expert_map, int32_t E_local,
+                                   int32_t block_m, const w4a16_routing* routing,
+                                   int32_t* topk_ids, float* topk_weights, uint32_t flags,
+                                   void* stream);
+
+/* Indexed routing -> grouped masked layout, on the device (Chord page,
+ * "Grouped SM90 kernels": the masked dispatch takes rows already placed per
+ * expert, [G, max_m, K], with each expert's valid count in masked_m; "vLLM
+ * integration": routing counts stay on the device).  Local slots f = t*k + j
+ * in ascending order: the i-th local slot of expert e goes to row e*max_m + i
+ * when i < max_m, a3 row = X[f / k] and row_of[f] = e*max_m + i; non-local
+ * slots and ranks i >= max_m get row_of[f] = -1 (the latter are dropped and
+ * counted in *dropped); masked_m[e] = min(count_e, max_m).  Rows of a3 not
+ * written keep their contents.
+ *   X       : device bf16 [X_rows >= T, H], H % 8 == 0, 16-byte aligned
+ *   scratch : caller-owned routing buffers for a sort with block_m = 1
+ *             (capacities from w4a16_moe_align_capacity(T, top_k, E_local,
+ *             1, 0)); row_of and expert_offsets required, tiles ignored;
+ *             overwritten by the call
+ *   a3      : device bf16 [E_local * max_m, H], 16-byte aligned
+ *   masked_m: device int32 [E_local]; row_of: device int32 [T * top_k];
+ *   dropped : device int32 [1] or NULL
+ * Two launches on `stream` (the sort, then the placement). */
+w4a16_status w4a16_moe_indexed_to_masked(const uint16_t* X, int64_t X_rows, int32_t H,
+                                         const int32_t* topk_ids, int32_t T, int32_t top_k,
+                                         int32_t E_global, const int32_t* expert_map,
+                                         int32_t E_local, int32_t max_m,
+                                         const w4a16_routing* scratch, uint16_t* a3,
+                                         int32_t* masked_m, int32_t* row_of, int32_t* dropped,
+                                         void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Grouped W4A16 GEMM (Chord page, "H200 prefill and TP8", "H200 and        */
 /* Blackwell indexed decode", "Grouped SM90 kernels").                       */
 /*   out[p, n] = bf16( sum_c A[row(p), c] * (q[e,n,c] - 8) * s[e,n,c/32] )   */
 /* with fp32 accumulation, for every routed row p of expert e.  The INT4     */
 /* codes are unpacked and scaled in registers; no dequantised copy exists.   */
 /* ------------------------------------------------------------------------ */
-typedef enum { W4A16_LAYOUT_INDEXED = 0, W4A16_LAYOUT_MASKED = 1 } w4a16_layout;
+typedef enum {
+    W4A16_LAYOUT_INDEXED = 0,    /* rows found through sorted_ids (vLLM routing) */
+    W4A16_LAYOUT_MASKED = 1,     /* [G * max_m] rows, masked_m valid per expert */
+    W4A16_LAYOUT_CONTIGUOUS = 2  /* [m] rows concatenated per expert, each expert's
+                                    segment padded to a multiple of 128 rows, the
+                                    expert of each row in m_indices (-1 on padding)
+                                    ("Grouped SM90 kernels", contiguous prefill and
+                                    Figure 3).  PREFILL-profile weights only */
+} w4a16_layout;
 
 /* How an indexed row position p finds its activation row. */
 typedef enum {
@@ -288,6 +351,30 @@ typedef struct {
        concurrently. */
     void* workspace;
     uint64_t workspace_bytes;
+    /* CONTIGUOUS: device int32 [A_rows]: expert of each row of A (and of out),
+       -1 on padding.  Every expert's segment starts on a 128-row boundary, so
+       a block of 128 (or 64) rows holds one expert: the expert of a block is
+       that of its first row (a block starting with padding is skipped), and
+       only the block's rows whose index equals it are stored.  A is [m, K] with
+       m = A_rows; out is [m, N] (N/2 with SILU_MUL), out_rows >= m.  split_k
+       overrides are refused (MODE_MISMATCH). */
+    const int32_t* m_indices;
+    /* Fused top-k weighted combine (the down GEMM's epilogue; Chord page,
+       "Measurements": the expert outputs are merged per token after the down
+       GEMM).  When comb_out != NULL the call also writes
+         comb_out[t, n] = bf16( sum_{j<k, row_of[t*k+j] >= 0} w[t, j] * out[row_of[t*k+j], n] )
+       in fp32, j ascending, on the bf16 rows it stores: the same bits as
+       w4a16_moe_combine on those rows.  The last of a token's rows to be
+       stored (per group of 256 columns) triggers its sum, so nothing waits
+       and the order of the sum is fixed; tokens with no local slot get +0.
+       Needs INDEXED with a tile table, OROW_POSITION, EPI_STORE, bf16 output
+       (no F32_OUT); out then holds the compact rows [sorted_cap, N] the sums
+       read.  Arrival counters (T * ceil(N / 256) ints) join the workspace's
+       counters. */
+    uint16_t* comb_out;             /* device bf16 [comb_T, N] */
+    const int32_t* comb_row_of;     /* device int32 [comb_T * top_k]: row_of from w4a16_moe_align */
+    const float* comb_weights;      /* device float [comb_T, top_k] */
+    int32_t comb_T;                 /* tokens */
 } w4a16_gemm_args;
 
 /* Workspace needed by this GEMM call (0 when none).  Host call. */
@@ -359,12 +446,20 @@ w4a16_status w4a16_moe_combine(const uint16_t* y, int64_t y_rows, int32_t H,
 /* constants are this library's own, measured on gfx950.                    */
 /* ------------------------------------------------------------------------ */
 typedef struct {
-    int32_t block_m;   /* align granule (sorted_ids padding) */
-    int32_t tile_m;    /* rows per GEMM tile */
-    int32_t split_k;   /* K splits (1 = none) */
-    int32_t kernel;    /* 1 = small-M streaming kernel, 2 = large-M LDS kernel */
+    int32_t block_m;     /* align granule (sorted_ids padding) */
+    int32_t tile_m;      /* rows per GEMM tile */
+    int32_t split_k;     /* K splits (1 = none) */
+    int32_t kernel;      /* 1 = small-M streaming kernel, 2 = large-M LDS kernel */
+    int32_t ring_groups; /* streaming kernel: K groups of codes in flight per
+                            wavefront, 8 (three workgroups per CU up to 32-row
+                            tiles) or 16; 0 for the large-M kernel */
 } w4a16_plan;
 
+/* INDEXED: rows_hint = routed rows expected on this GPU (0 = unknown), tile_m
+ * 0 = choose.  MASKED: expected_m > 0.  CONTIGUOUS (PREFILL profile, else
+ * MODE_MISMATCH): rows_hint = m; block_m is the 128-row segment alignment,
+ * tile_m is 128 when ceil(m / 128) blocks times the column pairs of the
+ * large-M kernel fill the 256 compute units, else 64. */
 w4a16_status w4a16_plan_gemm(const w4a16_desc* desc, int32_t layout, int32_t rows_hint,
                              int32_t expected_m, int32_t tile_m, w4a16_plan* plan /* host out */);
 

@@ -27,6 +27,10 @@ Workloads (the Kimi-K2.x-like serving shapes used throughout):
   masked   grouped-masked decode share: 12 local experts (EP32), 256 routed
            rows with Zipf(1.2) counts, 3 empty experts, padded to a multiple
            of expected_m = 32
+  contiguous  grouped-contiguous prefill share: 48 local experts (EP8), 768
+           tokens x top-8 over the local experts with exactly 128 rows per
+           expert, dispatched into the contiguous layout (rows concatenated
+           per expert, segments padded to 128 rows, m_indices)
 """
 from __future__ import annotations
 
@@ -50,6 +54,7 @@ class Workload:
     zipf_s: float = 0.0
     empty_experts: int = 0
     expected_m: int = 0
+    rows_per_expert: int = 0
 
 
 WORKLOADS = {
@@ -64,6 +69,8 @@ WORKLOADS = {
     "masked": Workload("masked", T=256, top_k=8, E_global=384, E_local=12, H=7168,
                        I=2048, routing="masked_zipf", masked_rows=256, zipf_s=1.2,
                        empty_experts=3, expected_m=32),
+    "contiguous": Workload("contiguous", T=768, top_k=8, E_global=384, E_local=48, H=7168,
+                           I=2048, routing="balanced_local", rows_per_expert=128),
 }
 
 
@@ -138,6 +145,17 @@ def make_routing(wl: Workload, rng) -> dict:
         w[: wl.E_local] += rng.uniform(-0.3, 0.3, size=wl.E_local)
         keys = np.log(w)[None, :] + rng.gumbel(size=(T, wl.E_global))
         ids = np.argsort(-keys, axis=1, kind="stable")[:, :k].astype(np.int32)
+    elif wl.routing == "balanced_local":
+        # every local expert gets exactly T * k / E_local rows: token t takes
+        # experts sigma((b_t + j * step) mod E) for j < k, where the offsets
+        # b_t run over each residue equally often (shuffled) and sigma is a
+        # random relabelling
+        E = wl.E_local
+        step = E // k
+        assert E % k == 0 and T % E == 0 and T * k // E == wl.rows_per_expert
+        b = rng.permutation(np.tile(np.arange(E), T // E))
+        sigma = rng.permutation(E)
+        ids = sigma[(b[:, None] + step * np.arange(k)[None, :]) % E].astype(np.int32)
     elif wl.routing == "masked_zipf":
         return _masked_routing(wl, rng)
     else:
@@ -210,6 +228,43 @@ def place_masked(X: np.ndarray, routing: dict, G: int, poison: bool = True) -> n
     return a3
 
 
+def place_contiguous(X: np.ndarray, topk_ids: np.ndarray, expert_map, E_local: int,
+                     align: int = 128, poison: bool = True) -> dict:
+    """Caller-side dispatch into the grouped contiguous layout.
+
+    Local expert e's routed slots (ascending flat slot f = t*k + j) become
+    consecutive rows holding X[f // k]; each expert's segment is padded to a
+    multiple of `align` rows (experts with no slot take none).  Returns a2
+    [m, H] (padding rows bf16 NaN when poison), m_indices [m] (expert of each
+    row, -1 on padding) and row_of [T*k] (row of slot f, -1 if not local).
+    """
+    T, k = topk_ids.shape
+    flat = topk_ids.ravel()
+    ok = (flat >= 0) & (flat < (len(expert_map) if expert_map is not None else E_local))
+    loc = np.full(flat.size, -1, np.int64)
+    loc[ok] = flat[ok] if expert_map is None else expert_map[flat[ok]]
+    loc[(loc < 0) | (loc >= E_local)] = -1
+    rows, mi = [], []
+    row_of = np.full(T * k, -1, np.int32)
+    m = 0
+    for e in range(E_local):
+        slots = np.nonzero(loc == e)[0]
+        if slots.size == 0:
+            continue
+        p = -(-slots.size // align) * align
+        row_of[slots] = m + np.arange(slots.size, dtype=np.int32)
+        rows.append(slots)
+        mi.append(np.concatenate([np.full(slots.size, e, np.int32),
+                                  np.full(p - slots.size, -1, np.int32)]))
+        m += p
+    m_indices = np.concatenate(mi) if mi else np.zeros(0, np.int32)
+    a2 = np.full((m, X.shape[1]), BF16_NAN if poison else 0, dtype=np.uint16)
+    for slots, mie in zip(rows, mi):
+        start = int(row_of[slots[0]])
+        a2[start:start + slots.size] = X[slots // k]
+    return {"a2": a2, "m_indices": m_indices, "row_of": row_of}
+
+
 def make_weights(E: int, H: int, I: int, seed: int = 0, which=("w13", "w2")) -> dict:
     """W13 codes [E, 2I, H/8] + scales [E, 2I, H/32]; W2 codes [E, H, I/8] + scales."""
     r = _streams(seed)
@@ -235,6 +290,8 @@ def make_workload(name: str, seed: int = 0, weights: bool = True) -> dict:
         d.update(make_weights(wl.E_local, wl.H, wl.I, seed))
     if wl.routing == "masked_zipf":
         d["a3"] = place_masked(d["X"], d, wl.E_local)
+    if wl.routing == "balanced_local":
+        d.update(place_contiguous(d["X"], d["topk_ids"], d["expert_map"], wl.E_local))
     return d
 
 

@@ -334,11 +334,21 @@ def test_plan_rules():
     d13 = host_desc(E=48, N=4096, K=7168)
     d2 = host_desc(E=48, N=7168, K=2048)
     p = capi.w4a16_plan_gemm(d13, capi.W4A16_LAYOUT_INDEXED, 512)       # ~10.7 rows/expert
-    assert p.tile_m == 16 and p.block_m == 16 and p.split_k >= 1
-    # 56 tiles x 16 column quads already exceed one round of resident workgroups: no K split
+    # every expert in one tile of up to 32 rows, the one-stage ring (three
+    # workgroups per CU)
+    assert p.tile_m == 32 and p.block_m == 16 and p.split_k >= 1 and p.ring_groups == 8
+    # 48+ tiles x 16 column quads already fill the resident workgroups: no K split
     assert p.split_k == 1
     p_small = capi.w4a16_plan_gemm(d13, capi.W4A16_LAYOUT_INDEXED, 96)
-    assert p_small.tile_m == 16
+    assert p_small.tile_m == 16 and p_small.ring_groups == 8
+    # ~21 rows per expert, deep K: two-stage ring; K of one record: one-stage ring
+    d13_tp = host_desc(E=24, N=128, K=7168)
+    d2_tp = host_desc(E=24, N=1024, K=256)
+    p_tp = capi.w4a16_plan_gemm(d13_tp, capi.W4A16_LAYOUT_INDEXED, 512)
+    assert p_tp.tile_m == 32 and p_tp.ring_groups == 16
+    assert capi.w4a16_plan_gemm(d2_tp, capi.W4A16_LAYOUT_INDEXED, 512, 0, 32).ring_groups == 8
+    assert capi.w4a16_plan_gemm(host_desc(profile=capi.W4A16_PROFILE_PREFILL, E=2, N=256,
+                                          K=512), capi.W4A16_LAYOUT_INDEXED, 512).ring_groups == 0
     assert p_small.split_k >= p.split_k                                   # fewer tiles -> more splits
     assert capi.w4a16_plan_gemm(d13, capi.W4A16_LAYOUT_INDEXED, 0, tile_m=48).tile_m == 48
     # masked: tiles of expected_m rows, in 16-row steps
@@ -350,3 +360,49 @@ def test_plan_rules():
         capi.W4A16_ERR_INVALID_ARG
     for pl in (p, p_small):
         assert 4096 // 64 * pl.split_k >= 1 and 224 // pl.split_k >= 8
+
+
+def test_contiguous_layout_checks_and_plan():
+    """The grouped contiguous layout runs on PREFILL-profile weights only,
+    needs m_indices and an output of m rows, refuses split_k overrides, and
+    takes 128-row blocks when the grid fills the machine, else 64."""
+    dp = host_desc(profile=capi.W4A16_PROFILE_PREFILL, N=4096, K=64)
+    dd = host_desc(profile=capi.W4A16_PROFILE_DECODE, N=4096, K=64)
+    c = dict(layout=capi.W4A16_LAYOUT_CONTIGUOUS, m_indices=1 << 20, A_rows=2048, out_rows=2048,
+             tiles=None, sorted_ids=None, num_tokens_padded=None)
+    assert capi.w4a16_gemm_workspace_bytes(gemm_args(dp, **c)) == 256     # work-queue block
+    assert ws_status(gemm_args(dd, **c)) == capi.W4A16_ERR_MODE_MISMATCH
+    assert ws_status(gemm_args(dp, **{**c, "m_indices": None})) == capi.W4A16_ERR_INVALID_ARG
+    assert ws_status(gemm_args(dp, **{**c, "split_k": 2})) == capi.W4A16_ERR_MODE_MISMATCH
+    assert ws_status(gemm_args(dp, **{**c, "out_rows": 2047})) == capi.W4A16_ERR_CAPACITY
+    # a plain W13 with the SiLU epilogue stages Y13 [m, N]
+    assert capi.w4a16_gemm_workspace_bytes(gemm_args(dp, epilogue=capi.W4A16_EPI_SILU_MUL, **c)) \
+        == 256 + 2048 * 4096 * 2
+    # N = 4096: 32 chunks of 128 columns, 16 column pairs; 2048 rows = 16 blocks
+    # of 128 -> 256 items fill 256 CUs; 1024 rows would not
+    L = capi.W4A16_LAYOUT_CONTIGUOUS
+    assert capi.w4a16_plan_gemm(dp, L, 2048).tile_m == 128
+    assert capi.w4a16_plan_gemm(dp, L, 1024).tile_m == 64
+    assert capi.w4a16_plan_gemm(dp, L, 2048).kernel == 2
+    assert status_of(capi.w4a16_plan_gemm, dd, L, 2048) == capi.W4A16_ERR_MODE_MISMATCH
+
+
+def test_fused_combine_checks():
+    """The fused combine needs the streaming kernel, the tile table,
+    position-indexed bf16 rows, its routing buffers and comb_T * top_k ==
+    num_slots; its arrival counters join the workspace's counters."""
+    d = host_desc(K=64)
+    fake = 1 << 20
+    c = dict(comb_out=fake, comb_row_of=fake, comb_weights=fake, comb_T=32, top_k=2,
+             num_slots=64)
+    base = capi.w4a16_gemm_workspace_bytes(gemm_args(d))
+    assert capi.w4a16_gemm_workspace_bytes(gemm_args(d, **c)) == base + 256   # 32 tokens x 1 group
+    assert ws_status(gemm_args(d, **{**c, "comb_T": 31})) == capi.W4A16_ERR_INVALID_ARG
+    assert ws_status(gemm_args(d, **{**c, "comb_row_of": None})) == capi.W4A16_ERR_INVALID_ARG
+    assert ws_status(gemm_args(d, orow=capi.W4A16_OROW_SLOT, **c)) == capi.W4A16_ERR_INVALID_ARG
+    assert ws_status(gemm_args(d, flags=capi.W4A16_GEMM_F32_OUT, **c)) == \
+        capi.W4A16_ERR_INVALID_ARG
+    assert ws_status(gemm_args(d, tiles=None, expert_ids=fake, blocks_cap=16, block_m=16, **c)) \
+        == capi.W4A16_ERR_INVALID_ARG
+    dp = host_desc(profile=capi.W4A16_PROFILE_PREFILL, K=64)
+    assert ws_status(gemm_args(dp, **c)) == capi.W4A16_ERR_UNSUPPORTED

@@ -868,3 +868,306 @@ def test_large_kernel_repeated_calls_fresh_buffers(m, H, tile_m):
         nbad.append(int(np.any(host(Y13, np.uint16)[pos] != ref13[f], axis=1).sum()))
     print(f"  bad rows per call {nbad}", flush=True)
     assert not any(nbad)
+
+
+# ------------------------------------------------ grouped contiguous layout ----
+
+def _contiguous_problem(seed, E, H, I, T, k, p=None, exact=False):
+    d = exact_problem(seed, E, H, I, T, k) if exact else synth.random_small(seed, E, H, I, T, k)
+    if p is not None:
+        rng = np.random.default_rng(seed + 1)
+        d["topk_ids"] = np.stack([rng.choice(E, size=k, replace=False, p=p)
+                                  for _ in range(T)]).astype(np.int32)
+    d.update(synth.place_contiguous(d["X"], d["topk_ids"], None, E))
+    return d
+
+
+@pytest.mark.parametrize("E,T,k,want_bm", [(3, 150, 2, 64), (8, 700, 3, 128)])
+def test_contiguous_exact_invariant_and_padding(m, E, T, k, want_bm):
+    """The contiguous layout through the large-M kernel under the exactness
+    invariant: skewed counts (one expert empty, segments padded to 128 rows
+    with NaN-poisoned activations), blocks of 64 rows on a small problem and
+    128 rows on one that fills the machine.  Every valid row of gate/up (bf16
+    and the fp32 accumulators) and of down is bit-identical to the oracle;
+    padding rows keep the output's previous contents."""
+    from w4a16_int4_mixture_amd import _capi
+    H, I = 512, 2048 if want_bm == 128 else 256
+    p = np.ones(E)
+    p[1] = 0
+    p[0] = 4
+    p /= p.sum()
+    d = _contiguous_problem(E * 7 + T, E, H, I, T, k, p=p, exact=True)
+    mi, a2 = d["m_indices"], d["a2"]
+    mrows = mi.size
+    print(f"contiguous exact: E={E} m={mrows} padding={int((mi < 0).sum())}", flush=True)
+    w13 = prepare(m, d["codes13"], d["scales13"], 2)
+    plan = _capi.w4a16_plan_gemm(w13.desc, _capi.W4A16_LAYOUT_CONTIGUOUS, mrows)
+    assert plan.tile_m == want_bm
+    A, M = dev(a2), dev(mi)
+    Y13 = torch.full((mrows, 2 * I), 0x1234, dtype=torch.int16, device="cuda")
+    m.run_gemm(m.gemm_args_contiguous(w13, A, M, Y13), "cuda")
+    Y13f = torch.zeros((mrows, 2 * I), dtype=torch.float32, device="cuda")
+    m.run_gemm(m.gemm_args_contiguous(w13, A, M, Y13f, flags=_capi.W4A16_GEMM_F32_OUT), "cuda")
+    torch.cuda.synchronize()
+    valid = mi >= 0
+    ref = oracle.contiguous_gemm(a2, mi, d["codes13"], d["scales13"])
+    got = host(Y13, np.uint16)
+    assert np.all(got[~valid] == 0x1234), "padding rows were written"
+    bad = np.nonzero(np.any(got[valid] != ref[valid], axis=1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ"
+    rows = np.nonzero(valid)[0]
+    ref_f = oracle.grouped_gemm(a2, rows.astype(np.int32), mi[rows].copy(), d["codes13"],
+                                d["scales13"], 2 * I, H, out_f32=True)
+    assert np.array_equal(host(Y13f)[rows], ref_f)
+    # down on integer activations (K = I)
+    w2 = prepare(m, d["codes2"], d["scales2"], 2)
+    rng = np.random.default_rng(9)
+    Zi = synth.bf16_trunc(rng.integers(-4, 5, size=(mrows, I)).astype(np.float32))
+    Y2 = torch.full((mrows, H), 0x1234, dtype=torch.int16, device="cuda")
+    m.run_gemm(m.gemm_args_contiguous(w2, dev(Zi), M, Y2), "cuda")
+    torch.cuda.synchronize()
+    ref2 = oracle.contiguous_gemm(Zi, mi, d["codes2"], d["scales2"])
+    got2 = host(Y2, np.uint16)
+    assert np.all(got2[~valid] == 0x1234)
+    assert np.array_equal(got2[valid], ref2[valid])
+
+
+@pytest.mark.parametrize("interleave", [False, True])
+def test_contiguous_path_random(m, interleave):
+    """General inputs through the contiguous path (gate/up with SiLU*gate
+    fused on an interleaved W13, or as its own kernel on a plain one -> down
+    -> combine through the slot -> row map): held to the oracle with
+    bf16-rounded weights at the tight bar and to the exact oracle within the
+    tolerance."""
+    E, H, I, T, k = 5, 1024, 256, 200, 3
+    d = _contiguous_problem(31, E, H, I, T, k)
+    mi, a2 = d["m_indices"], d["a2"]
+    w13 = prepare(m, d["codes13"], d["scales13"], 2, interleave)
+    w2 = prepare(m, d["codes2"], d["scales2"], 2)
+    path = m.ContiguousPath(w13, w2, mi.size, T, k)
+    path.Z.fill_(0x1234)
+    out = host(path(dev(a2), dev(mi), dev(d["row_of"]), dev(d["topk_weights"])), np.uint16)
+    torch.cuda.synchronize()
+    valid = mi >= 0
+    refZ = oracle.silu_mul(oracle.contiguous_gemm(a2, mi, d["codes13"], d["scales13"], wmode=1))
+    gotZ = host(path.Z, np.uint16)
+    assert np.all(gotZ[~valid] == 0x1234), "padding rows of Z were written"
+    check_close(gotZ[valid], refZ[valid], "contiguous Z (bf16 weights)")
+    refY2 = oracle.contiguous_gemm(refZ, mi, d["codes2"], d["scales2"], wmode=1)
+    check_close(host(path.Y2, np.uint16)[valid], refY2[valid], "contiguous Y2 (bf16 weights)")
+    check_close(out, oracle.combine(refY2, d["row_of"], d["topk_weights"]),
+                "contiguous out (bf16 weights)")
+    ref0 = oracle.moe_forward(d["X"], d["topk_ids"], d["topk_weights"], E, None, d["codes13"],
+                              d["scales13"], d["codes2"], d["scales2"])
+    check_close(out, ref0, "contiguous out (exact weights)", exact_frac=0.0)
+
+
+def test_contiguous_workload_full_parity(m):
+    """The grouped contiguous prefill share at full size: 48 local experts,
+    128 rows each (6144 rows), H 7168, I 2048, in the configuration the
+    benchmark times (interleaved W13, SiLU*gate fused): every row of Z, Y2
+    and the output against the oracle."""
+    d = synth.make_workload("contiguous")
+    wl = d["wl"]
+    mi, a2 = d["m_indices"], d["a2"]
+    print(f"contiguous workload: m={mi.size}", flush=True)
+    w13 = prepare(m, d["codes13"], d["scales13"], 2, interleave=True)
+    w2 = prepare(m, d["codes2"], d["scales2"], 2)
+    path = m.ContiguousPath(w13, w2, mi.size, wl.T, wl.top_k)
+    assert path.plan.tile_m == 128
+    out = host(path(dev(a2), dev(mi), dev(d["row_of"]), dev(d["topk_weights"])), np.uint16)
+    torch.cuda.synchronize()
+    ref = oracle.moe_forward(d["X"], d["topk_ids"], d["topk_weights"], wl.E_global,
+                             d["expert_map"], d["codes13"], d["scales13"], d["codes2"],
+                             d["scales2"], intermediates=True, wmode=1)
+    r = d["row_of"]
+    f = np.nonzero(r >= 0)[0]
+    check_close(host(path.Z, np.uint16)[r[f]], ref["Z"][f], "contiguous workload Z")
+    check_close(host(path.Y2, np.uint16)[r[f]], ref["Y2"][f], "contiguous workload Y2")
+    check_close(out, ref["out"], "contiguous workload out")
+
+
+# --------------------------------------------- fused top-k combine (down) ----
+
+@pytest.mark.parametrize("profile,split,T,Eg", [(1, 1, 40, 8), (1, 2, 40, 8), (1, 0, 300, 6),
+                                                 (1, 0, 9, 16), (1, 3, 120, 16)])
+def test_fused_combine_equals_separate_combine(m, profile, split, T, Eg):
+    """The top-k combine in the down GEMM's epilogue (last arrival per token
+    and 256 columns sums the token's rows in j order) gives the same bits as
+    the combine kernel on the same Y2, including tokens with no local slot
+    (EP share: +0 rows).  Three calls in a row, the output refilled with NaN
+    before each: an arrival counter left non-zero by a call would leave rows
+    of the next unwritten or summed early."""
+    E, H, I, k = 6, 768, 256, 4
+    d = synth.random_small(150 + T + profile, E, H, I, T, k, E_global=Eg)
+    w13 = prepare(m, d["codes13"], d["scales13"], profile, interleave=True)
+    w2 = prepare(m, d["codes2"], d["scales2"], profile)
+    print(f"fused combine: profile={profile} split={split} T={T} Eg={Eg}", flush=True)
+    pf = m.IndexedPath(w13, w2, T, k, Eg, rows_hint=T * k * E // Eg, split_k2=split,
+                       fuse_combine=True)
+    ps = m.IndexedPath(w13, w2, T, k, Eg, rows_hint=T * k * E // Eg, split_k2=split,
+                       fuse_combine=False)
+    args = (dev(d["X"]), dev(d["topk_ids"]), dev(d["topk_weights"]),
+            None if d["expert_map"] is None else dev(d["expert_map"]))
+    sep = host(ps(*args), np.uint16).copy()
+    torch.cuda.synchronize()
+    for call in range(3):
+        pf.out.fill_(0x7FC0)
+        got = host(pf(*args), np.uint16)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, sep), f"call {call}: fused combine differs from the combine kernel"
+    ref = oracle.moe_forward(d["X"], d["topk_ids"], d["topk_weights"], Eg, d["expert_map"],
+                             d["codes13"], d["scales13"], d["codes2"], d["scales2"],
+                             wmode=1 if profile == 2 else 0)
+    check_close(sep, ref, "fused combine out")
+    if d["expert_map"] is not None:
+        none_local = ~np.any(d["expert_map"][d["topk_ids"]] >= 0, axis=1)
+        assert np.all(sep[none_local] == 0)
+
+
+def test_fused_combine_decode_workload_equals_separate(m, decode_data):
+    """At the full decode size: the fused and the separate combine give the
+    same bits, and match the oracle."""
+    d = decode_data
+    wl = d["wl"]
+    w13 = prepare(m, d["codes13"], d["scales13"], 1, interleave=True)
+    w2 = prepare(m, d["codes2"], d["scales2"], 1)
+    args = (dev(d["X"]), dev(d["topk_ids"]), dev(d["topk_weights"]), dev(d["expert_map"]))
+    pf = m.IndexedPath(w13, w2, wl.T, wl.top_k, wl.E_global, rows_hint=512, fuse_combine=True)
+    ps = m.IndexedPath(w13, w2, wl.T, wl.top_k, wl.E_global, rows_hint=512)
+    got = host(pf(*args), np.uint16).copy()
+    sep = host(ps(*args), np.uint16)
+    torch.cuda.synchronize()
+    assert np.array_equal(got, sep)
+    ref = oracle.moe_forward(d["X"], d["topk_ids"], d["topk_weights"], wl.E_global,
+                             d["expert_map"], d["codes13"], d["scales13"], d["codes2"],
+                             d["scales2"])
+    check_close(got, ref, "decode out, fused combine")
+
+
+# --------------------------------------------------------- routing step ----
+
+def _router_logits(seed, T, E):
+    rng = np.random.default_rng(seed)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    lg[0, :] = 0.5                         # all equal: lowest ids win
+    if T > 1:
+        lg[1, [3, E // 2 + 1, E - 1]] = 4.0    # a tie among the largest
+    return lg
+
+
+def _check_router(ids, w, lg, k):
+    rid, rw = oracle.router_topk(lg, k)
+    assert np.array_equal(ids, rid), "router ids differ from the oracle"
+    rel = np.abs(w.astype(np.float64) - rw) / np.abs(rw)
+    print(f"  router weights: max rel {rel.max():.2e}", flush=True)
+    assert rel.max() <= 4e-7
+
+
+@pytest.mark.parametrize("T,E,k", [(100, 384, 8), (33, 64, 1), (7, 1024, 64), (3000, 256, 6)])
+def test_router_topk_matches_oracle(m, T, E, k):
+    """Top-k ids bit-exact (largest logits first, ties to the lower id) and
+    softmax weights within 4e-7 relative of the fp64 oracle."""
+    from w4a16_int4_mixture_amd import _capi
+    lg = _router_logits(T + E + k, T, E)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    _capi.w4a16_moe_router_topk(dev(lg), T, E, k, ids, w)
+    torch.cuda.synchronize()
+    _check_router(host(ids), host(w), lg, k)
+
+
+@pytest.mark.parametrize("T,k,Eg,El", [(64, 8, 384, 48), (1, 8, 384, 48), (4096, 8, 384, 48)])
+def test_route_align_matches_router_then_align(m, T, k, Eg, El):
+    """Router top-k fused with the routing sort (one launch at decode sizes,
+    router then sort above): the ids and weights of the router, and the sort
+    of those ids, bit-exact against the oracle."""
+    from w4a16_int4_mixture_amd import _capi
+    lg = _router_logits(T + 5, T, Eg)
+    em = np.full(Eg, -1, np.int32)
+    em[:El] = np.arange(El, dtype=np.int32)
+    r = m.Routing(T, k, El, 16, 32, "cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    _capi.w4a16_moe_route_align(dev(lg), T, Eg, k, dev(em), El, 16, r.c, ids, w)
+    torch.cuda.synchronize()
+    gids = host(ids)
+    _check_router(gids, host(w), lg, k)
+    ref = oracle.moe_align(gids, Eg, El, 16, em, sorted_cap=r.sorted_cap, blocks_cap=r.blocks_cap)
+    assert np.array_equal(host(r.sorted_ids), ref["sorted_ids"])
+    assert np.array_equal(host(r.expert_ids), ref["expert_ids"])
+    assert int(host(r.num_tokens_padded)[0]) == ref["num_tokens_padded"]
+    assert np.array_equal(host(r.row_of)[: T * k], ref["row_of"])
+    tiles = oracle.moe_tiles(gids, Eg, El, 16, 32, em)
+    assert np.array_equal(host(r.tiles)[: int(host(r.tile_count)[0])], tiles)
+
+
+def _placement(m, X, ids, Eg, em, El, max_m, poison=0x1234):
+    from w4a16_int4_mixture_amd import _capi
+    T, k = ids.shape
+    H = X.shape[1]
+    sc, bc, _ = _capi.w4a16_moe_align_capacity(T, k, El, 1, 0)
+    scratch = m.Routing(T, k, El, 1, 0, "cuda")
+    offs = torch.empty((El + 1,), dtype=torch.int32, device="cuda")
+    scratch.c.expert_offsets = offs.data_ptr()
+    a3 = torch.full((El * max_m, H), poison, dtype=torch.int16, device="cuda")
+    mm = torch.empty((El,), dtype=torch.int32, device="cuda")
+    row_of = torch.empty((T * k,), dtype=torch.int32, device="cuda")
+    dropped = torch.empty((1,), dtype=torch.int32, device="cuda")
+    Xd = dev(X)
+    _capi.w4a16_moe_indexed_to_masked(Xd, T, H, dev(ids), T, k, Eg,
+                                      None if em is None else dev(em), El, max_m, scratch.c, a3,
+                                      mm, row_of, dropped)
+    torch.cuda.synchronize()
+    return a3, mm, row_of, int(host(dropped)[0]), (scratch, offs, Xd)
+
+
+@pytest.mark.parametrize("T,k,Eg,El,max_m", [(256, 8, 384, 12, 32), (64, 8, 384, 48, 16),
+                                              (2000, 4, 64, 64, 160), (5, 2, 8, 8, 1)])
+def test_indexed_to_masked_matches_oracle(m, T, k, Eg, El, max_m):
+    """Placement of each local slot's row into [E_local, max_m, H] on the
+    device: rows, masked_m, the slot -> row map and the drop count bit-exact
+    against the oracle; rows never written keep the output's contents."""
+    rng = np.random.default_rng(T + El)
+    ids = np.argsort(rng.random((T, Eg)), axis=1)[:, :k].astype(np.int32)
+    em = np.full(Eg, -1, np.int32)
+    em[rng.permutation(Eg)[:El]] = rng.permutation(El).astype(np.int32)
+    if El == Eg:
+        em = None
+    X = synth.random_activations(rng, T, 256)
+    a3, mm, row_of, dropped, _ = _placement(m, X, ids, Eg, em, El, max_m)
+    ra3, rmm, rrow, rdrop = oracle.indexed_to_masked(
+        X, ids, Eg, em, El, max_m, a3=np.full((El * max_m, 256), 0x1234, np.uint16))
+    assert np.array_equal(host(mm), rmm) and dropped == rdrop
+    assert np.array_equal(host(row_of), rrow)
+    assert np.array_equal(host(a3, np.uint16), ra3)
+    print(f"  placement: dropped {dropped}, rows {int(rmm.sum())}", flush=True)
+
+
+def test_indexed_to_masked_feeds_masked_path(m):
+    """Router logits -> top-k -> placement into the masked layout -> masked
+    gate/up + down -> combine through the placement's row map, against the
+    oracle's indexed path on the same routing (max_m holds every row)."""
+    from w4a16_int4_mixture_amd import _capi
+    T, k, Eg, El, H, I = 96, 8, 64, 8, 512, 256
+    lg = _router_logits(7, T, Eg)
+    d = synth.random_small(8, El, H, I, T, k, E_global=Eg)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    _capi.w4a16_moe_router_topk(dev(lg), T, Eg, k, ids, w)
+    torch.cuda.synchronize()
+    gids = host(ids)
+    em = d["expert_map"]
+    counts = np.bincount(em[gids.ravel()][em[gids.ravel()] >= 0], minlength=El)
+    max_m = int(-(-counts.max() // 32) * 32)
+    a3, mm, row_of, dropped, keep = _placement(m, d["X"], gids, Eg, em, El, max_m,
+                                               poison=0x7FC0)
+    assert dropped == 0
+    w13 = prepare(m, d["codes13"], d["scales13"], 1, interleave=True)
+    w2 = prepare(m, d["codes2"], d["scales2"], 1)
+    path = m.MaskedPath(w13, w2, max_m, 32, T, k)
+    out = host(path(a3, mm, row_of, w), np.uint16)
+    torch.cuda.synchronize()
+    ref = oracle.moe_forward(d["X"], gids, host(w), Eg, em, d["codes13"], d["scales13"],
+                             d["codes2"], d["scales2"])
+    check_close(out, ref, "router -> placement -> masked path")

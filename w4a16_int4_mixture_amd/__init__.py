@@ -159,6 +159,28 @@ def gemm_args_masked(w: PreparedWeight, A, masked_m, max_m, expected_m, out, epi
     return a
 
 
+def gemm_args_contiguous(w: PreparedWeight, A, m_indices, out, epilogue=0, flags=0,
+                         workspace=None):
+    """Grouped contiguous layout: A [m, K] rows per expert (segments padded to
+    128 rows), m_indices int32 [m] (-1 on padding) -> out [m, N]."""
+    a = _capi.w4a16_gemm_args()
+    a.layout = _capi.W4A16_LAYOUT_CONTIGUOUS
+    a.epilogue = epilogue
+    a.flags = flags
+    a.A = A.data_ptr()
+    a.A_rows = A.shape[0]
+    a.m_indices = m_indices.data_ptr()
+    a.packed = w.packed.data_ptr()
+    a.desc = ctypes.pointer(w.desc)
+    a.out = out.data_ptr()
+    a.out_rows = out.shape[0]
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    a._refs = (w, A, out, workspace, m_indices)
+    return a
+
+
 def run_gemm(args: _capi.w4a16_gemm_args, device, keep=None, stream=None):
     """Run one GEMM stage, allocating its workspace when the call needs one."""
     need = _capi.w4a16_gemm_workspace_bytes(args)
@@ -181,11 +203,13 @@ class IndexedPath:
 
     With a W13 packed with gate/up interleave, SiLU*gate runs inside the
     gate/up GEMM (one launch that writes Z); with a plain W13 the gate/up GEMM
-    stores Y13 and SiLU*gate is a call of its own (act)."""
+    stores Y13 and SiLU*gate is a call of its own (act).  With fuse_combine
+    (DECODE-profile weights) the top-k combine runs in the down GEMM's
+    epilogue; by default it is a call of its own."""
 
     def __init__(self, w13: PreparedWeight, w2: PreparedWeight, T: int, top_k: int,
                  E_global: int, rows_hint: int = 0, tile_m: int = 0, split_k13: int = 0,
-                 split_k2: int = 0, device="cuda"):
+                 split_k2: int = 0, device="cuda", fuse_combine: bool = False):
         assert w13.E == w2.E and w13.N == 2 * w2.K and w13.K == w2.N
         self.w13, self.w2 = w13, w2
         self.T, self.top_k, self.E_global, self.E = T, top_k, E_global, w13.E
@@ -201,8 +225,10 @@ class IndexedPath:
         self.Y2 = _dev_empty((cap, self.H), BF16, device)
         self.out = _dev_empty((max(T, 1), self.H), BF16, device)
         self.split_k13, self.split_k2 = split_k13, split_k2
+        self.fuse_combine = fuse_combine
         self.device = device
         self._ws = {}
+        self._tw = None            # top-k weights the fused combine reads
 
     def _ws_for(self, key, args):
         need = _capi.w4a16_gemm_workspace_bytes(args)
@@ -223,19 +249,36 @@ class IndexedPath:
         self._ws_for(("g", epilogue, flags), a)
         return a
 
-    def down_args(self, Z=None, out=None, flags=0):
+    def down_args(self, Z=None, out=None, flags=0, topk_weights=None):
+        """Down GEMM arguments; with topk_weights (and fuse_combine) the
+        top-k combine into self.out runs in its epilogue."""
         Z = self.Z if Z is None else Z
         out = self.Y2 if out is None else out
         a = gemm_args_indexed(self.w2, Z, self.routing, out, _capi.W4A16_AROW_POSITION,
                               flags=flags, split_k=self.split_k2, rows_hint=self.rows_hint)
-        self._ws_for(("d", flags), a)
+        fused = self.fuse_combine and topk_weights is not None
+        if fused:
+            a.comb_out = self.out.data_ptr()
+            a.comb_row_of = self.routing.row_of.data_ptr()
+            a.comb_weights = topk_weights.data_ptr()
+            a.comb_T = self.T
+            a._refs = a._refs + (topk_weights, self.out)
+        self._ws_for(("d", flags, fused), a)
         return a
 
-    def stage_args(self, X):
-        """Argument structs of the two GEMM stages as the path launches them."""
+    def stage_args(self, X, topk_weights=None):
+        """Argument structs of the two GEMM stages as the path launches them
+        (the down GEMM with the fused combine when topk_weights is given and
+        fuse_combine is on)."""
+        da = self.down_args(topk_weights=topk_weights)
         if self.separate_act:
-            return self.gate_up_args(X, out=self.Y13, epilogue=_capi.W4A16_EPI_STORE), self.down_args()
-        return self.gate_up_args(X), self.down_args()
+            return self.gate_up_args(X, out=self.Y13, epilogue=_capi.W4A16_EPI_STORE), da
+        return self.gate_up_args(X), da
+
+    def combine(self, topk_weights, stream=None):
+        """The top-k combine as a call of its own (Y2 -> out)."""
+        _capi.w4a16_moe_combine(self.Y2, self.Y2.shape[0], self.H, self.routing.row_of,
+                                topk_weights, self.T, self.top_k, self.out, stream)
 
     def act(self, stream=None):
         """SiLU*gate on the rows of the padded routed layout (separate_act)."""
@@ -245,13 +288,13 @@ class IndexedPath:
 
     def __call__(self, X, topk_ids, topk_weights, expert_map=None, stream=None):
         self.routing.align(topk_ids, self.E_global, expert_map, stream=stream)
-        ga, da = self.stage_args(X)
+        ga, da = self.stage_args(X, topk_weights)
         _capi.w4a16_moe_w4a16_gemm(ga, stream)
         if self.separate_act:
             self.act(stream)
         _capi.w4a16_moe_w4a16_gemm(da, stream)
-        _capi.w4a16_moe_combine(self.Y2, self.Y2.shape[0], self.H, self.routing.row_of,
-                                topk_weights, self.T, self.top_k, self.out, stream)
+        if not self.fuse_combine:
+            self.combine(topk_weights, stream)
         return self.out
 
 
@@ -300,6 +343,55 @@ class MaskedPath:
     def __call__(self, a3, masked_m, row_of, topk_weights, stream=None):
         _capi.w4a16_moe_w4a16_gemm(self.gate_up_args(a3, masked_m), stream)
         _capi.w4a16_moe_w4a16_gemm(self.down_args(masked_m), stream)
+        _capi.w4a16_moe_combine(self.Y2, self.Y2.shape[0], self.H, row_of, topk_weights, self.T,
+                                self.top_k, self.out, stream)
+        return self.out
+
+
+class ContiguousPath:
+    """Grouped contiguous layout (prefill): gate/up (+ SiLU*gate) -> down on
+    the caller's [m] rows, then the top-k combine through the caller's row
+    map (slot -> row).  Weights packed with the PREFILL profile."""
+
+    def __init__(self, w13: PreparedWeight, w2: PreparedWeight, m: int, T: int, top_k: int,
+                 device="cuda"):
+        self.w13, self.w2 = w13, w2
+        self.m, self.T, self.top_k = m, T, top_k
+        self.H, self.I = w13.K, w2.K
+        self.plan = _capi.w4a16_plan_gemm(w13.desc, _capi.W4A16_LAYOUT_CONTIGUOUS, m)
+        self.Z = _dev_empty((max(m, 1), self.I), BF16, device)
+        self.Y2 = _dev_empty((max(m, 1), self.H), BF16, device)
+        self.out = _dev_empty((max(T, 1), self.H), BF16, device)
+        self.device = device
+        self._ws = {}
+
+    def _ws_for(self, key, args):
+        need = _capi.w4a16_gemm_workspace_bytes(args)
+        if need == 0:
+            return
+        buf = self._ws.get(key)
+        if buf is None or buf.numel() < need:
+            buf = _workspace(need, self.device)
+            self._ws[key] = buf
+        args.workspace = buf.data_ptr()
+        args.workspace_bytes = buf.numel()
+
+    def gate_up_args(self, a2, m_indices, out=None, epilogue=_capi.W4A16_EPI_SILU_MUL, flags=0):
+        out = self.Z if out is None else out
+        a = gemm_args_contiguous(self.w13, a2, m_indices, out, epilogue=epilogue, flags=flags)
+        self._ws_for(("g", epilogue, flags), a)
+        return a
+
+    def down_args(self, m_indices, Z=None, out=None, flags=0):
+        Z = self.Z if Z is None else Z
+        out = self.Y2 if out is None else out
+        a = gemm_args_contiguous(self.w2, Z, m_indices, out, flags=flags)
+        self._ws_for(("d", flags), a)
+        return a
+
+    def __call__(self, a2, m_indices, row_of, topk_weights, stream=None):
+        _capi.w4a16_moe_w4a16_gemm(self.gate_up_args(a2, m_indices), stream)
+        _capi.w4a16_moe_w4a16_gemm(self.down_args(m_indices), stream)
         _capi.w4a16_moe_combine(self.Y2, self.Y2.shape[0], self.H, row_of, topk_weights, self.T,
                                 self.top_k, self.out, stream)
         return self.out

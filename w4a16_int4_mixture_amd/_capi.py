@@ -34,6 +34,7 @@ W4A16_DESC_VERSION = 1
 W4A16_ALIGN_VALIDATE = 0x1
 W4A16_LAYOUT_INDEXED = 0
 W4A16_LAYOUT_MASKED = 1
+W4A16_LAYOUT_CONTIGUOUS = 2
 W4A16_AROW_TOKEN = 0
 W4A16_AROW_SLOT = 1
 W4A16_AROW_POSITION = 2
@@ -60,7 +61,8 @@ class w4a16_routing(ctypes.Structure):
                 ("expert_ids", ctypes.c_void_p), ("blocks_cap", ctypes.c_int32),
                 ("num_tokens_padded", ctypes.c_void_p), ("row_of", ctypes.c_void_p),
                 ("tiles", ctypes.c_void_p), ("tiles_cap", ctypes.c_int32),
-                ("tile_count", ctypes.c_void_p), ("tile_m", ctypes.c_int32)]
+                ("tile_count", ctypes.c_void_p), ("tile_m", ctypes.c_int32),
+                ("expert_offsets", ctypes.c_void_p)]
 
 
 class w4a16_gemm_args(ctypes.Structure):
@@ -79,12 +81,16 @@ class w4a16_gemm_args(ctypes.Structure):
                 ("expected_m", ctypes.c_int32),
                 ("packed", ctypes.c_void_p), ("desc", ctypes.POINTER(w4a16_desc)),
                 ("out", ctypes.c_void_p), ("out_rows", ctypes.c_int64),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
+                ("m_indices", ctypes.c_void_p),
+                ("comb_out", ctypes.c_void_p), ("comb_row_of", ctypes.c_void_p),
+                ("comb_weights", ctypes.c_void_p), ("comb_T", ctypes.c_int32)]
 
 
 class w4a16_plan(ctypes.Structure):
     _fields_ = [("block_m", ctypes.c_int32), ("tile_m", ctypes.c_int32),
-                ("split_k", ctypes.c_int32), ("kernel", ctypes.c_int32)]
+                ("split_k", ctypes.c_int32), ("kernel", ctypes.c_int32),
+                ("ring_groups", ctypes.c_int32)]
 
 
 # name -> (restype, argtypes); the full exported surface of the header
@@ -120,6 +126,23 @@ SIGNATURES = {
     "w4a16_moe_combine": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
+    "w4a16_moe_router_topk": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p]),
+    "w4a16_moe_route_align": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.POINTER(w4a16_routing),
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32,
+                                             ctypes.c_void_p]),
+    "w4a16_moe_indexed_to_masked": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64,
+                                                   ctypes.c_int32, ctypes.c_void_p,
+                                                   ctypes.c_int32, ctypes.c_int32,
+                                                   ctypes.c_int32, ctypes.c_void_p,
+                                                   ctypes.c_int32, ctypes.c_int32,
+                                                   ctypes.POINTER(w4a16_routing),
+                                                   ctypes.c_void_p, ctypes.c_void_p,
+                                                   ctypes.c_void_p, ctypes.c_void_p,
+                                                   ctypes.c_void_p]),
     "w4a16_plan_gemm": (ctypes.c_int, [ctypes.POINTER(w4a16_desc), ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.POINTER(w4a16_plan)]),
@@ -237,6 +260,28 @@ def w4a16_moe_silu_mul(y13, rows, rows_dev, I, z, stream=None) -> None:
 def w4a16_moe_combine(y, y_rows, H, row_of, topk_weights, T, top_k, out, stream=None) -> None:
     check(lib().w4a16_moe_combine(ptr(y), y_rows, H, ptr(row_of), ptr(topk_weights), T, top_k,
                                   ptr(out), stream_handle(stream)))
+
+
+def w4a16_moe_router_topk(logits, T, E_global, top_k, topk_ids, topk_weights,
+                          stream=None) -> None:
+    check(lib().w4a16_moe_router_topk(ptr(logits), T, E_global, top_k, ptr(topk_ids),
+                                      ptr(topk_weights), stream_handle(stream)))
+
+
+def w4a16_moe_route_align(logits, T, E_global, top_k, expert_map, E_local, block_m, routing,
+                          topk_ids, topk_weights, flags=0, stream=None) -> None:
+    check(lib().w4a16_moe_route_align(ptr(logits), T, E_global, top_k, ptr(expert_map),
+                                      E_local, block_m, ctypes.byref(routing), ptr(topk_ids),
+                                      ptr(topk_weights), flags, stream_handle(stream)))
+
+
+def w4a16_moe_indexed_to_masked(X, X_rows, H, topk_ids, T, top_k, E_global, expert_map,
+                                E_local, max_m, scratch, a3, masked_m, row_of, dropped=None,
+                                stream=None) -> None:
+    check(lib().w4a16_moe_indexed_to_masked(ptr(X), X_rows, H, ptr(topk_ids), T, top_k,
+                                            E_global, ptr(expert_map), E_local, max_m,
+                                            ctypes.byref(scratch), ptr(a3), ptr(masked_m),
+                                            ptr(row_of), ptr(dropped), stream_handle(stream)))
 
 
 def w4a16_plan_gemm(desc, layout, rows_hint=0, expected_m=0, tile_m=0) -> w4a16_plan:

@@ -91,7 +91,87 @@ __device__ int wave_exclusive_scan(int* v, int n, int lane) {
     return carry;
 }
 
+// ---- router top-k ------------------------------------------------------------
+//
+// One wavefront per token: lane l holds the logits of experts l, l + 64, ...
+// (at most kRouterPerLane).  k rounds: each lane offers its best remaining
+// expert (largest logit, lower id on equal logits), the wavefront reduces the
+// 64 offers with the same order, and the owner of the winner marks it taken.
+// Then weight j = e^(l_j - l_0) / sum_i e^(l_i - l_0) over the k winners, in
+// fp32, summed in j order.
+constexpr int kRouterPerLane = 16;   // E_global <= 1024
+static_assert(64 * kRouterPerLane == kRouterMaxExperts, "16 logits per lane");
+
+__device__ inline bool router_better(float va, int ia, float vb, int ib) {
+    return va > vb || (va == vb && ia < ib);
+}
+
+__device__ inline void router_token(const float* logits, int E, int k, int t, int lane,
+                                    int32_t* ids_out, float* w_out) {
+    float v[kRouterPerLane];
+    const float* l = logits + static_cast<int64_t>(t) * E;
+#pragma unroll
+    for (int i = 0; i < kRouterPerLane; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < E ? l[e] : -__builtin_inff();
+    }
+    uint32_t taken = 0;   // bit i: expert lane + 64 i already selected (or absent)
+#pragma unroll
+    for (int i = 0; i < kRouterPerLane; ++i)
+        if (lane + 64 * i >= E) taken |= 1u << i;
+    float top = 0.f, den = 0.f, my_val = 0.f;
+    int my_id = 0;
+    for (int j = 0; j < k; ++j) {
+        float bv = -__builtin_inff();
+        int bi = 0x7FFFFFFF;
+#pragma unroll
+        for (int i = 0; i < kRouterPerLane; ++i) {
+            if (taken & (1u << i)) continue;
+            if (router_better(v[i], lane + 64 * i, bv, bi)) {
+                bv = v[i];
+                bi = lane + 64 * i;
+            }
+        }
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) {
+            const float ov = __shfl_xor(bv, d, 64);
+            const int oi = __shfl_xor(bi, d, 64);
+            if (router_better(ov, oi, bv, bi)) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        // every lane now holds the winner (bv, bi)
+        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+        if (j == 0) top = bv;
+        const float ex = expf(bv - top);
+        den = j == 0 ? ex : den + ex;
+        if (lane == j) {
+            my_val = ex;
+            my_id = bi;
+        }
+    }
+    if (lane < k) {
+        ids_out[static_cast<int64_t>(t) * k + lane] = my_id;
+        w_out[static_cast<int64_t>(t) * k + lane] = my_val / den;
+    }
+}
+
 }  // namespace
+
+// Router top-k alone: one wavefront per token, four per workgroup.
+__global__ void __launch_bounds__(256) k_router_topk(const float* __restrict__ logits, int T, int E,
+                                                     int k, int32_t* __restrict__ ids,
+                                                     float* __restrict__ w) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t < T) router_token(logits, E, k, t, lane, ids, w);
+}
+
+void launch_router_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                        hipStream_t s) {
+    if (T > 0) k_router_topk<<<dim3((T + 3) / 4), dim3(256), 0, s>>>(logits, T, E, k, ids, w);
+}
 
 __global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
     extern __shared__ unsigned char smem[];
@@ -121,6 +201,16 @@ __global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
     const int64_t c_end = c_begin + cpw < b_end ? c_begin + cpw : b_end;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int bad = 0;
+
+    // ---- fused router (one-workgroup launches only): wavefront w takes the
+    // top-k of tokens w, w + W, ...; the ids it writes are read back below
+    // by every wavefront of this workgroup
+    if (a.logits) {
+        for (int t = w; t < a.T; t += W)
+            router_token(a.logits, a.E_global, a.top_k, t, lane, a.ids_out, a.weights_out);
+        __threadfence_block();
+        __syncthreads();
+    }
 
     // ---- pass 0: per-expert totals over all slots and counts before the
     // range.  The expert map is cached in LDS (when it fits) and the routing
@@ -258,6 +348,9 @@ __global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
             }
         }
     }
+    if (blockIdx.x == 0 && a.r.expert_offsets)
+        for (int e = threadIdx.x; e <= E; e += blockDim.x)
+            a.r.expert_offsets[e] = e < E ? pad[e] : total;
     if (threadIdx.x == 0 && blockIdx.x == 0) {
         a.r.num_tokens_padded[0] = total;
         if (a.r.tiles) a.r.tile_count[0] = red[1];
@@ -316,13 +409,22 @@ size_t align_lds_bytes(int W, int E_local, int E_global) {
            (E_global <= kMapLds ? static_cast<size_t>(E_global) * 4 : 0);
 }
 
-void launch_align(const AlignArgs& a, hipStream_t s) {
+void launch_align(const AlignArgs& a_in, hipStream_t s) {
+    AlignArgs a = a_in;
     int W = align_waves(a.E_local);
     // about one chunk of 64 slots per wavefront in each workgroup's range;
     // every workgroup also counts all slots once (pass 0)
     const int64_t chunks = (static_cast<int64_t>(a.T) * a.top_k + 63) / 64;
     int64_t nb = chunks / W;
     nb = nb < 1 ? 1 : (nb > 64 ? 64 : nb);
+    if (a.logits) {
+        a.topk_ids = a.ids_out;
+        if (nb > 1) {
+            // every workgroup counts all slots: the router runs first, alone
+            launch_router_topk(a.logits, a.T, a.E_global, a.top_k, a.ids_out, a.weights_out, s);
+            a.logits = nullptr;
+        }
+    }
     k_align<<<dim3(static_cast<unsigned>(nb)), dim3(64 * W),
               align_lds_bytes(W, a.E_local, a.E_global), s>>>(a);
 }

@@ -56,9 +56,14 @@ __device__ int32_t g_routing_errors;
 //
 // The indexed rule follows the shape of the page's resolver (block height from
 // routed rows per expert tok_e, not from the total), with CDNA4 constants:
-// the tile is sized to hold an expert's rows in one pass (about twice the mean
-// so that Poisson-like tails rarely spill into a second pass, which would
-// stream the expert's weights again), in 16-row MFMA steps.  The masked rule
+// the tile is sized to hold an expert's rows in one pass, in 16-row MFMA
+// steps: twice the mean up to 16 rows per expert (decode: every expert in one
+// tile of at most 32 rows, so that a 48-expert share is one item per
+// resident workgroup), 1.25 times the mean above.  The streaming kernel's
+// code ring is one stage ("wide": three workgroups per CU) for tiles of up to
+// two row blocks whose experts mostly fill one block, or whose K is a single
+// record (latency-bound items, where occupancy hides more than depth), and
+// two stages otherwise.  The masked rule
 // sizes tiles to expected_m itself: a tile of up to 32 rows keeps two
 // streaming workgroups per CU (three at 16), which is worth more than the
 // extra weight pass of an expert above expected_m (on the Zipf EP32 share,
@@ -87,6 +92,18 @@ static int choose_split(int64_t tiles_est, int64_t rows_est, int NC, int stages,
     return split;
 }
 
+// Contiguous layout: blocks of 128 rows when the (block, column pair) items
+// of the large-M kernel fill the machine's compute units once, else blocks of
+// 64 rows (twice the items).  Chord page, "Grouped SM90 kernels": BM128 on
+// large grids spreads the dequant over more rows; small problems fall back to
+// BM64 so that the M tiles fill the machine.
+static constexpr int64_t kComputeUnits = 256;
+
+static int contig_block_m(int NC, int64_t m) {
+    const int64_t pairs = (NC + 1) / 2;
+    return ceil_div(std::max<int64_t>(m, 1), 128) * pairs >= kComputeUnits ? 128 : 64;
+}
+
 // rows_cap: rows of the position-indexed output space when the caller's
 // buffers are known (0 = unknown); with no rows_hint it sizes the split-K
 // partials.
@@ -97,6 +114,17 @@ static w4a16_status plan_impl(const w4a16_desc* d, int layout, int rows_hint, in
     const int NC = d->N / d->chunk_n;
     int tile_m;
     int64_t tiles_est;
+    if (layout == W4A16_LAYOUT_CONTIGUOUS) {
+        if (d->profile != W4A16_PROFILE_PREFILL) {
+            set_error("the contiguous layout runs on weights packed with the PREFILL profile");
+            return W4A16_ERR_MODE_MISMATCH;
+        }
+        p->block_m = 128;
+        p->tile_m = contig_block_m(NC, rows_hint);
+        p->kernel = 2;
+        p->split_k = 1;
+        return W4A16_OK;
+    }
     if (layout == W4A16_LAYOUT_MASKED) {
         if (expected_m <= 0) {
             set_error("expected_m must be a positive integer (got %d)", expected_m);
@@ -122,9 +150,10 @@ static w4a16_status plan_impl(const w4a16_desc* d, int layout, int rows_hint, in
             } else {
                 // the streaming kernel's work per K group grows with the row
                 // blocks of a tile, while an expert cut into two tiles streams
-                // its weights twice: tiles of ~1.25x the mean, in 16-row steps
+                // its weights twice
+                const double want = tok_e <= 16.0 ? 2.0 * tok_e : 1.25 * tok_e;
                 tile_m = static_cast<int>(std::min<int64_t>(
-                    std::max<int64_t>(round_up(static_cast<int64_t>(1.25 * tok_e + 0.999), 16), 16),
+                    std::max<int64_t>(round_up(static_cast<int64_t>(want + 0.999), 16), 16),
                     kSmallMaxTile));
             }
         }
@@ -140,6 +169,14 @@ static w4a16_status plan_impl(const w4a16_desc* d, int layout, int rows_hint, in
     const int64_t active = std::min<int64_t>(E, std::max<int64_t>(tiles_est, 1));
     const int64_t weight_bytes = active * static_cast<int64_t>(d->N) * d->K * 18 / 32;
     p->split_k = p->kernel == 2 ? 1 : choose_split(tiles_est, rows_est, NC, stages, d->N, weight_bytes);
+    if (p->kernel == 2) {
+        p->ring_groups = 0;
+    } else {
+        const double mean = layout == W4A16_LAYOUT_MASKED ? static_cast<double>(expected_m)
+                            : rows_hint > 0 ? static_cast<double>(rows_hint) / E : 16.0;
+        const bool wide = tile_m <= 16 || (tile_m <= 32 && (mean <= 16.0 || stages == 1));
+        p->ring_groups = wide ? 8 : 16;
+    }
     return W4A16_OK;
 }
 
@@ -152,6 +189,7 @@ struct Resolved {
     GemmArgs g;
     int kernel;              // 1 streaming, 2 large-M
     int mt;
+    bool wide;               // streaming kernel: the 8-group code ring
     int split;
     int64_t rows_cap;        // rows of the position-indexed output space
     int64_t tiles_bound;     // tile indices a launch can visit
@@ -274,6 +312,7 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
         }
         r->tiles_bound = a->tiles ? a->tiles_cap : a->blocks_cap;
         r->mt = tile_m / 16;
+        r->wide = plan.ring_groups == 8;
         r->split = split;
         r->rows_cap = a->sorted_cap;
         const int64_t need_rows = a->orow == W4A16_OROW_SLOT ? a->num_slots : a->sorted_cap;
@@ -322,8 +361,36 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
         r->kernel = plan.kernel;
         r->tiles_bound = g.grid_tiles_total;
         r->mt = plan.tile_m / 16;
+        r->wide = plan.ring_groups == 8;
         r->split = std::max(1, std::min(split, g.KSP / 8));
         r->rows_cap = rows;
+    } else if (a->layout == W4A16_LAYOUT_CONTIGUOUS) {
+        W4A16_CHECK_ARG(a->m_indices, "contiguous layout needs m_indices");
+        if (a->split_k != 0) {
+            set_error("the grouped contiguous dispatch chooses its own schedule: split_k override refused");
+            return W4A16_ERR_MODE_MISMATCH;
+        }
+        const int64_t m = a->A_rows;
+        W4A16_CHECK_ARG(m < (1LL << 31), "contiguous layout: m must stay below 2^31 rows");
+        st = plan_impl(d, W4A16_LAYOUT_CONTIGUOUS, static_cast<int>(m), 0, 0, m, &plan);
+        if (st != W4A16_OK) return st;
+        if (a->out_rows < m) {
+            set_error("contiguous output has %lld rows, needs m = %lld",
+                      static_cast<long long>(a->out_rows), static_cast<long long>(m));
+            return W4A16_ERR_CAPACITY;
+        }
+        g.tile_src = TILE_CONTIG;
+        g.arow = W4A16_AROW_POSITION;
+        g.orow = W4A16_OROW_POSITION;
+        g.m_indices = a->m_indices;
+        g.tile_m = plan.tile_m;
+        g.grid_tiles_total = static_cast<int>(ceil_div(m, plan.tile_m));
+        g.grid_tiles = g.grid_tiles_total;
+        r->kernel = 2;
+        r->tiles_bound = g.grid_tiles_total;
+        r->mt = plan.tile_m / 16;
+        r->split = 1;
+        r->rows_cap = m;
     } else {
         W4A16_CHECK_ARG(false, "unknown layout %d", a->layout);
     }
@@ -337,6 +404,28 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
         }
         r->split = 1;
     }
+    // fused top-k combine in the epilogue (the down GEMM of the indexed path)
+    if (a->comb_out) {
+        W4A16_CHECK_ARG(a->layout == W4A16_LAYOUT_INDEXED && a->tiles,
+                        "the fused combine needs the indexed layout with a tile table");
+        if (r->kernel != 1) {
+            set_error("the fused combine runs in the streaming kernel (DECODE profile) only");
+            return W4A16_ERR_UNSUPPORTED;
+        }
+        W4A16_CHECK_ARG(a->orow == W4A16_OROW_POSITION, "the fused combine needs OROW_POSITION");
+        W4A16_CHECK_ARG(a->epilogue == W4A16_EPI_STORE && !f32_out,
+                        "the fused combine needs EPI_STORE with bf16 output");
+        W4A16_CHECK_ARG(a->comb_row_of && a->comb_weights && aligned(a->comb_out, 16),
+                        "the fused combine needs row_of, weights and a 16-byte aligned output");
+        W4A16_CHECK_ARG(a->top_k >= 1 && a->comb_T >= 0 &&
+                            static_cast<int64_t>(a->comb_T) * a->top_k == a->num_slots,
+                        "the fused combine needs comb_T * top_k == num_slots");
+        if (static_cast<uint64_t>(a->sorted_cap) * d->N * 2 >= 0xFFFFFFFFull) {
+            set_error("fused combine: rows of %d x %d bf16 exceed the 4 GiB a kernel addresses",
+                      a->sorted_cap, d->N);
+            return W4A16_ERR_UNSUPPORTED;
+        }
+    }
     g.split_k = r->split;
     g.tiles_cap = static_cast<int>(std::min<int64_t>(r->tiles_bound, 0x7FFFFFFF));
     g.unpack_mask = 0x000F000Fu;
@@ -345,15 +434,28 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
     const bool split = r->split > 1;
     r->silu_separate = a->epilogue == W4A16_EPI_SILU_MUL && !interleaved;
     const int64_t gx = (g.NC + 3) / 4;
-    // split-K arrival counters (one per tile and group of four chunks); the
-    // PREFILL kernel's work-queue counters (nine ints)
-    r->ws_counters = split ? round256(static_cast<uint64_t>(r->tiles_bound) * gx * 4)
-                     : r->kernel == 2 ? 256 : 0;
+    // split-K arrival counters (one per tile and group of four chunks) or the
+    // PREFILL kernel's work-queue counters (nine ints); then the fused
+    // combine's arrival counters (one per token and 256 columns)
+    const uint64_t ctr = split ? round256(static_cast<uint64_t>(r->tiles_bound) * gx * 4)
+                         : r->kernel == 2 ? 256 : 0;
+    const int comb_groups = (d->N + 255) / 256;
+    const uint64_t comb =
+        a->comb_out ? round256(static_cast<uint64_t>(a->comb_T) * comb_groups * 4) : 0;
+    r->ws_counters = ctr + comb;
     r->ws_partial = split ? round256(static_cast<uint64_t>(r->split) * r->rows_cap * d->N * 4) : 0;
     r->ws_y13 = r->silu_separate ? round256(static_cast<uint64_t>(r->rows_cap) * d->N * 2) : 0;
     g.ws_stride = r->rows_cap * d->N;
     char* ws = static_cast<char*>(a->workspace);
-    g.counters = r->ws_counters && ws ? reinterpret_cast<int32_t*>(ws) : nullptr;
+    g.counters = ctr && ws ? reinterpret_cast<int32_t*>(ws) : nullptr;
+    if (a->comb_out) {
+        g.comb_out = a->comb_out;
+        g.comb_row_of = a->comb_row_of;
+        g.comb_w = a->comb_weights;
+        g.comb_T = a->comb_T;
+        g.comb_groups = comb_groups;
+        g.comb_counters = ws ? reinterpret_cast<int32_t*>(ws + ctr) : nullptr;
+    }
     g.partials = split && ws ? reinterpret_cast<float*>(ws + r->ws_counters) : nullptr;
     if (a->epilogue == W4A16_EPI_SILU_MUL && interleaved) {
         g.out_kind = OUT_SILU;
@@ -374,7 +476,7 @@ static w4a16_status run_resolved(const w4a16_gemm_args* args, const Resolved& r,
     if (r.kernel == 2)
         launch_gemm_large(r.g, s);
     else
-        launch_gemm_small(r.g, r.mt, s);
+        launch_gemm_small(r.g, r.mt, r.wide, s);
     w4a16_status st = check_launch("w4a16 gemm");
     if (st != W4A16_OK) return st;
     if (r.silu_separate) {
@@ -383,12 +485,18 @@ static w4a16_status run_resolved(const w4a16_gemm_args* args, const Resolved& r,
         // the same rows and skips padding, so it writes only rows the caller's
         // output holds
         const bool masked = args->layout == W4A16_LAYOUT_MASKED;
-        launch_silu_mul(static_cast<const uint16_t*>(r.g.out), r.rows_cap,
-                        masked ? nullptr : args->num_tokens_padded, args->desc->N / 2,
-                        masked ? args->masked_m : nullptr, args->max_m,
-                        masked ? nullptr : args->sorted_ids, args->num_slots,
-                        !masked && args->orow == W4A16_OROW_SLOT,
-                        static_cast<uint16_t*>(args->out), s);
+        const bool contig = args->layout == W4A16_LAYOUT_CONTIGUOUS;
+        if (contig)   // rows whose index names an expert
+            launch_silu_mul(static_cast<const uint16_t*>(r.g.out), r.rows_cap, nullptr,
+                            args->desc->N / 2, nullptr, 1, args->m_indices, args->desc->E, false,
+                            static_cast<uint16_t*>(args->out), s);
+        else
+            launch_silu_mul(static_cast<const uint16_t*>(r.g.out), r.rows_cap,
+                            masked ? nullptr : args->num_tokens_padded, args->desc->N / 2,
+                            masked ? args->masked_m : nullptr, args->max_m,
+                            masked ? nullptr : args->sorted_ids, args->num_slots,
+                            !masked && args->orow == W4A16_OROW_SLOT,
+                            static_cast<uint16_t*>(args->out), s);
         st = check_launch("silu_mul");
     }
     return st;
@@ -445,7 +553,9 @@ w4a16_status w4a16_plan_gemm(const w4a16_desc* desc, int32_t layout, int32_t row
     W4A16_CHECK_ARG(plan, "null plan pointer");
     w4a16_status st = check_desc(desc);
     if (st != W4A16_OK) return st;
-    W4A16_CHECK_ARG(layout == W4A16_LAYOUT_INDEXED || layout == W4A16_LAYOUT_MASKED, "unknown layout %d", layout);
+    W4A16_CHECK_ARG(layout == W4A16_LAYOUT_INDEXED || layout == W4A16_LAYOUT_MASKED ||
+                        layout == W4A16_LAYOUT_CONTIGUOUS,
+                    "unknown layout %d", layout);
     W4A16_CHECK_ARG(tile_m == 0 || (tile_m >= 16 && tile_m % 16 == 0 && tile_m <= max_tile(desc)),
                     "tile_m must be 0 or a multiple of 16 up to %d for this profile", max_tile(desc));
     return plan_impl(desc, layout, rows_hint, expected_m, tile_m, 0, plan);
@@ -470,13 +580,16 @@ w4a16_status w4a16_moe_align_capacity(int32_t T, int32_t top_k, int32_t E_local,
     return W4A16_OK;
 }
 
-w4a16_status w4a16_moe_align(const int32_t* topk_ids, int32_t T, int32_t top_k, int32_t E_global,
-                             const int32_t* expert_map, int32_t E_local, int32_t block_m,
-                             const w4a16_routing* routing, uint32_t flags, void* stream) {
-    clear_error();
+// The align entry points: routing ids from topk_ids, or (logits != NULL)
+// from the router top-k of the logits, written to ids_out / w_out first.
+static w4a16_status align_entry(const int32_t* topk_ids, int32_t T, int32_t top_k,
+                                int32_t E_global, const int32_t* expert_map, int32_t E_local,
+                                int32_t block_m, const w4a16_routing* routing, uint32_t flags,
+                                void* stream, const float* logits, int32_t* ids_out,
+                                float* w_out) {
     W4A16_CHECK_ARG(routing, "null routing buffers");
     W4A16_CHECK_ARG(T >= 0 && top_k >= 1, "bad T=%d top_k=%d", T, top_k);
-    W4A16_CHECK_ARG(T == 0 || topk_ids, "null topk_ids");
+    W4A16_CHECK_ARG(T == 0 || topk_ids || logits, "null topk_ids");
     W4A16_CHECK_ARG(E_global >= 1, "E_global must be positive");
     W4A16_CHECK_ARG(E_local >= 1 && E_local <= 1024, "E_local must be in [1, 1024]");
     W4A16_CHECK_ARG(block_m >= 1 && block_m <= 256, "block_m must be in [1, 256]");
@@ -509,6 +622,9 @@ w4a16_status w4a16_moe_align(const int32_t* topk_ids, int32_t T, int32_t top_k, 
     a.block_m = block_m;
     a.expert_map = expert_map;
     a.r = r;
+    a.logits = logits;
+    a.ids_out = ids_out;
+    a.weights_out = w_out;
     int32_t* flag = nullptr;
     if (flags & W4A16_ALIGN_VALIDATE) {
         if (hipGetSymbolAddress(reinterpret_cast<void**>(&flag), HIP_SYMBOL(g_routing_errors)) != hipSuccess) {
@@ -538,6 +654,91 @@ w4a16_status w4a16_moe_align(const int32_t* topk_ids, int32_t T, int32_t top_k, 
         }
     }
     return W4A16_OK;
+}
+
+w4a16_status w4a16_moe_align(const int32_t* topk_ids, int32_t T, int32_t top_k, int32_t E_global,
+                             const int32_t* expert_map, int32_t E_local, int32_t block_m,
+                             const w4a16_routing* routing, uint32_t flags, void* stream) {
+    clear_error();
+    return align_entry(topk_ids, T, top_k, E_global, expert_map, E_local, block_m, routing, flags,
+                       stream, nullptr, nullptr, nullptr);
+}
+
+static w4a16_status check_router(const float* logits, int32_t T, int32_t E_global, int32_t top_k,
+                                 const int32_t* topk_ids, const float* topk_weights) {
+    W4A16_CHECK_ARG(T >= 0, "bad T=%d", T);
+    W4A16_CHECK_ARG(E_global >= 1 && E_global <= kRouterMaxExperts,
+                    "router: E_global must be in [1, %d]", kRouterMaxExperts);
+    W4A16_CHECK_ARG(top_k >= 1 && top_k <= kRouterMaxTopK && top_k <= E_global,
+                    "router: top_k must be in [1, min(%d, E_global)]", kRouterMaxTopK);
+    W4A16_CHECK_ARG(T == 0 || (logits && topk_ids && topk_weights), "router: null buffer");
+    return W4A16_OK;
+}
+
+w4a16_status w4a16_moe_router_topk(const float* logits, int32_t T, int32_t E_global, int32_t top_k,
+                                   int32_t* topk_ids, float* topk_weights, void* stream) {
+    clear_error();
+    w4a16_status st = check_router(logits, T, E_global, top_k, topk_ids, topk_weights);
+    if (st != W4A16_OK) return st;
+    launch_router_topk(logits, T, E_global, top_k, topk_ids, topk_weights,
+                       static_cast<hipStream_t>(stream));
+    return check_launch("router_topk");
+}
+
+w4a16_status w4a16_moe_route_align(const float* logits, int32_t T, int32_t E_global,
+                                   int32_t top_k, const int32_t* expert_map, int32_t E_local,
+                                   int32_t block_m, const w4a16_routing* routing,
+                                   int32_t* topk_ids, float* topk_weights, uint32_t flags,
+                                   void* stream) {
+    clear_error();
+    w4a16_status st = check_router(logits, T, E_global, top_k, topk_ids, topk_weights);
+    if (st != W4A16_OK) return st;
+    return align_entry(topk_ids, T, top_k, E_global, expert_map, E_local, block_m, routing, flags,
+                       stream, T > 0 ? logits : nullptr, topk_ids, topk_weights);
+}
+
+w4a16_status w4a16_moe_indexed_to_masked(const uint16_t* X, int64_t X_rows, int32_t H,
+                                         const int32_t* topk_ids, int32_t T, int32_t top_k,
+                                         int32_t E_global, const int32_t* expert_map,
+                                         int32_t E_local, int32_t max_m,
+                                         const w4a16_routing* scratch, uint16_t* a3,
+                                         int32_t* masked_m, int32_t* row_of, int32_t* dropped,
+                                         void* stream) {
+    clear_error();
+    W4A16_CHECK_ARG(scratch, "null routing scratch");
+    W4A16_CHECK_ARG(T >= 0 && top_k >= 1 && E_local >= 1 && max_m >= 1, "bad T/top_k/E_local/max_m");
+    W4A16_CHECK_ARG(H >= 8 && H % 8 == 0, "H must be a positive multiple of 8");
+    W4A16_CHECK_ARG(masked_m && (T == 0 || (X && topk_ids && a3 && row_of)), "null buffer");
+    W4A16_CHECK_ARG(T == 0 || (aligned(X, 16) && aligned(a3, 16)), "X and a3 must be 16-byte aligned");
+    W4A16_CHECK_ARG(X_rows >= T, "X has %lld rows, needs T = %d", static_cast<long long>(X_rows), T);
+    W4A16_CHECK_ARG(scratch->row_of && scratch->expert_offsets,
+                    "the routing scratch needs row_of and expert_offsets");
+    w4a16_routing r = *scratch;     // the sort without tiles, padding block 1
+    r.tiles = nullptr;
+    r.tile_count = nullptr;
+    r.tiles_cap = 0;
+    w4a16_status st = align_entry(topk_ids, T, top_k, E_global, expert_map, E_local, 1, &r, 0,
+                                  stream, nullptr, nullptr, nullptr);
+    if (st != W4A16_OK) return st;
+    MaskedPlaceArgs m{};
+    m.X = X;
+    m.H = H;
+    m.top_k = top_k;
+    m.num_slots = T * top_k;
+    m.sorted_ids = r.sorted_ids;
+    m.expert_ids = r.expert_ids;
+    m.ntp = r.num_tokens_padded;
+    m.sorted_cap = r.sorted_cap;
+    m.offsets = r.expert_offsets;
+    m.row_of = r.row_of;
+    m.E = E_local;
+    m.max_m = max_m;
+    m.a3 = a3;
+    m.masked_m = masked_m;
+    m.row_of_masked = row_of;
+    m.dropped = dropped;
+    launch_to_masked(m, static_cast<hipStream_t>(stream));
+    return check_launch("indexed_to_masked");
 }
 
 w4a16_status w4a16_gemm_workspace_bytes(const w4a16_gemm_args* args, uint64_t* bytes) {

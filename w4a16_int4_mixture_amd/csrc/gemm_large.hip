@@ -159,15 +159,21 @@ struct Slots {
 
 }  // namespace
 
+// How the store loop finds and filters output rows.
+enum RowMode {
+    ROWS_PLAIN = 0,   // out row = position
+    ROWS_MAP = 1,     // out row from sorted_ids (padding sentinels skipped)
+    ROWS_CONTIG = 2   // out row = position, stored only if m_indices names the item's expert
+};
+
 // Stores rows [r0, r1) of a work item from the fp32 staging tile in LDS
 // ([128 rows][256 columns]; rows 32 k .. 32 k + 31 of the pass in slot k):
 // 32 lanes per row, 8 staged values each; bf16 or fp32 rows, or SiLU(gate) *
-// up of the interleaved gate/up pairs (4 outputs per lane).  KIND and ROWMAP
-// (output row from sorted_ids) are template parameters so that each variant
-// is a straight loop: with the variants merged, the compiler could no longer
-// tell which registers came from memory and waited for every store in flight
-// before each new one.
-template <int KIND, bool ROWMAP>
+// up of the interleaved gate/up pairs (4 outputs per lane).  KIND and ROWS
+// are template parameters so that each variant is a straight loop: with the
+// variants merged, the compiler could no longer tell which registers came
+// from memory and waited for every store in flight before each new one.
+template <int KIND, int ROWS>
 __device__ __forceinline__ void store_rows_k(const GemmArgs& a, const Item& it, const Slots& sl,
                                           int r0, int r1) {
     constexpr bool silu = KIND == OUT_SILU;
@@ -186,10 +192,12 @@ __device__ __forceinline__ void store_rows_k(const GemmArgs& a, const Item& it, 
         const int r = r0 + 32 * k + rr;
         if (r >= r1) break;
         int64_t orow = it.p0 + r;
-        if (ROWMAP) {
+        if (ROWS == ROWS_MAP) {
             const int f = a.sorted_ids[it.p0 + r];
             if (f < 0 || f >= a.num_slots) continue;
             if (a.orow == W4A16_OROW_SLOT) orow = f;
+        } else if (ROWS == ROWS_CONTIG) {
+            if (a.m_indices[it.p0 + r] != it.e) continue;
         }
         const f32x4* src = reinterpret_cast<const f32x4*>(sl.p[k]) + rr * 64 + 2 * q;
         const f32x4 v0 = src[0], v1 = src[1];
@@ -213,19 +221,21 @@ __device__ __forceinline__ void store_rows_k(const GemmArgs& a, const Item& it, 
     }
 }
 
+template <int ROWS>
+__device__ __forceinline__ void store_rows_m(const GemmArgs& a, const Item& it, const Slots& sl,
+                                          int r0, int r1) {
+    if (a.out_kind == OUT_SILU) store_rows_k<OUT_SILU, ROWS>(a, it, sl, r0, r1);
+    else if (a.out_kind == OUT_BF16) store_rows_k<OUT_BF16, ROWS>(a, it, sl, r0, r1);
+    else store_rows_k<OUT_F32, ROWS>(a, it, sl, r0, r1);
+}
+
 __device__ __forceinline__ void store_rows(const GemmArgs& a, const Item& it, const Slots& sl,
                                         int r0, int r1) {
-    const bool row_map = a.tile_src != TILE_MASKED &&
-                         (a.tile_src == TILE_BLOCKS || a.orow == W4A16_OROW_SLOT);
-    if (row_map) {
-        if (a.out_kind == OUT_SILU) store_rows_k<OUT_SILU, true>(a, it, sl, r0, r1);
-        else if (a.out_kind == OUT_BF16) store_rows_k<OUT_BF16, true>(a, it, sl, r0, r1);
-        else store_rows_k<OUT_F32, true>(a, it, sl, r0, r1);
-    } else {
-        if (a.out_kind == OUT_SILU) store_rows_k<OUT_SILU, false>(a, it, sl, r0, r1);
-        else if (a.out_kind == OUT_BF16) store_rows_k<OUT_BF16, false>(a, it, sl, r0, r1);
-        else store_rows_k<OUT_F32, false>(a, it, sl, r0, r1);
-    }
+    const bool row_map = (a.tile_src == TILE_TABLE && a.orow == W4A16_OROW_SLOT) ||
+                         a.tile_src == TILE_BLOCKS;
+    if (row_map) store_rows_m<ROWS_MAP>(a, it, sl, r0, r1);
+    else if (a.tile_src == TILE_CONTIG) store_rows_m<ROWS_CONTIG>(a, it, sl, r0, r1);
+    else store_rows_m<ROWS_PLAIN>(a, it, sl, r0, r1);
 }
 
 // One work item with up to 32 * RB rows.
@@ -253,7 +263,9 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
     const int chunk = it.pair * 2 + (wave >> 1);
     const int h = wave & 1;
     const bool active = chunk < a.NC;
-    const bool slot_rows = a.tile_src != TILE_MASKED;
+    // rows found through sorted_ids (indexed layout); masked and contiguous
+    // rows are positions
+    const bool slot_rows = a.tile_src == TILE_TABLE || a.tile_src == TILE_BLOCKS;
     const int KS = a.KS;
     const int KSP = a.KSP;          // a multiple of 8; groups >= KS have zero weights
     const int SA = (KS + 1) >> 1;   // stages holding real activations
@@ -475,7 +487,7 @@ __device__ inline Item tile_of(const GemmArgs& a, int ty) {
         it.p0 = ty * a.block_m;
         it.e = a.expert_ids[ty];
         it.nrows = a.sorted_cap - it.p0 < a.block_m ? a.sorted_cap - it.p0 : a.block_m;
-    } else {
+    } else if (a.tile_src == TILE_MASKED) {
         // masked_m is the valid count of each expert; a count above max_m is
         // cut to max_m, so no tile reaches past the expert's rows
         const int g = ty / a.chunks_per_expert;
@@ -485,6 +497,15 @@ __device__ inline Item tile_of(const GemmArgs& a, int ty) {
         it.e = g;
         it.p0 = g * a.max_m + r0;
         it.nrows = cnt - r0 < a.tile_m ? cnt - r0 : a.tile_m;
+    } else {
+        // contiguous: block ty of tile_m rows; its expert is its first row's
+        // (every expert's segment starts on a 128-row boundary), a block that
+        // starts with padding holds no rows; rows of other experts inside the
+        // block are computed but not stored
+        it.p0 = ty * a.tile_m;
+        const int64_t left = a.A_rows - it.p0;
+        it.e = left > 0 ? a.m_indices[it.p0] : -1;
+        it.nrows = left < a.tile_m ? static_cast<int>(left) : a.tile_m;
     }
     if (it.e < 0 || it.e >= a.E) it.nrows = 0;
     it.nrows = it.nrows < 256 ? it.nrows : 256;
@@ -567,7 +588,7 @@ __global__ void __launch_bounds__(256) k_gemm_large(GemmArgs a) {
         n_tiles = a.ntp[0] / a.block_m;
         n_tiles = n_tiles < a.tiles_cap ? n_tiles : a.tiles_cap;
     } else {
-        n_tiles = a.grid_tiles_total;
+        n_tiles = a.grid_tiles_total;   // masked and contiguous: host-known
     }
     const int CP = (a.NC + 1) / 2;
     const int nwg = gridDim.x;

@@ -33,6 +33,7 @@
 //     leading slots before the range re-read its first group with zeroed
 //     scales (they add exactly zero).  A range of a single stage runs alone.
 
+#include "combine_epi.h"
 #include "device_common.h"
 #include "internal.h"
 
@@ -239,7 +240,10 @@ __device__ inline void barrier_ds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_ba
 // wait written for the full count then waits at least as long); activation
 // columns past K (padding groups, whose scales are zero) are clamped to the
 // last real group.
-template <int MT, int WPL, int MTMAX, bool MAYBE_VIRTUAL = false>
+// (D, the caller's ring depth, only keeps the instantiations of the two ring
+// variants apart: the host compilation pass rejects one instantiation reached
+// from both.)
+template <int MT, int WPL, int MTMAX, int D, bool MAYBE_VIRTUAL = false>
 __device__ inline void dma_stage(const Src<MT>& src, u32x4* buf, int base, int ks_min, int ks_real,
                                  int wave, int lane) {
     constexpr int kAStage = kSG * MTMAX * 64;   // u32x4 of activations per buffer
@@ -291,9 +295,10 @@ struct Stg {
 // the LDS layout).
 //
 // Codes: a ring of D groups in registers, refilled as consumed: one stage (D
-// = 8) in the one-block variant, so that three of its workgroups fit on a CU
-// (the HBM stream needs about eight wavefronts per CU in flight, and a
-// decode-sized grid then runs in one round); two stages (D = 16) otherwise.
+// = 8, the "wide" variants: the one- and two-block kernels then fit three
+// workgroups on a CU, and a decode-sized grid runs in one round) or two
+// stages (D = 16, the "deep" variants: more bytes in flight per wavefront,
+// for grids that do not fill the machine with resident workgroups).
 // Activation fragments and scales: two LDS buffers filled by buffer-to-LDS
 // loads one stage ahead.  A stage ends with a wait for this wavefront's loads
 // into the other buffer (vector-memory completions are counted in order, so
@@ -304,12 +309,12 @@ struct Stg {
 // by one virtual record (zero scales) when it holds an odd number of records.
 // Ring slot r0 + g of a stage holds its group g: r0 = 0 for the even stage,
 // and for the odd one kSG (D = 16) or 0 (D = 8).
-template <int MT, int WPL, int MTMAX>
+template <int MT, int WPL, int MTMAX, int D>
 __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1, int ks_real,
                                             int wave, int lane, const Stg& stg,
                                             f32x4 (&acc)[MT][WPL], uint32_t mask,
                                             uint32_t bits) {
-    constexpr int D = MTMAX == 1 ? kSG : 2 * kSG;
+    static_assert(D == kSG || D == 2 * kSG, "a ring of one or two stages");
     constexpr int IT = 2 * kSG;                    // groups per iteration
     constexpr int RO = D == IT ? kSG : 0;          // ring slot of the odd stage's first group
     constexpr int kRefill = kSG * kCodeLoads<WPL>;  // code loads of one stage's refills
@@ -330,7 +335,7 @@ __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1
     // without the virtual stage that pads other odd stage counts
     if (ks1 - ks0 == kSG) {
         Codes<WPL> one[kSG];
-        dma_stage<MT, WPL, MTMAX>(src, stg.b[0], ks0, ks0, ks_real, wave, lane);
+        dma_stage<MT, WPL, MTMAX, D>(src, stg.b[0], ks0, ks0, ks_real, wave, lane);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < kSG; ++i) load_codes<WPL>(one[i], src.w, src.code_off, ks0 + i);
@@ -352,12 +357,12 @@ __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1
     // buffer 1's loads after the ring's, as in the loop (where a stage's loads
     // follow the refills), so that the waits for ring slots match on both paths
     Codes<WPL> ring[D];
-    dma_stage<MT, WPL, MTMAX, true>(src, stg.b[0], kb, ks0, ks_real, wave, lane);
+    dma_stage<MT, WPL, MTMAX, D, true>(src, stg.b[0], kb, ks0, ks_real, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < D; ++i) load_codes<WPL>(ring[i], src.w, src.code_off, kb + i < ks0 ? ks0 : kb + i);
     __builtin_amdgcn_sched_barrier(0);
-    dma_stage<MT, WPL, MTMAX>(src, stg.b[1], kb + kSG, ks0, ks_real, wave, lane);
+    dma_stage<MT, WPL, MTMAX, D>(src, stg.b[1], kb + kSG, ks0, ks_real, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
     // issued: buffer 0, the ring (kRing), buffer 1 (kStage); the last two may
     // stay in flight
@@ -371,14 +376,14 @@ __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1
         // issued since buffer 1's loads: this stage's ring refills (kRefill)
         wait_vmcnt<kRefill>();                   // buffer 1 has landed
         barrier_ds();                            // (for every wavefront); buffer 0 is free
-        dma_stage<MT, WPL, MTMAX>(src, stg.b[0], base + IT, ks0, ks_real, wave, lane);
+        dma_stage<MT, WPL, MTMAX, D>(src, stg.b[0], base + IT, ks0, ks_real, wave, lane);
         // odd stage: buffer 1
         stage_groups<MT, WPL, D>(ring, RO, abuf1, srd1, src, base + D + kSG, true, acc, mask, bits,
                                  lane);
         // issued since buffer 0's loads: this stage's ring refills (kRefill)
         wait_vmcnt<kRefill>();                   // buffer 0 has landed
         barrier_ds();                            // buffer 1 is free
-        dma_stage<MT, WPL, MTMAX>(src, stg.b[1], base + IT + kSG, ks0, ks_real, wave, lane);
+        dma_stage<MT, WPL, MTMAX, D>(src, stg.b[1], base + IT + kSG, ks0, ks_real, wave, lane);
     }
     // last iteration: with a one-stage ring the even stage still refills it
     // with the odd stage's groups
@@ -463,10 +468,12 @@ __device__ __forceinline__ bool splitk_fixup(const GemmArgs& a, int p0, int nrow
     return true;
 }
 
-// One (row tile part, 4 column chunks, K split) with MT active row blocks.
-// `counter`: this part's arrival counter (split_k > 1).
-template <int MT, int WPL, int MTMAX>
-__device__ __forceinline__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, int nrows,
+// One (row tile, 4 column chunks, K split) with MT active row blocks.
+// `counter`: this tile's split-K arrival counter (split_k > 1).  Returns
+// whether this workgroup stored the tile's outputs (false in a K split that
+// did not arrive last); the value is the same in every thread.
+template <int MT, int WPL, int MTMAX, int D>
+__device__ __forceinline__ bool gemm_tile_mt(const GemmArgs& a, int e, int p0, int nrows,
                                              int chunk, int s, int wave, int lane, const Stg& stg,
                                              int32_t* counter) {
     const bool slot_rows = a.tile_src != TILE_MASKED;
@@ -513,11 +520,15 @@ __device__ __forceinline__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, i
     // only pins the register class and emits nothing
     uint32_t vbits = a.unpack_bits;
     asm volatile("" : "+v"(vbits));
-    stream_loop<MT, WPL, MTMAX>(src, ks0, ks1, a.KS, wave, lane, stg, acc, a.unpack_mask, vbits);
+    stream_loop<MT, WPL, MTMAX, D>(src, ks0, ks1, a.KS, wave, lane, stg, acc, a.unpack_mask, vbits);
 
     if (a.split_k > 1 && !splitk_fixup<MT, WPL>(a, p0, nrows, chunk, s, active, lane, counter, acc))
-        return;
-    if (!active) return;
+        return false;
+    if (!active) return true;
+    // with the fused combine, the rows are stored with device-scope stores:
+    // the workgroup that sums a token may run on another XCD
+    const __amdgpu_buffer_rsrc_t ydev =
+        make_rsrc(a.out, a.comb_out ? static_cast<uint64_t>(a.sorted_cap) * a.N * 2 : 0);
 
     // epilogue: lane holds rows 16t + 4*(lane/16) + i of column 16j + lane%16
 #pragma unroll
@@ -542,10 +553,20 @@ __device__ __forceinline__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, i
                     o[16 * j] =
                         f32_to_bf16_rne(silu_mul_bf16(acc[t][j][i], acc[t][j + WPL / 2][i]));
             } else if (a.out_kind == OUT_BF16) {
-                uint16_t* o =
-                    static_cast<uint16_t*>(a.out) + orow * a.N + chunk * a.CW + (lane & 15);
+                if (a.comb_out) {
+                    // sorted_cap * N * 2 < 4 GiB (host check)
+                    const uint32_t off =
+                        static_cast<uint32_t>((orow * a.N + chunk * a.CW + (lane & 15)) * 2);
 #pragma unroll
-                for (int j = 0; j < WPL; ++j) o[16 * j] = f32_to_bf16_rne(acc[t][j][i]);
+                    for (int j = 0; j < WPL; ++j)
+                        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(acc[t][j][i]), ydev,
+                                                              off, 32 * j, kDeviceScope);
+                } else {
+                    uint16_t* o =
+                        static_cast<uint16_t*>(a.out) + orow * a.N + chunk * a.CW + (lane & 15);
+#pragma unroll
+                    for (int j = 0; j < WPL; ++j) o[16 * j] = f32_to_bf16_rne(acc[t][j][i]);
+                }
             } else {
                 float* o = static_cast<float*>(a.out) + orow * a.N + chunk * a.CW + (lane & 15);
 #pragma unroll
@@ -553,47 +574,60 @@ __device__ __forceinline__ void gemm_tile_mt(const GemmArgs& a, int e, int p0, i
             }
         }
     }
+    return true;
 }
 
-template <int MT, int WPL>
-__device__ __forceinline__ void gemm_tile_part(const GemmArgs& a, int e, int p0, int nrows,
+template <int MT, int WPL, int D>
+__device__ __forceinline__ bool gemm_tile_part(const GemmArgs& a, int e, int p0, int nrows,
                                                int chunk, int s, int wave, int lane, const Stg& stg,
                                                int32_t* counter) {
     const int mt_active = (nrows + 15) >> 4;
     if (mt_active <= 1)
-        gemm_tile_mt<1, WPL, MT>(a, e, p0, nrows, chunk, s, wave, lane, stg, counter);
+        return gemm_tile_mt<1, WPL, MT, D>(a, e, p0, nrows, chunk, s, wave, lane, stg, counter);
     else if (MT >= 2 && mt_active == 2)
-        gemm_tile_mt<(MT >= 2 ? 2 : 1), WPL, MT>(a, e, p0, nrows, chunk, s, wave, lane, stg, counter);
+        return gemm_tile_mt<(MT >= 2 ? 2 : 1), WPL, MT, D>(a, e, p0, nrows, chunk, s, wave, lane, stg,
+                                                        counter);
     else if (MT >= 3 && mt_active == 3)
-        gemm_tile_mt<(MT >= 3 ? 3 : 1), WPL, MT>(a, e, p0, nrows, chunk, s, wave, lane, stg, counter);
-    else if (MT >= 4)
-        gemm_tile_mt<(MT >= 4 ? 4 : 1), WPL, MT>(a, e, p0, nrows, chunk, s, wave, lane, stg, counter);
+        return gemm_tile_mt<(MT >= 3 ? 3 : 1), WPL, MT, D>(a, e, p0, nrows, chunk, s, wave, lane, stg,
+                                                        counter);
+    else
+        return gemm_tile_mt<(MT >= 4 ? 4 : 1), WPL, MT, D>(a, e, p0, nrows, chunk, s, wave, lane, stg,
+                                                        counter);
 }
 
-// One tile of at most 16 * MT rows: `quad` is its group of four chunks, `s`
-// its K split; the split-K arrival counter is the (tile, quad) one.
-template <int MT, int WPL>
+// One tile of at most 16 * MT rows: `quad` is its group of four chunks (256
+// columns), `s` its K split; the split-K arrival counter is the (tile, quad)
+// one.  With the fused combine, the workgroup that stored the tile's rows
+// then counts their tokens' arrivals (s_tok, s_n: LDS scratch).
+template <int MT, int WPL, int D>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int ty, int e, int p0, int nrows,
-                                          int quad, int s, int wave, int lane, const Stg& stg) {
+                                          int quad, int s, int wave, int lane, const Stg& stg,
+                                          int* s_tok, int* s_n) {
     const int nquads = (a.NC + 3) / 4;
     int32_t* counter = a.counters + static_cast<int64_t>(ty) * nquads + quad;
-    gemm_tile_part<MT, WPL>(a, e, p0, nrows, quad * 4 + wave, s, wave, lane, stg, counter);
+    const bool stored =
+        gemm_tile_part<MT, WPL, D>(a, e, p0, nrows, quad * 4 + wave, s, wave, lane, stg, counter);
+    static_assert(4 * 64 == 256, "a quad of chunks is one 256-column combine group");
+    if (a.comb_out && stored) comb_arrive(a, p0, nrows, quad, s_tok, s_n);
 }
 
 // Workgroup w runs work items w, w + G, ... (G = the grid), an item being
 // (tile, group of four chunks, K split), splits of one chunk group adjacent;
 // the loop covers any device-side tile count whatever the grid.  The item
 // decision is uniform across the workgroup, so every barrier inside is
-// reached by all four wavefronts.
-template <int MT, int WPL>
-__global__ void __launch_bounds__(256) k_gemm_small(GemmArgs a) {
+// reached by all four wavefronts.  D: groups of the code ring (8 or 16).
+template <int MT, int WPL, int D>
+__device__ __forceinline__ void gemm_small_body(const GemmArgs& a) {
     __shared__ u32x4 stage0[Lds<MT, WPL>::buf];
     __shared__ u32x4 stage1[Lds<MT, WPL>::buf];
+    __shared__ int s_tok[16 * MT];
+    __shared__ int s_n;
     Stg stg;
     stg.b[0] = stage0;
     stg.b[1] = stage1;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (a.comb_out) comb_zero_unrouted(a);
     int n_tiles;
     if (a.tile_src == TILE_TABLE) {
         n_tiles = a.tile_count[0];
@@ -635,51 +669,79 @@ __global__ void __launch_bounds__(256) k_gemm_small(GemmArgs a) {
         // not computed, and nothing is stored outside the tile
         nrows = nrows < 16 * MT ? nrows : 16 * MT;
         if (e < 0 || e >= a.E || nrows <= 0) continue;
-        gemm_tile<MT, WPL>(a, ty, e, p0, nrows, quad, s, wave, lane, stg);
+        gemm_tile<MT, WPL, D>(a, ty, e, p0, nrows, quad, s, wave, lane, stg, s_tok, &s_n);
         __syncthreads();  // the next item reuses the staging buffers
     }
 }
 
+template <int MT, int WPL, int D>
+__global__ void __launch_bounds__(256) k_gemm_small(GemmArgs a) {
+    gemm_small_body<MT, WPL, D>(a);
+}
+
+// The two-block kernel with the one-stage ring, held to three workgroups per
+// CU (168 VGPRs: four registers are kept in scratch across the K loop, none
+// inside it).
+template <int MT, int WPL, int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8)))
+    k_gemm_small_w3(GemmArgs a) {
+    gemm_small_body<MT, WPL, D>(a);
+}
+
+template <int MT, int D>
+static void (*small_kernel())(GemmArgs) {
+    if constexpr (MT == 2 && D == 8)
+        return k_gemm_small_w3<MT, 4, D>;
+    else
+        return k_gemm_small<MT, 4, D>;
+}
+
 // Workgroups of one kernel variant resident on the device at once (from the
 // runtime's occupancy calculation: registers and LDS), cached per variant.
-static int g_resident[5] = {0, 0, 0, 0, 0};
+static int g_resident[5][2] = {};
 
-template <int MT>
+template <int MT, int D>
 static int resident_wgs() {
-    if (g_resident[MT] <= 0) {
+    int& cached = g_resident[MT][D == 8 ? 0 : 1];
+    if (cached <= 0) {
         int dev = 0, ncu = 0, per_cu = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             ncu = 256;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemm_small<MT, 4>, 256, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, small_kernel<MT, D>(), 256, 0) !=
                 hipSuccess ||
             per_cu <= 0)
             per_cu = 1;
-        g_resident[MT] = ncu * per_cu;
+        cached = ncu * per_cu;
     }
-    return g_resident[MT];
+    return cached;
 }
 
-template <int MT>
+template <int MT, int D>
 static void launch_mt(const GemmArgs& a, hipStream_t st) {
     // One workgroup per item (from the host's tile estimate) while they fit
     // in four rounds of resident workgroups: the hardware then hands items to
     // CUs as they free up, which balances items of unequal cost (empty
-    // masked tiles, parts).  Beyond that, items are dealt evenly to that many
+    // masked tiles).  Beyond that, items are dealt evenly to that many
     // workgroups, which saves the start-up of very short items (short K).
-    const int64_t cap = 4 * static_cast<int64_t>(resident_wgs<MT>());
+    const int64_t cap = 4 * static_cast<int64_t>(resident_wgs<MT, D>());
     const int64_t items = static_cast<int64_t>(a.grid_tiles) * ((a.NC + 3) / 4) * a.split_k;
     const int64_t rounds = (items + cap - 1) / cap;
     const int64_t g = rounds > 0 ? (items + rounds - 1) / rounds : 1;
-    k_gemm_small<MT, 4><<<dim3(static_cast<unsigned>(g < 1 ? 1 : g)), dim3(256), 0, st>>>(a);
+    small_kernel<MT, D>()<<<dim3(static_cast<unsigned>(g < 1 ? 1 : g)), dim3(256), 0, st>>>(a);
 }
 
-void launch_gemm_small(const GemmArgs& a, int mt, hipStream_t st) {
+void launch_gemm_small(const GemmArgs& a, int mt, bool wide, hipStream_t st) {
     switch (mt) {
-        case 1: launch_mt<1>(a, st); break;
-        case 2: launch_mt<2>(a, st); break;
-        case 3: launch_mt<3>(a, st); break;
-        default: launch_mt<4>(a, st); break;
+        case 1: launch_mt<1, 8>(a, st); break;
+        case 2:
+            if (wide)
+                launch_mt<2, 8>(a, st);
+            else
+                launch_mt<2, 16>(a, st);
+            break;
+        case 3: launch_mt<3, 16>(a, st); break;
+        default: launch_mt<4, 16>(a, st); break;
     }
 }
 

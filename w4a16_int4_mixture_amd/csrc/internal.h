@@ -87,11 +87,20 @@ struct AlignArgs {
     const int32_t* expert_map;
     w4a16_routing r;
     int32_t* err_flag;  // device int or nullptr (validation)
+    // router top-k first (logits != nullptr): float [T, E_global] in, ids_out
+    // [T, top_k] and weights_out [T, top_k] written, then sorted
+    const float* logits;
+    int32_t* ids_out;
+    float* weights_out;
 };
 void launch_align(const AlignArgs& a, hipStream_t s);
+void launch_router_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                        hipStream_t s);
+constexpr int kRouterMaxExperts = 1024;   // 16 logits per lane of a wavefront
+constexpr int kRouterMaxTopK = 64;        // one lane per selected expert
 
 // How a GEMM block finds its rows.
-enum TileSrc { TILE_TABLE = 0, TILE_BLOCKS = 1, TILE_MASKED = 2 };
+enum TileSrc { TILE_TABLE = 0, TILE_BLOCKS = 1, TILE_MASKED = 2, TILE_CONTIG = 3 };
 // What the GEMM stores: bf16 [rows, N], fp32 [rows, N], or SiLU(gate) * up
 // as bf16 [rows, N/2] from a gate/up-interleaved weight.
 enum OutKind { OUT_BF16 = 0, OUT_F32 = 1, OUT_SILU = 2 };
@@ -108,6 +117,7 @@ struct GemmArgs {
     int block_m, tile_m;
     const int32_t* masked_m;
     int max_m, chunks_per_expert;
+    const int32_t* m_indices;   // contiguous: expert of each row (-1 padding)
     int grid_tiles;        // tiles the host expects (sizes the persistent grids)
     int tiles_cap;         // tile indices that may hold work (bound of the device count)
     int grid_tiles_total;  // masked: experts * chunks_per_expert
@@ -128,11 +138,20 @@ struct GemmArgs {
     float* partials;
     int32_t* counters;
     int64_t ws_stride;
+    // fused top-k combine (comb_out != nullptr): arrival counters [comb_T]
+    // [comb_groups] (zero between calls), one per token and 256 columns
+    uint16_t* comb_out;
+    const int32_t* comb_row_of;
+    const float* comb_w;
+    int32_t* comb_counters;
+    int comb_T, comb_groups;
     uint32_t unpack_mask;  // 0x000F000F: one code in each 16-bit half
     uint32_t unpack_bits;  // 0x43004300: bf16 exponent of 128 in each half
     uint32_t nib_mask;     // 0x0F0F0F0F: one code in each byte
 };
-void launch_gemm_small(const GemmArgs& a, int mt, hipStream_t s);
+// wide: the 8-group code ring (three workgroups per CU up to two row blocks)
+// instead of the 16-group one, for two-block tiles.
+void launch_gemm_small(const GemmArgs& a, int mt, bool wide, hipStream_t s);
 // Large-M kernel (PREFILL profile only, tiles of up to 256 rows, no K split).
 void launch_gemm_large(const GemmArgs& a, hipStream_t s);
 
@@ -144,6 +163,25 @@ void launch_gemm_large(const GemmArgs& a, hipStream_t s);
 void launch_silu_mul(const uint16_t* y13, int64_t rows, const int32_t* rows_dev, int I,
                      const int32_t* masked_m, int max_m, const int32_t* sorted_ids, int num_slots,
                      bool slot_rows, uint16_t* z, hipStream_t s);
+// Indexed -> masked placement from a routing sort made with block_m = 1
+// (no padding): sorted position p of expert e has rank p - offsets[e].
+struct MaskedPlaceArgs {
+    const uint16_t* X;          // [T, H] bf16
+    int H, top_k, num_slots;
+    const int32_t* sorted_ids;
+    const int32_t* expert_ids;
+    const int32_t* ntp;
+    int sorted_cap;
+    const int32_t* offsets;     // [E + 1]
+    const int32_t* row_of;      // slot -> position, -1 if not local
+    int E, max_m;
+    uint16_t* a3;               // [E * max_m, H]
+    int32_t* masked_m;          // [E]
+    int32_t* row_of_masked;     // [num_slots]
+    int32_t* dropped;           // [1] or nullptr
+};
+void launch_to_masked(const MaskedPlaceArgs& a, hipStream_t s);
+
 // Zero `bytes` (a multiple of 16) at p, 16-byte aligned, with a kernel.
 void launch_zero(void* p, uint64_t bytes, hipStream_t s);
 void launch_combine(const uint16_t* y, int64_t y_rows, int H, const int32_t* row_of,
