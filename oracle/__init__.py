@@ -239,6 +239,53 @@ def contiguous_gemm(a2, m_indices, codes, scales, wmode=0, out=None):
     return out
 
 
+def dequant_mx(words: np.ndarray, scales_e8m0: np.ndarray, K: int) -> np.ndarray:
+    """MXFP4 weights: e2m1 codes (8 per int32 along K) times 2^(b - 127) per 32."""
+    words = _c(words, np.int32)
+    sc = _c(scales_e8m0, np.uint8)
+    rows = words.size // (K // 8)
+    w = np.empty(words.shape[:-1] + (K,), dtype=np.float32)
+    _load().oracle_dequant_mx(_p(words), _p(sc), ctypes.c_int64(rows), ctypes.c_int64(K), _p(w))
+    return w
+
+
+def grouped_gemm_mx(A, a_row, expert, codes, scales_e8m0, N: int, K: int) -> np.ndarray:
+    A = _c(A, np.uint16)
+    a_row = _c(a_row, np.int32)
+    expert = _c(expert, np.int32)
+    R = a_row.size
+    out = np.zeros((R, N), dtype=np.uint16)
+    _load().oracle_grouped_gemm_mx(_p(A), _p(a_row), _p(expert), ctypes.c_int64(R),
+                                   _p(_c(codes, np.int32)), _p(_c(scales_e8m0, np.uint8)), N, K,
+                                   _p(out))
+    return out
+
+
+def moe_forward_mx(X, topk_ids, topk_weights, E_global, expert_map, codes13, scales13,
+                   codes2, scales2, intermediates=False):
+    """The indexed path on MXFP4 weights (scales: E8M0 bytes [E, N, K/32])."""
+    X = _c(X, np.uint16)
+    ids = _c(topk_ids, np.int32)
+    T, k = ids.shape
+    E_local, N13, _ = codes13.shape
+    I = N13 // 2
+    H = X.shape[1]
+    out = np.empty((T, H), dtype=np.uint16)
+    Y13 = Z = Y2 = None
+    if intermediates:
+        Y13 = np.empty((T * k, 2 * I), dtype=np.uint16)
+        Z = np.empty((T * k, I), dtype=np.uint16)
+        Y2 = np.empty((T * k, H), dtype=np.uint16)
+    _load().oracle_moe_forward_mx(_p(X), _p(ids), _p(_c(topk_weights, np.float32)), T, k,
+                                  E_global, _p(_c(expert_map, np.int32)), E_local,
+                                  _p(_c(codes13, np.int32)), _p(_c(scales13, np.uint8)),
+                                  _p(_c(codes2, np.int32)), _p(_c(scales2, np.uint8)), H, I,
+                                  _p(out), _p(Y13), _p(Z), _p(Y2))
+    if intermediates:
+        return {"out": out, "Y13": Y13, "Z": Z, "Y2": Y2}
+    return out
+
+
 def router_topk(logits, k):
     """Router logits float32 [T, E] -> (topk_ids int32 [T, k], weights float32
     [T, k]): largest logits first (ties: lower id first), softmax over the k

@@ -101,6 +101,29 @@ inline float weight_at(const uint32_t* row_words, const uint16_t* row_scales,
     return w;
 }
 
+// MXFP4 weights (news.ainew.jp, "vLLM publishes Kimi K3 production support",
+// MXFP4 MoE section: 4-bit floating-point expert weights with one shared
+// power-of-two scale per block of 32, the OCP microscaling format).  A code
+// is an E2M1 number: sign bit 3, exponent bits 2..1, mantissa bit 0; value
+// (-1)^s * 2^(e - 1) * (1 + m / 2) for e > 0 and (-1)^s * m / 2 for e = 0.
+// A block scale is an E8M0 byte: 2^(b - 127), b = 255 reading as NaN.
+inline float e2m1_value(uint32_t code) {
+    const uint32_t e = (code >> 1) & 3u, m = code & 1u;
+    const float mag = e == 0 ? 0.5f * static_cast<float>(m)
+                             : std::ldexp(1.0f + 0.5f * static_cast<float>(m), static_cast<int>(e) - 1);
+    return (code & 8u) ? -mag : mag;
+}
+
+inline float e8m0_value(uint8_t b) {
+    return b == 255 ? std::nanf("") : std::ldexp(1.0f, static_cast<int>(b) - 127);
+}
+
+// Dequantised MXFP4 weight w[c] of one output row: e2m1(q) * 2^(b - 127),
+// exact in fp32 (a 2-bit significand times a power of two) inside fp32's range.
+inline float weight_at_mx(const uint32_t* row_words, const uint8_t* row_scales, int64_t c) {
+    return e2m1_value(code_at(row_words, c)) * e8m0_value(row_scales[c / 32]);
+}
+
 // Local expert of routed slot f, or -1 (non-local or out of range).
 inline int local_expert(const int32_t* topk_ids, int64_t f, int E_global,
                         const int32_t* expert_map, int E_local) {
@@ -125,6 +148,15 @@ inline double dot_row(const uint16_t* a, const uint32_t* row_words,
     float acc = 0.0f;
     for (int64_t c = 0; c < K; ++c)
         acc += bf16_to_float(a[c]) * weight_at(row_words, row_scales, c, wmode);
+    return static_cast<double>(acc);
+}
+
+// One output element on MXFP4 weights: sum over c ascending of a[c] * w[c] in
+// fp32.
+inline double dot_row_mx(const uint16_t* a, const uint32_t* row_words, const uint8_t* row_scales,
+                         int64_t K) {
+    float acc = 0.0f;
+    for (int64_t c = 0; c < K; ++c) acc += bf16_to_float(a[c]) * weight_at_mx(row_words, row_scales, c);
     return static_cast<double>(acc);
 }
 
@@ -394,6 +426,35 @@ void oracle_contiguous_gemm(const uint16_t* a2, const int32_t* m_indices, int64_
                         out);
 }
 
+// ---- MXFP4 weights ------------------------------------------------------------
+
+// Dequantised MXFP4 weights, rows x K, from codes [rows, K/8] and E8M0 scale
+// bytes [rows, K/32].
+void oracle_dequant_mx(const uint32_t* words, const uint8_t* scales, int64_t rows, int64_t K,
+                       float* w) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < K; ++c)
+            w[r * K + c] = weight_at_mx(words + r * (K / 8), scales + r * (K / 32), c);
+}
+
+// The grouped GEMM of O4 / O6 on MXFP4 weights: out[r, n] = bf16( sum_c
+// A[a_row[r], c] * w[expert[r], n, c] ) for every r with expert[r] >= 0.
+void oracle_grouped_gemm_mx(const uint16_t* A, const int32_t* a_row, const int32_t* expert,
+                            int64_t R, const uint32_t* codes, const uint8_t* scales, int N, int K,
+                            uint16_t* out) {
+    const int64_t wpr = K / 8, spr = K / 32;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < R; ++r) {
+        const int e = expert[r];
+        if (e < 0) continue;
+        const uint16_t* a = A + static_cast<int64_t>(a_row[r]) * K;
+        for (int n = 0; n < N; ++n) {
+            const int64_t wr = static_cast<int64_t>(e) * N + n;
+            out[r * N + n] = bf16_from_double(dot_row_mx(a, codes + wr * wpr, scales + wr * spr, K));
+        }
+    }
+}
+
 // ---- the step before the expert GEMMs: routing ----------------------------
 //
 // Router top-k (the pages name an optimised expert routing step ahead of the
@@ -481,6 +542,38 @@ void oracle_moe_forward(const uint16_t* X, const int32_t* topk_ids, const float*
     for (int64_t f = 0; f < slots; ++f)
         row_of[f] = local_expert(topk_ids, f, E_global, expert_map, E_local) >= 0
                         ? static_cast<int32_t>(f) : -1;
+    oracle_combine(Y2, row_of.data(), topk_w, T, top_k, H, out);
+}
+
+// The whole indexed path O4 -> O7 on MXFP4 weights (codes as in the INT4
+// path, E8M0 scale bytes instead of bf16 scales); same rounding points.
+void oracle_moe_forward_mx(const uint16_t* X, const int32_t* topk_ids, const float* topk_w,
+                           int T, int top_k, int E_global, const int32_t* expert_map,
+                           int E_local, const uint32_t* codes13, const uint8_t* scales13,
+                           const uint32_t* codes2, const uint8_t* scales2, int H, int I,
+                           uint16_t* out, uint16_t* Y13_opt, uint16_t* Z_opt, uint16_t* Y2_opt) {
+    const int64_t slots = static_cast<int64_t>(T) * top_k;
+    std::vector<uint16_t> y13v, zv, y2v;
+    uint16_t* Y13 = Y13_opt;
+    uint16_t* Z = Z_opt;
+    uint16_t* Y2 = Y2_opt;
+    if (!Y13) { y13v.resize(slots * 2 * I); Y13 = y13v.data(); }
+    if (!Z) { zv.resize(slots * I); Z = zv.data(); }
+    if (!Y2) { y2v.resize(slots * H); Y2 = y2v.data(); }
+    std::memset(Y13, 0, slots * 2 * I * sizeof(uint16_t));
+    std::memset(Z, 0, slots * I * sizeof(uint16_t));
+    std::memset(Y2, 0, slots * H * sizeof(uint16_t));
+    std::vector<int32_t> tok_row(slots), slot_row(slots), expert(slots), row_of(slots);
+    for (int64_t f = 0; f < slots; ++f) {
+        tok_row[f] = static_cast<int32_t>(f / top_k);
+        slot_row[f] = static_cast<int32_t>(f);
+        expert[f] = local_expert(topk_ids, f, E_global, expert_map, E_local);
+        row_of[f] = expert[f] >= 0 ? static_cast<int32_t>(f) : -1;
+    }
+    oracle_grouped_gemm_mx(X, tok_row.data(), expert.data(), slots, codes13, scales13, 2 * I, H,
+                           Y13);
+    oracle_silu_mul(Y13, slots, I, Z);
+    oracle_grouped_gemm_mx(Z, slot_row.data(), expert.data(), slots, codes2, scales2, H, I, Y2);
     oracle_combine(Y2, row_of.data(), topk_w, T, top_k, H, out);
 }
 

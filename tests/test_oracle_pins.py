@@ -595,3 +595,71 @@ def test_indexed_to_masked_matches_brute_force(T, k, Eg, E, max_m):
     assert np.array_equal(row_of, wrow) and dropped == wdrop
     if max_m == 1:
         assert dropped > 0
+
+
+# ----------------------------------------------------------------- MXFP4 ----
+
+# E2M1 values of codes 0..15 as the OCP microscaling format fixes them
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+              -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+def test_mxfp4_code_and_scale_values():
+    """Every E2M1 code (low nibble = lowest K) and E8M0 scales 127 (1), 0
+    (2^-127), 254 (2^127 with code 0.5), 124 (1/8); 255 reads as NaN."""
+    words = oracle.pack_codes(np.arange(32, dtype=np.uint8).reshape(1, 32) % 16)
+    for b, sc in [(127, 1.0), (0, 2.0 ** -127), (124, 0.125)]:
+        w = oracle.dequant_mx(words, np.array([[b]], np.uint8), 32)[0]
+        want = np.array(E2M1_TABLE * 2, np.float64) * sc
+        assert np.array_equal(w.astype(np.float64), want)
+        assert np.array_equal(np.signbit(w[8:16]), np.ones(8, bool))
+    w = oracle.dequant_mx(words, np.array([[254]], np.uint8), 32)[0]
+    assert w[1] == 2.0 ** 126
+    assert np.all(np.isnan(oracle.dequant_mx(words, np.array([[255]], np.uint8), 32)[0]))
+
+
+@pytest.mark.parametrize("c", [0, 7, 8, 31, 33, 63])
+def test_mxfp4_one_hot_reads_a_column(c):
+    """X = e_c reads column c of the dequantised MXFP4 matrix, each value
+    E2M1(q) * 2^(b - 127) exact in bf16."""
+    rng = np.random.default_rng(60 + c)
+    E, N, K = 2, 16, 64
+    codes = rng.integers(0, 2**32, size=(E, N, K // 8), dtype=np.uint32).view(np.int32)
+    sc = rng.integers(118, 130, size=(E, N, K // 32)).astype(np.uint8)
+    X = np.zeros((1, K), np.uint16)
+    X[0, c] = 0x3F80
+    q = (codes.view(np.uint32)[..., c // 8] >> (4 * (c % 8))) & 0xF
+    for e in range(E):
+        got = oracle.grouped_gemm_mx(X, np.zeros(1, np.int32), np.array([e], np.int32), codes,
+                                     sc, N, K)[0]
+        # the fp32 sum starts at +0, so a code of -0 reads as +0
+        want = [bf16_of_exact(E2M1_TABLE[int(q[e, n])] * 2.0 ** (int(sc[e, n, c // 32]) - 127)
+                              + 0.0) if E2M1_TABLE[int(q[e, n])] != 0 else 0
+                for n in range(N)]
+        assert np.array_equal(got, np.array(want, np.uint16))
+
+
+def test_mxfp4_path_equals_int4_path_on_shared_values():
+    """MXFP4 weights whose values all lie in {0, +-1, +-2, +-3, +-4, +-6} x 2^k are
+    INT4 weights too (q = v + 8, bf16 scale 2^k): the MXFP4 path must then give
+    the INT4 path's bits exactly, through gate/up, SiLU, down and combine."""
+    rng = np.random.default_rng(70)
+    E, H, I, T, k = 3, 128, 64, 7, 2
+    d = synth.random_small(70, E, H, I, T, k)
+    shared = [0, 2, 4, 5, 6, 7, 10, 12, 13, 14, 15]          # codes whose E2M1 value is an integer
+    def mx_and_int4(N, K):
+        qmx = rng.choice(shared, size=(E, N, K))
+        b = rng.integers(119, 123, size=(E, N, K // 32)).astype(np.uint8)
+        vals = np.array(E2M1_TABLE)[qmx]
+        qint = (vals + 8).astype(np.uint8)
+        sbf = synth.bf16_trunc(np.exp2(b.astype(np.float64) - 127).astype(np.float32))
+        return (oracle.pack_codes(qmx.astype(np.uint8)), b,
+                oracle.pack_codes(qint), sbf)
+    c13, s13, i13, b13 = mx_and_int4(2 * I, H)
+    c2, s2, i2, b2 = mx_and_int4(H, I)
+    mx = oracle.moe_forward_mx(d["X"], d["topk_ids"], d["topk_weights"], E, None, c13, s13, c2, s2,
+                               intermediates=True)
+    ref = oracle.moe_forward(d["X"], d["topk_ids"], d["topk_weights"], E, None, i13, b13, i2, b2,
+                             intermediates=True)
+    for key in ("Y13", "Z", "Y2", "out"):
+        assert np.array_equal(mx[key], ref[key]), key
