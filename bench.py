@@ -50,7 +50,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode",
-                   choices=["decode", "prefill", "tp8", "masked", "contiguous", "tiny"])
+                   choices=["decode", "prefill", "tp8", "masked", "contiguous", "decode_mxfp4",
+                            "tiny"])
     p.add_argument("--copies", type=int, default=2, help="prepacked weight copies rotated per call")
     p.add_argument("--no-prefill", action="store_true",
                    help="do not add the prefill sub-object to the decode line")
@@ -108,6 +109,8 @@ def workload_name(name, wl):
         "tp8": "TP8 share: 384 experts, H7168 I256, 1024 tokens x top-8",
         "masked": "grouped masked EP32 share: 12 experts, 256 rows Zipf(1.2), expected_m 32",
         "contiguous": "grouped contiguous EP8 prefill share: 48 experts x 128 rows, H7168 I2048",
+        "decode_mxfp4": "EP8 decode share with MXFP4 weights (E2M1 codes, E8M0 scales per 32): "
+                        "48 local experts, H7168 I2048, 64 tokens x top-8",
         "tiny": "tiny: 8 experts, top-2, H256 I128, 16 tokens",
     }[name]
 
@@ -128,8 +131,12 @@ def run_workload(name, args, src_hash, cpu_legs=True):
         return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
 
     t0 = time.time()
-    d = synth.make_workload(name, seed=0)
+    mxfp4 = name.endswith("_mxfp4")
+    base = name[: -len("_mxfp4")] if mxfp4 else name
+    d = synth.make_workload(base, seed=0, weights=not mxfp4)
     wl = d["wl"]
+    if mxfp4:
+        d.update(synth.make_weights_mxfp4(wl.E_local, wl.H, wl.I, seed=0))
     mfma_bound = name in ("prefill", "contiguous")
     profile = m.PROFILE_PREFILL if mfma_bound else m.PROFILE_DECODE
     print(f"[bench] workload {name}: generated inputs in {time.time() - t0:.1f}s",
@@ -140,8 +147,13 @@ def run_workload(name, args, src_hash, cpu_legs=True):
     copies = []
     for _ in range(max(1, args.copies)):
         # W13 with gate/up interleave: SiLU*gate runs in the gate/up epilogue
-        copies.append((m.prepare_weight(codes13, scales13, profile, m.PACK_GATE_UP_INTERLEAVE),
-                       m.prepare_weight(codes2, scales2, profile)))
+        if mxfp4:
+            copies.append((m.prepare_weight_mxfp4(codes13, scales13, m.PACK_GATE_UP_INTERLEAVE),
+                           m.prepare_weight_mxfp4(codes2, scales2)))
+        else:
+            copies.append((m.prepare_weight(codes13, scales13, profile,
+                                            m.PACK_GATE_UP_INTERLEAVE),
+                           m.prepare_weight(codes2, scales2, profile)))
     del codes13, scales13, codes2, scales2
     torch.cuda.synchronize()
 
@@ -166,8 +178,11 @@ def run_workload(name, args, src_hash, cpu_legs=True):
     rows = int(counts.sum())
     active = int((counts > 0).sum())
     H, I = wl.H, wl.I
-    w13_bytes_per_expert = 2 * I * H // 2 + 2 * I * (H // 32) * 2
-    w2_bytes_per_expert = H * I // 2 + H * (I // 32) * 2
+    # codes (half a byte per weight) + one scale per 32 (bf16, or an E8M0 byte
+    # for MXFP4)
+    sb = 1 if mxfp4 else 2
+    w13_bytes_per_expert = 2 * I * H // 2 + 2 * I * (H // 32) * sb
+    w2_bytes_per_expert = H * I // 2 + H * (I // 32) * sb
     bytes13 = active * w13_bytes_per_expert
     bytes2 = active * w2_bytes_per_expert
     flops13 = 2.0 * rows * (2 * I) * H
@@ -420,9 +435,10 @@ def _oracle_call(oracle, d, wl, workload, tokens):
     # contiguous workload computes the same rows as the indexed path
     wmode = 1 if workload in ("prefill", "contiguous") else 0
     n = tokens
-    oracle.moe_forward(d["X"][:n], d["topk_ids"][:n], d["topk_weights"][:n], wl.E_global,
-                       d["expert_map"], d["codes13"], d["scales13"], d["codes2"], d["scales2"],
-                       wmode=wmode)
+    fwd = oracle.moe_forward_mx if workload.endswith("_mxfp4") else oracle.moe_forward
+    kw = {} if workload.endswith("_mxfp4") else {"wmode": wmode}
+    fwd(d["X"][:n], d["topk_ids"][:n], d["topk_weights"][:n], wl.E_global, d["expert_map"],
+        d["codes13"], d["scales13"], d["codes2"], d["scales2"], **kw)
 
 
 def _timed_leg(oracle, d, wl, workload, budget_s):

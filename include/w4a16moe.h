@@ -87,6 +87,13 @@ typedef enum {
     column blocks so that one wavefront owns matching gate/up columns (allows
     the SiLU(gate)*up epilogue inside the gate/up GEMM) */
 
+#define W4A16_PACK_MXFP4 0x2u /* set by w4a16_prepack_mxfp4 (recorded in the
+    descriptor): the weights are MXFP4, E2M1 codes with one E8M0 scale per 32
+    (news.ainew.jp, "vLLM publishes Kimi K3 production support", MXFP4 MoE:
+    4-bit floating-point expert weights with shared power-of-two block
+    scales).  DECODE profile only; the GEMM then runs the streaming kernel's
+    MXFP4 variant */
+
 #define W4A16_DESC_MAGIC 0x4D413457u   /* "W4AM" as little-endian bytes */
 #define W4A16_DESC_VERSION 1u
 
@@ -129,6 +136,32 @@ w4a16_status w4a16_prepack(int32_t profile, uint32_t flags, const int32_t* codes
                            const uint16_t* scales, int32_t E, int32_t N, int32_t K,
                            int32_t group, void* packed, uint64_t packed_bytes,
                            w4a16_desc* desc /* host out */, void* stream);
+
+/* MXFP4 weights (W4A16_PACK_MXFP4): the same layout as w4a16_prepack's
+ * DECODE profile, from
+ *   codes       : device int32 [E, N, K/8]; code c of a row sits in word c/8 at
+ *                 bits 4*(c%8) .. +3; the code is an E2M1 number (bit 3 sign,
+ *                 bits 2..1 exponent, bit 0 mantissa: +-{0, 0.5, 1, 1.5, 2, 3,
+ *                 4, 6})
+ *   scales_e8m0 : device uint8 [E, N, K/32]; block scale 2^(b - 127), b = 255
+ *                 NaN
+ * so w[e][n][c] = e2m1(code) * 2^(b - 127).  Codes keep their canonical nibble
+ * order (byte b of a word holds K offsets 2b and 2b + 1, the operand order of
+ * the hardware E2M1 -> bf16 conversion); each scale is stored as the bf16
+ * 2^(b - 127), which is exact.  UNSUPPORTED with the PREFILL profile.  flags
+ * may hold W4A16_PACK_GATE_UP_INTERLEAVE; the descriptor records
+ * W4A16_PACK_MXFP4.  w4a16_prepack and w4a16_prepack_host refuse the MXFP4
+ * flag (their scales are bf16). */
+w4a16_status w4a16_prepack_mxfp4(int32_t profile, uint32_t flags, const int32_t* codes,
+                                 const uint8_t* scales_e8m0, int32_t E, int32_t N, int32_t K,
+                                 int32_t group, void* packed, uint64_t packed_bytes,
+                                 w4a16_desc* desc /* host out */, void* stream);
+
+/* Host-side reference of w4a16_prepack_mxfp4 (host buffers). */
+w4a16_status w4a16_prepack_mxfp4_host(int32_t profile, uint32_t flags, const int32_t* codes,
+                                      const uint8_t* scales_e8m0, int32_t E, int32_t N,
+                                      int32_t K, int32_t group, void* packed,
+                                      uint64_t packed_bytes, w4a16_desc* desc);
 
 /* Host-side reference of the same permutation (no GPU), for load-time
  * tooling and tests.  Buffers are host memory. */

@@ -265,6 +265,22 @@ def place_contiguous(X: np.ndarray, topk_ids: np.ndarray, expert_map, E_local: i
     return {"a2": a2, "m_indices": m_indices, "row_of": row_of}
 
 
+def random_scales_e8m0(rng, E: int, N: int, K: int, lo: int = 119, hi: int = 121) -> np.ndarray:
+    """E8M0 block-scale bytes [E, N, K/32], uniform over [lo, hi] (2^-8 .. 2^-6:
+    weights of about the INT4 weights' magnitude)."""
+    assert K % 32 == 0
+    return rng.integers(lo, hi + 1, size=(E, N, K // 32)).astype(np.uint8)
+
+
+def make_weights_mxfp4(E: int, H: int, I: int, seed: int = 0) -> dict:
+    """MXFP4 W13 and W2: uniform E2M1 codes (every 4-bit code), E8M0 scales."""
+    r = _streams(seed + 1000)
+    return {"codes13": random_codes(r[1], E, 2 * I, H),
+            "scales13": random_scales_e8m0(r[2], E, 2 * I, H),
+            "codes2": random_codes(r[3], E, H, I),
+            "scales2": random_scales_e8m0(r[4], E, H, I)}
+
+
 def make_weights(E: int, H: int, I: int, seed: int = 0, which=("w13", "w2")) -> dict:
     """W13 codes [E, 2I, H/8] + scales [E, 2I, H/32]; W2 codes [E, H, I/8] + scales."""
     r = _streams(seed)

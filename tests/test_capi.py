@@ -286,7 +286,11 @@ def decode_packed(packed, desc):
     rec = packed.view(np.uint32).reshape(E, NC, KSP // 8, 576 * WPL)
     words = rec[..., : 512 * WPL].reshape(E, NC, KSP // 8, 8, 4, 16, WPL)
     # axes: e, chunk, record, group-in-record, K octet (lane//16), lane%16, block j
-    off = np.array([2 * (i % 4) + i // 4 for i in range(8)])
+    # MXFP4 keeps the canonical nibble order (nibble i = K offset i)
+    if desc.flags & capi.W4A16_PACK_MXFP4:
+        off = np.arange(8)
+    else:
+        off = np.array([2 * (i % 4) + i // 4 for i in range(8)])
     nib = (words[..., None] >> (4 * np.arange(8, dtype=np.uint32))) & 0xF
     q = np.zeros(nib.shape, np.uint32)
     q[..., off] = nib                                       # -> K offset order
@@ -406,3 +410,38 @@ def test_fused_combine_checks():
         == capi.W4A16_ERR_INVALID_ARG
     dp = host_desc(profile=capi.W4A16_PROFILE_PREFILL, K=64)
     assert ws_status(gemm_args(dp, **c)) == capi.W4A16_ERR_UNSUPPORTED
+
+
+def test_host_prepack_mxfp4_matches_documented_layout():
+    """MXFP4 weights: the DECODE layout with the codes' canonical nibble order
+    and each E8M0 byte b stored as the bf16 2^(b - 127) (0x0040 for b = 0,
+    NaN for 255); the interleave permutes columns as for INT4; the PREFILL
+    profile and the INT4 packers refuse MXFP4."""
+    rng = np.random.default_rng(9)
+    E, N, K = 2, 128, 288
+    codes = rng.integers(0, 2**32, size=(E, N, K // 8), dtype=np.uint32).view(np.int32)
+    b = rng.integers(0, 256, size=(E, N, K // 32)).astype(np.uint8)
+    b[0, 0, 0], b[0, 1, 0], b[1, 2, 3] = 0, 255, 127
+    for flags in (0, capi.W4A16_PACK_GATE_UP_INTERLEAVE):
+        nb = capi.w4a16_prepack_bytes(capi.W4A16_PROFILE_DECODE, flags, E, N, K)
+        packed = np.zeros(nb, np.uint8)
+        desc = capi.w4a16_prepack_mxfp4_host(capi.W4A16_PROFILE_DECODE, flags, codes, b, E, N, K,
+                                             32, packed)
+        assert desc.flags == flags | capi.W4A16_PACK_MXFP4
+        got_codes, got_sc = decode_packed(packed, desc)
+        if flags:
+            perm = np.array([(nn // 64) * 32 + (nn % 64) if nn % 64 < 32 else
+                             N // 2 + (nn // 64) * 32 + (nn % 64) - 32 for nn in range(N)])
+            want_codes, want_b = codes[:, perm], b[:, perm]
+        else:
+            want_codes, want_b = codes, b
+        assert np.array_equal(got_codes, want_codes)
+        want_sc = np.where(want_b == 255, 0x7FC0,
+                           np.where(want_b == 0, 0x0040, want_b.astype(np.uint32) << 7))
+        assert np.array_equal(got_sc, want_sc.astype(np.uint16))
+    packed = np.zeros(capi.w4a16_prepack_bytes(capi.W4A16_PROFILE_DECODE, 0, E, N, K), np.uint8)
+    assert status_of(capi.w4a16_prepack_mxfp4_host, capi.W4A16_PROFILE_PREFILL, 0, codes, b, E, N,
+                     K, 32, packed) == capi.W4A16_ERR_UNSUPPORTED
+    sc16 = np.zeros((E, N, K // 32), np.uint16)
+    assert status_of(capi.w4a16_prepack_host, capi.W4A16_PROFILE_DECODE, capi.W4A16_PACK_MXFP4,
+                     codes, sc16, E, N, K, 32, packed) == capi.W4A16_ERR_INVALID_ARG

@@ -1171,3 +1171,108 @@ def test_indexed_to_masked_feeds_masked_path(m):
     ref = oracle.moe_forward(d["X"], gids, host(w), Eg, em, d["codes13"], d["scales13"],
                              d["codes2"], d["scales2"])
     check_close(out, ref, "router -> placement -> masked path")
+
+
+# ----------------------------------------------------------------- MXFP4 ----
+
+def prepare_mx(m, codes, scales_e8m0, interleave=False):
+    return m.prepare_weight_mxfp4(dev(codes), dev(scales_e8m0),
+                                  m.PACK_GATE_UP_INTERLEAVE if interleave else 0)
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_prepack_mxfp4_device_equals_host(m, flags):
+    from w4a16_int4_mixture_amd import _capi
+    rng = np.random.default_rng(50 + flags)
+    E, N, K = 3, 256, 160
+    codes = rng.integers(0, 2**32, size=(E, N, K // 8), dtype=np.uint32).view(np.int32)
+    b = rng.integers(0, 256, size=(E, N, K // 32)).astype(np.uint8)
+    w = m.prepare_weight_mxfp4(dev(codes), dev(b), flags)
+    torch.cuda.synchronize()
+    ref = np.zeros(w.desc.bytes, np.uint8)
+    _capi.w4a16_prepack_mxfp4_host(1, flags, codes, b, E, N, K, 32, ref)
+    assert np.array_equal(host(w.packed), ref)
+
+
+@pytest.mark.parametrize("tile_m,split", [(16, 1), (32, 1), (32, 3), (48, 2), (64, 1)])
+def test_mxfp4_gemm_exact_invariant(m, tile_m, split):
+    """MXFP4 weights (every E2M1 code, E8M0 scales 2^-8 .. 2^-6) with integer
+    activations in [-4, 4]: every product and every sum is exact in fp32
+    (at most 17 significant bits), so gate/up (bf16 and the fp32 accumulator)
+    and down are bit-identical to the oracle, for every tile height and K
+    split (both ring depths)."""
+    from w4a16_int4_mixture_amd import _capi
+    E, H, I, T, k = 4, 512, 128, 40, 3
+    d = exact_problem(90 + tile_m + split, E, H, I, T, k)
+    mx = synth.make_weights_mxfp4(E, H, I, seed=tile_m)
+    print(f"mxfp4 exact: tile_m={tile_m} split={split}", flush=True)
+    w13 = prepare_mx(m, mx["codes13"], mx["scales13"])
+    w2 = prepare_mx(m, mx["codes2"], mx["scales2"])
+    path = m.IndexedPath(w13, w2, T, k, E, rows_hint=T * k, tile_m=tile_m, split_k13=split,
+                         split_k2=split)
+    X = dev(d["X"])
+    path.routing.align(dev(d["topk_ids"]), E)
+    pos, f = slot_rows(path.routing, T, k)
+    e = d["topk_ids"].ravel()[f]
+    Y13 = torch.full((path.routing.sorted_cap, 2 * I), -1, dtype=torch.int16, device="cuda")
+    m.run_gemm(path.gate_up_args(X, out=Y13, epilogue=0), "cuda")
+    Y13f = torch.zeros((path.routing.sorted_cap, 2 * I), dtype=torch.float32, device="cuda")
+    m.run_gemm(path.gate_up_args(X, out=Y13f, epilogue=0, flags=1), "cuda")
+    torch.cuda.synchronize()
+    ref13 = oracle.grouped_gemm_mx(d["X"], f // k, e, mx["codes13"], mx["scales13"], 2 * I, H)
+    assert np.array_equal(host(Y13, np.uint16)[pos], ref13)
+    w_deq = oracle.dequant_mx(mx["codes13"], mx["scales13"], H).astype(np.float64)
+    xi = synth.bf16_bits_to_f32(d["X"]).astype(np.float64)
+    ref13f = np.einsum("rk,rnk->rn", xi[f // k], w_deq[e])
+    assert np.array_equal(host(Y13f)[pos].astype(np.float64), ref13f)
+    rng = np.random.default_rng(3)
+    Zi = synth.bf16_trunc(rng.integers(-4, 5, size=(path.routing.sorted_cap, I)).astype(np.float32))
+    Y2 = torch.zeros((path.routing.sorted_cap, H), dtype=torch.int16, device="cuda")
+    m.run_gemm(path.down_args(Z=dev(Zi), out=Y2), "cuda")
+    torch.cuda.synchronize()
+    ref2 = oracle.grouped_gemm_mx(Zi, pos.astype(np.int32), e, mx["codes2"], mx["scales2"], H, I)
+    assert np.array_equal(host(Y2, np.uint16)[pos], ref2)
+
+
+@pytest.mark.parametrize("interleave", [False, True])
+def test_mxfp4_path_random(m, interleave):
+    """General inputs through the MXFP4 path (SiLU*gate fused on an
+    interleaved W13, or its own kernel) against the oracle on MXFP4 weights."""
+    E, H, I, T, k, Eg = 6, 768, 256, 50, 4, 9
+    d = synth.random_small(95, E, H, I, T, k, E_global=Eg)
+    mx = synth.make_weights_mxfp4(E, H, I, seed=95)
+    w13 = prepare_mx(m, mx["codes13"], mx["scales13"], interleave)
+    w2 = prepare_mx(m, mx["codes2"], mx["scales2"])
+    path = m.IndexedPath(w13, w2, T, k, Eg, rows_hint=T * k * E // Eg)
+    out = host(path(dev(d["X"]), dev(d["topk_ids"]), dev(d["topk_weights"]),
+                    dev(d["expert_map"])), np.uint16)
+    torch.cuda.synchronize()
+    ref = oracle.moe_forward_mx(d["X"], d["topk_ids"], d["topk_weights"], Eg, d["expert_map"],
+                                mx["codes13"], mx["scales13"], mx["codes2"], mx["scales2"],
+                                intermediates=True)
+    pos, f = slot_rows(path.routing, T, k)
+    check_close(host(path.Z, np.uint16)[pos], ref["Z"][f], "mxfp4 Z")
+    check_close(host(path.Y2, np.uint16)[pos], ref["Y2"][f], "mxfp4 Y2")
+    check_close(out, ref["out"], "mxfp4 out")
+
+
+def test_mxfp4_decode_workload_full_parity(m, decode_data):
+    """The decode share with MXFP4 weights at full size (48 experts, H 7168,
+    I 2048, 64 tokens x top-8), in the benchmark's configuration: every
+    routed row of Z and Y2 and the output against the oracle."""
+    d = decode_data
+    wl = d["wl"]
+    mx = synth.make_weights_mxfp4(wl.E_local, wl.H, wl.I, seed=0)
+    w13 = prepare_mx(m, mx["codes13"], mx["scales13"], interleave=True)
+    w2 = prepare_mx(m, mx["codes2"], mx["scales2"])
+    path = m.IndexedPath(w13, w2, wl.T, wl.top_k, wl.E_global, rows_hint=512)
+    out = host(path(dev(d["X"]), dev(d["topk_ids"]), dev(d["topk_weights"]),
+                    dev(d["expert_map"])), np.uint16)
+    torch.cuda.synchronize()
+    ref = oracle.moe_forward_mx(d["X"], d["topk_ids"], d["topk_weights"], wl.E_global,
+                                d["expert_map"], mx["codes13"], mx["scales13"], mx["codes2"],
+                                mx["scales2"], intermediates=True)
+    pos, f = slot_rows(path.routing, wl.T, wl.top_k)
+    check_close(host(path.Z, np.uint16)[pos], ref["Z"][f], "mxfp4 decode Z")
+    check_close(host(path.Y2, np.uint16)[pos], ref["Y2"][f], "mxfp4 decode Y2")
+    check_close(out, ref["out"], "mxfp4 decode out")

@@ -68,6 +68,19 @@ def prepare_weight(codes: torch.Tensor, scales: torch.Tensor, profile: int, flag
     return PreparedWeight(packed, desc)
 
 
+def prepare_weight_mxfp4(codes: torch.Tensor, scales_e8m0: torch.Tensor, flags: int = 0,
+                         stream=None) -> PreparedWeight:
+    """MXFP4 weights: E2M1 codes int32 [E, N, K/8], E8M0 scale bytes uint8
+    [E, N, K/32] (device) -> packed weight (DECODE profile)."""
+    E, N, K8 = codes.shape
+    K = K8 * 8
+    nbytes = _capi.w4a16_prepack_bytes(PROFILE_DECODE, flags, E, N, K, 32)
+    packed = _dev_empty((nbytes,), torch.uint8, codes.device)
+    desc = _capi.w4a16_prepack_mxfp4(PROFILE_DECODE, flags, codes.contiguous(),
+                                     scales_e8m0.contiguous(), E, N, K, 32, packed, stream)
+    return PreparedWeight(packed, desc)
+
+
 class Routing:
     """Device buffers of the indexed routing metadata (over-allocated)."""
 

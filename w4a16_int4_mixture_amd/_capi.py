@@ -29,6 +29,7 @@ STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "MODE_MISMATCH",
 W4A16_PROFILE_DECODE = 1
 W4A16_PROFILE_PREFILL = 2
 W4A16_PACK_GATE_UP_INTERLEAVE = 0x1
+W4A16_PACK_MXFP4 = 0x2
 W4A16_DESC_MAGIC = 0x4D413457
 W4A16_DESC_VERSION = 1
 W4A16_ALIGN_VALIDATE = 0x1
@@ -109,6 +110,16 @@ SIGNATURES = {
                                           ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                           ctypes.c_uint64, ctypes.POINTER(w4a16_desc)]),
+    "w4a16_prepack_mxfp4": (ctypes.c_int, [ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                           ctypes.c_uint64, ctypes.POINTER(w4a16_desc),
+                                           ctypes.c_void_p]),
+    "w4a16_prepack_mxfp4_host": (ctypes.c_int, [ctypes.c_int32, ctypes.c_uint32,
+                                                ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_void_p, ctypes.c_uint64,
+                                                ctypes.POINTER(w4a16_desc)]),
     "w4a16_moe_align_capacity": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                 ctypes.c_int32, ctypes.c_int32, _i32p, _i32p,
                                                 _i32p]),
@@ -222,6 +233,26 @@ def w4a16_prepack_host(profile, flags, codes, scales, E, N, K, group, packed) ->
     check(lib().w4a16_prepack_host(profile, flags, codes.ctypes.data, scales.ctypes.data, E, N,
                                    K, group, packed.ctypes.data, packed.nbytes,
                                    ctypes.byref(desc)))
+    return desc
+
+
+def w4a16_prepack_mxfp4(profile, flags, codes, scales_e8m0, E, N, K, group, packed,
+                        stream=None) -> w4a16_desc:
+    desc = w4a16_desc()
+    nbytes = packed.numel() * packed.element_size()
+    check(lib().w4a16_prepack_mxfp4(profile, flags, ptr(codes), ptr(scales_e8m0), E, N, K, group,
+                                    ptr(packed), nbytes, ctypes.byref(desc),
+                                    stream_handle(stream)))
+    return desc
+
+
+def w4a16_prepack_mxfp4_host(profile, flags, codes, scales_e8m0, E, N, K, group,
+                             packed) -> w4a16_desc:
+    """Host reference of the MXFP4 permutation; numpy arrays in and out."""
+    desc = w4a16_desc()
+    check(lib().w4a16_prepack_mxfp4_host(profile, flags, codes.ctypes.data,
+                                         scales_e8m0.ctypes.data, E, N, K, group,
+                                         packed.ctypes.data, packed.nbytes, ctypes.byref(desc)))
     return desc
 
 

@@ -431,6 +431,7 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
     g.unpack_mask = 0x000F000Fu;
     g.unpack_bits = 0x43004300u;
     g.nib_mask = 0x0F0F0F0Fu;
+    g.fp4 = (d->flags & W4A16_PACK_MXFP4) ? 1 : 0;   // DECODE profile only (checked at prepack)
     const bool split = r->split > 1;
     r->silu_separate = a->epilogue == W4A16_EPI_SILU_MUL && !interleaved;
     const int64_t gx = (g.NC + 3) / 4;

@@ -63,6 +63,19 @@ __device__ inline bf16x8 codes_to_b(uint32_t w, uint32_t mask, uint32_t bits) {
     return __builtin_bit_cast(bf16x8, d);
 }
 
+// B operand of one 16-column block from MXFP4 codes: byte b of the word holds
+// the E2M1 codes of K offsets 2b (low nibble) and 2b + 1, which the hardware
+// conversion turns into two exact bf16 values (scale operand 1).
+__device__ inline bf16x8 codes_to_b_fp4(uint32_t w) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    u32x4 d;
+    d.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0));
+    d.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1));
+    d.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2));
+    d.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3));
+    return __builtin_bit_cast(bf16x8, d);
+}
+
 // Codes of one K group for one lane.
 template <int WPL>
 struct Codes {
@@ -117,7 +130,7 @@ struct Prep {
     u32x4 av[MT];
 };
 
-template <int MT, int WPL>
+template <int MT, int WPL, bool FP4>
 __device__ inline void prep_group(Prep<MT, WPL>& p, const Codes<WPL>& c, const u32x4* a_lds,
                                   const uint16_t* s_lds, uint32_t mask, uint32_t bits) {
 #pragma unroll
@@ -136,10 +149,17 @@ __device__ inline void prep_group(Prep<MT, WPL>& p, const Codes<WPL>& c, const u
     }
 #pragma unroll
     for (int i = 0; i < WPL / 4; ++i) {
-        p.b[4 * i + 0] = codes_to_b(c.w[i].x, mask, bits);
-        p.b[4 * i + 1] = codes_to_b(c.w[i].y, mask, bits);
-        p.b[4 * i + 2] = codes_to_b(c.w[i].z, mask, bits);
-        p.b[4 * i + 3] = codes_to_b(c.w[i].w, mask, bits);
+        if constexpr (FP4) {
+            p.b[4 * i + 0] = codes_to_b_fp4(c.w[i].x);
+            p.b[4 * i + 1] = codes_to_b_fp4(c.w[i].y);
+            p.b[4 * i + 2] = codes_to_b_fp4(c.w[i].z);
+            p.b[4 * i + 3] = codes_to_b_fp4(c.w[i].w);
+        } else {
+            p.b[4 * i + 0] = codes_to_b(c.w[i].x, mask, bits);
+            p.b[4 * i + 1] = codes_to_b(c.w[i].y, mask, bits);
+            p.b[4 * i + 2] = codes_to_b(c.w[i].z, mask, bits);
+            p.b[4 * i + 3] = codes_to_b(c.w[i].w, mask, bits);
+        }
     }
 #pragma unroll
     for (int i = 0; i < WPL / 2; ++i) {
@@ -158,7 +178,9 @@ __device__ inline void unpacked(const Prep<MT, WPL>& p) {
     for (int j = 0; j < WPL; ++j) asm volatile("" ::"v"(p.b[j]));
 }
 
-template <int MT, int WPL>
+// FP4 (MXFP4 weights): the operand already holds the weight values, so the
+// MFMA starts from zero instead of the -136 sum x offset.
+template <int MT, int WPL, bool FP4>
 __device__ inline void mfma_group(const Prep<MT, WPL>& p, f32x4 (&d)[MT][WPL]) {
     const bf16x8 c136 = __builtin_bit_cast(bf16x8, u32x4{0xC308C308u, 0xC308C308u,
                                                          0xC308C308u, 0xC308C308u});  // -136
@@ -166,7 +188,8 @@ __device__ inline void mfma_group(const Prep<MT, WPL>& p, f32x4 (&d)[MT][WPL]) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
         const bf16x8 a = __builtin_bit_cast(bf16x8, p.av[t]);
-        const f32x4 off = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, c136, zero, 0, 0, 0);
+        const f32x4 off =
+            FP4 ? zero : __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, c136, zero, 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < WPL; ++j)
             d[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p.b[j], off, 0, 0, 0);
@@ -185,23 +208,23 @@ __device__ inline void fma_group(const Prep<MT, WPL>& p, const f32x4 (&d)[MT][WP
 // The kSG groups of one LDS stage, software-pipelined.  `refill` = false in
 // the ring's last turn.  ring[r0 + g] holds group g of the stage; after its
 // unpack it is refilled with group `next + g`.
-template <int MT, int WPL, int D>
+template <int MT, int WPL, int D, bool FP4>
 __device__ inline void stage_groups(Codes<WPL> (&ring)[D], int r0, const u32x4* acur,
                                     const uint16_t* scur, const Src<MT>& src, int next,
                                     bool refill, f32x4 (&acc)[MT][WPL], uint32_t mask,
                                     uint32_t bits, int lane) {
     Prep<MT, WPL> pc, pn;
-    prep_group<MT, WPL>(pc, ring[r0], acur + lane, scur, mask, bits);
+    prep_group<MT, WPL, FP4>(pc, ring[r0], acur + lane, scur, mask, bits);
     unpacked<MT, WPL>(pc);
     __builtin_amdgcn_sched_barrier(0);
     if (refill) load_codes<WPL>(ring[r0], src.w, src.code_off, next);
 #pragma unroll
     for (int g = 0; g < kSG; ++g) {
         f32x4 d[MT][WPL];
-        mfma_group<MT, WPL>(pc, d);
+        mfma_group<MT, WPL, FP4>(pc, d);
         __builtin_amdgcn_sched_barrier(0);
         if (g + 1 < kSG) {
-            prep_group<MT, WPL>(pn, ring[r0 + g + 1], acur + (g + 1) * MT * 64 + lane,
+            prep_group<MT, WPL, FP4>(pn, ring[r0 + g + 1], acur + (g + 1) * MT * 64 + lane,
                                 scur + (g + 1) * 16 * WPL, mask, bits);
             unpacked<MT, WPL>(pn);
             __builtin_amdgcn_sched_barrier(0);
@@ -243,7 +266,7 @@ __device__ inline void barrier_ds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_ba
 // (D, the caller's ring depth, only keeps the instantiations of the two ring
 // variants apart: the host compilation pass rejects one instantiation reached
 // from both.)
-template <int MT, int WPL, int MTMAX, int D, bool MAYBE_VIRTUAL = false>
+template <int MT, int WPL, int MTMAX, int D, bool FP4, bool MAYBE_VIRTUAL = false>
 __device__ inline void dma_stage(const Src<MT>& src, u32x4* buf, int base, int ks_min, int ks_real,
                                  int wave, int lane) {
     constexpr int kAStage = kSG * MTMAX * 64;   // u32x4 of activations per buffer
@@ -309,7 +332,7 @@ struct Stg {
 // by one virtual record (zero scales) when it holds an odd number of records.
 // Ring slot r0 + g of a stage holds its group g: r0 = 0 for the even stage,
 // and for the odd one kSG (D = 16) or 0 (D = 8).
-template <int MT, int WPL, int MTMAX, int D>
+template <int MT, int WPL, int MTMAX, int D, bool FP4>
 __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1, int ks_real,
                                             int wave, int lane, const Stg& stg,
                                             f32x4 (&acc)[MT][WPL], uint32_t mask,
@@ -335,7 +358,7 @@ __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1
     // without the virtual stage that pads other odd stage counts
     if (ks1 - ks0 == kSG) {
         Codes<WPL> one[kSG];
-        dma_stage<MT, WPL, MTMAX, D>(src, stg.b[0], ks0, ks0, ks_real, wave, lane);
+        dma_stage<MT, WPL, MTMAX, D, FP4>(src, stg.b[0], ks0, ks0, ks_real, wave, lane);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < kSG; ++i) load_codes<WPL>(one[i], src.w, src.code_off, ks0 + i);
@@ -344,7 +367,7 @@ __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1
         // loads) that may stay in flight
         wait_vmcnt<kRefill>();                   // the stage's buffer has landed
         barrier_ds();
-        stage_groups<MT, WPL, kSG>(one, 0, abuf0, srd0, src, 0, false, acc, mask, bits, lane);
+        stage_groups<MT, WPL, kSG, FP4>(one, 0, abuf0, srd0, src, 0, false, acc, mask, bits, lane);
         return;
     }
 
@@ -357,12 +380,12 @@ __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1
     // buffer 1's loads after the ring's, as in the loop (where a stage's loads
     // follow the refills), so that the waits for ring slots match on both paths
     Codes<WPL> ring[D];
-    dma_stage<MT, WPL, MTMAX, D, true>(src, stg.b[0], kb, ks0, ks_real, wave, lane);
+    dma_stage<MT, WPL, MTMAX, D, FP4, true>(src, stg.b[0], kb, ks0, ks_real, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < D; ++i) load_codes<WPL>(ring[i], src.w, src.code_off, kb + i < ks0 ? ks0 : kb + i);
     __builtin_amdgcn_sched_barrier(0);
-    dma_stage<MT, WPL, MTMAX, D>(src, stg.b[1], kb + kSG, ks0, ks_real, wave, lane);
+    dma_stage<MT, WPL, MTMAX, D, FP4>(src, stg.b[1], kb + kSG, ks0, ks_real, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
     // issued: buffer 0, the ring (kRing), buffer 1 (kStage); the last two may
     // stay in flight
@@ -372,27 +395,27 @@ __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1
     for (int it = 0; it < nit - 1; ++it) {
         const int base = kb + it * IT;
         // even stage: buffer 0; its ring slots take groups D ahead
-        stage_groups<MT, WPL, D>(ring, 0, abuf0, srd0, src, base + D, true, acc, mask, bits, lane);
+        stage_groups<MT, WPL, D, FP4>(ring, 0, abuf0, srd0, src, base + D, true, acc, mask, bits, lane);
         // issued since buffer 1's loads: this stage's ring refills (kRefill)
         wait_vmcnt<kRefill>();                   // buffer 1 has landed
         barrier_ds();                            // (for every wavefront); buffer 0 is free
-        dma_stage<MT, WPL, MTMAX, D>(src, stg.b[0], base + IT, ks0, ks_real, wave, lane);
+        dma_stage<MT, WPL, MTMAX, D, FP4>(src, stg.b[0], base + IT, ks0, ks_real, wave, lane);
         // odd stage: buffer 1
-        stage_groups<MT, WPL, D>(ring, RO, abuf1, srd1, src, base + D + kSG, true, acc, mask, bits,
+        stage_groups<MT, WPL, D, FP4>(ring, RO, abuf1, srd1, src, base + D + kSG, true, acc, mask, bits,
                                  lane);
         // issued since buffer 0's loads: this stage's ring refills (kRefill)
         wait_vmcnt<kRefill>();                   // buffer 0 has landed
         barrier_ds();                            // buffer 1 is free
-        dma_stage<MT, WPL, MTMAX, D>(src, stg.b[1], base + IT + kSG, ks0, ks_real, wave, lane);
+        dma_stage<MT, WPL, MTMAX, D, FP4>(src, stg.b[1], base + IT + kSG, ks0, ks_real, wave, lane);
     }
     // last iteration: with a one-stage ring the even stage still refills it
     // with the odd stage's groups
     const int last = kb + (nit - 1) * IT;
-    stage_groups<MT, WPL, D>(ring, 0, abuf0, srd0, src, last + kSG, D < IT, acc, mask, bits, lane);
+    stage_groups<MT, WPL, D, FP4>(ring, 0, abuf0, srd0, src, last + kSG, D < IT, acc, mask, bits, lane);
     // issued since buffer 1's loads: the refills of this stage, if any
     wait_vmcnt<(D < IT ? kRefill : 0)>();        // buffer 1 has landed
     barrier_ds();
-    stage_groups<MT, WPL, D>(ring, RO, abuf1, srd1, src, 0, false, acc, mask, bits, lane);
+    stage_groups<MT, WPL, D, FP4>(ring, RO, abuf1, srd1, src, 0, false, acc, mask, bits, lane);
 }
 
 // Split-K fix-up.  Every split writes its fp32 partial of the tile part, then
@@ -472,7 +495,7 @@ __device__ __forceinline__ bool splitk_fixup(const GemmArgs& a, int p0, int nrow
 // `counter`: this tile's split-K arrival counter (split_k > 1).  Returns
 // whether this workgroup stored the tile's outputs (false in a K split that
 // did not arrive last); the value is the same in every thread.
-template <int MT, int WPL, int MTMAX, int D>
+template <int MT, int WPL, int MTMAX, int D, bool FP4>
 __device__ __forceinline__ bool gemm_tile_mt(const GemmArgs& a, int e, int p0, int nrows,
                                              int chunk, int s, int wave, int lane, const Stg& stg,
                                              int32_t* counter) {
@@ -520,7 +543,7 @@ __device__ __forceinline__ bool gemm_tile_mt(const GemmArgs& a, int e, int p0, i
     // only pins the register class and emits nothing
     uint32_t vbits = a.unpack_bits;
     asm volatile("" : "+v"(vbits));
-    stream_loop<MT, WPL, MTMAX, D>(src, ks0, ks1, a.KS, wave, lane, stg, acc, a.unpack_mask, vbits);
+    stream_loop<MT, WPL, MTMAX, D, FP4>(src, ks0, ks1, a.KS, wave, lane, stg, acc, a.unpack_mask, vbits);
 
     if (a.split_k > 1 && !splitk_fixup<MT, WPL>(a, p0, nrows, chunk, s, active, lane, counter, acc))
         return false;
@@ -577,21 +600,21 @@ __device__ __forceinline__ bool gemm_tile_mt(const GemmArgs& a, int e, int p0, i
     return true;
 }
 
-template <int MT, int WPL, int D>
+template <int MT, int WPL, int D, bool FP4>
 __device__ __forceinline__ bool gemm_tile_part(const GemmArgs& a, int e, int p0, int nrows,
                                                int chunk, int s, int wave, int lane, const Stg& stg,
                                                int32_t* counter) {
     const int mt_active = (nrows + 15) >> 4;
     if (mt_active <= 1)
-        return gemm_tile_mt<1, WPL, MT, D>(a, e, p0, nrows, chunk, s, wave, lane, stg, counter);
+        return gemm_tile_mt<1, WPL, MT, D, FP4>(a, e, p0, nrows, chunk, s, wave, lane, stg, counter);
     else if (MT >= 2 && mt_active == 2)
-        return gemm_tile_mt<(MT >= 2 ? 2 : 1), WPL, MT, D>(a, e, p0, nrows, chunk, s, wave, lane, stg,
+        return gemm_tile_mt<(MT >= 2 ? 2 : 1), WPL, MT, D, FP4>(a, e, p0, nrows, chunk, s, wave, lane, stg,
                                                         counter);
     else if (MT >= 3 && mt_active == 3)
-        return gemm_tile_mt<(MT >= 3 ? 3 : 1), WPL, MT, D>(a, e, p0, nrows, chunk, s, wave, lane, stg,
+        return gemm_tile_mt<(MT >= 3 ? 3 : 1), WPL, MT, D, FP4>(a, e, p0, nrows, chunk, s, wave, lane, stg,
                                                         counter);
     else
-        return gemm_tile_mt<(MT >= 4 ? 4 : 1), WPL, MT, D>(a, e, p0, nrows, chunk, s, wave, lane, stg,
+        return gemm_tile_mt<(MT >= 4 ? 4 : 1), WPL, MT, D, FP4>(a, e, p0, nrows, chunk, s, wave, lane, stg,
                                                         counter);
 }
 
@@ -599,14 +622,14 @@ __device__ __forceinline__ bool gemm_tile_part(const GemmArgs& a, int e, int p0,
 // columns), `s` its K split; the split-K arrival counter is the (tile, quad)
 // one.  With the fused combine, the workgroup that stored the tile's rows
 // then counts their tokens' arrivals (s_tok, s_n: LDS scratch).
-template <int MT, int WPL, int D>
+template <int MT, int WPL, int D, bool FP4>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int ty, int e, int p0, int nrows,
                                           int quad, int s, int wave, int lane, const Stg& stg,
                                           int* s_tok, int* s_n) {
     const int nquads = (a.NC + 3) / 4;
     int32_t* counter = a.counters + static_cast<int64_t>(ty) * nquads + quad;
     const bool stored =
-        gemm_tile_part<MT, WPL, D>(a, e, p0, nrows, quad * 4 + wave, s, wave, lane, stg, counter);
+        gemm_tile_part<MT, WPL, D, FP4>(a, e, p0, nrows, quad * 4 + wave, s, wave, lane, stg, counter);
     static_assert(4 * 64 == 256, "a quad of chunks is one 256-column combine group");
     if (a.comb_out && stored) comb_arrive(a, p0, nrows, quad, s_tok, s_n);
 }
@@ -616,7 +639,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int ty, int e, int 
 // the loop covers any device-side tile count whatever the grid.  The item
 // decision is uniform across the workgroup, so every barrier inside is
 // reached by all four wavefronts.  D: groups of the code ring (8 or 16).
-template <int MT, int WPL, int D>
+template <int MT, int WPL, int D, bool FP4>
 __device__ __forceinline__ void gemm_small_body(const GemmArgs& a) {
     __shared__ u32x4 stage0[Lds<MT, WPL>::buf];
     __shared__ u32x4 stage1[Lds<MT, WPL>::buf];
@@ -669,46 +692,46 @@ __device__ __forceinline__ void gemm_small_body(const GemmArgs& a) {
         // not computed, and nothing is stored outside the tile
         nrows = nrows < 16 * MT ? nrows : 16 * MT;
         if (e < 0 || e >= a.E || nrows <= 0) continue;
-        gemm_tile<MT, WPL, D>(a, ty, e, p0, nrows, quad, s, wave, lane, stg, s_tok, &s_n);
+        gemm_tile<MT, WPL, D, FP4>(a, ty, e, p0, nrows, quad, s, wave, lane, stg, s_tok, &s_n);
         __syncthreads();  // the next item reuses the staging buffers
     }
 }
 
-template <int MT, int WPL, int D>
+template <int MT, int WPL, int D, bool FP4>
 __global__ void __launch_bounds__(256) k_gemm_small(GemmArgs a) {
-    gemm_small_body<MT, WPL, D>(a);
+    gemm_small_body<MT, WPL, D, FP4>(a);
 }
 
 // The two-block kernel with the one-stage ring, held to three workgroups per
 // CU (168 VGPRs: four registers are kept in scratch across the K loop, none
 // inside it).
-template <int MT, int WPL, int D>
+template <int MT, int WPL, int D, bool FP4>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8)))
     k_gemm_small_w3(GemmArgs a) {
-    gemm_small_body<MT, WPL, D>(a);
+    gemm_small_body<MT, WPL, D, FP4>(a);
 }
 
-template <int MT, int D>
+template <int MT, int D, bool FP4>
 static void (*small_kernel())(GemmArgs) {
     if constexpr (MT == 2 && D == 8)
-        return k_gemm_small_w3<MT, 4, D>;
+        return k_gemm_small_w3<MT, 4, D, FP4>;
     else
-        return k_gemm_small<MT, 4, D>;
+        return k_gemm_small<MT, 4, D, FP4>;
 }
 
 // Workgroups of one kernel variant resident on the device at once (from the
 // runtime's occupancy calculation: registers and LDS), cached per variant.
-static int g_resident[5][2] = {};
+static int g_resident[5][2][2] = {};
 
-template <int MT, int D>
+template <int MT, int D, bool FP4>
 static int resident_wgs() {
-    int& cached = g_resident[MT][D == 8 ? 0 : 1];
+    int& cached = g_resident[MT][D == 8 ? 0 : 1][FP4 ? 1 : 0];
     if (cached <= 0) {
         int dev = 0, ncu = 0, per_cu = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             ncu = 256;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, small_kernel<MT, D>(), 256, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, small_kernel<MT, D, FP4>(), 256, 0) !=
                 hipSuccess ||
             per_cu <= 0)
             per_cu = 1;
@@ -717,32 +740,40 @@ static int resident_wgs() {
     return cached;
 }
 
-template <int MT, int D>
+template <int MT, int D, bool FP4>
 static void launch_mt(const GemmArgs& a, hipStream_t st) {
     // One workgroup per item (from the host's tile estimate) while they fit
     // in four rounds of resident workgroups: the hardware then hands items to
     // CUs as they free up, which balances items of unequal cost (empty
     // masked tiles).  Beyond that, items are dealt evenly to that many
     // workgroups, which saves the start-up of very short items (short K).
-    const int64_t cap = 4 * static_cast<int64_t>(resident_wgs<MT, D>());
+    const int64_t cap = 4 * static_cast<int64_t>(resident_wgs<MT, D, FP4>());
     const int64_t items = static_cast<int64_t>(a.grid_tiles) * ((a.NC + 3) / 4) * a.split_k;
     const int64_t rounds = (items + cap - 1) / cap;
     const int64_t g = rounds > 0 ? (items + rounds - 1) / rounds : 1;
-    small_kernel<MT, D>()<<<dim3(static_cast<unsigned>(g < 1 ? 1 : g)), dim3(256), 0, st>>>(a);
+    small_kernel<MT, D, FP4>()<<<dim3(static_cast<unsigned>(g < 1 ? 1 : g)), dim3(256), 0, st>>>(a);
+}
+
+template <bool FP4>
+static void launch_variant(const GemmArgs& a, int mt, bool wide, hipStream_t st) {
+    switch (mt) {
+        case 1: launch_mt<1, 8, FP4>(a, st); break;
+        case 2:
+            if (wide)
+                launch_mt<2, 8, FP4>(a, st);
+            else
+                launch_mt<2, 16, FP4>(a, st);
+            break;
+        case 3: launch_mt<3, 16, FP4>(a, st); break;
+        default: launch_mt<4, 16, FP4>(a, st); break;
+    }
 }
 
 void launch_gemm_small(const GemmArgs& a, int mt, bool wide, hipStream_t st) {
-    switch (mt) {
-        case 1: launch_mt<1, 8>(a, st); break;
-        case 2:
-            if (wide)
-                launch_mt<2, 8>(a, st);
-            else
-                launch_mt<2, 16>(a, st);
-            break;
-        case 3: launch_mt<3, 16>(a, st); break;
-        default: launch_mt<4, 16>(a, st); break;
-    }
+    if (a.fp4)
+        launch_variant<true>(a, mt, wide, st);
+    else
+        launch_variant<false>(a, mt, wide, st);
 }
 
 }  // namespace w4a16

@@ -56,6 +56,7 @@ w4a16_status check_launch(const char* what);
 struct PackGeom {
     int E, N, K, CW, NC, KS, KSP, WPL;
     bool interleave;
+    bool mxfp4;                          // E2M1 codes in canonical nibble order, E8M0 scales as bf16
     uint64_t stage_words, chunk_words;   // 32-bit words per record / per chunk
     uint64_t stage_bytes, chunk_bytes, bytes;
 };
@@ -78,7 +79,7 @@ w4a16_status check_desc(const w4a16_desc* d);
 
 // ---- launchers (defined next to their kernels) ------------------------------
 
-void launch_prepack(const PackGeom& g, const uint32_t* codes, const uint16_t* scales,
+void launch_prepack(const PackGeom& g, const uint32_t* codes, const void* scales,
                     void* packed, hipStream_t s);
 
 struct AlignArgs {
@@ -148,6 +149,7 @@ struct GemmArgs {
     uint32_t unpack_mask;  // 0x000F000F: one code in each 16-bit half
     uint32_t unpack_bits;  // 0x43004300: bf16 exponent of 128 in each half
     uint32_t nib_mask;     // 0x0F0F0F0F: one code in each byte
+    int fp4;               // MXFP4 weights (E2M1 codes): streaming kernel only
 };
 // wide: the 8-group code ring (three workgroups per CU up to two row blocks)
 // instead of the 16-group one, for two-block tiles.

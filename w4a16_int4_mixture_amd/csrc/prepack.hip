@@ -31,8 +31,12 @@ w4a16_status make_geom(int profile, uint32_t flags, int E, int N, int K, int gro
         set_error("unknown profile %d", profile);
         return W4A16_ERR_UNSUPPORTED;
     }
-    if (flags & ~W4A16_PACK_GATE_UP_INTERLEAVE) {
+    if (flags & ~(W4A16_PACK_GATE_UP_INTERLEAVE | W4A16_PACK_MXFP4)) {
         set_error("unknown prepack flags 0x%x", flags);
+        return W4A16_ERR_UNSUPPORTED;
+    }
+    if ((flags & W4A16_PACK_MXFP4) && profile != W4A16_PROFILE_DECODE) {
+        set_error("MXFP4 weights are packed with the DECODE profile only");
         return W4A16_ERR_UNSUPPORTED;
     }
     if (E <= 0 || N <= 0 || K <= 0) {
@@ -60,6 +64,7 @@ w4a16_status make_geom(int profile, uint32_t flags, int E, int N, int K, int gro
     g->KSP = static_cast<int>(round_up(static_cast<uint64_t>(g->KS), 8));
     g->WPL = cw / 16;
     g->interleave = (flags & W4A16_PACK_GATE_UP_INTERLEAVE) != 0;
+    g->mxfp4 = (flags & W4A16_PACK_MXFP4) != 0;
     g->stage_words = 576ull * g->WPL;                    // 512 WPL code words + 64 WPL scale words
     g->chunk_words = g->stage_words * (g->KSP / 8);
     g->stage_bytes = g->stage_words * 4;
@@ -96,10 +101,20 @@ __host__ __device__ static inline uint32_t permute_word(uint32_t w) {
     return out;
 }
 
+// The bf16 scale of (row, group): the bf16 scale itself, or for MXFP4 the
+// E8M0 byte b as the bf16 2^(b - 127) (exact: exponent field b, or the
+// subnormal 2^-127 for b = 0; b = 255 is NaN).
+__host__ __device__ static inline uint32_t scale_bits(const void* scales, const PackGeom& g,
+                                                      int64_t idx) {
+    if (!g.mxfp4) return static_cast<const uint16_t*>(scales)[idx];
+    const uint32_t b = static_cast<const uint8_t*>(scales)[idx];
+    return b == 255 ? 0x7FC0u : b == 0 ? 0x0040u : b << 7;
+}
+
 // PREFILL record word `in` (see the layout in internal.h): codes in their
 // canonical nibble order, one 16-byte group per (group, half, lane).
 __host__ __device__ static inline uint32_t prefill_word(const uint32_t* codes,
-                                                        const uint16_t* scales, const PackGeom& g,
+                                                        const void* scales, const PackGeom& g,
                                                         int64_t e, int c, int stage, int in) {
     if (in < 4096) {
         const int v = in & 3, lane = (in >> 2) & 63, h = (in >> 8) & 1;
@@ -117,7 +132,7 @@ __host__ __device__ static inline uint32_t prefill_word(const uint32_t* codes,
         uint32_t v = 0;
         if (ks < g.KS) {
             const int n = canonical_column(c * 128 + 32 * (h + 2 * jj) + c32, g.N, 128, g.interleave);
-            v = scales[(e * g.N + n) * g.KS + ks];
+            v = scale_bits(scales, g, (e * g.N + n) * g.KS + ks);
         }
         out |= v << (16 * hh);
     }
@@ -125,7 +140,7 @@ __host__ __device__ static inline uint32_t prefill_word(const uint32_t* codes,
 }
 
 // Word w of the packed buffer, from the canonical codes and scales.
-__host__ __device__ static inline uint32_t packed_word(const uint32_t* codes, const uint16_t* scales,
+__host__ __device__ static inline uint32_t packed_word(const uint32_t* codes, const void* scales,
                                                        const PackGeom& g, uint64_t w) {
     const uint64_t chunk_id = w / g.chunk_words;        // e * NC + c
     const int64_t e = static_cast<int64_t>(chunk_id / g.NC);
@@ -141,7 +156,10 @@ __host__ __device__ static inline uint32_t packed_word(const uint32_t* codes, co
         const int ks = stage * 8 + in / (64 * g.WPL);
         if (ks >= g.KS) return 0u;
         const int n = canonical_column(c * g.CW + 16 * j + (lane & 15), g.N, g.CW, g.interleave);
-        return permute_word(codes[(e * g.N + n) * (g.K / 8) + ks * 4 + (lane >> 4)]);
+        // INT4: nibbles permuted for the 128 + q operand trick; MXFP4: the
+        // canonical order, byte b holding K offsets 2b (low) and 2b + 1
+        const uint32_t cw = codes[(e * g.N + n) * (g.K / 8) + ks * 4 + (lane >> 4)];
+        return g.mxfp4 ? cw : permute_word(cw);
     }
     uint32_t out = 0;
     for (int h = 0; h < 2; ++h) {
@@ -152,21 +170,21 @@ __host__ __device__ static inline uint32_t packed_word(const uint32_t* codes, co
         uint32_t v = 0;
         if (ks < g.KS) {
             const int n = canonical_column(c * g.CW + 16 * j + c16, g.N, g.CW, g.interleave);
-            v = scales[(e * g.N + n) * g.KS + ks];
+            v = scale_bits(scales, g, (e * g.N + n) * g.KS + ks);
         }
         out |= v << (16 * h);
     }
     return out;
 }
 
-__global__ void k_prepack(const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+__global__ void k_prepack(const uint32_t* __restrict__ codes, const void* __restrict__ scales,
                           uint32_t* __restrict__ out, PackGeom g, uint64_t total) {
     const uint64_t w = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (w >= total) return;
     out[w] = packed_word(codes, scales, g, w);
 }
 
-void launch_prepack(const PackGeom& g, const uint32_t* codes, const uint16_t* scales,
+void launch_prepack(const PackGeom& g, const uint32_t* codes, const void* scales,
                     void* packed, hipStream_t s) {
     const uint64_t total = g.bytes / 4;
     k_prepack<<<dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s>>>(
@@ -174,7 +192,7 @@ void launch_prepack(const PackGeom& g, const uint32_t* codes, const uint16_t* sc
 }
 
 // Host reference of the same permutation.
-static void prepack_host(const PackGeom& g, const uint32_t* codes, const uint16_t* scales,
+static void prepack_host(const PackGeom& g, const uint32_t* codes, const void* scales,
                          void* packed) {
     uint32_t* out = static_cast<uint32_t*>(packed);
     const uint64_t total = g.bytes / 4;
@@ -198,7 +216,7 @@ static void fill_desc(const PackGeom& g, int profile, uint32_t flags, w4a16_desc
 }
 
 static w4a16_status prepack_common(int32_t profile, uint32_t flags, const int32_t* codes,
-                                   const uint16_t* scales, int32_t E, int32_t N, int32_t K,
+                                   const void* scales, int32_t E, int32_t N, int32_t K,
                                    int32_t group, void* packed, uint64_t packed_bytes,
                                    w4a16_desc* desc, PackGeom* g, bool device) {
     w4a16_status st = make_geom(profile, flags, E, N, K, group, g);
@@ -207,7 +225,7 @@ static w4a16_status prepack_common(int32_t profile, uint32_t flags, const int32_
     W4A16_CHECK_ARG(!device || (reinterpret_cast<uintptr_t>(packed) & 255) == 0,
                     "packed buffer must be 256-byte aligned");
     W4A16_CHECK_ARG((reinterpret_cast<uintptr_t>(codes) & 3) == 0 &&
-                        (reinterpret_cast<uintptr_t>(scales) & 1) == 0,
+                        ((flags & W4A16_PACK_MXFP4) || (reinterpret_cast<uintptr_t>(scales) & 1) == 0),
                     "codes/scales misaligned");
     if ((flags & W4A16_PACK_GATE_UP_INTERLEAVE) && (N % 2 != 0)) {
         set_error("gate/up interleave needs an even N");
@@ -238,11 +256,10 @@ extern "C" w4a16_status w4a16_prepack_bytes(int32_t profile, uint32_t flags, int
     return W4A16_OK;
 }
 
-extern "C" w4a16_status w4a16_prepack(int32_t profile, uint32_t flags, const int32_t* codes,
-                                      const uint16_t* scales, int32_t E, int32_t N, int32_t K,
-                                      int32_t group, void* packed, uint64_t packed_bytes,
-                                      w4a16_desc* desc, void* stream) {
-    clear_error();
+static w4a16_status prepack_device(int32_t profile, uint32_t flags, const int32_t* codes,
+                                   const void* scales, int32_t E, int32_t N, int32_t K,
+                                   int32_t group, void* packed, uint64_t packed_bytes,
+                                   w4a16_desc* desc, void* stream) {
     PackGeom g;
     w4a16_status st = prepack_common(profile, flags, codes, scales, E, N, K, group, packed,
                                      packed_bytes, desc, &g, true);
@@ -255,11 +272,10 @@ extern "C" w4a16_status w4a16_prepack(int32_t profile, uint32_t flags, const int
     return W4A16_OK;
 }
 
-extern "C" w4a16_status w4a16_prepack_host(int32_t profile, uint32_t flags, const int32_t* codes,
-                                           const uint16_t* scales, int32_t E, int32_t N,
-                                           int32_t K, int32_t group, void* packed,
-                                           uint64_t packed_bytes, w4a16_desc* desc) {
-    clear_error();
+static w4a16_status prepack_on_host(int32_t profile, uint32_t flags, const int32_t* codes,
+                                    const void* scales, int32_t E, int32_t N, int32_t K,
+                                    int32_t group, void* packed, uint64_t packed_bytes,
+                                    w4a16_desc* desc) {
     PackGeom g;
     w4a16_status st = prepack_common(profile, flags, codes, scales, E, N, K, group, packed,
                                      packed_bytes, desc, &g, false);
@@ -267,4 +283,44 @@ extern "C" w4a16_status w4a16_prepack_host(int32_t profile, uint32_t flags, cons
     prepack_host(g, reinterpret_cast<const uint32_t*>(codes), scales, packed);
     fill_desc(g, profile, flags, desc);
     return W4A16_OK;
+}
+
+extern "C" w4a16_status w4a16_prepack(int32_t profile, uint32_t flags, const int32_t* codes,
+                                      const uint16_t* scales, int32_t E, int32_t N, int32_t K,
+                                      int32_t group, void* packed, uint64_t packed_bytes,
+                                      w4a16_desc* desc, void* stream) {
+    clear_error();
+    W4A16_CHECK_ARG(!(flags & W4A16_PACK_MXFP4), "MXFP4 weights go through w4a16_prepack_mxfp4");
+    return prepack_device(profile, flags, codes, scales, E, N, K, group, packed, packed_bytes,
+                          desc, stream);
+}
+
+extern "C" w4a16_status w4a16_prepack_host(int32_t profile, uint32_t flags, const int32_t* codes,
+                                           const uint16_t* scales, int32_t E, int32_t N,
+                                           int32_t K, int32_t group, void* packed,
+                                           uint64_t packed_bytes, w4a16_desc* desc) {
+    clear_error();
+    W4A16_CHECK_ARG(!(flags & W4A16_PACK_MXFP4), "MXFP4 weights go through w4a16_prepack_mxfp4_host");
+    return prepack_on_host(profile, flags, codes, scales, E, N, K, group, packed, packed_bytes,
+                           desc);
+}
+
+extern "C" w4a16_status w4a16_prepack_mxfp4(int32_t profile, uint32_t flags, const int32_t* codes,
+                                            const uint8_t* scales_e8m0, int32_t E, int32_t N,
+                                            int32_t K, int32_t group, void* packed,
+                                            uint64_t packed_bytes, w4a16_desc* desc,
+                                            void* stream) {
+    clear_error();
+    return prepack_device(profile, flags | W4A16_PACK_MXFP4, codes, scales_e8m0, E, N, K, group,
+                          packed, packed_bytes, desc, stream);
+}
+
+extern "C" w4a16_status w4a16_prepack_mxfp4_host(int32_t profile, uint32_t flags,
+                                                 const int32_t* codes, const uint8_t* scales_e8m0,
+                                                 int32_t E, int32_t N, int32_t K, int32_t group,
+                                                 void* packed, uint64_t packed_bytes,
+                                                 w4a16_desc* desc) {
+    clear_error();
+    return prepack_on_host(profile, flags | W4A16_PACK_MXFP4, codes, scales_e8m0, E, N, K, group,
+                           packed, packed_bytes, desc);
 }
