@@ -445,3 +445,26 @@ def test_host_prepack_mxfp4_matches_documented_layout():
     sc16 = np.zeros((E, N, K // 32), np.uint16)
     assert status_of(capi.w4a16_prepack_host, capi.W4A16_PROFILE_DECODE, capi.W4A16_PACK_MXFP4,
                      codes, sc16, E, N, K, 32, packed) == capi.W4A16_ERR_INVALID_ARG
+
+
+def test_prepare_weight_refuses_codes_it_would_misread():
+    """The packer sizes its reads from the codes' shape (eight 4-bit codes per
+    int32 word): codes of another dtype, or scales of another shape or dtype,
+    are refused on the host before any kernel runs."""
+    import torch
+    import w4a16_int4_mixture_amd as m
+    E, N, K = 2, 64, 256
+    good_c = torch.zeros((E, N, K // 8), dtype=torch.int32)
+    good_s = torch.zeros((E, N, K // 32), dtype=torch.int16)
+    for c, s in [(torch.zeros((E, N, K), dtype=torch.uint8), good_s),        # one code per byte
+                 (good_c.to(torch.int64), good_s),
+                 (good_c, torch.zeros((E, N, K // 16), dtype=torch.int16)),  # wrong group count
+                 (good_c, good_s.to(torch.float32)),
+                 (good_c[0], good_s[0])]:
+        with pytest.raises(ValueError):
+            m.prepare_weight(c, s, m.PROFILE_DECODE)
+    with pytest.raises(ValueError):
+        m.prepare_weight_mxfp4(good_c, good_s)                               # E8M0 scales are bytes
+    with pytest.raises(ValueError):
+        m.prepare_weight_mxfp4(torch.zeros((E, N, K), dtype=torch.uint8),
+                               torch.zeros((E, N, K // 32), dtype=torch.uint8))

@@ -233,6 +233,71 @@ def test_pipelined_main_loop_exact(m, H, tile_m, profile):
     assert bad.size == 0, f"{bad.size} rows differ, first positions {pos[bad[:8]]}"
 
 
+def many_items_problem(seed, E, K, N, T, k):
+    """Integer activations, power-of-two scales (every fp32 sum exact), and
+    routing of T tokens to k distinct experts of E, for a grouped GEMM of
+    [E, N, K] codes."""
+    rng = np.random.default_rng(seed)
+    X = synth.bf16_trunc(rng.integers(-4, 5, size=(T, K)).astype(np.float32))
+    codes = synth.random_codes(rng, E, N, K)            # int32 [E, N, K/8]
+    scales = synth.bf16_trunc(np.exp2(-rng.integers(6, 9, size=(E, N, K // 32))).astype(np.float32))
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    return X, codes, scales, ids
+
+
+# (K, N, tile_m): one, two and three stages per item, one- and two-block
+# tiles; about 12 rows per expert over 128 experts: 1500 - 2300 items, two or
+# more per resident workgroup of the streaming kernel
+@pytest.mark.parametrize("K,N,tile_m", [(256, 4096, 16), (512, 4096, 16), (256, 3072, 32),
+                                        (768, 3072, 32)])
+def test_many_item_launches_exact(m, K, N, tile_m):
+    """Launches of the streaming kernel with more items than resident
+    workgroups, bit-exact under the exactness invariant: fp32 and bf16
+    outputs of every routed row."""
+    E, T, k = 128, 192, 8
+    X, codes, scales, ids = many_items_problem(K + N + tile_m, E, K, N, T, k)
+    print(f"many items: K={K} N={N} tile_m={tile_m}", flush=True)
+    from w4a16_int4_mixture_amd import _capi
+    w = prepare(m, codes, scales, 1)
+    r = m.Routing(T, k, E, 16, tile_m, "cuda")
+    r.align(dev(ids), E)
+    pos, f = slot_rows(r, T, k)
+    ref = oracle.grouped_gemm(X, f // k, ids.ravel()[f], codes, scales, N, K, out_f32=True)
+    Yf = torch.full((r.sorted_cap, N), float("nan"), dtype=torch.float32, device="cuda")
+    m.run_gemm(m.gemm_args_indexed(w, dev(X), r, Yf, _capi.W4A16_AROW_TOKEN, flags=1, split_k=1,
+                                   rows_hint=T * k), "cuda")
+    got = host(Yf)[pos]
+    bad = np.nonzero(np.any(got != ref, axis=1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first positions {pos[bad[:8]]}"
+    Yb = torch.full((r.sorted_cap, N), -1, dtype=torch.int16, device="cuda")
+    m.run_gemm(m.gemm_args_indexed(w, dev(X), r, Yb, _capi.W4A16_AROW_TOKEN, split_k=1,
+                                   rows_hint=T * k), "cuda")
+    assert np.array_equal(host(Yb, np.uint16)[pos], oracle.bf16_from_f64(ref.astype(np.float64)))
+
+
+def test_many_item_launch_fused_silu(m):
+    """The SiLU * gate epilogue (gate/up interleave) of a launch of ~2300
+    items: within one bf16 ulp of the oracle's SiLU of its gate/up rows."""
+    E, T, k, K, I = 128, 192, 8, 256, 2048
+    X, codes, scales, ids = many_items_problem(77, E, K, 2 * I, T, k)
+    w = prepare(m, codes, scales, 1, interleave=True)
+    r = m.Routing(T, k, E, 16, 16, "cuda")
+    r.align(dev(ids), E)
+    from w4a16_int4_mixture_amd import _capi
+    Z = torch.full((r.sorted_cap, I), -1, dtype=torch.int16, device="cuda")
+    m.run_gemm(m.gemm_args_indexed(w, dev(X), r, Z, _capi.W4A16_AROW_TOKEN,
+                                   epilogue=_capi.W4A16_EPI_SILU_MUL, split_k=1, rows_hint=T * k),
+               "cuda")
+    pos, f = slot_rows(r, T, k)
+    ref13 = oracle.moe_gate_up(X, ids, E, None, codes, scales)
+    def ordinal(b):   # bf16 bits -> integers in value order (+0 and -0 both 0)
+        b = b.astype(np.int32)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b)
+    got = ordinal(host(Z, np.uint16)[pos])
+    refz = ordinal(oracle.silu_mul(ref13)[f])
+    assert np.abs(got - refz).max() <= 1
+
+
 # ------------------------------------------------------ large-M kernel ----
 
 @pytest.mark.parametrize("H", [1024, 1056, 1248])

@@ -56,11 +56,25 @@ class PreparedWeight:
         return self.desc.K
 
 
+def _check_weight_inputs(codes: torch.Tensor, scales: torch.Tensor, scale_dtypes, what: str):
+    """The packer reads codes and scales through raw pointers sized from the
+    codes' shape: refuse a dtype or shape that does not match it."""
+    if codes.dim() != 3 or codes.dtype != torch.int32:
+        raise ValueError(f"{what}: codes must be int32 [E, N, K/8] (eight 4-bit codes per word), "
+                         f"got {codes.dtype} {tuple(codes.shape)}")
+    E, N, K8 = codes.shape
+    if scales.dtype not in scale_dtypes or tuple(scales.shape) != (E, N, K8 * 8 // 32):
+        raise ValueError(f"{what}: scales must be {[str(d) for d in scale_dtypes]} "
+                         f"[{E}, {N}, {K8 * 8 // 32}], got {scales.dtype} {tuple(scales.shape)}")
+    if codes.device != scales.device:
+        raise ValueError(f"{what}: codes and scales on different devices")
+    return E, N, K8 * 8
+
+
 def prepare_weight(codes: torch.Tensor, scales: torch.Tensor, profile: int, flags: int = 0,
                    stream=None) -> PreparedWeight:
     """codes int32 [E, N, K/8], scales bf16 bits [E, N, K/32] (device) -> packed weight."""
-    E, N, K8 = codes.shape
-    K = K8 * 8
+    E, N, K = _check_weight_inputs(codes, scales, (torch.int16, torch.bfloat16), "prepare_weight")
     nbytes = _capi.w4a16_prepack_bytes(profile, flags, E, N, K, 32)
     packed = _dev_empty((nbytes,), torch.uint8, codes.device)
     desc = _capi.w4a16_prepack(profile, flags, codes.contiguous(), scales.contiguous(), E, N, K,
@@ -72,8 +86,7 @@ def prepare_weight_mxfp4(codes: torch.Tensor, scales_e8m0: torch.Tensor, flags: 
                          stream=None) -> PreparedWeight:
     """MXFP4 weights: E2M1 codes int32 [E, N, K/8], E8M0 scale bytes uint8
     [E, N, K/32] (device) -> packed weight (DECODE profile)."""
-    E, N, K8 = codes.shape
-    K = K8 * 8
+    E, N, K = _check_weight_inputs(codes, scales_e8m0, (torch.uint8,), "prepare_weight_mxfp4")
     nbytes = _capi.w4a16_prepack_bytes(PROFILE_DECODE, flags, E, N, K, 32)
     packed = _dev_empty((nbytes,), torch.uint8, codes.device)
     desc = _capi.w4a16_prepack_mxfp4(PROFILE_DECODE, flags, codes.contiguous(),

@@ -67,7 +67,6 @@ __device__ inline bf16x8 codes_to_b(uint32_t w, uint32_t mask, uint32_t bits) {
 // the E2M1 codes of K offsets 2b (low nibble) and 2b + 1, which the hardware
 // conversion turns into two exact bf16 values (scale operand 1).
 __device__ inline bf16x8 codes_to_b_fp4(uint32_t w) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     u32x4 d;
     d.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0));
     d.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1));
@@ -491,19 +490,16 @@ __device__ __forceinline__ bool splitk_fixup(const GemmArgs& a, int p0, int nrow
     return true;
 }
 
-// One (row tile, 4 column chunks, K split) with MT active row blocks.
-// `counter`: this tile's split-K arrival counter (split_k > 1).  Returns
-// whether this workgroup stored the tile's outputs (false in a K split that
-// did not arrive last); the value is the same in every thread.
-template <int MT, int WPL, int MTMAX, int D, bool FP4>
-__device__ __forceinline__ bool gemm_tile_mt(const GemmArgs& a, int e, int p0, int nrows,
-                                             int chunk, int s, int wave, int lane, const Stg& stg,
-                                             int32_t* counter) {
+// Where the wavefront on `chunk` of a tile reads: the activation row of each
+// of this lane's MFMA A rows (rows past the tile reuse its first row: MFMA
+// rows are independent and are not stored) and the expert's packed chunk.  A
+// wavefront past the last chunk re-streams the last chunk (cache hits, only
+// when N / CW is not a multiple of 4) and stores nothing: the loop stays free
+// of wavefront-dependent branches.
+template <int MT, int WPL>
+__device__ __forceinline__ Src<MT> make_src(const GemmArgs& a, int e, int p0, int nrows,
+                                             int chunk, int lane) {
     const bool slot_rows = a.tile_src != TILE_MASKED;
-    const bool active = chunk < a.NC;
-
-    // activation row of each of this lane's MFMA A rows (rows past the tile
-    // reuse its first row: MFMA rows are independent and are not stored)
     Src<MT> src;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
@@ -521,39 +517,22 @@ __device__ __forceinline__ bool gemm_tile_mt(const GemmArgs& a, int e, int p0, i
         src.a_off[t] = static_cast<uint32_t>(row * a.K * 2 + 16 * (lane >> 4));
     }
     src.x = make_rsrc(a.A, static_cast<uint64_t>(a.A_rows) * a.K * 2);
-
-    // K split s covers whole records [ks0, ks1)
-    const int nrec = a.KSP / 8;
-    const int ks0 = 8 * static_cast<int>(static_cast<int64_t>(s) * nrec / a.split_k);
-    const int ks1 = 8 * static_cast<int>(static_cast<int64_t>(s + 1) * nrec / a.split_k);
-    // a wavefront past the last chunk re-streams the last chunk (cache hits,
-    // only when N / CW is not a multiple of 4) and stores nothing: the loop
-    // stays free of wavefront-dependent branches
-    const int64_t cbase = static_cast<int64_t>(e) * a.NC + (active ? chunk : a.NC - 1);
+    const int64_t cbase = static_cast<int64_t>(e) * a.NC + (chunk < a.NC ? chunk : a.NC - 1);
     src.w = make_rsrc(a.packed + cbase * a.chunk_words, static_cast<uint64_t>(a.chunk_words) * 4);
     src.code_off = static_cast<uint32_t>(lane * WPL * 4);
+    return src;
+}
 
-    f32x4 acc[MT][WPL];
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-        for (int j = 0; j < WPL; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // the exponent pattern lives in a VGPR so that (x & mask) | bits is one
-    // v_and_or_b32 (a VALU op reads at most one scalar operand); the empty asm
-    // only pins the register class and emits nothing
-    uint32_t vbits = a.unpack_bits;
-    asm volatile("" : "+v"(vbits));
-    stream_loop<MT, WPL, MTMAX, D, FP4>(src, ks0, ks1, a.KS, wave, lane, stg, acc, a.unpack_mask, vbits);
-
-    if (a.split_k > 1 && !splitk_fixup<MT, WPL>(a, p0, nrows, chunk, s, active, lane, counter, acc))
-        return false;
-    if (!active) return true;
+// Stores the tile's rows from the accumulators: lane holds rows 16t +
+// 4*(lane/16) + i of column 16j + lane%16 of the chunk.
+template <int MT, int WPL>
+__device__ __forceinline__ void store_tile(const GemmArgs& a, int p0, int nrows, int chunk,
+                                           int lane, const f32x4 (&acc)[MT][WPL]) {
+    const bool slot_rows = a.tile_src != TILE_MASKED;
     // with the fused combine, the rows are stored with device-scope stores:
     // the workgroup that sums a token may run on another XCD
     const __amdgpu_buffer_rsrc_t ydev =
         make_rsrc(a.out, a.comb_out ? static_cast<uint64_t>(a.sorted_cap) * a.N * 2 : 0);
-
-    // epilogue: lane holds rows 16t + 4*(lane/16) + i of column 16j + lane%16
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
 #pragma unroll
@@ -597,6 +576,39 @@ __device__ __forceinline__ bool gemm_tile_mt(const GemmArgs& a, int e, int p0, i
             }
         }
     }
+}
+
+// One (row tile, 4 column chunks, K split) with MT active row blocks.
+// `counter`: this tile's split-K arrival counter (split_k > 1).  Returns
+// whether this workgroup stored the tile's outputs (false in a K split that
+// did not arrive last); the value is the same in every thread.
+template <int MT, int WPL, int MTMAX, int D, bool FP4>
+__device__ __forceinline__ bool gemm_tile_mt(const GemmArgs& a, int e, int p0, int nrows,
+                                             int chunk, int s, int wave, int lane, const Stg& stg,
+                                             int32_t* counter) {
+    const bool active = chunk < a.NC;
+    const Src<MT> src = make_src<MT, WPL>(a, e, p0, nrows, chunk, lane);
+
+    // K split s covers whole records [ks0, ks1)
+    const int nrec = a.KSP / 8;
+    const int ks0 = 8 * static_cast<int>(static_cast<int64_t>(s) * nrec / a.split_k);
+    const int ks1 = 8 * static_cast<int>(static_cast<int64_t>(s + 1) * nrec / a.split_k);
+
+    f32x4 acc[MT][WPL];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int j = 0; j < WPL; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the exponent pattern lives in a VGPR so that (x & mask) | bits is one
+    // v_and_or_b32 (a VALU op reads at most one scalar operand); the empty asm
+    // only pins the register class and emits nothing
+    uint32_t vbits = a.unpack_bits;
+    asm volatile("" : "+v"(vbits));
+    stream_loop<MT, WPL, MTMAX, D, FP4>(src, ks0, ks1, a.KS, wave, lane, stg, acc, a.unpack_mask, vbits);
+
+    if (a.split_k > 1 && !splitk_fixup<MT, WPL>(a, p0, nrows, chunk, s, active, lane, counter, acc))
+        return false;
+    if (active) store_tile<MT, WPL>(a, p0, nrows, chunk, lane, acc);
     return true;
 }
 
@@ -723,16 +735,13 @@ static void (*small_kernel())(GemmArgs) {
 // runtime's occupancy calculation: registers and LDS), cached per variant.
 static int g_resident[5][2][2] = {};
 
-template <int MT, int D, bool FP4>
-static int resident_wgs() {
-    int& cached = g_resident[MT][D == 8 ? 0 : 1][FP4 ? 1 : 0];
+static int resident_of(void (*kern)(GemmArgs), int& cached) {
     if (cached <= 0) {
         int dev = 0, ncu = 0, per_cu = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             ncu = 256;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, small_kernel<MT, D, FP4>(), 256, 0) !=
-                hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess ||
             per_cu <= 0)
             per_cu = 1;
         cached = ncu * per_cu;
@@ -741,14 +750,19 @@ static int resident_wgs() {
 }
 
 template <int MT, int D, bool FP4>
+static int resident_wgs() {
+    return resident_of(small_kernel<MT, D, FP4>(), g_resident[MT][D == 8 ? 0 : 1][FP4 ? 1 : 0]);
+}
+
+template <int MT, int D, bool FP4>
 static void launch_mt(const GemmArgs& a, hipStream_t st) {
+    const int64_t items = static_cast<int64_t>(a.grid_tiles) * ((a.NC + 3) / 4) * a.split_k;
     // One workgroup per item (from the host's tile estimate) while they fit
     // in four rounds of resident workgroups: the hardware then hands items to
     // CUs as they free up, which balances items of unequal cost (empty
     // masked tiles).  Beyond that, items are dealt evenly to that many
     // workgroups, which saves the start-up of very short items (short K).
     const int64_t cap = 4 * static_cast<int64_t>(resident_wgs<MT, D, FP4>());
-    const int64_t items = static_cast<int64_t>(a.grid_tiles) * ((a.NC + 3) / 4) * a.split_k;
     const int64_t rounds = (items + cap - 1) / cap;
     const int64_t g = rounds > 0 ? (items + rounds - 1) / rounds : 1;
     small_kernel<MT, D, FP4>()<<<dim3(static_cast<unsigned>(g < 1 ? 1 : g)), dim3(256), 0, st>>>(a);
