@@ -286,6 +286,74 @@ def moe_forward_mx(X, topk_ids, topk_weights, E_global, expert_map, codes13, sca
     return out
 
 
+def e4m3_value(b: int) -> float:
+    """Value of an E4M3 byte (OCP 8-bit float, NaN at 0x7F / 0xFF)."""
+    f = _load().oracle_e4m3_value
+    f.restype = ctypes.c_double
+    return float(f(ctypes.c_int(int(b))))
+
+
+def e4m3_from_double(v: float) -> int:
+    """Nearest E4M3 code (ties to even mantissa; saturating at 448)."""
+    f = _load().oracle_e4m3_from_double
+    f.argtypes = [ctypes.c_double]
+    return int(f(float(v)))
+
+
+def quantize_mxfp8(x, K: int | None = None):
+    """bf16 bits [rows, K] -> (E4M3 codes uint8 [rows, K], E8M0 scales uint8
+    [rows, K/32]): the OCP microscaling conversion per block of 32."""
+    x = _c(x, np.uint16)
+    K = x.shape[-1] if K is None else K
+    rows = x.size // K
+    codes = np.empty(x.shape[:-1] + (K,), dtype=np.uint8)
+    scales = np.empty(x.shape[:-1] + (K // 32,), dtype=np.uint8)
+    _load().oracle_quantize_mxfp8(_p(x), ctypes.c_int64(rows), ctypes.c_int64(K), _p(codes),
+                                  _p(scales))
+    return codes, scales
+
+
+def grouped_gemm_a8w4(A8, A_sc, a_row, expert, codes, scales_e8m0, N: int, K: int,
+                      out_f32: bool = False) -> np.ndarray:
+    """Grouped GEMM on MXFP8 activations (codes A8 [rows, K], scales A_sc
+    [rows, K/32]) and MXFP4 weights; bf16 bits or fp32 out."""
+    A8 = _c(A8, np.uint8)
+    A_sc = _c(A_sc, np.uint8)
+    a_row = _c(a_row, np.int32)
+    expert = _c(expert, np.int32)
+    R = a_row.size
+    out = np.zeros((R, N), dtype=np.float32 if out_f32 else np.uint16)
+    _load().oracle_grouped_gemm_a8w4(_p(A8), _p(A_sc), _p(a_row), _p(expert), ctypes.c_int64(R),
+                                     _p(_c(codes, np.int32)), _p(_c(scales_e8m0, np.uint8)), N, K,
+                                     int(out_f32), _p(out))
+    return out
+
+
+def moe_forward_a8w4(X, topk_ids, topk_weights, E_global, expert_map, codes13, scales13,
+                     codes2, scales2, intermediates=False):
+    """The indexed path in A8W4: MXFP8 activations (X and Z quantized per row)
+    on MXFP4 weights."""
+    X = _c(X, np.uint16)
+    ids = _c(topk_ids, np.int32)
+    T, k = ids.shape
+    E_local, N13, _ = codes13.shape
+    I = N13 // 2
+    H = X.shape[1]
+    out = np.empty((T, H), dtype=np.uint16)
+    Z = Y2 = None
+    if intermediates:
+        Z = np.empty((T * k, I), dtype=np.uint16)
+        Y2 = np.empty((T * k, H), dtype=np.uint16)
+    _load().oracle_moe_forward_a8w4(_p(X), _p(ids), _p(_c(topk_weights, np.float32)), T, k,
+                                    E_global, _p(_c(expert_map, np.int32)), E_local,
+                                    _p(_c(codes13, np.int32)), _p(_c(scales13, np.uint8)),
+                                    _p(_c(codes2, np.int32)), _p(_c(scales2, np.uint8)), H, I,
+                                    _p(out), _p(Z), _p(Y2))
+    if intermediates:
+        return {"out": out, "Z": Z, "Y2": Y2}
+    return out
+
+
 def router_topk(logits, k):
     """Router logits float32 [T, E] -> (topk_ids int32 [T, k], weights float32
     [T, k]): largest logits first (ties: lower id first), softmax over the k

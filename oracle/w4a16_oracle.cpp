@@ -160,6 +160,74 @@ inline double dot_row_mx(const uint16_t* a, const uint32_t* row_words, const uin
     return static_cast<double>(acc);
 }
 
+// ---- A8W4: MXFP8 activations on MXFP4 weights ----------------------------
+//
+// The pages name A8W4 fused operators (8-bit activations, 4-bit weights)
+// beside the A16W4 ones on AMD ("vLLM publishes Kimi K3 production support",
+// MXFP4 MoE section) and give no format.  Reading: the activations take the
+// same OCP microscaling form as the MXFP4 weights, with E4M3 elements: one
+// E8M0 scale per block of 32 along K.
+//
+// E4M3 (OCP 8-bit float, no infinities): sign bit 7, exponent bits 6..3
+// (bias 7), mantissa bits 2..0; value (-1)^s 2^(e-7) (1 + m/8) for e > 0 and
+// (-1)^s 2^-6 m/8 for e = 0; exponent 15 with mantissa 7 is NaN, so the
+// largest finite magnitude is 448 (code 0x7E).
+inline double e4m3_value(uint8_t b) {
+    const int e = (b >> 3) & 15, m = b & 7;
+    if (e == 15 && m == 7) return std::nan("");
+    const double mag = e == 0 ? std::ldexp(m / 8.0, -6) : std::ldexp(1.0 + m / 8.0, e - 7);
+    return (b & 0x80) ? -mag : mag;
+}
+
+// The E4M3 code nearest to v, ties to the code with an even mantissa; a
+// magnitude above 448 saturates to 448.  By search over the 127 finite
+// non-negative codes (their values increase with the code).
+inline uint8_t e4m3_from_double(double v) {
+    const uint8_t sign = std::signbit(v) ? 0x80 : 0x00;
+    const double a = std::fabs(v);
+    if (a >= 448.0) return sign | 0x7E;
+    int best = 0;
+    for (int c = 1; c <= 0x7E; ++c) {
+        const double dc = std::fabs(e4m3_value(static_cast<uint8_t>(c)) - a);
+        const double db = std::fabs(e4m3_value(static_cast<uint8_t>(best)) - a);
+        if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+    }
+    return sign | static_cast<uint8_t>(best);
+}
+
+// One block of 32 activations -> (E8M0 scale byte, 32 E4M3 codes), after the
+// OCP microscaling conversion: X = 2^(floor(log2 amax) - 8), 8 being the
+// exponent of E4M3's largest normal, kept inside E8M0's range [2^-127,
+// 2^127]; each element is the E4M3 code nearest to x / X (saturating).  An
+// all-zero block takes the scale byte 0 and zero codes.
+inline uint8_t mx_block_quantize(const uint16_t* x, uint8_t* codes) {
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i) amax = std::max(amax, std::fabs(static_cast<double>(bf16_to_float(x[i]))));
+    if (amax == 0.0) {
+        for (int i = 0; i < 32; ++i) codes[i] = 0;
+        return 0;
+    }
+    int ex = 0;
+    std::frexp(amax, &ex);              // amax = f 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1
+    int b = (ex - 1) - 8 + 127;
+    b = b < 0 ? 0 : b > 254 ? 254 : b;
+    for (int i = 0; i < 32; ++i)
+        codes[i] = e4m3_from_double(std::ldexp(static_cast<double>(bf16_to_float(x[i])), 127 - b));
+    return static_cast<uint8_t>(b);
+}
+
+// One output element of A8W4: sum over c ascending of a[c] * w[c] in fp32,
+// a[c] = e4m3(code) * 2^(scale - 127) (exact in fp32 within its range).
+inline double dot_row_a8w4(const uint8_t* a8, const uint8_t* a_sc, const uint32_t* row_words,
+                           const uint8_t* row_scales, int64_t K) {
+    float acc = 0.0f;
+    for (int64_t c = 0; c < K; ++c) {
+        const float a = static_cast<float>(e4m3_value(a8[c])) * e8m0_value(a_sc[c / 32]);
+        acc += a * weight_at_mx(row_words, row_scales, c);
+    }
+    return static_cast<double>(acc);
+}
+
 }  // namespace
 
 extern "C" {
@@ -453,6 +521,78 @@ void oracle_grouped_gemm_mx(const uint16_t* A, const int32_t* a_row, const int32
             out[r * N + n] = bf16_from_double(dot_row_mx(a, codes + wr * wpr, scales + wr * spr, K));
         }
     }
+}
+
+// ---- A8W4 ---------------------------------------------------------------------
+
+int oracle_e4m3_from_double(double v) { return e4m3_from_double(v); }
+double oracle_e4m3_value(int b) { return e4m3_value(static_cast<uint8_t>(b)); }
+
+// MXFP8 form of rows x K bf16 activations (K a multiple of 32): E4M3 codes
+// [rows, K] and E8M0 scale bytes [rows, K/32].
+void oracle_quantize_mxfp8(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes,
+                           uint8_t* scales) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < K / 32; ++b)
+            scales[r * (K / 32) + b] = mx_block_quantize(x + r * K + 32 * b, codes + r * K + 32 * b);
+}
+
+// The grouped GEMM of O4 / O6 in A8W4: out[r, n] = sum_c a[a_row[r], c] *
+// w[expert[r], n, c] over MXFP8 activations and MXFP4 weights, fp32
+// accumulation; bf16 out (out_f32 = 0) or fp32.
+void oracle_grouped_gemm_a8w4(const uint8_t* A8, const uint8_t* A_sc, const int32_t* a_row,
+                              const int32_t* expert, int64_t R, const uint32_t* codes,
+                              const uint8_t* scales, int N, int K, int out_f32, void* out) {
+    const int64_t wpr = K / 8, spr = K / 32;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < R; ++r) {
+        const int e = expert[r];
+        if (e < 0) continue;
+        const int64_t ar = a_row[r];
+        for (int n = 0; n < N; ++n) {
+            const int64_t wr = static_cast<int64_t>(e) * N + n;
+            const double v = dot_row_a8w4(A8 + ar * K, A_sc + ar * (K / 32), codes + wr * wpr,
+                                          scales + wr * spr, K);
+            if (out_f32) static_cast<float*>(out)[r * N + n] = static_cast<float>(v);
+            else static_cast<uint16_t*>(out)[r * N + n] = bf16_from_double(v);
+        }
+    }
+}
+
+// The whole indexed path O4 -> O7 in A8W4: X is quantized to MXFP8 per token
+// row before gate/up, and Z per slot row before down; the other rounding
+// points are those of the W4A16 path.
+void oracle_moe_forward_a8w4(const uint16_t* X, const int32_t* topk_ids, const float* topk_w,
+                             int T, int top_k, int E_global, const int32_t* expert_map,
+                             int E_local, const uint32_t* codes13, const uint8_t* scales13,
+                             const uint32_t* codes2, const uint8_t* scales2, int H, int I,
+                             uint16_t* out, uint16_t* Z_opt, uint16_t* Y2_opt) {
+    const int64_t slots = static_cast<int64_t>(T) * top_k;
+    std::vector<uint16_t> y13(slots * 2 * I, 0), zv, y2v;
+    uint16_t* Z = Z_opt;
+    uint16_t* Y2 = Y2_opt;
+    if (!Z) { zv.resize(slots * I); Z = zv.data(); }
+    if (!Y2) { y2v.resize(slots * H); Y2 = y2v.data(); }
+    std::memset(Z, 0, slots * I * sizeof(uint16_t));
+    std::memset(Y2, 0, slots * H * sizeof(uint16_t));
+    std::vector<uint8_t> x8(static_cast<size_t>(T) * H), xs(static_cast<size_t>(T) * (H / 32));
+    oracle_quantize_mxfp8(X, T, H, x8.data(), xs.data());
+    std::vector<int32_t> tok_row(slots), slot_row(slots), expert(slots), row_of(slots);
+    for (int64_t f = 0; f < slots; ++f) {
+        tok_row[f] = static_cast<int32_t>(f / top_k);
+        slot_row[f] = static_cast<int32_t>(f);
+        expert[f] = local_expert(topk_ids, f, E_global, expert_map, E_local);
+        row_of[f] = expert[f] >= 0 ? static_cast<int32_t>(f) : -1;
+    }
+    oracle_grouped_gemm_a8w4(x8.data(), xs.data(), tok_row.data(), expert.data(), slots, codes13,
+                             scales13, 2 * I, H, 0, y13.data());
+    oracle_silu_mul(y13.data(), slots, I, Z);
+    std::vector<uint8_t> z8(slots * I), zs(slots * (I / 32));
+    oracle_quantize_mxfp8(Z, slots, I, z8.data(), zs.data());
+    oracle_grouped_gemm_a8w4(z8.data(), zs.data(), slot_row.data(), expert.data(), slots, codes2,
+                             scales2, H, I, 0, Y2);
+    oracle_combine(Y2, row_of.data(), topk_w, T, top_k, H, out);
 }
 
 // ---- the step before the expert GEMMs: routing ----------------------------

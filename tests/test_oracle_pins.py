@@ -663,3 +663,134 @@ def test_mxfp4_path_equals_int4_path_on_shared_values():
                              intermediates=True)
     for key in ("Y13", "Z", "Y2", "out"):
         assert np.array_equal(mx[key], ref[key]), key
+
+
+# ------------------------------------------------------------------ A8W4 ----
+
+def test_e4m3_values_closed_forms():
+    """E4M3 bytes by the format's definition: 1.0, the largest finite 448, the
+    smallest subnormal 2^-9, the smallest normal 2^-6, -3, -0 and the two NaNs."""
+    assert oracle.e4m3_value(0x38) == 1.0
+    assert oracle.e4m3_value(0x7E) == 448.0
+    assert oracle.e4m3_value(0x01) == 2.0 ** -9
+    assert oracle.e4m3_value(0x07) == 7 * 2.0 ** -9
+    assert oracle.e4m3_value(0x08) == 2.0 ** -6
+    assert oracle.e4m3_value(0xC4) == -3.0
+    v = oracle.e4m3_value(0x80)
+    assert v == 0.0 and np.signbit(v)
+    assert np.isnan(oracle.e4m3_value(0x7F)) and np.isnan(oracle.e4m3_value(0xFF))
+
+
+def test_e4m3_rounding_matches_torch_and_saturates():
+    """Nearest-even E4M3 rounding against torch's float8_e4m3fn conversion on
+    every code, every midpoint between neighbouring codes (ties) and random
+    values up to torch's last non-NaN input; beyond 448 + 16 the encoder
+    saturates to 448."""
+    import torch
+    vals = [oracle.e4m3_value(b) for b in range(0x7F)]
+    mids = [(a + b) / 2 for a, b in zip(vals[:-1], vals[1:])]
+    rng = np.random.default_rng(80)
+    rand = list(rng.uniform(-463.9, 463.9, 2000)) + list(np.exp2(rng.uniform(-12, 8, 2000)))
+    xs = np.array(vals + mids + [-v for v in mids] + rand, np.float32)
+    want = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_from_double(float(x)) for x in xs], np.uint8)
+    assert np.array_equal(got, want)
+    assert oracle.e4m3_from_double(1e6) == 0x7E and oracle.e4m3_from_double(-470.0) == 0xFE
+
+
+def test_mxfp8_block_scale_and_codes():
+    """Block rules of the microscaling conversion: amax = 2^k gives scale byte
+    k - 8 + 127 and code 0x78 (256) for that element; amax = 3 * 2^k gives
+    k + 1 - 8 + 127 and 0x7C (384), 1.5 * 2^k gives k - 8 + 127 and 0x7C; an all-zero block gives byte 0 and zero
+    codes; other elements are x / 2^(b - 127) rounded as torch rounds them."""
+    import torch
+    rng = np.random.default_rng(81)
+    for k_exp, mant, b_want, c_want in [(0, 1.0, 119, 0x78), (5, 3.0, 125, 0x7C),
+                                        (-20, 1.0, 99, 0x78), (100, 1.5, 219, 0x7C)]:
+        x = rng.uniform(-1, 1, 32) * mant * 2.0 ** k_exp * 0.9
+        x[7] = mant * 2.0 ** k_exp
+        xb = synth.bf16_trunc(x.astype(np.float32)).reshape(1, 32)
+        codes, sc = oracle.quantize_mxfp8(xb)
+        assert sc[0, 0] == b_want and codes[0, 7] == c_want
+        xf = synth.bf16_bits_to_f32(xb[0]).astype(np.float64) / 2.0 ** (int(sc[0, 0]) - 127)
+        want = torch.from_numpy(xf.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8)
+        assert np.array_equal(codes[0], want.numpy())
+    codes, sc = oracle.quantize_mxfp8(np.zeros((1, 64), np.uint16))
+    assert np.all(codes == 0) and np.all(sc == 0)
+
+
+def test_mxfp8_quantization_error_bound():
+    """Every element of a block lies within half an E4M3 step of x: 2^-4 |x|
+    in the normal range, 2^-10 X below it (X the block scale); elements of
+    blocks whose amax/X exceeds 448 saturate at 448 X."""
+    rng = np.random.default_rng(82)
+    x = synth.bf16_trunc((rng.standard_normal((64, 256)) * np.exp2(rng.integers(-30, 30, (64, 1))))
+                         .astype(np.float32))
+    codes, sc = oracle.quantize_mxfp8(x)
+    xf = synth.bf16_bits_to_f32(x).astype(np.float64)
+    X = np.repeat(np.exp2(sc.astype(np.float64) - 127), 32, axis=1)
+    deq = np.vectorize(oracle.e4m3_value)(codes) * X
+    err = np.abs(deq - xf)
+    sat = np.abs(xf) > 448 * X
+    assert np.all(np.abs(deq[sat]) == 448 * X[sat])
+    ok = ~sat
+    assert np.all(err[ok] <= np.maximum(np.abs(xf[ok]) * 2.0 ** -4, X[ok] * 2.0 ** -10))
+
+
+def test_a8w4_gemm_reads_dequantized_activations():
+    """The A8W4 GEMM on MXFP8 activations equals the MXFP4 GEMM on the
+    activations' dequantised values (exact in bf16), bit for bit; and a one-hot
+    MXFP8 row reads one weight column times e4m3 * 2^(b - 127)."""
+    rng = np.random.default_rng(83)
+    E, N, K, R = 3, 32, 128, 20
+    codes = rng.integers(0, 2**32, size=(E, N, K // 8), dtype=np.uint32).view(np.int32)
+    ws = rng.integers(120, 134, size=(E, N, K // 32)).astype(np.uint8)
+    X = synth.bf16_trunc(rng.standard_normal((R, K)).astype(np.float32))
+    x8, xs = oracle.quantize_mxfp8(X)
+    deq = np.vectorize(oracle.e4m3_value)(x8) * np.repeat(np.exp2(xs.astype(np.float64) - 127), 32, 1)
+    Xd = synth.bf16_trunc(deq.astype(np.float32))
+    assert np.array_equal(synth.bf16_bits_to_f32(Xd).astype(np.float64), deq)   # exact in bf16
+    a_row = np.arange(R, dtype=np.int32)
+    ex = rng.integers(-1, E, R).astype(np.int32)
+    got = oracle.grouped_gemm_a8w4(x8, xs, a_row, ex, codes, ws, N, K)
+    want = oracle.grouped_gemm_mx(Xd, a_row, ex, codes, ws, N, K)
+    assert np.array_equal(got[ex >= 0], want[ex >= 0])
+    # one-hot: code 0x44 (3) at K position 37 with scale byte 130 (x8)
+    a8 = np.zeros((1, K), np.uint8); a8[0, 37] = 0x44
+    asc = np.full((1, K // 32), 127, np.uint8); asc[0, 1] = 130
+    w = oracle.dequant_mx(codes, ws, K)
+    for e in range(E):
+        got = oracle.grouped_gemm_a8w4(a8, asc, np.zeros(1, np.int32), np.array([e], np.int32),
+                                       codes, ws, N, K, out_f32=True)[0]
+        assert np.array_equal(got.astype(np.float64), 24.0 * w[e, :, 37].astype(np.float64) + 0.0)
+
+
+def test_a8w4_forward_is_the_composition_and_close_to_mxfp4():
+    """The A8W4 indexed path equals its stages run one by one (X quantized per
+    token, Z per slot row), and stays close to the bf16-activation MXFP4 path
+    on the same weights (the activations' 3-bit mantissas cost at most a few
+    per cent)."""
+    rng = np.random.default_rng(84)
+    E, H, I, T, k = 4, 256, 128, 9, 2
+    d = synth.random_small(84, E, H, I, T, k)
+    w = synth.make_weights_mxfp4(E, H, I, seed=84)
+    r = oracle.moe_forward_a8w4(d["X"], d["topk_ids"], d["topk_weights"], E, None, w["codes13"],
+                                w["scales13"], w["codes2"], w["scales2"], intermediates=True)
+    slots = T * k
+    ex = d["topk_ids"].ravel().astype(np.int32)
+    x8, xs = oracle.quantize_mxfp8(d["X"])
+    y13 = oracle.grouped_gemm_a8w4(x8, xs, np.arange(slots, dtype=np.int32) // k, ex,
+                                   w["codes13"], w["scales13"], 2 * I, H)
+    z = oracle.silu_mul(y13)
+    assert np.array_equal(z, r["Z"])
+    z8, zs = oracle.quantize_mxfp8(z)
+    y2 = oracle.grouped_gemm_a8w4(z8, zs, np.arange(slots, dtype=np.int32), ex, w["codes2"],
+                                  w["scales2"], H, I)
+    assert np.array_equal(y2, r["Y2"])
+    out = oracle.combine(y2, np.arange(slots, dtype=np.int32), d["topk_weights"])
+    assert np.array_equal(out, r["out"])
+    ref = oracle.moe_forward_mx(d["X"], d["topk_ids"], d["topk_weights"], E, None, w["codes13"],
+                                w["scales13"], w["codes2"], w["scales2"])
+    a = synth.bf16_bits_to_f32(r["out"]).astype(np.float64)
+    b = synth.bf16_bits_to_f32(ref).astype(np.float64)
+    assert np.abs(a - b).max() <= 0.1 * np.abs(b).max()
