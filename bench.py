@@ -51,7 +51,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode",
                    choices=["decode", "prefill", "tp8", "masked", "contiguous", "decode_mxfp4",
-                            "tiny"])
+                            "decode_a8w4", "tiny"])
     p.add_argument("--copies", type=int, default=2, help="prepacked weight copies rotated per call")
     p.add_argument("--no-prefill", action="store_true",
                    help="do not add the prefill sub-object to the decode line")
@@ -111,6 +111,8 @@ def workload_name(name, wl):
         "contiguous": "grouped contiguous EP8 prefill share: 48 experts x 128 rows, H7168 I2048",
         "decode_mxfp4": "EP8 decode share with MXFP4 weights (E2M1 codes, E8M0 scales per 32): "
                         "48 local experts, H7168 I2048, 64 tokens x top-8",
+        "decode_a8w4": "EP8 decode share in A8W4 (MXFP8 activations, MXFP4 weights, E8M0 scales "
+                       "per 32): 48 local experts, H7168 I2048, 64 tokens x top-8",
         "tiny": "tiny: 8 experts, top-2, H256 I128, 16 tokens",
     }[name]
 
@@ -131,8 +133,9 @@ def run_workload(name, args, src_hash, cpu_legs=True):
         return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
 
     t0 = time.time()
-    mxfp4 = name.endswith("_mxfp4")
-    base = name[: -len("_mxfp4")] if mxfp4 else name
+    a8 = name.endswith("_a8w4")
+    mxfp4 = name.endswith("_mxfp4") or a8
+    base = name.rsplit("_", 1)[0] if mxfp4 else name
     d = synth.make_workload(base, seed=0, weights=not mxfp4)
     wl = d["wl"]
     if mxfp4:
@@ -148,8 +151,10 @@ def run_workload(name, args, src_hash, cpu_legs=True):
     for _ in range(max(1, args.copies)):
         # W13 with gate/up interleave: SiLU*gate runs in the gate/up epilogue
         if mxfp4:
-            copies.append((m.prepare_weight_mxfp4(codes13, scales13, m.PACK_GATE_UP_INTERLEAVE),
-                           m.prepare_weight_mxfp4(codes2, scales2)))
+            fa8 = m.PACK_MXFP8_ACT if a8 else 0
+            copies.append((m.prepare_weight_mxfp4(codes13, scales13,
+                                                  m.PACK_GATE_UP_INTERLEAVE | fa8),
+                           m.prepare_weight_mxfp4(codes2, scales2, fa8)))
         else:
             copies.append((m.prepare_weight(codes13, scales13, profile,
                                             m.PACK_GATE_UP_INTERLEAVE),
@@ -223,10 +228,14 @@ def run_workload(name, args, src_hash, cpu_legs=True):
 
         def stages(p):
             ga, da = p.stage_args(X, tw)
-            st = [("align", lambda: p.routing.align(ids, wl.E_global, em)),
-                  ("gate_up", lambda: m._capi.w4a16_moe_w4a16_gemm(ga))]
+            st = [("align", lambda: p.routing.align(ids, wl.E_global, em))]
+            if p.a8:
+                st.append(("quant_x", lambda: p.quant_x(X)))
+            st.append(("gate_up", lambda: m._capi.w4a16_moe_w4a16_gemm(ga)))
             if p.separate_act:
                 st.append(("act", lambda: p.act()))
+            if p.a8:
+                st.append(("quant_z", lambda: p.quant_z()))
             st.append(("down", lambda: m._capi.w4a16_moe_w4a16_gemm(da)))
             if not p.fuse_combine:
                 st.append(("combine", lambda: p.combine(tw)))
@@ -435,8 +444,9 @@ def _oracle_call(oracle, d, wl, workload, tokens):
     # contiguous workload computes the same rows as the indexed path
     wmode = 1 if workload in ("prefill", "contiguous") else 0
     n = tokens
-    fwd = oracle.moe_forward_mx if workload.endswith("_mxfp4") else oracle.moe_forward
-    kw = {} if workload.endswith("_mxfp4") else {"wmode": wmode}
+    fwd = (oracle.moe_forward_a8w4 if workload.endswith("_a8w4") else
+           oracle.moe_forward_mx if workload.endswith("_mxfp4") else oracle.moe_forward)
+    kw = {} if workload.endswith(("_mxfp4", "_a8w4")) else {"wmode": wmode}
     fwd(d["X"][:n], d["topk_ids"][:n], d["topk_weights"][:n], wl.E_global, d["expert_map"],
         d["codes13"], d["scales13"], d["codes2"], d["scales2"], **kw)
 

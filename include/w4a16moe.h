@@ -94,6 +94,14 @@ typedef enum {
     scales).  DECODE profile only; the GEMM then runs the streaming kernel's
     MXFP4 variant */
 
+#define W4A16_PACK_MXFP8_ACT 0x4u /* with W4A16_PACK_MXFP4 (w4a16_prepack_mxfp4,
+    DECODE profile): A8W4, MXFP4 weights for MXFP8 activations (news.ainew.jp,
+    "vLLM publishes Kimi K3 production support", MXFP4 MoE: A8W4 fused
+    operators on AMD, 8-bit activations on 4-bit weights).  The weights are
+    laid out for CDNA4's block-scaled matrix instruction (E4M3 x E2M1, 128 K
+    per instruction, E8M0 scales applied by the hardware), and every GEMM on
+    them takes MXFP8 activations (w4a16_gemm_args.A_scales) */
+
 #define W4A16_DESC_MAGIC 0x4D413457u   /* "W4AM" as little-endian bytes */
 #define W4A16_DESC_VERSION 1u
 
@@ -408,6 +416,16 @@ typedef struct {
     const int32_t* comb_row_of;     /* device int32 [comb_T * top_k]: row_of from w4a16_moe_align */
     const float* comb_weights;      /* device float [comb_T, top_k] */
     int32_t comb_T;                 /* tokens */
+    /* A8W4 (a weight packed with W4A16_PACK_MXFP8_ACT; NULL otherwise, else
+       MODE_MISMATCH): A then holds MXFP8 activations, E4M3 bytes [A_rows, K],
+       and A_scales their E8M0 block scales, bytes [A_rows, K/32] (both as
+       w4a16_quantize_mxfp8 writes them), so that
+         out[p, n] = sum_c e4m3(A[row, c]) 2^(A_scales[row, c/32] - 127) * w[e][n][c]
+       with fp32 accumulation inside the matrix instruction (an order the
+       hardware fixes: the sum is exact whenever every partial sum is).
+       INDEXED layout only, no K split (split_k overrides ignored), no fused
+       combine (UNSUPPORTED); A_rows * K bytes below 4 GiB. */
+    const uint8_t* A_scales;
 } w4a16_gemm_args;
 
 /* Workspace needed by this GEMM call (0 when none).  Host call. */
@@ -455,6 +473,23 @@ w4a16_status w4a16_moe_w4a16_gemm_noalloc(const w4a16_gemm_args* args, void* str
 /* ------------------------------------------------------------------------ */
 w4a16_status w4a16_moe_silu_mul(const uint16_t* y13, int64_t rows, const int32_t* rows_dev,
                                 int32_t I, uint16_t* z, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* MXFP8 activations for A8W4 (news.ainew.jp, "vLLM publishes Kimi K3        */
+/* production support", MXFP4 MoE: A8W4 operators, 8-bit activations).  The */
+/* OCP microscaling conversion of each block of 32 along a row:              */
+/*   scale byte b = clamp(floor(log2 amax) - 8 + 127, 0, 254)  (8: exponent  */
+/*   of E4M3's largest normal; an all-zero block takes b = 0)                */
+/*   code_i = E4M3 nearest to x_i / 2^(b - 127), ties to the even mantissa,  */
+/*            saturating at +-448                                            */
+/*   x: device bf16 [rows, K], finite; codes: device uint8 [rows, K];        */
+/*   scales: device uint8 [rows, K/32]; K a positive multiple of 32.         */
+/* Rows [0, min(*rows_dev, rows)) when rows_dev != NULL (device count, e.g.  */
+/* num_tokens_padded), else [0, rows).  INVALID_ARG on null or misaligned    */
+/* buffers (x and codes 16 bytes) or a bad K.                                */
+/* ------------------------------------------------------------------------ */
+w4a16_status w4a16_quantize_mxfp8(const uint16_t* x, int64_t rows, const int32_t* rows_dev,
+                                  int32_t K, uint8_t* codes, uint8_t* scales, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Top-k weighted combine (Chord page, "Measurements": the expert outputs of */

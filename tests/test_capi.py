@@ -447,6 +447,56 @@ def test_host_prepack_mxfp4_matches_documented_layout():
                      codes, sc16, E, N, K, 32, packed) == capi.W4A16_ERR_INVALID_ARG
 
 
+def test_host_prepack_a8w4_matches_documented_layout():
+    """MXFP4 weights for MXFP8 activations (PACK_MXFP8_ACT): per record of 256
+    K, the B-operand slices of the block-scaled instruction (lane l: column
+    16j + l%16, 32 canonical codes from K = 256r + 128s + 32(l/16)), then one
+    word of four E8M0 bytes per (step, lane); padding groups zero; the
+    interleave permutes columns as for INT4.  The flag needs MXFP4."""
+    rng = np.random.default_rng(19)
+    E, N, K = 2, 128, 288                   # 9 groups: the second record is mostly padding
+    KS, nrec, NC = K // 32, 2, N // 64
+    codes = rng.integers(0, 2**32, size=(E, N, K // 8), dtype=np.uint32)
+    b = rng.integers(0, 256, size=(E, N, KS)).astype(np.uint8)
+    for flags in (capi.W4A16_PACK_MXFP8_ACT,
+                  capi.W4A16_PACK_MXFP8_ACT | capi.W4A16_PACK_GATE_UP_INTERLEAVE):
+        nb = capi.w4a16_prepack_bytes(capi.W4A16_PROFILE_DECODE, flags | capi.W4A16_PACK_MXFP4,
+                                      E, N, K)
+        assert nb == E * NC * nrec * 544 * 4 * 4
+        packed = np.zeros(nb, np.uint8)
+        desc = capi.w4a16_prepack_mxfp4_host(capi.W4A16_PROFILE_DECODE, flags,
+                                             codes.view(np.int32), b, E, N, K, 32, packed)
+        assert desc.flags == flags | capi.W4A16_PACK_MXFP4
+        if flags & capi.W4A16_PACK_GATE_UP_INTERLEAVE:
+            perm = np.array([(nn // 64) * 32 + (nn % 64) if nn % 64 < 32 else
+                             N // 2 + (nn // 64) * 32 + (nn % 64) - 32 for nn in range(N)])
+        else:
+            perm = np.arange(N)
+        cw = np.zeros((E, N, nrec * 32), np.uint32)           # codes padded to whole records
+        cw[:, :, :K // 8] = codes[:, perm]
+        bw = np.zeros((E, N, nrec * 8), np.uint32)
+        bw[:, :, :KS] = b[:, perm]
+        words = packed.view(np.uint32).reshape(E, NC, nrec, 2176)
+        for r in range(nrec):
+            for s_ in range(2):
+                for j in range(4):
+                    for lane in range(64):
+                        n = np.arange(NC) * 64 + 16 * j + lane % 16
+                        base = ((s_ * 4 + j) * 64 + lane) * 4
+                        kw = r * 32 + s_ * 16 + 4 * (lane // 16)
+                        assert np.array_equal(words[:, :, r, base:base + 4], cw[:, n, kw:kw + 4])
+                for lane in range(64):
+                    blk = r * 8 + 4 * s_ + lane // 16
+                    want = sum(bw[:, np.arange(NC) * 64 + 16 * j + lane % 16, blk] << (8 * j)
+                               for j in range(4))
+                    assert np.array_equal(words[:, :, r, 2048 + s_ * 64 + lane], want)
+    packed = np.zeros(capi.w4a16_prepack_bytes(capi.W4A16_PROFILE_DECODE, 0, E, N, K), np.uint8)
+    sc16 = np.zeros((E, N, KS), np.uint16)
+    assert status_of(capi.w4a16_prepack_host, capi.W4A16_PROFILE_DECODE,
+                     capi.W4A16_PACK_MXFP8_ACT, codes.view(np.int32), sc16, E, N, K, 32,
+                     packed) == capi.W4A16_ERR_UNSUPPORTED
+
+
 def test_prepare_weight_refuses_codes_it_would_misread():
     """The packer sizes its reads from the codes' shape (eight 4-bit codes per
     int32 word): codes of another dtype, or scales of another shape or dtype,
@@ -468,3 +518,31 @@ def test_prepare_weight_refuses_codes_it_would_misread():
     with pytest.raises(ValueError):
         m.prepare_weight_mxfp4(torch.zeros((E, N, K), dtype=torch.uint8),
                                torch.zeros((E, N, K // 32), dtype=torch.uint8))
+
+
+def test_a8w4_argument_checks():
+    """A weight packed for MXFP8 activations needs A_scales, and A_scales needs
+    such a weight (MODE_MISMATCH either way); A8W4 runs the indexed layout
+    without K splits (an override is ignored: no workspace) and without the
+    fused combine; the quantizer refuses a K that is not a multiple of 32."""
+    E, N, K = 2, 128, 256
+    codes = np.zeros((E, N, K // 8), np.int32)
+    b = np.zeros((E, N, K // 32), np.uint8)
+    fl = capi.W4A16_PACK_MXFP8_ACT
+    packed = np.zeros(capi.w4a16_prepack_bytes(capi.W4A16_PROFILE_DECODE,
+                                               fl | capi.W4A16_PACK_MXFP4, E, N, K), np.uint8)
+    d8 = capi.w4a16_prepack_mxfp4_host(capi.W4A16_PROFILE_DECODE, fl, codes, b, E, N, K, 32,
+                                       packed)
+    fake = 1 << 20
+    assert ws_status(gemm_args(d8, A_scales=fake)) == capi.W4A16_OK
+    assert ws_status(gemm_args(d8)) == capi.W4A16_ERR_MODE_MISMATCH
+    assert ws_status(gemm_args(host_desc(K=K), A_scales=fake)) == capi.W4A16_ERR_MODE_MISMATCH
+    assert capi.w4a16_gemm_workspace_bytes(gemm_args(d8, A_scales=fake, split_k=2)) == 0
+    m = dict(layout=capi.W4A16_LAYOUT_MASKED, masked_m=fake, max_m=32, expected_m=32,
+             A_rows=64, out_rows=64, A_scales=fake)
+    assert ws_status(gemm_args(d8, **m)) == capi.W4A16_ERR_UNSUPPORTED
+    assert ws_status(gemm_args(d8, A_scales=fake, comb_out=fake, comb_row_of=fake,
+                               comb_weights=fake, comb_T=32)) == capi.W4A16_ERR_UNSUPPORTED
+    for bad_k in (0, 48):
+        assert capi.lib().w4a16_quantize_mxfp8(fake, 4, None, bad_k, fake, fake, None) == \
+            capi.W4A16_ERR_INVALID_ARG

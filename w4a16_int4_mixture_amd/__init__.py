@@ -23,7 +23,8 @@ import torch
 from . import _capi
 from ._capi import (W4A16Error, W4A16_PROFILE_DECODE as PROFILE_DECODE,  # noqa: F401
                     W4A16_PROFILE_PREFILL as PROFILE_PREFILL,
-                    W4A16_PACK_GATE_UP_INTERLEAVE as PACK_GATE_UP_INTERLEAVE)
+                    W4A16_PACK_GATE_UP_INTERLEAVE as PACK_GATE_UP_INTERLEAVE,
+                    W4A16_PACK_MXFP8_ACT as PACK_MXFP8_ACT)
 
 BF16 = torch.int16  # bf16 tensors travel as raw 16-bit patterns
 
@@ -85,9 +86,10 @@ def prepare_weight(codes: torch.Tensor, scales: torch.Tensor, profile: int, flag
 def prepare_weight_mxfp4(codes: torch.Tensor, scales_e8m0: torch.Tensor, flags: int = 0,
                          stream=None) -> PreparedWeight:
     """MXFP4 weights: E2M1 codes int32 [E, N, K/8], E8M0 scale bytes uint8
-    [E, N, K/32] (device) -> packed weight (DECODE profile)."""
+    [E, N, K/32] (device) -> packed weight (DECODE profile).  flags may add
+    PACK_MXFP8_ACT (A8W4: the GEMMs then take MXFP8 activations)."""
     E, N, K = _check_weight_inputs(codes, scales_e8m0, (torch.uint8,), "prepare_weight_mxfp4")
-    nbytes = _capi.w4a16_prepack_bytes(PROFILE_DECODE, flags, E, N, K, 32)
+    nbytes = _capi.w4a16_prepack_bytes(PROFILE_DECODE, flags | _capi.W4A16_PACK_MXFP4, E, N, K, 32)
     packed = _dev_empty((nbytes,), torch.uint8, codes.device)
     desc = _capi.w4a16_prepack_mxfp4(PROFILE_DECODE, flags, codes.contiguous(),
                                      scales_e8m0.contiguous(), E, N, K, 32, packed, stream)
@@ -120,9 +122,32 @@ class Routing:
                               self.block_m, self.c, flags, stream)
 
 
+class MXFP8:
+    """MXFP8 activations (A8W4): E4M3 codes uint8 [rows, K] and E8M0 scale
+    bytes uint8 [rows, K/32] on the device."""
+
+    def __init__(self, rows: int, K: int, device="cuda"):
+        self.codes = _dev_empty((rows, K), torch.uint8, device)
+        self.scales = _dev_empty((rows, K // 32), torch.uint8, device)
+        self.shape = (rows, K)
+
+    def data_ptr(self):
+        return self.codes.data_ptr()
+
+
+def quantize_mxfp8(x: torch.Tensor, out: MXFP8 = None, rows_dev=None, stream=None) -> MXFP8:
+    """bf16 bits [rows, K] -> MXFP8 (the library's microscaling conversion),
+    rows [0, min(*rows_dev, rows)) when rows_dev (device int32 [1]) is given."""
+    rows, K = x.shape
+    out = MXFP8(rows, K, x.device) if out is None else out
+    _capi.w4a16_quantize_mxfp8(x, rows, rows_dev, K, out.codes, out.scales, stream)
+    return out
+
+
 def gemm_args_indexed(w: PreparedWeight, A, routing: Routing, out, arow, epilogue=0, flags=0,
                       split_k=0, rows_hint=0, workspace=None, orow=_capi.W4A16_OROW_POSITION,
                       use_tiles=True):
+    """A: bf16 bits [rows, K], or MXFP8 for a weight packed with PACK_MXFP8_ACT."""
     a = _capi.w4a16_gemm_args()
     a.layout = _capi.W4A16_LAYOUT_INDEXED
     a.epilogue = epilogue
@@ -130,6 +155,8 @@ def gemm_args_indexed(w: PreparedWeight, A, routing: Routing, out, arow, epilogu
     a.split_k = split_k
     a.A = A.data_ptr()
     a.A_rows = A.shape[0]
+    if isinstance(A, MXFP8):
+        a.A_scales = A.scales.data_ptr()
     a.arow = arow
     a.orow = orow
     a.top_k = routing.top_k
@@ -246,6 +273,12 @@ class IndexedPath:
         self.routing = Routing(T, top_k, self.E, plan.block_m, plan.tile_m, device)
         cap = self.routing.sorted_cap
         self.separate_act = not (w13.desc.flags & PACK_GATE_UP_INTERLEAVE)
+        # A8W4: X and Z go to the GEMMs as MXFP8
+        self.a8 = bool(w13.desc.flags & PACK_MXFP8_ACT)
+        assert self.a8 == bool(w2.desc.flags & PACK_MXFP8_ACT)
+        assert not (self.a8 and fuse_combine), "A8W4 keeps the combine as a call of its own"
+        self.X8 = MXFP8(max(T, 1), self.H, device) if self.a8 else None
+        self.Z8 = MXFP8(cap, self.I, device) if self.a8 else None
         self.Y13 = _dev_empty((cap, 2 * self.I), BF16, device) if self.separate_act else None
         self.Z = _dev_empty((cap, self.I), BF16, device)
         self.Y2 = _dev_empty((cap, self.H), BF16, device)
@@ -268,7 +301,10 @@ class IndexedPath:
         args.workspace_bytes = buf.numel()
 
     def gate_up_args(self, X, out=None, epilogue=_capi.W4A16_EPI_SILU_MUL, flags=0):
+        """X: bf16 bits [T, H], or (A8W4) its MXFP8 form (quant_x)."""
         out = self.Z if out is None else out
+        if self.a8 and not isinstance(X, MXFP8):
+            X = self.X8
         a = gemm_args_indexed(self.w13, X, self.routing, out, _capi.W4A16_AROW_TOKEN,
                               epilogue=epilogue, flags=flags, split_k=self.split_k13,
                               rows_hint=self.rows_hint)
@@ -278,7 +314,7 @@ class IndexedPath:
     def down_args(self, Z=None, out=None, flags=0, topk_weights=None):
         """Down GEMM arguments; with topk_weights (and fuse_combine) the
         top-k combine into self.out runs in its epilogue."""
-        Z = self.Z if Z is None else Z
+        Z = (self.Z8 if self.a8 else self.Z) if Z is None else Z
         out = self.Y2 if out is None else out
         a = gemm_args_indexed(self.w2, Z, self.routing, out, _capi.W4A16_AROW_POSITION,
                               flags=flags, split_k=self.split_k2, rows_hint=self.rows_hint)
@@ -301,6 +337,14 @@ class IndexedPath:
             return self.gate_up_args(X, out=self.Y13, epilogue=_capi.W4A16_EPI_STORE), da
         return self.gate_up_args(X), da
 
+    def quant_x(self, X, stream=None):
+        """A8W4: X (bf16 bits [T, H]) -> self.X8."""
+        quantize_mxfp8(X, self.X8, stream=stream)
+
+    def quant_z(self, stream=None):
+        """A8W4: the routed rows of Z -> self.Z8 (rows below num_tokens_padded)."""
+        quantize_mxfp8(self.Z, self.Z8, rows_dev=self.routing.num_tokens_padded, stream=stream)
+
     def combine(self, topk_weights, stream=None):
         """The top-k combine as a call of its own (Y2 -> out)."""
         _capi.w4a16_moe_combine(self.Y2, self.Y2.shape[0], self.H, self.routing.row_of,
@@ -315,9 +359,13 @@ class IndexedPath:
     def __call__(self, X, topk_ids, topk_weights, expert_map=None, stream=None):
         self.routing.align(topk_ids, self.E_global, expert_map, stream=stream)
         ga, da = self.stage_args(X, topk_weights)
+        if self.a8:
+            self.quant_x(X, stream)
         _capi.w4a16_moe_w4a16_gemm(ga, stream)
         if self.separate_act:
             self.act(stream)
+        if self.a8:
+            self.quant_z(stream)
         _capi.w4a16_moe_w4a16_gemm(da, stream)
         if not self.fuse_combine:
             self.combine(topk_weights, stream)

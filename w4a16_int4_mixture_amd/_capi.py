@@ -30,6 +30,7 @@ W4A16_PROFILE_DECODE = 1
 W4A16_PROFILE_PREFILL = 2
 W4A16_PACK_GATE_UP_INTERLEAVE = 0x1
 W4A16_PACK_MXFP4 = 0x2
+W4A16_PACK_MXFP8_ACT = 0x4
 W4A16_DESC_MAGIC = 0x4D413457
 W4A16_DESC_VERSION = 1
 W4A16_ALIGN_VALIDATE = 0x1
@@ -85,7 +86,8 @@ class w4a16_gemm_args(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
                 ("m_indices", ctypes.c_void_p),
                 ("comb_out", ctypes.c_void_p), ("comb_row_of", ctypes.c_void_p),
-                ("comb_weights", ctypes.c_void_p), ("comb_T", ctypes.c_int32)]
+                ("comb_weights", ctypes.c_void_p), ("comb_T", ctypes.c_int32),
+                ("A_scales", ctypes.c_void_p)]
 
 
 class w4a16_plan(ctypes.Structure):
@@ -134,6 +136,9 @@ SIGNATURES = {
                                                     ctypes.c_void_p]),
     "w4a16_moe_silu_mul": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
+    "w4a16_quantize_mxfp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                            ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p]),
     "w4a16_moe_combine": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
@@ -286,6 +291,11 @@ def w4a16_moe_w4a16_gemm_noalloc(args: w4a16_gemm_args, stream=None) -> None:
 def w4a16_moe_silu_mul(y13, rows, rows_dev, I, z, stream=None) -> None:
     check(lib().w4a16_moe_silu_mul(ptr(y13), rows, ptr(rows_dev), I, ptr(z),
                                    stream_handle(stream)))
+
+
+def w4a16_quantize_mxfp8(x, rows, rows_dev, K, codes, scales, stream=None) -> None:
+    check(lib().w4a16_quantize_mxfp8(ptr(x), rows, ptr(rows_dev), K, ptr(codes), ptr(scales),
+                                     stream_handle(stream)))
 
 
 def w4a16_moe_combine(y, y_rows, H, row_of, topk_weights, T, top_k, out, stream=None) -> None:

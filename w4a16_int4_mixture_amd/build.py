@@ -34,10 +34,11 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 
-# Per-source extra flags.  The streaming GEMM keeps its MFMA accumulators in
-# VGPRs (no accumulator-register copies in its loop); the large-M GEMM holds
-# 256 accumulators per lane and needs the accumulator registers.
-EXTRA = {"gemm_small.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extra flags.  The streaming GEMMs keep their MFMA accumulators
+# in VGPRs (no accumulator-register copies in their loops); the large-M GEMM
+# holds 256 accumulators per lane and needs the accumulator registers.
+EXTRA = {"gemm_small.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "gemm_mx.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -404,6 +404,20 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
         }
         r->split = 1;
     }
+    // A8W4: MXFP8 activations on a weight laid out for them, and only there
+    const bool a8 = (d->flags & W4A16_PACK_MXFP8_ACT) != 0;
+    if (a8 != (a->A_scales != nullptr)) {
+        set_error(a8 ? "a weight packed for MXFP8 activations needs A_scales"
+                     : "A_scales given for a weight not packed for MXFP8 activations");
+        return W4A16_ERR_MODE_MISMATCH;
+    }
+    if (a8) {
+        if (a->layout != W4A16_LAYOUT_INDEXED || a->comb_out) {
+            set_error("A8W4 runs the indexed layout without the fused combine");
+            return W4A16_ERR_UNSUPPORTED;
+        }
+        r->split = 1;
+    }
     // fused top-k combine in the epilogue (the down GEMM of the indexed path)
     if (a->comb_out) {
         W4A16_CHECK_ARG(a->layout == W4A16_LAYOUT_INDEXED && a->tiles,
@@ -432,6 +446,8 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
     g.unpack_bits = 0x43004300u;
     g.nib_mask = 0x0F0F0F0Fu;
     g.fp4 = (d->flags & W4A16_PACK_MXFP4) ? 1 : 0;   // DECODE profile only (checked at prepack)
+    g.a8 = a8 ? 1 : 0;
+    g.A_scales = a->A_scales;
     const bool split = r->split > 1;
     r->silu_separate = a->epilogue == W4A16_EPI_SILU_MUL && !interleaved;
     const int64_t gx = (g.NC + 3) / 4;
@@ -476,6 +492,8 @@ static w4a16_status resolve(const w4a16_gemm_args* a, Resolved* r) {
 static w4a16_status run_resolved(const w4a16_gemm_args* args, const Resolved& r, hipStream_t s) {
     if (r.kernel == 2)
         launch_gemm_large(r.g, s);
+    else if (r.g.a8)
+        launch_gemm_mx(r.g, r.mt, s);
     else
         launch_gemm_small(r.g, r.mt, r.wide, s);
     w4a16_status st = check_launch("w4a16 gemm");
@@ -815,6 +833,18 @@ w4a16_status w4a16_moe_silu_mul(const uint16_t* y13, int64_t rows, const int32_t
     launch_silu_mul(y13, rows, rows_dev, I, nullptr, 1, nullptr, 0, false, z,
                     static_cast<hipStream_t>(stream));
     return check_launch("silu_mul");
+}
+
+w4a16_status w4a16_quantize_mxfp8(const uint16_t* x, int64_t rows, const int32_t* rows_dev,
+                                  int32_t K, uint8_t* codes, uint8_t* scales, void* stream) {
+    clear_error();
+    W4A16_CHECK_ARG(x && codes && scales && aligned(x, 16) && aligned(codes, 16),
+                    "null or misaligned buffers");
+    W4A16_CHECK_ARG(rows >= 0 && K >= 32 && K % 32 == 0,
+                    "rows must be >= 0 and K a positive multiple of 32");
+    if (rows == 0) return W4A16_OK;
+    launch_quant_mxfp8(x, rows, rows_dev, K, codes, scales, static_cast<hipStream_t>(stream));
+    return check_launch("quantize_mxfp8");
 }
 
 w4a16_status w4a16_moe_combine(const uint16_t* y, int64_t y_rows, int32_t H, const int32_t* row_of,

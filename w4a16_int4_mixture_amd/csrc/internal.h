@@ -51,12 +51,23 @@ w4a16_status check_launch(const char* what);
 //   scales: bf16 (h, c32, g8, jj) at 4096 words + ((h * 32 + c32) * 8 + g8) * 2 + jj
 //           = the scale of column c*CW + 32*(h + 2*jj) + c32, group ks (a
 //           lane's scales of the record's 8 groups are 32 contiguous bytes)
+// DECODE, MXFP4 for MXFP8 activations (W4A16_PACK_MXFP8_ACT; operands of
+// v_mfma_scale_f32_16x16x128_f8f6f4, B in E2M1: lane l holds column l%16 for
+// K = 32*(l/16) + o, o = 0..31, nibble o of its 16 bytes, low nibble first;
+// a record is two 128-K steps s):
+//   codes : word (s, j, lane, w) at ((s * WPL + j) * 64 + lane) * 4 + w
+//           = canonical word (K/8 index) r*32 + s*16 + 4*(lane/16) + w of
+//             column c*CW + 16*j + lane%16 (record r): 32 consecutive codes
+//   scales: word (s, lane) at 512*WPL words + s * 64 + lane; byte j = the
+//           E8M0 scale of column c*CW + 16*j + lane%16, group r*8 + 4*s +
+//           lane/16 (the B-scale operand of block j, selected by op_sel)
 // Padding groups (ks >= K/32) hold zero codes and zero scales.
 // WPL = CW / 16 words (and scales) per lane per group.
 struct PackGeom {
     int E, N, K, CW, NC, KS, KSP, WPL;
     bool interleave;
     bool mxfp4;                          // E2M1 codes in canonical nibble order, E8M0 scales as bf16
+    bool a8;                             // MXFP4 laid out for MXFP8 activations (block-scaled MFMA)
     uint64_t stage_words, chunk_words;   // 32-bit words per record / per chunk
     uint64_t stage_bytes, chunk_bytes, bytes;
 };
@@ -150,10 +161,15 @@ struct GemmArgs {
     uint32_t unpack_bits;  // 0x43004300: bf16 exponent of 128 in each half
     uint32_t nib_mask;     // 0x0F0F0F0F: one code in each byte
     int fp4;               // MXFP4 weights (E2M1 codes): streaming kernel only
+    int a8;                // A8W4: A holds E4M3 bytes [A_rows, K], A_scales E8M0 [A_rows, K/32]
+    const uint8_t* A_scales;
 };
 // wide: the 8-group code ring (three workgroups per CU up to two row blocks)
 // instead of the 16-group one, for two-block tiles.
 void launch_gemm_small(const GemmArgs& a, int mt, bool wide, hipStream_t s);
+// A8W4 kernel (weights packed with W4A16_PACK_MXFP8_ACT, MXFP8 activations;
+// tiles of up to 16 * mt rows, no K split).
+void launch_gemm_mx(const GemmArgs& a, int mt, hipStream_t s);
 // Large-M kernel (PREFILL profile only, tiles of up to 256 rows, no K split).
 void launch_gemm_large(const GemmArgs& a, hipStream_t s);
 
@@ -165,6 +181,10 @@ void launch_gemm_large(const GemmArgs& a, hipStream_t s);
 void launch_silu_mul(const uint16_t* y13, int64_t rows, const int32_t* rows_dev, int I,
                      const int32_t* masked_m, int max_m, const int32_t* sorted_ids, int num_slots,
                      bool slot_rows, uint16_t* z, hipStream_t s);
+// MXFP8 conversion (A8W4 activations) of rows [0, min(*rows_dev, rows)) of
+// x [rows, K] bf16 into codes [rows, K] and scale bytes [rows, K/32].
+void launch_quant_mxfp8(const uint16_t* x, int64_t rows, const int32_t* rows_dev, int K,
+                        uint8_t* codes, uint8_t* scales, hipStream_t s);
 // Indexed -> masked placement from a routing sort made with block_m = 1
 // (no padding): sorted position p of expert e has rank p - offsets[e].
 struct MaskedPlaceArgs {

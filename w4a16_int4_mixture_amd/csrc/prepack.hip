@@ -31,8 +31,12 @@ w4a16_status make_geom(int profile, uint32_t flags, int E, int N, int K, int gro
         set_error("unknown profile %d", profile);
         return W4A16_ERR_UNSUPPORTED;
     }
-    if (flags & ~(W4A16_PACK_GATE_UP_INTERLEAVE | W4A16_PACK_MXFP4)) {
+    if (flags & ~(W4A16_PACK_GATE_UP_INTERLEAVE | W4A16_PACK_MXFP4 | W4A16_PACK_MXFP8_ACT)) {
         set_error("unknown prepack flags 0x%x", flags);
+        return W4A16_ERR_UNSUPPORTED;
+    }
+    if ((flags & W4A16_PACK_MXFP8_ACT) && !(flags & W4A16_PACK_MXFP4)) {
+        set_error("the MXFP8-activation layout is for MXFP4 weights (w4a16_prepack_mxfp4)");
         return W4A16_ERR_UNSUPPORTED;
     }
     if ((flags & W4A16_PACK_MXFP4) && profile != W4A16_PROFILE_DECODE) {
@@ -65,7 +69,9 @@ w4a16_status make_geom(int profile, uint32_t flags, int E, int N, int K, int gro
     g->WPL = cw / 16;
     g->interleave = (flags & W4A16_PACK_GATE_UP_INTERLEAVE) != 0;
     g->mxfp4 = (flags & W4A16_PACK_MXFP4) != 0;
-    g->stage_words = 576ull * g->WPL;                    // 512 WPL code words + 64 WPL scale words
+    g->a8 = (flags & W4A16_PACK_MXFP8_ACT) != 0;
+    // 512 WPL code words, then 64 WPL words of bf16 scales or 32 WPL of E8M0
+    g->stage_words = (g->a8 ? 544ull : 576ull) * g->WPL;
     g->chunk_words = g->stage_words * (g->KSP / 8);
     g->stage_bytes = g->stage_words * 4;
     g->chunk_bytes = g->chunk_words * 4;
@@ -139,6 +145,34 @@ __host__ __device__ static inline uint32_t prefill_word(const uint32_t* codes,
     return out;
 }
 
+// A8W4 record word `in` (layout in internal.h): canonical E2M1 words in the
+// block-scaled MFMA's B-operand order, then E8M0 bytes four to a word.
+__host__ __device__ static inline uint32_t a8_word(const uint32_t* codes, const void* scales,
+                                                   const PackGeom& g, int64_t e, int c, int stage,
+                                                   int in) {
+    const int code_words = 512 * g.WPL;
+    if (in < code_words) {
+        const int w = in & 3, lane = (in >> 2) & 63, sj = in >> 8;
+        const int j = sj % g.WPL, s = sj / g.WPL;
+        const int kw = (stage * 256 + s * 128 + 32 * (lane >> 4)) / 8 + w;   // word along K
+        if (kw * 8 >= g.K) return 0u;
+        const int n = canonical_column(c * g.CW + 16 * j + (lane & 15), g.N, g.CW, g.interleave);
+        return codes[(e * g.N + n) * (g.K / 8) + kw];
+    }
+    const int idx = in - code_words, s = idx >> 6, lane = idx & 63;
+    const int ks = stage * 8 + 4 * s + (lane >> 4);
+    uint32_t out = 0;
+    for (int j = 0; j < g.WPL; ++j) {
+        uint32_t b = 0;
+        if (ks < g.KS) {
+            const int n = canonical_column(c * g.CW + 16 * j + (lane & 15), g.N, g.CW, g.interleave);
+            b = static_cast<const uint8_t*>(scales)[(e * g.N + n) * g.KS + ks];
+        }
+        out |= b << (8 * j);
+    }
+    return out;
+}
+
 // Word w of the packed buffer, from the canonical codes and scales.
 __host__ __device__ static inline uint32_t packed_word(const uint32_t* codes, const void* scales,
                                                        const PackGeom& g, uint64_t w) {
@@ -149,6 +183,7 @@ __host__ __device__ static inline uint32_t packed_word(const uint32_t* codes, co
     const int stage = static_cast<int>(r / g.stage_words);
     const int in = static_cast<int>(r % g.stage_words);
     if (g.CW == 128) return prefill_word(codes, scales, g, e, c, stage, in);
+    if (g.a8) return a8_word(codes, scales, g, e, c, stage, in);
     const int code_words = 512 * g.WPL;
     if (in < code_words) {
         const int j = in % g.WPL;
