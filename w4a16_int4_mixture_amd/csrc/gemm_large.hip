@@ -85,16 +85,6 @@ __device__ inline bf16x8 dequant_word(uint32_t w, uint32_t nib, float s, float c
     return __builtin_bit_cast(bf16x8, d);
 }
 
-// b[jj][step]; sw: the group's bf16 scales of blocks h (low half), h + 2
-__device__ inline void dequant_group(const WGroup& g, uint32_t sw, uint32_t nib, bf16x8 (&b)[2][2]) {
-    const float s0 = __uint_as_float(sw << 16), s1 = __uint_as_float(sw & 0xFFFF0000u);
-    const float c0 = -8.0f * s0, c1 = -8.0f * s1;
-    b[0][0] = dequant_word(g.w.x, nib, s0, c0);
-    b[0][1] = dequant_word(g.w.y, nib, s0, c0);
-    b[1][0] = dequant_word(g.w.z, nib, s1, c1);
-    b[1][1] = dequant_word(g.w.w, nib, s1, c1);
-}
-
 // Vector-memory instructions one wavefront issues per helper call; the K
 // loop's waits (s_waitcnt vmcnt, completions counted in issue order) are
 // written in these counts.
@@ -340,34 +330,37 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
             aread[hh][st] = static_cast<uint32_t>((lane & 31) * 128) +
                             16 * ((static_cast<uint32_t>(4 * hh + 2 * st + (lane >> 5))) ^ fl);
 
-    bf16x8 av[2][RB][2];
+    // A operands of one K step of 16 (all row blocks), double-buffered by K
+    // step; B operands of a group (both K steps), double-buffered by group
+    bf16x8 av[2][RB];
     bf16x8 b[2][2][2];
-    auto read_a = [&](int slot, int hh, bf16x8 (&dst)[RB][2]) {
+    auto read_a = [&](int slot, int hh, int st, bf16x8 (&dst)[RB]) {
+#pragma unroll
+        for (int t = 0; t < RB; ++t)
+            dst[t] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(sl.p[slot] + t * 4096 + aread[hh][st]));
+    };
+    // the B operands of K step st of a group: blocks h and h + 2
+    auto dequant_step = [&](const WGroup& g, uint32_t sw, int st, bf16x8 (&bb)[2][2]) {
+        const float s0 = __uint_as_float(sw << 16), s1 = __uint_as_float(sw & 0xFFFF0000u);
+        bb[0][st] = dequant_word(st == 0 ? g.w.x : g.w.y, nib, s0, -8.0f * s0);
+        bb[1][st] = dequant_word(st == 0 ? g.w.z : g.w.w, nib, s1, -8.0f * s1);
+    };
+    // The 2 RB MFMAs of K step st (row block outer: an accumulator's next MFMA
+    // is a whole K step later).  Spread over them: one LDS read of the next
+    // step's A after every other MFMA, about 48 / (2 RB) VALU ops of a half
+    // group's dequant after each, and nvm buffer loads after odd MFMAs, so
+    // that no burst holds up the wave's issue.
+    auto mfma_step = [&](const bf16x8 (&av_)[RB], const bf16x8 (&b_)[2][2], int st, int nvm) {
 #pragma unroll
         for (int t = 0; t < RB; ++t)
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
-                dst[t][st] = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4*>(sl.p[slot] + t * 4096 + aread[hh][st]));
-    };
-    // nvm: buffer loads of a batch to spread over the MFMAs (one after every
-    // other MFMA), so that no burst of them holds up the wave's issue
-    auto mfmas = [&](const bf16x8 (&av_)[RB][2], const bf16x8 (&b_)[2][2], int nvm) {
-        // K step outermost: the two MFMAs on one accumulator are 2 RB MFMAs
-        // apart, so none waits for the result of the one before
+            for (int jj = 0; jj < 2; ++jj)
+                acc[t][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av_[t], b_[jj][st], acc[t][jj],
+                                                                     0, 0, 0);
+        constexpr int kV = (48 + 2 * RB - 1) / (2 * RB);
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int t = 0; t < RB; ++t)
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj)
-                    acc[t][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av_[t][st], b_[jj][st],
-                                                                         acc[t][jj], 0, 0, 0);
-        // each MFMA followed by about 96 / (4 RB) VALU ops of the next
-        // group's dequant and half an LDS read, which issue while it runs
-        constexpr int kV = (96 + 4 * RB - 1) / (4 * RB);
-#pragma unroll
-        for (int i = 0; i < 4 * RB; ++i) {
+        for (int i = 0; i < 2 * RB; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             if (i % 2 == 1 && i / 2 < nvm) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
@@ -397,27 +390,45 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
     // activations of stage 0 have landed
     wait_vmcnt<2 * kStageOps>();
     barrier_lds();
-    read_a(0, 0, av[0]);
-    dequant_group(ring[0][0], rscale(sc_cur, 0), nib, b[0]);
+    read_a(0, 0, 0, av[0]);
+    dequant_step(ring[0][0], rscale(sc_cur, 0), 0, b[0]);
+    dequant_step(ring[0][0], rscale(sc_cur, 0), 1, b[0]);
 
-    // Four stages per trip (slot and ring indices static; KSP / 2 is even).
-    // Even group 2 s: read the activations of group 2 s + 1 (same stage) and
-    // dequantise its weights while the MFMAs of group 2 s run.  Odd group
-    // 2 s + 1: wait for this wave's batch of stage s - 2 (activations of s + 1;
-    // the batch of s - 1 may stay in flight), barrier (they all landed; every
-    // wave is done with the slot of stage s - 1), then, spread over the MFMAs
-    // of group 2 s + 1, load the activations of stage s + 3 into that slot and
-    // the weights of stage s + 4 into ring entry s % 4, and read the
-    // activations of group 2 s + 2.
+    // Four stages per trip (slot and ring indices static; KSP / 2 is even),
+    // four K steps per stage: (group 2 s, step 0), (2 s, 1), (2 s + 1, 0),
+    // (2 s + 1, 1).  While the MFMAs of one K step run, the A operands of the
+    // next step are read from LDS and half a group's B operands dequantised
+    // (group 2 s + 1 during the first two steps, group 2 s + 2 during the
+    // last two: each into the buffer half its own group no longer reads).
+    // Before the last step: wait for this wave's batch of stage s - 2
+    // (activations of s + 1; the batch of s - 1 may stay in flight) and
+    // barrier (they all landed; every wave is done with the slot of stage
+    // s - 1); then, spread over the MFMAs of the last step, load the
+    // activations of stage s + 3 into that slot and the weights of stage
+    // s + 4 into ring entry s % 4, and read the first A operands of stage
+    // s + 1.
     const int NST = KSP >> 1;
     for (int s0 = 0; s0 < NST; s0 += 4) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int s = s0 + u;
+            const uint32_t sw1 = rscale(sc_cur, 2 * u + 1);
             __builtin_amdgcn_sched_barrier(0);
-            read_a(u, 1, av[1]);
-            dequant_group(ring[u][1], rscale(sc_cur, 2 * u + 1), nib, b[1]);
-            mfmas(av[0], b[0], 0);
+            read_a(u, 0, 1, av[1]);
+            dequant_step(ring[u][1], sw1, 0, b[1]);
+            mfma_step(av[0], b[0], 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            read_a(u, 1, 0, av[0]);
+            dequant_step(ring[u][1], sw1, 1, b[1]);
+            mfma_step(av[1], b[0], 1, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            // (group 2 s + 2's codes sit in ring[(u + 1) & 3][0], three
+            // stages old; its scales in sc_cur, or at u == 3 in sc_nxt,
+            // loaded at u == 0)
+            const uint32_t sw2 = u < 3 ? rscale(sc_cur, 2 * u + 2) : rscale(sc_nxt, 0);
+            read_a(u, 1, 1, av[1]);
+            dequant_step(ring[(u + 1) & 3][0], sw2, 0, b[0]);
+            mfma_step(av[0], b[1], 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             // issued since the batch that holds the activations of stage s + 1:
             // the batch of the previous step (kStageOps), which may stay in
@@ -428,17 +439,16 @@ __device__ __forceinline__ void large_item(const GemmArgs& a, const Item& it, in
                 wait_vmcnt<kStageOps>();
             barrier_lds();
             __builtin_amdgcn_sched_barrier(0);
-            // (the batch's codes go to ring[u], whose last group was
-            // dequantised above)
+            // (the batch's codes go to ring[u], both of whose groups are
+            // dequantised)
             issue(s + 3, (u + 3) & 3, s + 4, ring[u]);
             if (u == 0) {
                 const int rn = (s0 >> 2) + 1;
                 load_rscales(sc_nxt, w, scale_off, rn < NREC ? rn : NREC - 1);
             }
-            read_a((u + 1) & 3, 0, av[0]);
-            dequant_group(ring[(u + 1) & 3][0], u < 3 ? rscale(sc_cur, 2 * u + 2) : rscale(sc_nxt, 0),
-                          nib, b[0]);
-            mfmas(av[1], b[1], u == 0 ? kStageOps + 2 : kStageOps);
+            read_a((u + 1) & 3, 0, 0, av[0]);
+            dequant_step(ring[(u + 1) & 3][0], sw2, 1, b[0]);
+            mfma_step(av[1], b[1], 1, u == 0 ? kStageOps + kRScaleLoads : kStageOps);
         }
         sc_cur[0] = sc_nxt[0];
         sc_cur[1] = sc_nxt[1];
