@@ -651,7 +651,11 @@ __device__ __forceinline__ void gemm_small_body(const GemmArgs& a) {
         nrows = nrows < 16 * MT ? nrows : 16 * MT;
         if (e < 0 || e >= a.E || nrows <= 0) continue;
         gemm_tile<MT, WPL, D, FP4>(a, ty, e, p0, nrows, quad, s, wave, lane, stg, s_tok, &s_n);
-        __syncthreads();  // the next item reuses the staging buffers
+        // the next item reuses the staging buffers: every wavefront's LDS
+        // reads have completed.  The tile's global stores need not have (a
+        // release fence here would wait for all of them before the next
+        // item's loads could even be issued)
+        barrier_ds();
     }
 }
 
