@@ -316,7 +316,9 @@ def run_workload(name, args, src_hash, cpu_legs=True):
     # the dominant kernel is the gate/up GEMM; its algorithmic HBM bytes per
     # launch are the active experts' codes + scales, the activations read once
     # and the routed rows' outputs written once
-    x_bytes = (rows if masked or contig else wl.T) * H * 2
+    # (A8W4 reads the activations as E4M3 bytes plus one E8M0 byte per 32)
+    x_rows = rows if masked or contig else wl.T
+    x_bytes = x_rows * H + x_rows * (H // 32) if a8 else x_rows * H * 2
     out_bytes = rows * I * 2           # Z: SiLU*gate is applied in the epilogue
     alg_bytes13 = bytes13 + x_bytes + out_bytes
     if mfma_bound:
@@ -331,7 +333,10 @@ def run_workload(name, args, src_hash, cpu_legs=True):
     kname = {"prefill": "k_gemm_large (gate/up GEMM of the PREFILL profile, SiLU*gate in its "
                         "epilogue: one launch per call)",
              "contiguous": "k_gemm_large (gate/up GEMM, grouped contiguous layout, SiLU*gate in "
-                           "its epilogue: one launch per call)"}.get(
+                           "its epilogue: one launch per call)",
+             "decode_a8w4": "k_gemm_mx (A8W4 gate/up GEMM on the block-scaled MFMA, MXFP8 "
+                            "activations x MXFP4 weights, SiLU*gate in its epilogue: one launch "
+                            "per call)"}.get(
         name, "k_gemm_small (gate/up GEMM with SiLU*gate epilogue and in-kernel split-K fix-up: "
               "one launch per call)")
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit_rf,
