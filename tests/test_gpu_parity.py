@@ -703,6 +703,23 @@ def sampled_reference(d, E_global, tokens, wmode=0):
                               d["scales13"], d["codes2"], d["scales2"], wmode=wmode)
 
 
+def chunked_forward(d, E_global, wmode, chunk=1024):
+    """oracle.moe_forward with intermediates over token chunks (rows are
+    independent; slots are token-major, f = t * top_k + j), printing a line
+    per chunk so that a long oracle run shows progress."""
+    T = d["X"].shape[0]
+    parts = []
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        parts.append(oracle.moe_forward(d["X"][t0:t1], d["topk_ids"][t0:t1],
+                                        d["topk_weights"][t0:t1], E_global, d["expert_map"],
+                                        d["codes13"], d["scales13"], d["codes2"], d["scales2"],
+                                        intermediates=True, wmode=wmode))
+        print(f"  oracle tokens {t1}/{T}", flush=True)
+    return {key: np.concatenate([p[key] for p in parts]) for key in ("out", "Z", "Y2")}
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["prefill", "tp8"])
 def test_large_workloads_full_parity(m, name):
     """The full-size EP8 prefill share (large-M kernel, per-XCD work queue,
@@ -719,9 +736,7 @@ def test_large_workloads_full_parity(m, name):
     path, out = run_indexed(m, d, wl.E_global, profile, rows_hint=rows_hint)
     # the large-M kernel (prefill) rounds each dequantised weight to bf16 once
     wmode = 1 if path.plan.kernel == 2 else 0
-    ref = oracle.moe_forward(d["X"], d["topk_ids"], d["topk_weights"], wl.E_global,
-                             d["expert_map"], d["codes13"], d["scales13"], d["codes2"],
-                             d["scales2"], intermediates=True, wmode=wmode)
+    ref = chunked_forward(d, wl.E_global, wmode)
     pos, f = slot_rows(path.routing, wl.T, wl.top_k)
     assert pos.size == rows_hint
     check_close(host(path.Z, np.uint16)[pos], ref["Z"][f], f"{name} Z (wmode {wmode})")
@@ -845,6 +860,47 @@ def test_masked_count_above_max_m_stays_inside_its_rows(m, profile, interleave):
         inside[g * max_m: g * max_m + min(int(c), max_m)] = True
     assert np.all(got[~inside] == 0x1234), "a row outside the valid rows changed"
     check_close(got[inside], refZ[inside[: G * max_m]], "masked rows under overflowing counts")
+
+
+@pytest.mark.parametrize("profile", [1, 2])
+@pytest.mark.parametrize("pattern", ["sparse", "empty"])
+def test_masked_many_experts_sparse_counts(m, profile, pattern):
+    """130 experts, so the device-side scan of masked_m spans three steps of
+    64, with most counts zero, some exact multiples of the 16-row tile, one
+    above max_m and one negative (no rows); or every count zero.  The valid
+    rows equal the oracle, no other row and no guard row changes, and a
+    second call gives the same bits (the split-K arrival counters were left
+    at zero)."""
+    from w4a16_int4_mixture_amd import _capi
+    G, H, I, max_m, guard = 130, 1024, 64, 48, 24
+    rng = np.random.default_rng(131)
+    counts = np.zeros(G, np.int32)
+    if pattern == "sparse":
+        counts = np.where(rng.random(G) < 0.75, 0, rng.integers(1, max_m + 1, G)).astype(np.int32)
+        counts[[3, 64, 70, 129]] = [16, 47, 32, 48]
+        counts[5], counts[6] = 500, -3
+    d = synth.random_small(133 + profile, G, H, I, 8, 1)
+    a3 = synth.random_activations(rng, G * max_m, H)
+    print(f"masked sparse: profile={profile} pattern={pattern} filled={(counts > 0).sum()}",
+          flush=True)
+    w13 = prepare(m, d["codes13"], d["scales13"], profile)
+    outs = []
+    for call in range(2):
+        out = torch.full((G * max_m + guard, 2 * I), 0x1234, dtype=torch.int16, device="cuda")
+        a = m.gemm_args_masked(w13, dev(a3), dev(counts), max_m, 16, out)
+        m.run_gemm(a, "cuda")
+        torch.cuda.synchronize()
+        outs.append(host(out, np.uint16))
+    assert np.array_equal(outs[0], outs[1]), "second call differs"
+    got = outs[0]
+    inside = np.zeros(G * max_m + guard, bool)
+    for g, c in enumerate(counts):
+        inside[g * max_m: g * max_m + min(max(int(c), 0), max_m)] = True
+    assert np.all(got[~inside] == 0x1234), "a row outside the valid rows changed"
+    if inside.any():
+        wmode = 1 if profile == 2 else 0
+        ref = oracle.masked_gemm(a3, counts, d["codes13"], d["scales13"], wmode=wmode)
+        check_close(got[inside], ref[inside[: G * max_m]], "masked rows, sparse counts")
 
 
 def test_separate_silu_with_slot_rows_writes_only_local_slots(m):
@@ -1027,6 +1083,7 @@ def test_contiguous_path_random(m, interleave):
     check_close(out, ref0, "contiguous out (exact weights)", exact_frac=0.0)
 
 
+@pytest.mark.timeout(900)
 def test_contiguous_workload_full_parity(m):
     """The grouped contiguous prefill share at full size: 48 local experts,
     128 rows each (6144 rows), H 7168, I 2048, in the configuration the
@@ -1042,9 +1099,7 @@ def test_contiguous_workload_full_parity(m):
     assert path.plan.tile_m == 128
     out = host(path(dev(a2), dev(mi), dev(d["row_of"]), dev(d["topk_weights"])), np.uint16)
     torch.cuda.synchronize()
-    ref = oracle.moe_forward(d["X"], d["topk_ids"], d["topk_weights"], wl.E_global,
-                             d["expert_map"], d["codes13"], d["scales13"], d["codes2"],
-                             d["scales2"], intermediates=True, wmode=1)
+    ref = chunked_forward(d, wl.E_global, 1, chunk=128)
     r = d["row_of"]
     f = np.nonzero(r >= 0)[0]
     check_close(host(path.Z, np.uint16)[r[f]], ref["Z"][f], "contiguous workload Z")

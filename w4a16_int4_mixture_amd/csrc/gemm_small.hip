@@ -592,12 +592,74 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int ty, int e, int 
     if (a.comb_out && stored) comb_arrive(a, p0, nrows, quad, s_tok, s_n);
 }
 
+// Masked layout: the tiles that hold rows, in expert order.  Expert g holds
+// ceil(c / tile_m) of them, c = min(masked_m[g], max_m) (a negative count is
+// none).  Every wavefront scans the counts itself, 64 experts per step, so
+// the results are uniform without a barrier.  Work items walk the non-empty
+// tiles only: a launch's items past them are all at its end, and no empty
+// (expert, chunk) slot delays the start of a real one.
+__device__ inline int masked_rows_of(const GemmArgs& a, const int32_t* mm, int g) {
+    if (g >= a.E) return 0;
+    const int m = mm[g];
+    return m < 0 ? 0 : (m < a.max_m ? m : a.max_m);
+}
+
+__device__ inline int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(v, d, 64);
+        if (lane >= d) v += u;
+    }
+    return v;
+}
+
+__device__ inline int masked_tile_count(const GemmArgs& a, int lane) {
+    int total = 0;
+    for (int g0 = 0; g0 < a.E; g0 += 64) {
+        const int t = (masked_rows_of(a, a.masked_m, g0 + lane) + a.tile_m - 1) / a.tile_m;
+        total += __builtin_amdgcn_readlane(wave_incl_scan(t, lane), 63);
+    }
+    return total;
+}
+
+// Expert and rows of non-empty tile ty; e = -1 past the last one.  The
+// counts are read again for every tile (the empty asm hides that they do not
+// change), so that no per-lane scan value is kept live across the K loop.
+__device__ inline void masked_tile_at(const GemmArgs& a, int ty, int lane, int& e, int& p0,
+                                      int& nrows) {
+    const int32_t* mm = a.masked_m;
+    asm volatile("" : "+s"(mm));
+    int base = 0;
+    for (int g0 = 0; g0 < a.E; g0 += 64) {
+        const int c = masked_rows_of(a, mm, g0 + lane);
+        const int t = (c + a.tile_m - 1) / a.tile_m;
+        const int incl = wave_incl_scan(t, lane);
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        if (ty < base + total) {
+            const int L = static_cast<int>(__builtin_ctzll(__ballot(base + incl > ty)));
+            const int first = base + __builtin_amdgcn_readlane(incl - t, L);
+            const int cnt = __builtin_amdgcn_readlane(c, L);
+            const int r0 = (ty - first) * a.tile_m;
+            e = g0 + L;
+            p0 = e * a.max_m + r0;
+            nrows = cnt - r0 < a.tile_m ? cnt - r0 : a.tile_m;
+            return;
+        }
+        base += total;
+    }
+    e = -1;
+    p0 = 0;
+    nrows = 0;
+}
+
 // Workgroup w runs work items w, w + G, ... (G = the grid), an item being
 // (tile, group of four chunks, K split), splits of one chunk group adjacent;
 // the loop covers any device-side tile count whatever the grid.  The item
 // decision is uniform across the workgroup, so every barrier inside is
-// reached by all four wavefronts.  D: groups of the code ring (8 or 16).
-template <int MT, int WPL, int D, bool FP4>
+// reached by all four wavefronts.  D: groups of the code ring (8 or 16).  MK:
+// the masked layout (its own instantiation, so that the tile scan's registers
+// do not weigh on the other layouts' kernels).
+template <int MT, int WPL, int D, bool FP4, bool MK>
 __device__ __forceinline__ void gemm_small_body(const GemmArgs& a) {
     __shared__ u32x4 stage0[Lds<MT, WPL>::buf];
     __shared__ u32x4 stage1[Lds<MT, WPL>::buf];
@@ -610,12 +672,12 @@ __device__ __forceinline__ void gemm_small_body(const GemmArgs& a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (a.comb_out) comb_zero_unrouted(a);
     int n_tiles;
-    if (a.tile_src == TILE_TABLE) {
+    if constexpr (MK) {
+        n_tiles = masked_tile_count(a, lane);
+    } else if (a.tile_src == TILE_TABLE) {
         n_tiles = a.tile_count[0];
-    } else if (a.tile_src == TILE_BLOCKS) {
-        n_tiles = a.ntp[0] / a.block_m;
     } else {
-        n_tiles = a.grid_tiles_total;
+        n_tiles = a.ntp[0] / a.block_m;
     }
     n_tiles = n_tiles < a.tiles_cap ? n_tiles : a.tiles_cap;
     const int qs = ((a.NC + 3) / 4) * a.split_k;   // items per tile
@@ -625,25 +687,19 @@ __device__ __forceinline__ void gemm_small_body(const GemmArgs& a) {
         const int rem = static_cast<int>(item % qs);
         const int quad = rem / a.split_k, s = rem % a.split_k;
         int e, p0, nrows;
-        if (a.tile_src == TILE_TABLE) {
+        if constexpr (MK) {
+            // masked_m is the valid count of each expert; a count above max_m
+            // is cut to max_m, so no tile reaches past the expert's rows
+            masked_tile_at(a, ty, lane, e, p0, nrows);
+        } else if (a.tile_src == TILE_TABLE) {
             const int4 t = reinterpret_cast<const int4*>(a.tiles)[ty];
             e = t.x;
             p0 = t.y;
             nrows = t.z;
-        } else if (a.tile_src == TILE_BLOCKS) {
+        } else {
             p0 = ty * a.block_m;
             e = a.expert_ids[ty];
             nrows = a.sorted_cap - p0 < a.block_m ? a.sorted_cap - p0 : a.block_m;
-        } else {
-            // masked_m is the valid count of each expert; a count above max_m
-            // is cut to max_m, so no tile reaches past the expert's rows
-            const int g = ty / a.chunks_per_expert;
-            const int r0 = (ty % a.chunks_per_expert) * a.tile_m;
-            const int mg = a.masked_m[g];
-            const int cnt = mg < a.max_m ? mg : a.max_m;
-            e = g;
-            p0 = g * a.max_m + r0;
-            nrows = cnt - r0 < a.tile_m ? cnt - r0 : a.tile_m;
         }
         // a tile-table entry taller than the launch's tile height (a table
         // written for another tile_m) is cut to it: its rows past 16 * MT are
@@ -659,31 +715,31 @@ __device__ __forceinline__ void gemm_small_body(const GemmArgs& a) {
     }
 }
 
-template <int MT, int WPL, int D, bool FP4>
+template <int MT, int WPL, int D, bool FP4, bool MK>
 __global__ void __launch_bounds__(256) k_gemm_small(GemmArgs a) {
-    gemm_small_body<MT, WPL, D, FP4>(a);
+    gemm_small_body<MT, WPL, D, FP4, MK>(a);
 }
 
 // The two-block kernel with the one-stage ring, held to three workgroups per
 // CU (168 VGPRs: four registers are kept in scratch across the K loop, none
 // inside it).
-template <int MT, int WPL, int D, bool FP4>
+template <int MT, int WPL, int D, bool FP4, bool MK>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8)))
     k_gemm_small_w3(GemmArgs a) {
-    gemm_small_body<MT, WPL, D, FP4>(a);
+    gemm_small_body<MT, WPL, D, FP4, MK>(a);
 }
 
-template <int MT, int D, bool FP4>
+template <int MT, int D, bool FP4, bool MK>
 static void (*small_kernel())(GemmArgs) {
     if constexpr (MT == 2 && D == 8)
-        return k_gemm_small_w3<MT, 4, D, FP4>;
+        return k_gemm_small_w3<MT, 4, D, FP4, MK>;
     else
-        return k_gemm_small<MT, 4, D, FP4>;
+        return k_gemm_small<MT, 4, D, FP4, MK>;
 }
 
 // Workgroups of one kernel variant resident on the device at once (from the
 // runtime's occupancy calculation: registers and LDS), cached per variant.
-static int g_resident[5][2][2] = {};
+static int g_resident[5][2][2][2] = {};
 
 static int resident_of(void (*kern)(GemmArgs), int& cached) {
     if (cached <= 0) {
@@ -699,45 +755,53 @@ static int resident_of(void (*kern)(GemmArgs), int& cached) {
     return cached;
 }
 
-template <int MT, int D, bool FP4>
+template <int MT, int D, bool FP4, bool MK>
 static int resident_wgs() {
-    return resident_of(small_kernel<MT, D, FP4>(), g_resident[MT][D == 8 ? 0 : 1][FP4 ? 1 : 0]);
+    return resident_of(small_kernel<MT, D, FP4, MK>(),
+                       g_resident[MT][D == 8 ? 0 : 1][FP4 ? 1 : 0][MK ? 1 : 0]);
 }
 
-template <int MT, int D, bool FP4>
+template <int MT, int D, bool FP4, bool MK>
 static void launch_mt(const GemmArgs& a, hipStream_t st) {
     const int64_t items = static_cast<int64_t>(a.grid_tiles) * ((a.NC + 3) / 4) * a.split_k;
     // One workgroup per item (from the host's tile estimate) while they fit
     // in four rounds of resident workgroups: the hardware then hands items to
-    // CUs as they free up, which balances items of unequal cost (empty
-    // masked tiles).  Beyond that, items are dealt evenly to that many
-    // workgroups, which saves the start-up of very short items (short K).
-    const int64_t cap = 4 * static_cast<int64_t>(resident_wgs<MT, D, FP4>());
+    // CUs as they free up, which balances items of unequal cost.  Beyond
+    // that, items are dealt evenly to that many workgroups, which saves the
+    // start-up of very short items (short K).  The masked layout's count is
+    // the worst case (every expert at max_m) and its items walk the non-empty
+    // tiles only, so one round of resident workgroups is launched: the items
+    // past the filled tiles then cost no dispatch after the real ones.
+    const int64_t resident = resident_wgs<MT, D, FP4, MK>();
+    const int64_t cap = MK ? resident : 4 * resident;
     const int64_t rounds = (items + cap - 1) / cap;
     const int64_t g = rounds > 0 ? (items + rounds - 1) / rounds : 1;
-    small_kernel<MT, D, FP4>()<<<dim3(static_cast<unsigned>(g < 1 ? 1 : g)), dim3(256), 0, st>>>(a);
+    small_kernel<MT, D, FP4, MK>()<<<dim3(static_cast<unsigned>(g < 1 ? 1 : g)), dim3(256), 0, st>>>(
+        a);
 }
 
-template <bool FP4>
+template <bool FP4, bool MK>
 static void launch_variant(const GemmArgs& a, int mt, bool wide, hipStream_t st) {
     switch (mt) {
-        case 1: launch_mt<1, 8, FP4>(a, st); break;
+        case 1: launch_mt<1, 8, FP4, MK>(a, st); break;
         case 2:
             if (wide)
-                launch_mt<2, 8, FP4>(a, st);
+                launch_mt<2, 8, FP4, MK>(a, st);
             else
-                launch_mt<2, 16, FP4>(a, st);
+                launch_mt<2, 16, FP4, MK>(a, st);
             break;
-        case 3: launch_mt<3, 16, FP4>(a, st); break;
-        default: launch_mt<4, 16, FP4>(a, st); break;
+        case 3: launch_mt<3, 16, FP4, MK>(a, st); break;
+        default: launch_mt<4, 16, FP4, MK>(a, st); break;
     }
 }
 
 void launch_gemm_small(const GemmArgs& a, int mt, bool wide, hipStream_t st) {
+    const bool mk = a.tile_src == TILE_MASKED;
     if (a.fp4)
-        launch_variant<true>(a, mt, wide, st);
+        mk ? launch_variant<true, true>(a, mt, wide, st) : launch_variant<true, false>(a, mt, wide, st);
     else
-        launch_variant<false>(a, mt, wide, st);
+        mk ? launch_variant<false, true>(a, mt, wide, st)
+           : launch_variant<false, false>(a, mt, wide, st);
 }
 
 }  // namespace w4a16
