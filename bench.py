@@ -265,24 +265,36 @@ def run_workload(name, args, src_hash, cpu_legs=True):
         step(i)
     torch.cuda.synchronize()
 
-    # timed steps (wall clock between synchronisations), stage events per step;
-    # every launch goes to torch's current stream, where the events are recorded
-    n_st = len(stage_lists[0])
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_st + 1)] for _ in range(args.steps)]
+    # timed steps: wall clock between synchronisations, nothing recorded
+    # between the launches (a call as a caller makes it)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
-        step(i, ev[i])
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1000.0 / args.steps
+    us_call = ms_per_step * 1000.0
+
+    # the same steps again with HIP events between the stages (per-stage
+    # times); every launch goes to torch's current stream, where the events
+    # are recorded
+    # (warm-up steps first, with no synchronisation before the events, so the
+    # GPU runs without a pause into the measured steps)
+    n_st = len(stage_lists[0])
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_st + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        step(i)
+    for i in range(args.steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
     stage_us = {}
     for j, (sname, _) in enumerate(stage_lists[0]):
         vals = [ev[i][j].elapsed_time(ev[i][j + 1]) * 1000.0 for i in range(args.steps)]
         stage_us[sname] = float(np.median(vals))
     event_total = float(np.median([ev[i][0].elapsed_time(ev[i][n_st]) * 1000.0
                                    for i in range(args.steps)]))
-    ms_per_step = wall * 1000.0 / args.steps
-    us_call = ms_per_step * 1000.0
 
     # HIP graph of one step per weight copy, replayed alternately
     graph_us = None
@@ -380,6 +392,7 @@ def main():
     wl = r["wl"]
     plan13 = r["plan13"]
     gu, dn, us_call = r["gu"], r["dn"], r["us_call"]
+    span = gu + dn
     line = {
         "metric": METRIC,
         "value": round(us_call, 2),
@@ -401,13 +414,13 @@ def main():
                    "gate_up_split_k": None if plan13 is None else plan13.split_k},
         "stages_us": {k: round(v, 2) for k, v in r["stage_us"].items()},
         "event_total_us": round(r["event_total"], 2),
-        "gate_up_plus_down_us": round(gu + dn, 2),
+        "gate_up_plus_down_us": round(span, 2),
         "graph_us_per_call": None if r["graph_us"] is None else round(r["graph_us"], 2),
         "weight_GBps_path": round(r["weight_bytes"] / (us_call * 1e-6) / 1e9, 1),
-        "weight_GBps_gate_up_plus_down": round(r["weight_bytes"] / ((gu + dn) * 1e-6) / 1e9, 1),
-        "frac_hbm_gate_up_plus_down": round(r["weight_bytes"] / ((gu + dn) * 1e-6) / 1e9
+        "weight_GBps_gate_up_plus_down": round(r["weight_bytes"] / (span * 1e-6) / 1e9, 1),
+        "frac_hbm_gate_up_plus_down": round(r["weight_bytes"] / (span * 1e-6) / 1e9
                                             / HBM_PEAK_GBS, 4),
-        "tflops_gate_up_plus_down": round(r["flops"] / ((gu + dn) * 1e-6) / 1e12, 2),
+        "tflops_gate_up_plus_down": round(r["flops"] / (span * 1e-6) / 1e12, 2),
         "roofline": r["roofline"],
         "cpu_baseline": r["cpu"],
         "kernel_source_hash": src_hash,
@@ -416,14 +429,15 @@ def main():
     if args.workload == "decode" and not args.no_prefill:
         p = run_workload("prefill", args, src_hash)
         pg, pd, pu = p["gu"], p["dn"], p["us_call"]
+        ps = pg + pd
         line["prefill"] = {
             "workload": workload_name("prefill", p["wl"]),
             "routed_rows": p["rows"],
             "us_per_call": round(pu, 2),
             "stages_us": {k: round(v, 2) for k, v in p["stage_us"].items()},
-            "gate_up_plus_down_us": round(pg + pd, 2),
-            "tflops_gate_up_plus_down": round(p["flops"] / ((pg + pd) * 1e-6) / 1e12, 2),
-            "frac_mfma_gate_up_plus_down": round(p["flops"] / ((pg + pd) * 1e-6) / 1e12
+            "gate_up_plus_down_us": round(ps, 2),
+            "tflops_gate_up_plus_down": round(p["flops"] / (ps * 1e-6) / 1e12, 2),
+            "frac_mfma_gate_up_plus_down": round(p["flops"] / (ps * 1e-6) / 1e12
                                                  / BF16_PEAK_TFLOPS, 4),
             "tflops_path": round(p["flops"] / (pu * 1e-6) / 1e12, 2),
             "graph_us_per_call": None if p["graph_us"] is None else round(p["graph_us"], 2),
