@@ -275,6 +275,35 @@ def test_many_item_launches_exact(m, K, N, tile_m):
     assert np.array_equal(host(Yb, np.uint16)[pos], oracle.bf16_from_f64(ref.astype(np.float64)))
 
 
+@pytest.mark.parametrize("tile_m", [16, 32])
+def test_one_stage_items_several_per_workgroup_exact(m, tile_m):
+    """K of one stage (256) with more items than four rounds of resident
+    workgroups, so that every workgroup runs several one-stage items in a row
+    (the TP8 down GEMM's regime).  Bit-exact under the exactness invariant,
+    fp32 and bf16 outputs of every routed row."""
+    E, K, N, T, k = 128, 256, 4096, 768, 8
+    X, codes, scales, ids = many_items_problem(991 + tile_m, E, K, N, T, k)
+    from w4a16_int4_mixture_amd import _capi
+    w = prepare(m, codes, scales, 1)
+    r = m.Routing(T, k, E, 16, tile_m, "cuda")
+    r.align(dev(ids), E)
+    n_items = int(host(r.tile_count)[0]) * (N // 256)
+    print(f"one-stage items: tile_m={tile_m} items={n_items}", flush=True)
+    assert n_items > 4 * 768   # four rounds of three workgroups on 256 CUs
+    pos, f = slot_rows(r, T, k)
+    ref = oracle.grouped_gemm(X, f // k, ids.ravel()[f], codes, scales, N, K, out_f32=True)
+    Yf = torch.full((r.sorted_cap, N), float("nan"), dtype=torch.float32, device="cuda")
+    m.run_gemm(m.gemm_args_indexed(w, dev(X), r, Yf, _capi.W4A16_AROW_TOKEN, flags=1, split_k=1,
+                                   rows_hint=T * k), "cuda")
+    got = host(Yf)[pos]
+    bad = np.nonzero(np.any(got != ref, axis=1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first positions {pos[bad[:8]]}"
+    Yb = torch.full((r.sorted_cap, N), -1, dtype=torch.int16, device="cuda")
+    m.run_gemm(m.gemm_args_indexed(w, dev(X), r, Yb, _capi.W4A16_AROW_TOKEN, rows_hint=T * k),
+               "cuda")
+    assert np.array_equal(host(Yb, np.uint16)[pos], oracle.bf16_from_f64(ref.astype(np.float64)))
+
+
 def test_many_item_launch_fused_silu(m):
     """The SiLU * gate epilogue (gate/up interleave) of a launch of ~2300
     items: within one bf16 ulp of the oracle's SiLU of its gate/up rows."""
