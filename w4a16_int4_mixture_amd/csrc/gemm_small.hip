@@ -106,8 +106,9 @@ template <int MT, int WPL>
 constexpr int kStageLoads = kStageActLoads<MT, WPL> + kStageScaleLoads<WPL>;
 
 // Codes of group ks (record ks / 8, slot ks % 8) for this lane; lane_off =
-// lane * WPL words, in bytes.  Issues kCodeLoads<WPL> loads.
-template <int WPL>
+// lane * WPL words, in bytes; POL: the loads' cache policy.  Issues
+// kCodeLoads<WPL> loads.
+template <int WPL, int POL>
 __device__ inline void load_codes(Codes<WPL>& c, __amdgpu_buffer_rsrc_t w, uint32_t lane_off,
                                   int ks) {
     const int soff = ((ks >> 3) * (576 * WPL) + (ks & 7) * (64 * WPL)) * 4;
@@ -115,7 +116,7 @@ __device__ inline void load_codes(Codes<WPL>& c, __amdgpu_buffer_rsrc_t w, uint3
 #pragma unroll
     for (int i = 0; i < kCodeLoads<WPL>; ++i)
         c.w[i] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(w, lane_off + 16 * i, soff, kNonTemporal));
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(w, lane_off + 16 * i, soff, POL));
 }
 
 // One K group is processed in three phases so that consecutive groups overlap:
@@ -208,7 +209,7 @@ __device__ inline void fma_group(const Prep<MT, WPL>& p, const f32x4 (&d)[MT][WP
 // The kSG groups of one LDS stage, software-pipelined.  `refill` = false in
 // the ring's last turn.  ring[r0 + g] holds group g of the stage; after its
 // unpack it is refilled with group `next + g`.
-template <int MT, int WPL, int D, bool FP4>
+template <int MT, int WPL, int D, bool FP4, int POL>
 __device__ inline void stage_groups(Codes<WPL> (&ring)[D], int r0, const u32x4* acur,
                                     const uint16_t* scur, const Src<MT>& src, int next,
                                     bool refill, f32x4 (&acc)[MT][WPL], uint32_t mask,
@@ -217,7 +218,7 @@ __device__ inline void stage_groups(Codes<WPL> (&ring)[D], int r0, const u32x4* 
     prep_group<MT, WPL, FP4>(pc, ring[r0], acur + lane, scur, mask, bits);
     unpacked<MT, WPL>(pc);
     __builtin_amdgcn_sched_barrier(0);
-    if (refill) load_codes<WPL>(ring[r0], src.w, src.code_off, next);
+    if (refill) load_codes<WPL, POL>(ring[r0], src.w, src.code_off, next);
 #pragma unroll
     for (int g = 0; g < kSG; ++g) {
         f32x4 d[MT][WPL];
@@ -228,7 +229,7 @@ __device__ inline void stage_groups(Codes<WPL> (&ring)[D], int r0, const u32x4* 
                                 scur + (g + 1) * 16 * WPL, mask, bits);
             unpacked<MT, WPL>(pn);
             __builtin_amdgcn_sched_barrier(0);
-            if (refill) load_codes<WPL>(ring[r0 + g + 1], src.w, src.code_off, next + g + 1);
+            if (refill) load_codes<WPL, POL>(ring[r0 + g + 1], src.w, src.code_off, next + g + 1);
         }
         __builtin_amdgcn_sched_barrier(0);
         fma_group<MT, WPL>(pc, d, acc);
@@ -263,10 +264,10 @@ __device__ inline void barrier_ds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_ba
 // wait written for the full count then waits at least as long); activation
 // columns past K (padding groups, whose scales are zero) are clamped to the
 // last real group.
-// (D, the caller's ring depth, only keeps the instantiations of the two ring
-// variants apart: the host compilation pass rejects one instantiation reached
-// from both.)
-template <int MT, int WPL, int MTMAX, int D, bool FP4, bool MAYBE_VIRTUAL = false>
+// (D and POL, the caller's ring depth and code-load policy, only keep the
+// instantiations of the kernel variants apart: the host compilation pass
+// rejects one instantiation reached from several.)
+template <int MT, int WPL, int MTMAX, int D, bool FP4, int POL, bool MAYBE_VIRTUAL = false>
 __device__ inline void dma_stage(const Src<MT>& src, u32x4* buf, int base, int ks_min, int ks_real,
                                  int wave, int lane) {
     constexpr int kAStage = kSG * MTMAX * 64;   // u32x4 of activations per buffer
@@ -332,7 +333,7 @@ struct Stg {
 // by one virtual record (zero scales) when it holds an odd number of records.
 // Ring slot r0 + g of a stage holds its group g: r0 = 0 for the even stage,
 // and for the odd one kSG (D = 16) or 0 (D = 8).
-template <int MT, int WPL, int MTMAX, int D, bool FP4>
+template <int MT, int WPL, int MTMAX, int D, bool FP4, int POL>
 __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1, int ks_real,
                                             int wave, int lane, const Stg& stg,
                                             f32x4 (&acc)[MT][WPL], uint32_t mask,
@@ -358,16 +359,16 @@ __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1
     // without the virtual stage that pads other odd stage counts
     if (ks1 - ks0 == kSG) {
         Codes<WPL> one[kSG];
-        dma_stage<MT, WPL, MTMAX, D, FP4>(src, stg.b[0], ks0, ks0, ks_real, wave, lane);
+        dma_stage<MT, WPL, MTMAX, D, FP4, POL>(src, stg.b[0], ks0, ks0, ks_real, wave, lane);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < kSG; ++i) load_codes<WPL>(one[i], src.w, src.code_off, ks0 + i);
+        for (int i = 0; i < kSG; ++i) load_codes<WPL, POL>(one[i], src.w, src.code_off, ks0 + i);
         __builtin_amdgcn_sched_barrier(0);
         // issued: the stage's buffer, then kSG groups of codes (= kRefill
         // loads) that may stay in flight
         wait_vmcnt<kRefill>();                   // the stage's buffer has landed
         barrier_ds();
-        stage_groups<MT, WPL, kSG, FP4>(one, 0, abuf0, srd0, src, 0, false, acc, mask, bits, lane);
+        stage_groups<MT, WPL, kSG, FP4, POL>(one, 0, abuf0, srd0, src, 0, false, acc, mask, bits, lane);
         return;
     }
 
@@ -380,12 +381,12 @@ __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1
     // buffer 1's loads after the ring's, as in the loop (where a stage's loads
     // follow the refills), so that the waits for ring slots match on both paths
     Codes<WPL> ring[D];
-    dma_stage<MT, WPL, MTMAX, D, FP4, true>(src, stg.b[0], kb, ks0, ks_real, wave, lane);
+    dma_stage<MT, WPL, MTMAX, D, FP4, POL, true>(src, stg.b[0], kb, ks0, ks_real, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < D; ++i) load_codes<WPL>(ring[i], src.w, src.code_off, kb + i < ks0 ? ks0 : kb + i);
+    for (int i = 0; i < D; ++i) load_codes<WPL, POL>(ring[i], src.w, src.code_off, kb + i < ks0 ? ks0 : kb + i);
     __builtin_amdgcn_sched_barrier(0);
-    dma_stage<MT, WPL, MTMAX, D, FP4>(src, stg.b[1], kb + kSG, ks0, ks_real, wave, lane);
+    dma_stage<MT, WPL, MTMAX, D, FP4, POL>(src, stg.b[1], kb + kSG, ks0, ks_real, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
     // issued: buffer 0, the ring (kRing), buffer 1 (kStage); the last two may
     // stay in flight
@@ -395,27 +396,27 @@ __device__ __forceinline__ void stream_loop(const Src<MT>& src, int ks0, int ks1
     for (int it = 0; it < nit - 1; ++it) {
         const int base = kb + it * IT;
         // even stage: buffer 0; its ring slots take groups D ahead
-        stage_groups<MT, WPL, D, FP4>(ring, 0, abuf0, srd0, src, base + D, true, acc, mask, bits, lane);
+        stage_groups<MT, WPL, D, FP4, POL>(ring, 0, abuf0, srd0, src, base + D, true, acc, mask, bits, lane);
         // issued since buffer 1's loads: this stage's ring refills (kRefill)
         wait_vmcnt<kRefill>();                   // buffer 1 has landed
         barrier_ds();                            // (for every wavefront); buffer 0 is free
-        dma_stage<MT, WPL, MTMAX, D, FP4>(src, stg.b[0], base + IT, ks0, ks_real, wave, lane);
+        dma_stage<MT, WPL, MTMAX, D, FP4, POL>(src, stg.b[0], base + IT, ks0, ks_real, wave, lane);
         // odd stage: buffer 1
-        stage_groups<MT, WPL, D, FP4>(ring, RO, abuf1, srd1, src, base + D + kSG, true, acc, mask, bits,
+        stage_groups<MT, WPL, D, FP4, POL>(ring, RO, abuf1, srd1, src, base + D + kSG, true, acc, mask, bits,
                                  lane);
         // issued since buffer 0's loads: this stage's ring refills (kRefill)
         wait_vmcnt<kRefill>();                   // buffer 0 has landed
         barrier_ds();                            // buffer 1 is free
-        dma_stage<MT, WPL, MTMAX, D, FP4>(src, stg.b[1], base + IT + kSG, ks0, ks_real, wave, lane);
+        dma_stage<MT, WPL, MTMAX, D, FP4, POL>(src, stg.b[1], base + IT + kSG, ks0, ks_real, wave, lane);
     }
     // last iteration: with a one-stage ring the even stage still refills it
     // with the odd stage's groups
     const int last = kb + (nit - 1) * IT;
-    stage_groups<MT, WPL, D, FP4>(ring, 0, abuf0, srd0, src, last + kSG, D < IT, acc, mask, bits, lane);
+    stage_groups<MT, WPL, D, FP4, POL>(ring, 0, abuf0, srd0, src, last + kSG, D < IT, acc, mask, bits, lane);
     // issued since buffer 1's loads: the refills of this stage, if any
     wait_vmcnt<(D < IT ? kRefill : 0)>();        // buffer 1 has landed
     barrier_ds();
-    stage_groups<MT, WPL, D, FP4>(ring, RO, abuf1, srd1, src, 0, false, acc, mask, bits, lane);
+    stage_groups<MT, WPL, D, FP4, POL>(ring, RO, abuf1, srd1, src, 0, false, acc, mask, bits, lane);
 }
 
 // Split-K fix-up.  Every split writes its fp32 partial of the tile part, then
@@ -528,7 +529,7 @@ __device__ __forceinline__ Src<MT> make_src(const GemmArgs& a, int e, int p0, in
 // `counter`: this tile's split-K arrival counter (split_k > 1).  Returns
 // whether this workgroup stored the tile's outputs (false in a K split that
 // did not arrive last); the value is the same in every thread.
-template <int MT, int WPL, int MTMAX, int D, bool FP4>
+template <int MT, int WPL, int MTMAX, int D, bool FP4, int POL>
 __device__ __forceinline__ bool gemm_tile_mt(const GemmArgs& a, int e, int p0, int nrows,
                                              int chunk, int s, int wave, int lane, const Stg& stg,
                                              int32_t* counter) {
@@ -550,7 +551,7 @@ __device__ __forceinline__ bool gemm_tile_mt(const GemmArgs& a, int e, int p0, i
     // only pins the register class and emits nothing
     uint32_t vbits = a.unpack_bits;
     asm volatile("" : "+v"(vbits));
-    stream_loop<MT, WPL, MTMAX, D, FP4>(src, ks0, ks1, a.KS, wave, lane, stg, acc, a.unpack_mask, vbits);
+    stream_loop<MT, WPL, MTMAX, D, FP4, POL>(src, ks0, ks1, a.KS, wave, lane, stg, acc, a.unpack_mask, vbits);
 
     if (a.split_k > 1 && !splitk_fixup<MT, WPL>(a, p0, nrows, chunk, s, active, lane, counter, acc))
         return false;
@@ -558,21 +559,21 @@ __device__ __forceinline__ bool gemm_tile_mt(const GemmArgs& a, int e, int p0, i
     return true;
 }
 
-template <int MT, int WPL, int D, bool FP4>
+template <int MT, int WPL, int D, bool FP4, int POL>
 __device__ __forceinline__ bool gemm_tile_part(const GemmArgs& a, int e, int p0, int nrows,
                                                int chunk, int s, int wave, int lane, const Stg& stg,
                                                int32_t* counter) {
     const int mt_active = (nrows + 15) >> 4;
     if (mt_active <= 1)
-        return gemm_tile_mt<1, WPL, MT, D, FP4>(a, e, p0, nrows, chunk, s, wave, lane, stg, counter);
+        return gemm_tile_mt<1, WPL, MT, D, FP4, POL>(a, e, p0, nrows, chunk, s, wave, lane, stg, counter);
     else if (MT >= 2 && mt_active == 2)
-        return gemm_tile_mt<(MT >= 2 ? 2 : 1), WPL, MT, D, FP4>(a, e, p0, nrows, chunk, s, wave, lane, stg,
+        return gemm_tile_mt<(MT >= 2 ? 2 : 1), WPL, MT, D, FP4, POL>(a, e, p0, nrows, chunk, s, wave, lane, stg,
                                                         counter);
     else if (MT >= 3 && mt_active == 3)
-        return gemm_tile_mt<(MT >= 3 ? 3 : 1), WPL, MT, D, FP4>(a, e, p0, nrows, chunk, s, wave, lane, stg,
+        return gemm_tile_mt<(MT >= 3 ? 3 : 1), WPL, MT, D, FP4, POL>(a, e, p0, nrows, chunk, s, wave, lane, stg,
                                                         counter);
     else
-        return gemm_tile_mt<(MT >= 4 ? 4 : 1), WPL, MT, D, FP4>(a, e, p0, nrows, chunk, s, wave, lane, stg,
+        return gemm_tile_mt<(MT >= 4 ? 4 : 1), WPL, MT, D, FP4, POL>(a, e, p0, nrows, chunk, s, wave, lane, stg,
                                                         counter);
 }
 
@@ -580,14 +581,14 @@ __device__ __forceinline__ bool gemm_tile_part(const GemmArgs& a, int e, int p0,
 // columns), `s` its K split; the split-K arrival counter is the (tile, quad)
 // one.  With the fused combine, the workgroup that stored the tile's rows
 // then counts their tokens' arrivals (s_tok, s_n: LDS scratch).
-template <int MT, int WPL, int D, bool FP4>
+template <int MT, int WPL, int D, bool FP4, int POL>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int ty, int e, int p0, int nrows,
                                           int quad, int s, int wave, int lane, const Stg& stg,
                                           int* s_tok, int* s_n) {
     const int nquads = (a.NC + 3) / 4;
     int32_t* counter = a.counters + static_cast<int64_t>(ty) * nquads + quad;
     const bool stored =
-        gemm_tile_part<MT, WPL, D, FP4>(a, e, p0, nrows, quad * 4 + wave, s, wave, lane, stg, counter);
+        gemm_tile_part<MT, WPL, D, FP4, POL>(a, e, p0, nrows, quad * 4 + wave, s, wave, lane, stg, counter);
     static_assert(4 * 64 == 256, "a quad of chunks is one 256-column combine group");
     if (a.comb_out && stored) comb_arrive(a, p0, nrows, quad, s_tok, s_n);
 }
@@ -652,6 +653,14 @@ __device__ inline void masked_tile_at(const GemmArgs& a, int ty, int lane, int& 
     nrows = 0;
 }
 
+// Cache policy of the code loads.  Non-temporal in general: one tile per
+// expert streams the weights once.  The masked layout cuts an expert above
+// the tile height into several tiles; their items (same column group and K
+// split, a multiple of 8 apart in the grid) run on one XCD at the same time,
+// so its code lines are kept in that XCD's L2 for the other tiles.
+template <bool MK>
+constexpr int kCodePolicy = MK ? 0 : kNonTemporal;
+
 // Workgroup w runs work items w, w + G, ... (G = the grid), an item being
 // (tile, group of four chunks, K split), splits of one chunk group adjacent;
 // the loop covers any device-side tile count whatever the grid.  The item
@@ -706,7 +715,8 @@ __device__ __forceinline__ void gemm_small_body(const GemmArgs& a) {
         // not computed, and nothing is stored outside the tile
         nrows = nrows < 16 * MT ? nrows : 16 * MT;
         if (e < 0 || e >= a.E || nrows <= 0) continue;
-        gemm_tile<MT, WPL, D, FP4>(a, ty, e, p0, nrows, quad, s, wave, lane, stg, s_tok, &s_n);
+        gemm_tile<MT, WPL, D, FP4, kCodePolicy<MK>>(a, ty, e, p0, nrows, quad, s, wave, lane, stg, s_tok,
+                                                    &s_n);
         // the next item reuses the staging buffers: every wavefront's LDS
         // reads have completed.  The tile's global stores need not have (a
         // release fence here would wait for all of them before the next
