@@ -69,11 +69,15 @@ def parse():
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources and of the build script that holds their
+    compiler flags (a profile taken on other code reads as stale)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "w4a16_int4_mixture_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
+    with open(os.path.join(ROOT, "w4a16_int4_mixture_amd", "build.py"), "rb") as fh:
+        h.update(b"build.py" + fh.read())
     return h.hexdigest()[:16]
 
 

@@ -36,9 +36,13 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 
 # Per-source extra flags.  The streaming GEMMs keep their MFMA accumulators
 # in VGPRs (no accumulator-register copies in their loops); the large-M GEMM
-# holds 256 accumulators per lane and needs the accumulator registers.
+# holds 256 accumulators per lane and needs the accumulator registers, and
+# its MFMA loop is scheduled for instruction-level parallelism (measured
+# about 1.5 % faster than the default strategy on the prefill shapes, same
+# registers, no spills).
 EXTRA = {"gemm_small.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "gemm_mx.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "gemm_mx.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "gemm_large.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def _compile(src: str) -> str:
