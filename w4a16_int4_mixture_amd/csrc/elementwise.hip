@@ -75,7 +75,12 @@ __global__ void k_silu_mul(const uint16_t* __restrict__ y13, int64_t rows,
 }
 
 // grid (T, ceil(H / 512)), one wavefront per block; each lane accumulates 8
-// consecutive columns of one token.
+// consecutive columns of one token.  The token's routing entries are loaded in
+// batches of kBatch, then the rows of a batch's local slots all at once (the
+// entries are the same for every lane, so the skips are uniform branches), so
+// that one memory latency covers a batch; the sum still runs in j order.
+constexpr int kBatch = 8;
+
 __global__ void __launch_bounds__(64) k_combine(const uint16_t* __restrict__ y, int64_t y_rows,
                                                 int H, const int32_t* __restrict__ row_of,
                                                 const float* __restrict__ w, int top_k,
@@ -85,15 +90,32 @@ __global__ void __launch_bounds__(64) k_combine(const uint16_t* __restrict__ y, 
         const int h = (blockIdx.y * 64 + threadIdx.x) * 8;
         if (h >= H) return;
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < top_k; ++j) {
-            const int r = row_of[static_cast<int64_t>(t) * top_k + j];
-            if (r < 0 || r >= y_rows) continue;
-            const float wt = w[static_cast<int64_t>(t) * top_k + j];
-            const u32x4 v = *reinterpret_cast<const u32x4*>(y + static_cast<int64_t>(r) * H + h);
-            const float yv[8] = {lo_f(v.x), hi_f(v.x), lo_f(v.y), hi_f(v.y),
-                                 lo_f(v.z), hi_f(v.z), lo_f(v.w), hi_f(v.w)};
+        const int32_t* ro = row_of + static_cast<int64_t>(t) * top_k;
+        const float* wr = w + static_cast<int64_t>(t) * top_k;
+        for (int j0 = 0; j0 < top_k; j0 += kBatch) {
+            int r[kBatch];
+            float wt[kBatch];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = __fadd_rn(acc[i], __fmul_rn(wt, yv[i]));
+            for (int q = 0; q < kBatch; ++q) {
+                const bool in = j0 + q < top_k;
+                r[q] = in ? ro[j0 + q] : -1;
+                wt[q] = in ? wr[j0 + q] : 0.f;
+            }
+            u32x4 v[kBatch];
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                v[q] = u32x4{0u, 0u, 0u, 0u};
+                if (r[q] >= 0 && r[q] < y_rows)
+                    v[q] = *reinterpret_cast<const u32x4*>(y + static_cast<int64_t>(r[q]) * H + h);
+            }
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                if (!(r[q] >= 0 && r[q] < y_rows)) continue;
+                const float yv[8] = {lo_f(v[q].x), hi_f(v[q].x), lo_f(v[q].y), hi_f(v[q].y),
+                                     lo_f(v[q].z), hi_f(v[q].z), lo_f(v[q].w), hi_f(v[q].w)};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = __fadd_rn(acc[i], __fmul_rn(wt[q], yv[i]));
+            }
         }
         u32x4 o;
         o.x = pack2(acc[0], acc[1]);
