@@ -145,6 +145,54 @@ def test_align_large_slot_counts_and_maps(m, T, k, Eg, El):
     check_align(m, ids, Eg, El, em, 16, 32)
 
 
+@pytest.mark.parametrize("T", [64, 8192])
+@pytest.mark.parametrize("kind", ["shifted", "past_end", "swapped", "duplicate_zero", "identity",
+                                  "identity_narrow"])
+def test_align_contiguous_range_maps(m, T, kind):
+    """The sort looks an expert map that is one contiguous range (local e =
+    g - base, -1 elsewhere) up by arithmetic; near misses (two local ids
+    swapped, a second global id on local 0) and a null map with fewer local
+    than global experts keep the table lookup.  One workgroup (64 x 8 slots)
+    and 64 workgroups (8192 x 8); out-of-range ids are skipped and reported
+    under validation."""
+    from w4a16_int4_mixture_amd import _capi
+    print(f"align range map: T={T} kind={kind}", flush=True)
+    Eg, El, k = 384, 48, 8
+    em = np.full(Eg, -1, np.int32)
+    if kind == "shifted":
+        em[96:144] = np.arange(48)
+    elif kind == "past_end":
+        em[360:] = np.arange(24)                    # local 24..47 have no global id
+    elif kind == "swapped":
+        em[96:144] = np.arange(48)
+        em[[100, 101]] = em[[101, 100]]
+    elif kind == "duplicate_zero":
+        em[96:144] = np.arange(48)
+        em[200] = 0
+    elif kind == "identity":
+        Eg, em = 48, None
+    else:
+        em = None                                   # ids >= El are not local
+    rng = np.random.default_rng(T + len(kind))
+    ids = np.argsort(rng.random((T, Eg)), axis=1)[:, :k].astype(np.int32)
+    r = check_align(m, ids, Eg, El, em, 16, 32)
+    emd = None if em is None else dev(em)
+    if kind == "identity_narrow":
+        # a null map is the identity: ids >= E_local are out-of-range local ids
+        with pytest.raises(_capi.W4A16Error) as ei:
+            r.align(dev(ids), Eg, emd, flags=_capi.W4A16_ALIGN_VALIDATE)
+        assert ei.value.status == _capi.W4A16_ERR_ROUTING
+    else:
+        r.align(dev(ids), Eg, emd, flags=_capi.W4A16_ALIGN_VALIDATE)
+    bad = ids.copy()
+    bad[1, 0] = Eg + 3
+    with pytest.raises(_capi.W4A16Error) as ei:
+        r.align(dev(bad), Eg, emd, flags=_capi.W4A16_ALIGN_VALIDATE)
+    assert ei.value.status == _capi.W4A16_ERR_ROUTING
+    bad[0, 0] = -1
+    check_align(m, bad, Eg, El, em, 16, 32)
+
+
 def test_align_validate_reports_bad_ids(m):
     from w4a16_int4_mixture_amd import _capi
     ids = np.array([[0, 1], [2, 9]], np.int32)

@@ -45,17 +45,32 @@ constexpr int kBatch = 16;
 // Largest expert map kept in LDS.
 constexpr int kMapLds = 4096;
 
-// Local experts of slots c0*64 + lane .. for kBatch chunks (-1: none or past
-// the end); all loads of the batch are issued before any is used.  lmap: the
-// expert map cached in LDS, or null (then read from global memory).
-__device__ inline void load_batch(const AlignArgs& a, const int* lmap, int64_t c0, int64_t c_end,
-                                  int64_t S, int lane, int (&eb)[kBatch], int* bad) {
-    int g[kBatch];
+// Routing ids of slots c0*64 + lane .. for kBatch chunks (0 past the end),
+// all loads issued at once.
+__device__ inline void load_ids(const AlignArgs& a, int64_t c0, int64_t c_end, int64_t S, int lane,
+                                int (&g)[kBatch]) {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
         const int64_t f = (c0 + j) * 64 + lane;
         g[j] = (c0 + j < c_end && f < S) ? a.topk_ids[f] : 0;
     }
+}
+
+// An expert map as the lookup sees it: one contiguous range (local e = g -
+// base for g in [base, base + E_local), -1 elsewhere; the usual
+// expert-parallel share, or the identity) is looked up by arithmetic;
+// otherwise lmap is the map cached in LDS, or null (then read from global
+// memory).
+struct MapView {
+    const int* lmap;
+    int base;
+    bool range;
+};
+
+// Local experts of those slots (-1: none or past the end).
+__device__ inline void map_ids(const AlignArgs& a, const MapView& m, int64_t c0, int64_t c_end,
+                               int64_t S, int lane, const int (&g)[kBatch], int (&eb)[kBatch],
+                               int* bad) {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
         const int64_t f = (c0 + j) * 64 + lane;
@@ -63,8 +78,10 @@ __device__ inline void load_batch(const AlignArgs& a, const int* lmap, int64_t c
         if (c0 + j < c_end && f < S) {
             if (g[j] < 0 || g[j] >= a.E_global) {
                 *bad = 1;
+            } else if (m.range) {
+                e = (g[j] >= m.base && g[j] - m.base < a.E_local) ? g[j] - m.base : -1;
             } else {
-                e = lmap ? lmap[g[j]] : a.expert_map ? a.expert_map[g[j]] : g[j];
+                e = m.lmap ? m.lmap[g[j]] : a.expert_map ? a.expert_map[g[j]] : g[j];
                 if (e < -1 || e >= a.E_local) *bad = 1;
                 if (e < 0 || e >= a.E_local) e = -1;
             }
@@ -73,23 +90,55 @@ __device__ inline void load_batch(const AlignArgs& a, const int* lmap, int64_t c
     }
 }
 
-// In-place exclusive prefix sum of v[0..n) by one wavefront; returns the total.
-__device__ int wave_exclusive_scan(int* v, int n, int lane) {
-    int carry = 0;
-    for (int base = 0; base < n; base += 64) {
-        int i = base + lane;
-        int x = i < n ? v[i] : 0;
-        int incl = x;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            int y = __shfl_up(incl, d, 64);
-            if (lane >= d) incl += y;
-        }
-        if (i < n) v[i] = carry + incl - x;
-        carry += __shfl(incl, 63, 64);
-    }
-    return carry;
+__device__ inline void load_batch(const AlignArgs& a, const MapView& m, int64_t c0, int64_t c_end,
+                                  int64_t S, int lane, int (&eb)[kBatch], int* bad) {
+    int g[kBatch];
+    load_ids(a, c0, c_end, S, lane, g);
+    map_ids(a, m, c0, c_end, S, lane, g, eb, bad);
 }
+
+// In-place exclusive prefix sums of v[0..n) and u[0..n) by one wavefront,
+// totals in tv and tu.  Lane l first sums its own run of ceil(n / 64)
+// entries, so that one 64-lane scan serves any n.
+__device__ void wave_exclusive_scan2(int* v, int* u, int n, int lane, int& tv, int& tu) {
+    const int per = (n + 63) / 64;
+    const int lo = lane * per < n ? lane * per : n;
+    const int hi = lo + per < n ? lo + per : n;
+    int sv = 0, su = 0;
+    for (int i = lo; i < hi; ++i) {
+        sv += v[i];
+        su += u[i];
+    }
+    int iv = sv, iu = su;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int yv = __shfl_up(iv, d, 64);
+        const int yu = __shfl_up(iu, d, 64);
+        if (lane >= d) {
+            iv += yv;
+            iu += yu;
+        }
+    }
+    int ev = iv - sv, eu = iu - su;
+    for (int i = lo; i < hi; ++i) {
+        const int x = v[i], y = u[i];
+        v[i] = ev;
+        u[i] = eu;
+        ev += x;
+        eu += y;
+    }
+    tv = __shfl(iv, 63, 64);
+    tu = __shfl(iu, 63, 64);
+}
+
+// Workgroup barrier for LDS data: this wavefront's LDS accesses have
+// completed; its global stores may still be in flight (nothing in this
+// kernel reads back what another wavefront stored to global memory, except
+// after the fused router, which uses a full barrier).
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Most wavefronts of a workgroup (blockDim.x / 64).
+constexpr int kMaxWaves = 16;
 
 // ---- router top-k ------------------------------------------------------------
 //
@@ -212,24 +261,53 @@ __global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
         __syncthreads();
     }
 
-    // ---- pass 0: per-expert totals over all slots and counts before the
-    // range.  The expert map is cached in LDS (when it fits) and the routing
-    // ids are read 16 bytes at a time, all of a thread's loads issued first.
+    // ---- pass 0: per-expert counts of the slots before the range (pre)
+    // and of the others (tot; pass 2 adds pre to it).  The expert map is
+    // cached in LDS (when it fits); the routing ids are read 16 bytes at a
+    // time, all of a thread's loads issued first, then all its map lookups,
+    // then one LDS atomic per local slot.
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         tot[e] = 0;
         pre[e] = 0;
     }
     int* lmap = red + 4;                                          // [E_global] if cached
     const bool map_lds = a.E_global <= kMapLds;
+    if (threadIdx.x == 0) {
+        red[2] = a.E_global;
+        red[3] = 1;
+    }
     if (map_lds)
         for (int i = threadIdx.x; i < a.E_global; i += blockDim.x)
             lmap[i] = a.expert_map ? a.expert_map[i] : i;
-    __syncthreads();
+    lds_barrier();
+    // Is the cached map one contiguous range?  base = the global id of local
+    // expert 0; then every entry is checked against g - base or -1, so the
+    // arithmetic lookup gives exactly the map's values for every valid id.
+    // (Only where every workgroup counts all slots: a one-workgroup sort
+    // looks up too few ids to pay for the check's two barriers.)
+    const bool multi = gridDim.x > 1;
+    if (map_lds && multi) {
+        for (int i = threadIdx.x; i < a.E_global; i += blockDim.x)
+            if (lmap[i] == 0) atomicMin(&red[2], i);
+        lds_barrier();
+        const int base = red[2];
+        for (int i = threadIdx.x; i < a.E_global; i += blockDim.x) {
+            const int want = (i >= base && i - base < E) ? i - base : -1;
+            if (lmap[i] != want) red[3] = 0;
+        }
+        lds_barrier();
+    }
+    MapView mv;
+    mv.base = __builtin_amdgcn_readfirstlane(red[2]);
+    mv.range = map_lds && multi && mv.base < a.E_global &&
+               __builtin_amdgcn_readfirstlane(red[3]) != 0;
+    mv.lmap = map_lds ? lmap : nullptr;
     auto local_of = [&](int g) {
         if (g < 0 || g >= a.E_global) {
             bad = 1;
             return -1;
         }
+        if (mv.range) return (g >= mv.base && g - mv.base < E) ? g - mv.base : -1;
         int e = map_lds ? lmap[g] : (a.expert_map ? a.expert_map[g] : g);
         if (e < -1 || e >= E) bad = 1;
         return (e >= 0 && e < E) ? e : -1;
@@ -237,7 +315,6 @@ __global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
     const int64_t pre_end = b_begin * 64;                         // slots before the range
     const bool vec = (reinterpret_cast<uintptr_t>(a.topk_ids) & 15) == 0;
     // (a single workgroup takes its totals from pass 1 instead)
-    const bool multi = gridDim.x > 1;
     const int64_t n4 = multi && vec ? S / 4 : 0;                  // 4-id groups read as int4
     for (int64_t i0 = threadIdx.x; i0 < n4; i0 += static_cast<int64_t>(blockDim.x) * kBatch) {
         int4 v[kBatch];
@@ -249,38 +326,45 @@ __global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             const int64_t i = i0 + static_cast<int64_t>(j) * blockDim.x;
+            if (i < n4) {
+                v[j].x = local_of(v[j].x);
+                v[j].y = local_of(v[j].y);
+                v[j].z = local_of(v[j].z);
+                v[j].w = local_of(v[j].w);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int64_t i = i0 + static_cast<int64_t>(j) * blockDim.x;
             if (i >= n4) break;
-            const int gs[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+            const int es[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int e = local_of(gs[q]);
+                const int e = es[q];
                 if (e < 0) continue;
-                atomicAdd(&tot[e], 1);
-                if (4 * i + q < pre_end) atomicAdd(&pre[e], 1);
+                atomicAdd(4 * i + q < pre_end ? &pre[e] : &tot[e], 1);
             }
         }
     }
     for (int64_t f = 4 * n4 + threadIdx.x; multi && f < S; f += blockDim.x) {
         const int e = local_of(a.topk_ids[f]);
         if (e < 0) continue;
-        atomicAdd(&tot[e], 1);
-        if (f < pre_end) atomicAdd(&pre[e], 1);
+        atomicAdd(f < pre_end ? &pre[e] : &tot[e], 1);
     }
     // one workgroup reports out-of-range ids
     if (multi && bad && a.err_flag && blockIdx.x == 0) atomicAdd(a.err_flag, 1);
     bad = 0;
-    __syncthreads();
+    lds_barrier();
 
     // ---- pass 1: counts per (wave, expert).  The routing ids of kBatch
     // chunks are loaded together, so that one memory latency covers them;
     // when one batch covers all of this wave's chunks, pass 3 reuses it.
-    const int* lm = map_lds ? lmap : nullptr;
     const bool one_batch = c_end - c_begin <= kBatch;
     int kept[kBatch];
     for (int e = lane; e < E; e += 64) my_cnt[e] = 0;
     for (int64_t c0 = c_begin; c0 < c_end; c0 += kBatch) {
         int eb[kBatch];
-        load_batch(a, lm, c0, c_end, S, lane, eb, &bad);
+        load_batch(a, mv, c0, c_end, S, lane, eb, &bad);
         if (one_batch) {
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) kept[j] = eb[j];
@@ -297,39 +381,49 @@ __global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
         }
     }
     if (!multi && bad && a.err_flag) atomicAdd(a.err_flag, 1);
-    __syncthreads();
+    lds_barrier();
 
     // ---- pass 2: offsets, metadata
     const int bm = a.block_m;
     const int tm = a.r.tile_m > 0 ? a.r.tile_m : 1;
+    // (the W per-wave counts of an expert are read at once, then written)
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        int c;
         if (!multi) {
-            int c = 0;
-            for (int ww = 0; ww < W; ++ww) c += cnt[ww * E + e];
-            tot[e] = c;
+            int cw[kMaxWaves];
+#pragma unroll
+            for (int ww = 0; ww < kMaxWaves; ++ww) cw[ww] = ww < W ? cnt[ww * E + e] : 0;
+            c = 0;
+#pragma unroll
+            for (int ww = 0; ww < kMaxWaves; ++ww) c += cw[ww];
+        } else {
+            c = tot[e] + pre[e];
         }
-        const int c = tot[e];
+        tot[e] = c;
         pad[e] = (c + bm - 1) / bm * bm;
         ntile[e] = (c + tm - 1) / tm;
     }
-    __syncthreads();
+    lds_barrier();
     if (w == 0) {
-        int total = wave_exclusive_scan(pad, E, lane);
-        int ntiles = wave_exclusive_scan(ntile, E, lane);
+        int total, ntiles;
+        wave_exclusive_scan2(pad, ntile, E, lane, total, ntiles);
         if (lane == 0) {
             red[0] = total;
             red[1] = ntiles;
         }
     }
-    __syncthreads();
+    lds_barrier();
     const int total = red[0];
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         const int off = pad[e];
         int run = off + pre[e];
-        for (int ww = 0; ww < W; ++ww) {
-            int b = cnt[ww * E + e];
-            cnt[ww * E + e] = run;
-            run += b;
+        int cw[kMaxWaves];
+#pragma unroll
+        for (int ww = 0; ww < kMaxWaves; ++ww) cw[ww] = ww < W ? cnt[ww * E + e] : 0;
+#pragma unroll
+        for (int ww = 0; ww < kMaxWaves; ++ww) {
+            if (ww < W) cnt[ww * E + e] = run;
+            run += cw[ww];
         }
         if (blockIdx.x != 0) continue;
         const int c = tot[e];
@@ -337,7 +431,7 @@ __global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
         for (int j = c; j < p; ++j) a.r.sorted_ids[off + j] = sentinel;
         for (int b = 0; b < p / bm; ++b) a.r.expert_ids[off / bm + b] = e;
         if (a.r.tiles) {
-            int t0 = ntile[e];
+            const int t0 = ntile[e];
             for (int i = 0; i * tm < c; ++i) {
                 int4 v;
                 v.x = e;
@@ -359,7 +453,8 @@ __global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
     const int64_t gsize = static_cast<int64_t>(gridDim.x) * blockDim.x;
     for (int64_t i = total + gtid; i < a.r.sorted_cap; i += gsize) a.r.sorted_ids[i] = sentinel;
     for (int64_t b = total / bm + gtid; b < a.r.blocks_cap; b += gsize) a.r.expert_ids[b] = -1;
-    __syncthreads();
+    // (pass 3 stores only to positions that pass 2 does not write)
+    lds_barrier();
 
     // ---- pass 3: scatter
     for (int64_t c0 = c_begin; c0 < c_end; c0 += kBatch) {
@@ -368,7 +463,7 @@ __global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) eb[j] = kept[j];
         } else {
-            load_batch(a, lm, c0, c_end, S, lane, eb, &bad);
+            load_batch(a, mv, c0, c_end, S, lane, eb, &bad);
         }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
