@@ -137,7 +137,8 @@ __device__ void wave_exclusive_scan2(int* v, int* u, int n, int lane, int& tv, i
 // after the fused router, which uses a full barrier).
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Most wavefronts of a workgroup (blockDim.x / 64).
+// Most wavefronts of a workgroup: k_align's launch bound is 64 * kMaxWaves
+// threads, and align_waves never asks for more.
 constexpr int kMaxWaves = 16;
 
 // ---- router top-k ------------------------------------------------------------
@@ -222,7 +223,7 @@ void launch_router_topk(const float* logits, int T, int E, int k, int32_t* ids, 
     if (T > 0) k_router_topk<<<dim3((T + 3) / 4), dim3(256), 0, s>>>(logits, T, E, k, ids, w);
 }
 
-__global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
+__global__ void __launch_bounds__(64 * kMaxWaves) k_align(AlignArgs a) {
     extern __shared__ unsigned char smem[];
     const int E = a.E_local;
     const int W = blockDim.x / 64;
@@ -293,7 +294,7 @@ __global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
         const int base = red[2];
         for (int i = threadIdx.x; i < a.E_global; i += blockDim.x) {
             const int want = (i >= base && i - base < E) ? i - base : -1;
-            if (lmap[i] != want) red[3] = 0;
+            if (lmap[i] != want) red[3] = 0;                  // (all writers store 0)
         }
         lds_barrier();
     }
@@ -491,7 +492,7 @@ __global__ void __launch_bounds__(1024) k_align(AlignArgs a) {
 
 int align_waves(int E_local) {
     // keep the LDS footprint (12 bytes per wave and expert) under 60 KiB
-    int w = 16;
+    int w = kMaxWaves;
     // (plus 16 per expert and the cached expert map, at most 16 KiB)
     while (w > 1 && static_cast<int64_t>(w) * E_local * 12 + E_local * 16 + 64 + 4 * kMapLds >
                         60 * 1024)
